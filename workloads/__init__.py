@@ -1,0 +1,158 @@
+"""Seeded synthetic workloads for the blockwise ring-attention forward.
+
+This module only *generates inputs*: shapes, seeds, Gaussian draws and
+document-length segment ids.  It holds none of the attention arithmetic, so
+both the GPU library's tests/benchmark and the CPU oracle can be fed from it
+without sharing any of the method's code.
+
+The workloads stand in for the pages' training runs (7B- and 65B-parameter
+models at up to 4M-token context on TPUv4-1024, "Ring Attention with
+Blockwise Transformers for Near-Infinite Context", section 五 "实验结果"):
+one device's share of the ring at the real per-device shape, with Gaussian
+Q/K/V.  No dataset or trained weight is involved.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = ["Workload", "WORKLOADS", "get", "block_seed", "document_segments",
+           "make_block", "make_qkv", "make_segments"]
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    seq_q: int                 # local query block length Lq (= KV block length)
+    ring_size: int             # N
+    ring_indices: Tuple[int, ...]
+    heads: int
+    head_dim: int
+    dtype: str                 # "bf16" | "f32"
+    causal_block_size: Optional[int]   # None = non-causal
+    q_chunk: int
+    k_chunk: int
+    segments: bool = False
+    std: float = 1.0           # Q, K, V ~ std * N(0, 1)
+    seed: int = 0
+    poison_unused: bool = False  # fill KV blocks that no chunk pair reads with NaN
+    notes: str = field(default="", compare=False)
+
+    @property
+    def seq_k(self) -> int:
+        return self.ring_size * self.seq_q
+
+
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("tiny_plumbing", 1, 64, 4, (0, 1, 2, 3), 2, 64, "f32", None,
+                 32, 32, seed=20261201,
+                 notes="seq 256 = 4 ring blocks of 64; non-causal; fp32"),
+        Workload("small_causal", 1, 1024, 8, tuple(range(8)), 8, 128, "bf16", 1,
+                 512, 512, seed=20261202,
+                 notes="seq 8192 = 8 ring blocks of 1024; token causal"),
+        Workload("share_7b_512k", 1, 32768, 16, (15,), 32, 128, "bf16", 1,
+                 2048, 2048, seed=20261203,
+                 notes="7B-shaped share: ring position 15 of 16, 512K context"),
+        Workload("packed_documents", 4, 2048, 8, tuple(range(8)), 32, 128, "bf16", 1,
+                 512, 512, segments=True, seed=20261204,
+                 notes="seq 16384 = 8 blocks of 2048; causal + document segments"),
+        Workload("share_65b_4m", 1, 16384, 256, (128,), 64, 128, "bf16", 16384,
+                 512, 512, std=0.5, seed=20261205, poison_unused=True,
+                 notes="65B-shaped share: ring position 128 of 256, 4M context, "
+                       "block-causal with causal_block_size 16384"),
+    ]
+}
+
+
+def get(name: str) -> Workload:
+    return WORKLOADS[name]
+
+
+def block_seed(base: int, tensor: str, block: int) -> int:
+    """Seed of one ring block of one tensor, so that any block can be
+    regenerated on its own (q: 0, k: 1, v: 2)."""
+    return base * 4099 + {"q": 0, "k": 1, "v": 2}[tensor] * 1_000_003 + block
+
+
+def document_segments(batch: int, seq: int, seed: int, mean: int = 2048,
+                      lo: int = 64, hi: int = 16384) -> np.ndarray:
+    """Segment ids of packed documents: lengths ~ Geometric(1/mean) clipped to
+    [lo, hi], drawn until the row is full; the last document is truncated to
+    fit.  The id of a token is the ordinal of its document in the row."""
+    rng = np.random.default_rng(seed)
+    out = np.empty((batch, seq), dtype=np.int32)
+    for b in range(batch):
+        pos = 0
+        doc = 0
+        while pos < seq:
+            n = int(np.clip(rng.geometric(1.0 / mean), lo, hi))
+            n = min(n, seq - pos)
+            out[b, pos:pos + n] = doc
+            pos += n
+            doc += 1
+    return out
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype(name: str):
+    torch = _torch()
+    return {"bf16": torch.bfloat16, "f32": torch.float32}[name]
+
+
+def make_block(shape: Sequence[int], seed: int, std: float, dtype: str,
+               device) -> "object":
+    """One Gaussian block: N(0,1) drawn in fp32 with a seeded generator on
+    ``device``, scaled by ``std`` and rounded (RNE) to ``dtype``."""
+    torch = _torch()
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x.to(_dtype(dtype))
+
+
+def make_qkv(w: Workload, ring_index: int, device="cpu",
+             kv_blocks: Optional[Sequence[int]] = None):
+    """Q for ring position ``ring_index`` and K, V for the whole ring.
+
+    Each ring block is drawn with its own seed.  Blocks not listed in
+    ``kv_blocks`` (default: all) are filled with NaN: a poisoned block must
+    never influence the result.
+    """
+    torch = _torch()
+    B, Lq, H, D = w.batch, w.seq_q, w.heads, w.head_dim
+    q = make_block((B, Lq, H, D), block_seed(w.seed, "q", ring_index), w.std,
+                   w.dtype, device)
+    k = torch.empty((B, w.seq_k, H, D), dtype=_dtype(w.dtype), device=device)
+    v = torch.empty_like(k)
+    blocks = set(range(w.ring_size) if kv_blocks is None else kv_blocks)
+    for kb in range(w.ring_size):
+        sl = slice(kb * Lq, (kb + 1) * Lq)
+        if kb in blocks:
+            k[:, sl] = make_block((B, Lq, H, D), block_seed(w.seed, "k", kb),
+                                  w.std, w.dtype, device)
+            v[:, sl] = make_block((B, Lq, H, D), block_seed(w.seed, "v", kb),
+                                  w.std, w.dtype, device)
+        else:
+            k[:, sl] = float("nan")
+            v[:, sl] = float("nan")
+    return q, k, v
+
+
+def make_segments(w: Workload, device="cpu"):
+    """Segment ids [B, S] (int32) for workloads with packed documents, else None."""
+    if not w.segments:
+        return None
+    torch = _torch()
+    seg = document_segments(w.batch, w.seq_k, w.seed + 3)
+    return torch.from_numpy(seg).to(device)
