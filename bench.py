@@ -1,0 +1,196 @@
+"""Benchmark of the blockwise ring-attention forward on one MI355X.
+
+One step = one forward of a device's whole ring share (every KV block in
+ring order, skipping, softmax carry, normalisation, lse) through the C ABI,
+on the 7B-shaped share: batch 1, 32 heads, head_dim 128, bf16, local query
+block 32768 at ring position 15 of 16 (512K context), token causal, chunks
+2048.  Inputs are seeded Gaussian tensors already resident in HBM.
+
+Prints one JSON line with the causal-adjusted TFLOP/s, the roofline of the
+kernel (MFMA bound, bf16 dense peak) and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+WORKLOAD = "share_7b_512k"
+PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA
+KERNEL_SRC = os.path.join(ROOT, "long_context_exact_ra_amd", "csrc", "blockwise_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "blockwise_fwd_share_7b_512k_traffic.json")
+
+
+def visible_keys_per_row(seq_q: int, ring_size: int, ring_index: int, causal) -> np.ndarray:
+    """Causally visible keys of each local query row (segments ignored)."""
+    S = ring_size * seq_q
+    pq = ring_index * seq_q + np.arange(seq_q, dtype=np.int64)
+    if not causal:
+        return np.full(seq_q, S, dtype=np.int64)
+    c = int(causal)
+    return np.minimum((pq // c + 1) * c, S)
+
+
+def causal_flops(w, ring_index: int) -> float:
+    """F = 4 * D * H * B * sum over rows of causally visible keys: two
+    GEMMs, two flops per multiply-add, per visible (query, key) pair."""
+    n = int(visible_keys_per_row(w.seq_q, w.ring_size, ring_index, w.causal_block_size).sum())
+    return 4.0 * w.head_dim * w.heads * w.batch * n
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch measured with rocprofv3 counters, valid only for
+    the kernel source they were taken on."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, ring_index: int, rows: int):
+    """The CPU oracle, as it stands, on a bounded sample: one head and
+    ``rows`` query rows of the same workload (each row over all its visible
+    keys).  Rate in the metric's unit (causal-adjusted TFLOP/s)."""
+    import oracle
+    import torch
+    head = 0
+    sel = np.linspace(0, w.seq_q - 1, rows).astype(np.int64)
+    kv_len = w.seq_k if not w.causal_block_size else int(
+        min(w.seq_k, ((ring_index * w.seq_q + w.seq_q - 1) // w.causal_block_size + 1)
+            * w.causal_block_size))
+    qh = q[:, :, head:head + 1].contiguous().cpu()
+    kh = k[:, :kv_len, head:head + 1].contiguous().cpu()
+    vh = v[:, :kv_len, head:head + 1].contiguous().cpu()
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover - informational only
+        cores = torch.get_num_threads()
+    t0 = time.perf_counter()
+    oracle.attention_fwd(qh, kh, vh, None, w.causal_block_size, w.ring_size, ring_index,
+                         rows=sel, kv_len=kv_len)
+    dt = time.perf_counter() - t0
+    pairs = int(visible_keys_per_row(w.seq_q, w.ring_size, ring_index,
+                                     w.causal_block_size)[sel].sum())
+    flops = 4.0 * w.head_dim * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{WORKLOAD}: head 0, {rows} query rows spread over the block, "
+                      f"each over its {kv_len}-key visible range; numpy fp64; "
+                      f"{dt:.1f} s for {flops / 1e9:.1f} GFLOP"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--cpu-rows", type=int, default=256,
+                    help="query rows of the CPU oracle sample (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the ring exchange between GPUs is not part of this library)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import long_context_exact_ra_amd as ra
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ra.load_library()
+    dev = torch.device("cuda:0")
+    w = workloads.get(WORKLOAD)
+    r = w.ring_indices[0]
+    print(f"[bench] generating {WORKLOAD} inputs", file=sys.stderr, flush=True)
+    q, k, v = workloads.make_qkv(w, r, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.heads, w.seq_q), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        ra.blockwise_attn_fwd(q, k, v, None, w.causal_block_size, w.q_chunk, w.k_chunk,
+                              w.ring_size, r, out=out, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms = float(np.mean(per))
+    if not (torch.isfinite(out).all() and torch.isfinite(lse).all()):
+        raise RuntimeError("non-finite output")
+
+    flops = causal_flops(w, r)
+    tflops = flops / (ms * 1e-3) / 1e12
+    traffic = measured_traffic()
+    rec = {
+        "metric": "causal-adjusted attention TFLOP/s per MI355X (% of bf16 MFMA peak in roofline.frac)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) Q/K/V, bf16",
+        "config": {"workload": WORKLOAD, "batch": w.batch, "seq_q": w.seq_q,
+                   "ring_size": w.ring_size, "ring_index": r, "context": w.seq_k,
+                   "heads": w.heads, "head_dim": w.head_dim,
+                   "causal_block_size": w.causal_block_size,
+                   "q_chunk": w.q_chunk, "k_chunk": w.k_chunk,
+                   "flops_per_step": flops, "ms_min": round(min(per), 3),
+                   "wall_s": round(wall, 3)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if args.cpu_rows > 0:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, r, args.cpu_rows)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,146 @@
+/*
+ * ra_attn.h -- C ABI of the blockwise exact-attention forward of Ring
+ * Attention for AMD MI355X (gfx950).
+ *
+ * What is computed.  One device's share of Ring Attention: the local query
+ * block Q_r (ring position r of N) attends to all N key/value blocks,
+ * visited in ring order -- at outer step t the block (r - t) mod N -- with a
+ * running max / numerator / denominator carry that is rescaled per block
+ * ("Ring Attention with Blockwise Transformers for Near-Infinite Context",
+ * section 三: the self-attention equation, "分块注意力", "环形注意力算法"
+ * and "排列不变性"; the carry update and chunk skipping of
+ * "从论文到代码：深入理解RingAttention的块注意力计算逻辑", sections
+ * "2. 数值稳定的注意力计算" and "3. 因果注意力掩码支持").  The result is
+ * exact softmax(Q K^T / sqrt(D)) V over the visible keys:
+ *
+ *   query row i has global position pq = r * Lq + i, key j has position j;
+ *   key j is visible from row i iff
+ *     (causal_block_size == 0 or floor(pq / c) >= floor(j / c))   and
+ *     (segment_ids == NULL or segment_ids[b][pq] == segment_ids[b][j]).
+ *
+ * Tensor layouts (row-major, contiguous, element strides implied):
+ *   q, out   [batch, seq_q, heads, head_dim]             dtype
+ *   k, v     [batch, ring_size * seq_q, heads, head_dim]  dtype, all N
+ *            blocks in global order (block kb = rows kb*seq_q .. +seq_q-1)
+ *   segment_ids [batch, ring_size * seq_q] int32, or NULL
+ *   lse      [batch, heads, seq_q] float32, natural log of the softmax
+ *            denominator (log-sum-exp of the scaled logits over visible keys)
+ *
+ * Arithmetic: logits, the running max, the denominator and the numerator
+ * are float32.  bf16 inputs multiply on bf16 matrix cores with float32
+ * accumulation; the probabilities are rounded to bf16 (round to nearest
+ * even) before the P.V product while the denominator sums them unrounded.
+ * out is rounded to the input dtype.  A query row with no visible key gets
+ * out = 0 and lse = -inf.
+ *
+ * Ownership and synchronisation: all pointers except those marked "host"
+ * are device pointers allocated by the caller; the library allocates no
+ * device memory and keeps no pointer after a call returns.  Work is enqueued
+ * on `stream` (a hipStream_t; NULL = the default stream) and the call
+ * returns after the launch; the caller synchronises.  Calls are thread-safe.
+ *
+ * Errors: every entry point returns a status; nothing throws or aborts
+ * across the ABI.  Argument errors are detected on the host before any
+ * device work is enqueued.  ra_last_error() describes the last failure on
+ * the calling thread.
+ */
+#ifndef RA_ATTN_H
+#define RA_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RA_OK = 0,
+  RA_E_INVALID = 1,     /* malformed argument (null pointer, bad size, ...)   */
+  RA_E_UNSUPPORTED = 2, /* well-formed but outside what the kernels handle    */
+  RA_E_HIP = 3          /* the HIP runtime reported an error at launch        */
+} ra_status_t;
+
+typedef enum { RA_BF16 = 0, RA_F32 = 1 } ra_dtype_t;
+
+/*
+ * ra_blockwise_attn_fwd -- the forward of one ring position.
+ *
+ *   q, k, v, segment_ids, out, lse: see the layouts above.
+ *   causal_block_size: 0 = non-causal; 1 = token-level causal; c > 1 =
+ *       block-causal with blocks of c positions ("3. 因果注意力掩码支持").
+ *   q_chunk, k_chunk: query / key chunk sizes of the blockwise scheme
+ *       ("1. 分块处理机制"); both must divide seq_q and be multiples of 32.
+ *       A key chunk of a KV block is skipped for a query chunk when no pair
+ *       in the two chunks is causally visible.
+ *   ring_size N >= 1, ring_index r in [0, N).
+ *   batch, seq_q (= Lq, the local block length), heads >= 0; a zero size
+ *       is a valid empty call.  head_dim in {64, 128}.
+ *
+ * Returns RA_E_INVALID for null required pointers, negative sizes,
+ * ring_index outside [0, ring_size), causal_block_size < 0, non-positive
+ * chunks or chunks that do not divide seq_q; RA_E_UNSUPPORTED for other
+ * head_dim, dtype, chunks not a multiple of 32 or sizes beyond the index
+ * range of the kernels; RA_E_HIP if the launch fails.
+ */
+ra_status_t ra_blockwise_attn_fwd(const void* q, const void* k, const void* v,
+                                  const int32_t* segment_ids,
+                                  int64_t causal_block_size, int64_t q_chunk,
+                                  int64_t k_chunk, int32_t ring_size,
+                                  int32_t ring_index, int64_t batch,
+                                  int64_t seq_q, int64_t heads,
+                                  int64_t head_dim, ra_dtype_t dtype,
+                                  void* out, float* lse, void* stream);
+
+/*
+ * ra_blockwise_attn_fwd_ex -- the same forward, additionally recording the
+ * chunk-pair skip decisions the kernel took.
+ *
+ *   run_map: device bytes [ring_size][seq_q / q_chunk][seq_q / k_chunk] in
+ *       ring-step order, or NULL.  The library clears it and the kernel sets
+ *       run_map[t][a][b] = 1 when it computed any part of query chunk a
+ *       against key chunk b of the block used at ring step t.  Intended for
+ *       debugging and parity checks; it costs extra stores.
+ *
+ * Errors as for ra_blockwise_attn_fwd.
+ */
+ra_status_t ra_blockwise_attn_fwd_ex(const void* q, const void* k,
+                                     const void* v, const int32_t* segment_ids,
+                                     int64_t causal_block_size, int64_t q_chunk,
+                                     int64_t k_chunk, int32_t ring_size,
+                                     int32_t ring_index, int64_t batch,
+                                     int64_t seq_q, int64_t heads,
+                                     int64_t head_dim, ra_dtype_t dtype,
+                                     void* out, float* lse, uint8_t* run_map,
+                                     void* stream);
+
+/*
+ * ra_blockwise_plan -- host-only: the ring order and the chunk-pair skip
+ * decisions for one ring position, without touching a GPU.
+ *
+ *   kv_block_of_step: host int32 [ring_size]; entry t = (ring_index - t) mod
+ *       ring_size, the block used at ring step t ("环形注意力算法").
+ *   run_bits: host bytes [ring_size][seq_q / q_chunk][seq_q / k_chunk], or
+ *       NULL; 1 = the chunk pair runs (below or on the causal diagonal).
+ *   n_run_chunk_pairs: host, optional; the number of ones in run_bits.
+ *
+ * Validation as for ra_blockwise_attn_fwd (chunks need not be multiples of
+ * 32 here).  Returns RA_OK or RA_E_INVALID.
+ */
+ra_status_t ra_blockwise_plan(int64_t causal_block_size, int64_t q_chunk,
+                              int64_t k_chunk, int64_t seq_q,
+                              int32_t ring_size, int32_t ring_index,
+                              int32_t* kv_block_of_step, uint8_t* run_bits,
+                              int64_t* n_run_chunk_pairs);
+
+/* Text of the last error on the calling thread ("" if none).  The pointer
+ * stays valid until the next ra_* call on the same thread. */
+const char* ra_last_error(void);
+
+/* Library version as "major.minor.patch" (static storage). */
+const char* ra_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA_ATTN_H */

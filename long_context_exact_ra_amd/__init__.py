@@ -1,0 +1,158 @@
+"""Blockwise exact-attention forward of Ring Attention on MI355X (gfx950).
+
+A thin ctypes binding over the C ABI in ``include/ra_attn.h`` (library
+``libra_attn.so`` next to this file).  It only marshals arguments: every
+step of the forward runs in the HIP kernels of the library.  PyTorch
+provides device memory and the stream.  There is no fallback: if the
+library is missing every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = ["RaError", "blockwise_attn_fwd", "blockwise_plan", "last_error", "lib_path",
+           "load_library", "version", "RA_OK", "RA_E_INVALID", "RA_E_UNSUPPORTED",
+           "RA_E_HIP", "RA_BF16", "RA_F32"]
+
+RA_OK, RA_E_INVALID, RA_E_UNSUPPORTED, RA_E_HIP = 0, 1, 2, 3
+RA_BF16, RA_F32 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libra_attn.so")
+
+
+class RaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"ra_attn status {status}: {message}")
+        self.status = status
+
+
+def load_library():
+    """Load ``libra_attn.so`` (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; run __graft_entry__.build() or "
+            "python -m long_context_exact_ra_amd.build")
+    lib = ctypes.CDLL(path)
+    c_i64, c_i32, c_vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    fwd_args = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_i32,
+                c_i64, c_i64, c_i64, c_i64, ctypes.c_int, c_vp, c_vp]
+    lib.ra_blockwise_attn_fwd.argtypes = fwd_args + [c_vp]
+    lib.ra_blockwise_attn_fwd.restype = ctypes.c_int
+    lib.ra_blockwise_attn_fwd_ex.argtypes = fwd_args + [c_vp, c_vp]
+    lib.ra_blockwise_attn_fwd_ex.restype = ctypes.c_int
+    lib.ra_blockwise_plan.argtypes = [c_i64, c_i64, c_i64, c_i64, c_i32, c_i32,
+                                      c_vp, c_vp, c_vp]
+    lib.ra_blockwise_plan.restype = ctypes.c_int
+    lib.ra_last_error.argtypes = []
+    lib.ra_last_error.restype = ctypes.c_char_p
+    lib.ra_version.argtypes = []
+    lib.ra_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load_library().ra_last_error().decode()
+
+
+def version() -> str:
+    return load_library().ra_version().decode()
+
+
+def _check(status: int):
+    if status != RA_OK:
+        raise RaError(status, last_error())
+
+
+def blockwise_plan(causal_block_size: Optional[int], q_chunk: int, k_chunk: int,
+                   seq_q: int, ring_size: int, ring_index: int):
+    """Host-only ring order and chunk-pair skip decisions.
+
+    Returns (kv_block_of_step int32 [N], run_bits uint8 [N, Lq/qc, Lq/kc],
+    n_run_chunk_pairs).
+    """
+    import numpy as np
+    lib = load_library()
+    order = np.zeros(max(ring_size, 1), dtype=np.int32)
+    nq = seq_q // q_chunk if q_chunk > 0 else 0
+    nk = seq_q // k_chunk if k_chunk > 0 else 0
+    run = np.zeros((max(ring_size, 1), nq, nk), dtype=np.uint8)
+    n = ctypes.c_int64(0)
+    _check(lib.ra_blockwise_plan(int(causal_block_size or 0), q_chunk, k_chunk, seq_q,
+                                 ring_size, ring_index, order.ctypes.data,
+                                 run.ctypes.data, ctypes.addressof(n)))
+    return order, run, n.value
+
+
+def blockwise_attn_fwd(q, k, v, segment_ids=None, causal_block_size: Optional[int] = None,
+                       q_chunk: int = 512, k_chunk: int = 512, ring_size: int = 1,
+                       ring_index: int = 0, *, out=None, lse=None, run_map=None,
+                       stream=None) -> Tuple[object, object]:
+    """Forward of ring position ``ring_index``: returns (out, lse).
+
+    q: [B, Lq, H, D] and k, v: [B, ring_size * Lq, H, D], contiguous CUDA
+    (HIP) tensors of one dtype (bfloat16 or float32); segment_ids: int32
+    [B, ring_size * Lq] or None; causal_block_size None/0 = non-causal.
+    out ([B, Lq, H, D], q's dtype) and lse ([B, H, Lq], float32) are
+    allocated when not given.  run_map: optional uint8 device tensor
+    [ring_size, Lq / q_chunk, Lq / k_chunk] that receives the kernel's
+    chunk-pair decisions.  The work is enqueued on ``stream`` (default: the
+    current torch stream).
+    """
+    import torch
+    lib = load_library()
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-D device tensor")
+    B, Lq, H, D = q.shape
+    if tuple(k.shape) != (B, ring_size * Lq, H, D) or k.shape != v.shape:
+        raise ValueError(f"k/v shape {tuple(k.shape)} != {(B, ring_size * Lq, H, D)}")
+    seg_ptr = None
+    if segment_ids is not None:
+        if (segment_ids.dtype != torch.int32 or not segment_ids.is_cuda
+                or not segment_ids.is_contiguous()
+                or tuple(segment_ids.shape) != (B, ring_size * Lq)):
+            raise ValueError("segment_ids must be a contiguous int32 device tensor [B, S]")
+        seg_ptr = segment_ids.data_ptr()
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be contiguous with q's shape and dtype")
+    if tuple(lse.shape) != (B, H, Lq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, Lq]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    dt = RA_BF16 if q.dtype == torch.bfloat16 else RA_F32
+    args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), seg_ptr, int(causal_block_size or 0),
+            q_chunk, k_chunk, ring_size, ring_index, B, Lq, H, D, dt,
+            out.data_ptr(), lse.data_ptr()]
+    if run_map is not None:
+        nq = Lq // q_chunk if q_chunk else 0
+        nk = Lq // k_chunk if k_chunk else 0
+        if (run_map.dtype != torch.uint8 or not run_map.is_cuda
+                or not run_map.is_contiguous()
+                or tuple(run_map.shape) != (ring_size, nq, nk)):
+            raise ValueError("run_map must be a contiguous uint8 device tensor [N, nq, nk]")
+        _check(lib.ra_blockwise_attn_fwd_ex(*args, run_map.data_ptr(), sptr))
+    else:
+        _check(lib.ra_blockwise_attn_fwd(*args, sptr))
+    return out, lse

@@ -1,0 +1,65 @@
+"""Build the C-ABI shared library ``libra_attn.so`` in-tree for gfx950.
+
+The HIP kernels are compiled with hipcc for ``--offload-arch=gfx950``; the
+host-side C ABI (validation, planner, errors) is plain C++ built with g++.
+Packed-FP32 VALU instructions are disabled for all device code.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(HERE, "libra_attn.so")
+
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.path.join(ROCM, "bin", "hipcc")
+ARCH = "gfx950"
+
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE, "-I", CSRC,
+]
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Werror",
+             "-I", INCLUDE, "-I", CSRC]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print("+", " ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every source and link ``libra_attn.so``; returns its path."""
+    if not os.path.exists(HIPCC):
+        raise RuntimeError(f"hipcc not found at {HIPCC}")
+    os.makedirs(BUILD, exist_ok=True)
+    cxx = shutil.which("g++") or "g++"
+    objs = []
+    for src in sorted(os.listdir(CSRC)):
+        path = os.path.join(CSRC, src)
+        obj = os.path.join(BUILD, src + ".o")
+        if src.endswith(".hip"):
+            _run([HIPCC, *HIP_FLAGS, "-c", path, "-o", obj], verbose)
+        elif src.endswith(".cpp"):
+            _run([cxx, *CXX_FLAGS, "-c", path, "-o", obj], verbose)
+        else:
+            continue
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
+          f"-Wl,-rpath,{ROCM}/lib"], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build()

@@ -1,0 +1,178 @@
+// Host side of the C ABI declared in include/ra_attn.h: argument
+// validation, the ring-step planner and error reporting.  Plain C++; the
+// only device work is delegated to ra::launch_fwd (blockwise_fwd.hip).
+
+#include "ra_attn.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "ra_internal.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+ra_status_t fail(ra_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+constexpr int64_t kInt32Max = 2147483647LL;
+
+// Checks shared by the forward and the planner.  `kernel_chunks` adds the
+// kernels' requirement that chunks are multiples of their 32-row sub-tiles.
+ra_status_t check_ring(int64_t causal_block_size, int64_t q_chunk, int64_t k_chunk,
+                       int64_t seq_q, int32_t ring_size, int32_t ring_index,
+                       bool kernel_chunks) {
+  if (ring_size < 1) return fail(RA_E_INVALID, "ring_size must be >= 1 (got %d)", ring_size);
+  if (ring_index < 0 || ring_index >= ring_size)
+    return fail(RA_E_INVALID, "ring_index %d outside [0, %d)", ring_index, ring_size);
+  if (causal_block_size < 0)
+    return fail(RA_E_INVALID, "causal_block_size must be >= 0 (got %lld)",
+                (long long)causal_block_size);
+  if (seq_q < 0) return fail(RA_E_INVALID, "seq_q must be >= 0 (got %lld)", (long long)seq_q);
+  if (q_chunk <= 0 || k_chunk <= 0)
+    return fail(RA_E_INVALID, "q_chunk and k_chunk must be positive (got %lld, %lld)",
+                (long long)q_chunk, (long long)k_chunk);
+  // The blockwise scheme splits a block with integer division
+  // ("1. 分块处理机制"): the chunk sizes have to divide the block length.
+  if (seq_q % q_chunk != 0 || seq_q % k_chunk != 0)
+    return fail(RA_E_INVALID, "q_chunk %lld and k_chunk %lld must divide seq_q %lld",
+                (long long)q_chunk, (long long)k_chunk, (long long)seq_q);
+  if (seq_q * (int64_t)ring_size > kInt32Max)
+    return fail(kernel_chunks ? RA_E_UNSUPPORTED : RA_E_INVALID,
+                "ring_size * seq_q = %lld exceeds 2^31 - 1 positions",
+                (long long)(seq_q * (int64_t)ring_size));
+  if (kernel_chunks && (q_chunk % 32 != 0 || k_chunk % 32 != 0))
+    return fail(RA_E_UNSUPPORTED, "q_chunk %lld and k_chunk %lld must be multiples of 32",
+                (long long)q_chunk, (long long)k_chunk);
+  return RA_OK;
+}
+
+// The chunk-pair run test of "3. 因果注意力掩码支持": the pair runs iff it
+// holds at least one causally visible pair, i.e. the causal block of the
+// pair's last query is not before the causal block of its first key.
+inline bool pair_runs(int64_t c, int64_t last_q, int64_t first_k) {
+  return c == 0 || last_q / c >= first_k / c;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ra_last_error(void) { return g_err; }
+
+const char* ra_version(void) { return "0.1.0"; }
+
+ra_status_t ra_blockwise_plan(int64_t causal_block_size, int64_t q_chunk, int64_t k_chunk,
+                              int64_t seq_q, int32_t ring_size, int32_t ring_index,
+                              int32_t* kv_block_of_step, uint8_t* run_bits,
+                              int64_t* n_run_chunk_pairs) {
+  clear_error();
+  ra_status_t st = check_ring(causal_block_size, q_chunk, k_chunk, seq_q, ring_size,
+                              ring_index, false);
+  if (st != RA_OK) return st;
+  if (kv_block_of_step == nullptr) return fail(RA_E_INVALID, "kv_block_of_step is NULL");
+  const int64_t nq = seq_q / q_chunk, nk = seq_q / k_chunk;
+  int64_t n_run = 0;
+  for (int32_t t = 0; t < ring_size; ++t) {
+    // Ring order: at outer step t the device uses block (index - t) mod N.
+    const int32_t kb = ((ring_index - t) % ring_size + ring_size) % ring_size;
+    kv_block_of_step[t] = kb;
+    for (int64_t a = 0; a < nq; ++a) {
+      const int64_t last_q = (int64_t)ring_index * seq_q + (a + 1) * q_chunk - 1;
+      for (int64_t b = 0; b < nk; ++b) {
+        const int64_t first_k = (int64_t)kb * seq_q + b * k_chunk;
+        const bool run = pair_runs(causal_block_size, last_q, first_k);
+        n_run += run;
+        if (run_bits) run_bits[((int64_t)t * nq + a) * nk + b] = run ? 1 : 0;
+      }
+    }
+  }
+  if (n_run_chunk_pairs) *n_run_chunk_pairs = n_run;
+  return RA_OK;
+}
+
+ra_status_t ra_blockwise_attn_fwd_ex(const void* q, const void* k, const void* v,
+                                     const int32_t* segment_ids, int64_t causal_block_size,
+                                     int64_t q_chunk, int64_t k_chunk, int32_t ring_size,
+                                     int32_t ring_index, int64_t batch, int64_t seq_q,
+                                     int64_t heads, int64_t head_dim, ra_dtype_t dtype,
+                                     void* out, float* lse, uint8_t* run_map, void* stream) {
+  clear_error();
+  if (batch < 0 || heads < 0)
+    return fail(RA_E_INVALID, "batch and heads must be >= 0 (got %lld, %lld)",
+                (long long)batch, (long long)heads);
+  if (head_dim <= 0) return fail(RA_E_INVALID, "head_dim must be positive");
+  ra_status_t st = check_ring(causal_block_size, q_chunk, k_chunk, seq_q, ring_size,
+                              ring_index, true);
+  if (st != RA_OK) return st;
+  if (dtype != RA_BF16 && dtype != RA_F32)
+    return fail(RA_E_UNSUPPORTED, "dtype %d is not supported (RA_BF16, RA_F32)", (int)dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(RA_E_UNSUPPORTED, "head_dim %lld is not supported (64, 128)",
+                (long long)head_dim);
+  if (batch == 0 || seq_q == 0 || heads == 0) return RA_OK;  // empty call
+  if (!q || !k || !v || !out || !lse)
+    return fail(RA_E_INVALID, "q, k, v, out and lse must be non-NULL");
+  if (heads * head_dim > (1LL << 24))
+    return fail(RA_E_UNSUPPORTED, "heads * head_dim = %lld exceeds 2^24",
+                (long long)(heads * head_dim));
+  const int64_t n_qtiles = (seq_q + ra::kBlockM - 1) / ra::kBlockM;
+  const int64_t n_wg = batch * heads * n_qtiles;
+  if (n_wg > kInt32Max || batch > kInt32Max)
+    return fail(RA_E_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)n_wg);
+
+  const int64_t seq_k = seq_q * ring_size;
+  ra::FwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.seg = segment_ids;
+  p.out = out;
+  p.lse = lse;
+  p.run_map = run_map;
+  // A causal block at least as long as the whole sequence puts every
+  // position in block 0: every key is visible, exactly as without a mask.
+  p.causal = causal_block_size >= seq_k ? 0 : causal_block_size;
+  p.seq_q = (int32_t)seq_q;
+  p.seq_k = (int32_t)seq_k;
+  p.q_chunk = (int32_t)q_chunk;
+  p.k_chunk = (int32_t)k_chunk;
+  p.batch = (int32_t)batch;
+  p.heads = (int32_t)heads;
+  p.ring_size = ring_size;
+  p.ring_index = ring_index;
+  p.n_qtiles = (int32_t)n_qtiles;
+  p.n_wg = (int32_t)n_wg;
+  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+  const int64_t map_bytes =
+      run_map ? (int64_t)ring_size * (seq_q / q_chunk) * (seq_q / k_chunk) : 0;
+
+  char err[256];
+  if (ra::launch_fwd(p, dtype == RA_BF16 ? ra::Dtype::BF16 : ra::Dtype::F32, (int)head_dim,
+                     map_bytes, stream, err, (int)sizeof(err)) != 0)
+    return fail(RA_E_HIP, "%s", err);
+  return RA_OK;
+}
+
+ra_status_t ra_blockwise_attn_fwd(const void* q, const void* k, const void* v,
+                                  const int32_t* segment_ids, int64_t causal_block_size,
+                                  int64_t q_chunk, int64_t k_chunk, int32_t ring_size,
+                                  int32_t ring_index, int64_t batch, int64_t seq_q,
+                                  int64_t heads, int64_t head_dim, ra_dtype_t dtype,
+                                  void* out, float* lse, void* stream) {
+  return ra_blockwise_attn_fwd_ex(q, k, v, segment_ids, causal_block_size, q_chunk, k_chunk,
+                                  ring_size, ring_index, batch, seq_q, heads, head_dim, dtype,
+                                  out, lse, nullptr, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// Internal interface between the host-side C ABI (ra_host.cpp, plain C++)
+// and the HIP side (blockwise_fwd.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <stdint.h>
+
+namespace ra {
+
+// Everything the forward kernel needs, validated and derived on the host.
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* seg;   // [B, S] or nullptr
+  void* out;
+  float* lse;
+  uint8_t* run_map;     // [N][Lq/qc][Lq/kc] or nullptr
+  int64_t causal;       // effective causal block size; 0 = non-causal
+  int32_t seq_q;        // Lq
+  int32_t seq_k;        // S = N * Lq
+  int32_t q_chunk;
+  int32_t k_chunk;
+  int32_t batch;
+  int32_t heads;
+  int32_t ring_size;
+  int32_t ring_index;
+  int32_t n_qtiles;     // query tiles per (batch, head)
+  int32_t n_wg;         // workgroups in the grid
+  float scale_log2;     // log2(e) / sqrt(head_dim)
+};
+
+// Query rows per workgroup; every dtype and head_dim uses the same tiling
+// of the query block.
+constexpr int kBlockM = 128;
+
+enum class Dtype : int { BF16 = 0, F32 = 1 };
+
+// Enqueue the forward on `stream` (a hipStream_t).  Returns 0 on success,
+// otherwise writes a message into err (size errlen) and returns nonzero.
+int launch_fwd(const FwdParams& p, Dtype dtype, int head_dim, int64_t run_map_bytes,
+               void* stream, char* err, int errlen);
+
+}  // namespace ra

@@ -1,0 +1,103 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol,
+and rejects malformed arguments on the host before any device work."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_exact_ra_amd as ra
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "ra_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("ra_blockwise_attn_fwd", "ra_blockwise_attn_fwd_ex", "ra_blockwise_plan",
+              "ra_last_error", "ra_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ra.load_library()
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_version_and_error_string():
+    assert re.fullmatch(r"\d+\.\d+\.\d+", ra.version())
+    assert isinstance(ra.last_error(), str)
+
+
+# A forward call with fake (never dereferenced) pointers: every case below
+# must fail validation on the host, so no pointer is touched and no HIP call
+# is made.
+FAKE = 0x1000
+
+
+def fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, seg=None, c=1, qc=64, kc=64, N=4, r=0, B=1, Lq=128,
+             H=2, D=128, dt=ra.RA_BF16, out=FAKE, lse=FAKE)
+    a.update(kw)
+    lib = ra.load_library()
+    return lib.ra_blockwise_attn_fwd(a["q"], a["k"], a["v"], a["seg"], a["c"], a["qc"],
+                                     a["kc"], a["N"], a["r"], a["B"], a["Lq"], a["H"],
+                                     a["D"], a["dt"], a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(N=0), ra.RA_E_INVALID, "ring_size"),
+    (dict(r=4), ra.RA_E_INVALID, "ring_index"),
+    (dict(r=-1), ra.RA_E_INVALID, "ring_index"),
+    (dict(c=-1), ra.RA_E_INVALID, "causal_block_size"),
+    (dict(qc=0), ra.RA_E_INVALID, "positive"),
+    (dict(kc=-64), ra.RA_E_INVALID, "positive"),
+    (dict(qc=96), ra.RA_E_INVALID, "divide"),
+    (dict(qc=48, kc=48, Lq=96), ra.RA_E_UNSUPPORTED, "multiples of 32"),
+    (dict(B=-1), ra.RA_E_INVALID, "batch"),
+    (dict(H=-2), ra.RA_E_INVALID, "batch and heads"),
+    (dict(Lq=-128), ra.RA_E_INVALID, "seq_q"),
+    (dict(D=0), ra.RA_E_INVALID, "head_dim"),
+    (dict(D=96), ra.RA_E_UNSUPPORTED, "head_dim"),
+    (dict(dt=7), ra.RA_E_UNSUPPORTED, "dtype"),
+    (dict(q=None), ra.RA_E_INVALID, "non-NULL"),
+    (dict(v=None), ra.RA_E_INVALID, "non-NULL"),
+    (dict(lse=None), ra.RA_E_INVALID, "non-NULL"),
+    (dict(N=1 << 20, Lq=1 << 12, qc=64, kc=64), ra.RA_E_UNSUPPORTED, "2^31"),
+    (dict(H=1 << 20, D=128), ra.RA_E_UNSUPPORTED, "2^24"),
+])
+def test_invalid_arguments(kw, status, needle):
+    assert fwd(**kw) == status
+    assert needle in ra.last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(Lq=0),
+                                dict(B=0, q=None, k=None, v=None, out=None, lse=None)])
+def test_empty_call_is_a_noop(kw):
+    assert fwd(**kw) == ra.RA_OK
+    assert ra.last_error() == ""
+
+
+def test_plan_rejects_bad_arguments():
+    lib = ra.load_library()
+    order = (ctypes.c_int32 * 4)()
+    assert lib.ra_blockwise_plan(1, 64, 64, 128, 4, 4, order, None, None) == ra.RA_E_INVALID
+    assert lib.ra_blockwise_plan(1, 64, 48, 128, 4, 0, order, None, None) == ra.RA_E_INVALID
+    assert lib.ra_blockwise_plan(1, 64, 64, 128, 4, 0, None, None, None) == ra.RA_E_INVALID
+    # The planner itself has no 32-multiple restriction.
+    assert lib.ra_blockwise_plan(1, 3, 5, 15, 4, 0, order, None, None) == ra.RA_OK
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 64, 1, 64)
+    with pytest.raises(ValueError):
+        ra.blockwise_attn_fwd(q, q, q, None, 1, 32, 32)
