@@ -105,7 +105,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--cpu-rows", type=int, default=256,
+    ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="query rows of the CPU oracle sample (0 = skip)")
     args = ap.parse_args()
     if args.gpus != 1:
