@@ -107,6 +107,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="query rows of the CPU oracle sample (0 = skip)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first; its "
+                         "FETCH_SIZE/WRITE_SIZE counters calibrate HBM byte counts")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -131,6 +134,14 @@ def main():
     out = torch.empty_like(q)
     lse = torch.empty((w.batch, w.heads, w.seq_q), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1, out=dst)  # one elementwise kernel: reads n bytes, writes n
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         ra.blockwise_attn_fwd(q, k, v, None, w.causal_block_size, w.q_chunk, w.k_chunk,
