@@ -97,9 +97,12 @@ ra_status_t ra_blockwise_attn_fwd(const void* q, const void* k, const void* v,
  *
  *   run_map: device bytes [ring_size][seq_q / q_chunk][seq_q / k_chunk] in
  *       ring-step order, or NULL.  The library clears it and the kernel sets
- *       run_map[t][a][b] = 1 when it computed any part of query chunk a
- *       against key chunk b of the block used at ring step t.  Intended for
- *       debugging and parity checks; it costs extra stores.
+ *       run_map[t][a][b] = 1 when it folded into the softmax carry of query
+ *       chunk a a 32-key part of key chunk b (block of ring step t) that
+ *       holds at least one visible pair.  Parts without a visible pair are
+ *       never folded in: a 64-key tile with none is skipped outright, and
+ *       inside a processed tile such a part is masked to exactly zero weight.
+ *       Intended for debugging and parity checks; it costs extra stores.
  *
  * Errors as for ra_blockwise_attn_fwd.
  */

@@ -1,13 +1,12 @@
 // Blockwise exact-attention forward for one Ring Attention device share,
 // written for gfx950 (MI355X, CDNA4).
 //
-// One workgroup of 4 waves owns 128 query rows of one (batch, head); each
-// wave owns 32 of them.  The workgroup walks the N key/value blocks in ring
+// A workgroup owns a tile of query rows of one (batch, head) (256 rows = 8
+// waves for bf16, 128 rows = 4 waves for fp32); each wave owns 32 of them.  The workgroup walks the N key/value blocks in ring
 // order -- step t uses block (r - t) mod N ("Ring Attention with Blockwise
 // Transformers for Near-Infinite Context", section 三 "环形注意力算法") --
-// and inside a block the keys in tiles.  Tiles are staged through
-// double-buffered LDS; the next tile's global loads are issued before the
-// current tile is computed, also across block boundaries, which is the
+// and inside a block the keys in tiles.  Tiles are staged through LDS and
+// fetched ahead of use, also across block boundaries, which is the
 // single-device stand-in for receiving the next block while computing.
 //
 // Per tile and wave:
@@ -61,17 +60,6 @@ constexpr int kRsrcWord3 = 0x00020000;
 
 __device__ __forceinline__ float ninf() { return -__builtin_inff(); }
 
-// A raw buffer descriptor over [base, base + bytes).  Both are uniform across
-// the wave; readfirstlane makes that explicit so the descriptor lives in
-// scalar registers.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((hi << 32) | lo), 0,
-                                           __builtin_amdgcn_readfirstlane((int)bytes), kRsrcWord3);
-}
-
 // ---------------------------------------------------------------------------
 // Work decomposition shared by both kernels
 // ---------------------------------------------------------------------------
@@ -85,6 +73,7 @@ struct WgCoord {
   int b, h, m0;
 };
 
+template <int BM>
 __device__ __forceinline__ WgCoord wg_coord(const FwdParams& p) {
   const int pid = blockIdx.x, n = p.n_wg;
   const int xcd = pid & 7, idx = pid >> 3, cnt = n >> 3, rem = n & 7;
@@ -96,7 +85,7 @@ __device__ __forceinline__ WgCoord wg_coord(const FwdParams& p) {
   // descriptors derived from them stay in scalar registers.
   return WgCoord{__builtin_amdgcn_readfirstlane(bh / p.heads),
                  __builtin_amdgcn_readfirstlane(bh % p.heads),
-                 __builtin_amdgcn_readfirstlane(qt * kBlockM)};
+                 __builtin_amdgcn_readfirstlane(qt * BM)};
 }
 
 // Position of the workgroup's current tile in the ring walk.
@@ -146,6 +135,14 @@ __device__ __forceinline__ void cursor_next(const FwdParams& p, Cursor& c, int64
   cursor_seek<TN>(p, c, kend);
 }
 
+// A wave-uniform 64-bit value that the compiler computed in vector registers
+// (64-bit division has no scalar form), moved back to scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Per-wave causal limits: a 32-key sub-tile starting at key position pk0
 // holds a visible pair iff pk0 < run_lim, and needs no causal mask iff
 // pk0 + 31 < full_lim; key position pk is visible from this lane's row iff
@@ -160,17 +157,18 @@ __device__ __forceinline__ WaveLimits wave_limits(const FwdParams& p, int64_t pq
   WaveLimits w{INT64_MAX, INT64_MAX, p.seq_k};
   if (p.causal > 0) {
     const int64_t c = p.causal;
-    w.run_lim = ((pq_first + 31) / c + 1) * c;
-    w.full_lim = (pq_first / c + 1) * c;
+    w.run_lim = uniform64(((pq_first + 31) / c + 1) * c);
+    w.full_lim = uniform64((pq_first / c + 1) * c);
     w.lane_lim = (int32_t)std::min<int64_t>(((pq_first + lrow) / c + 1) * c, p.seq_k);
   }
   return w;
 }
 
+template <int BM>
 __device__ __forceinline__ int64_t wg_kend(const FwdParams& p, int m0) {
   if (p.causal == 0) return INT64_MAX;
-  const int64_t q_last = (int64_t)p.ring_index * p.seq_q + std::min(m0 + kBlockM, p.seq_q) - 1;
-  return (q_last / p.causal + 1) * p.causal;
+  const int64_t q_last = (int64_t)p.ring_index * p.seq_q + std::min(m0 + BM, p.seq_q) - 1;
+  return uniform64((q_last / p.causal + 1) * p.causal);
 }
 
 __device__ __forceinline__ void write_run_map(const FwdParams& p, int t, int qg0, int key0) {
@@ -182,29 +180,33 @@ __device__ __forceinline__ void write_run_map(const FwdParams& p, int t, int qg0
 // bf16 kernel
 // ---------------------------------------------------------------------------
 //
-// 64-key tiles.  LDS per stage: K row-major [64][D + 8] (the 16-byte pad
-// spreads the A-operand reads of 8 consecutive rows over all banks), V
-// row-major [64][D + 16] read with ds_read_b64_tr_b16, and 64 segment ids.
-// Within each 16-lane group that instruction hands destination lane i,
-// element e the element i % 4 of source lane 4e + i / 4.  A lane of group g
-// therefore sources row base + (lane % 16) / 4 at column
-// 16 * (g % 2) + 4 * (lane % 4) and receives, for its own column
-// (lane % 32), the 4 consecutive rows base .. base + 3: exactly four k-slots
-// of the P.V A operand V^T.
+// 8 waves, 256 query rows per workgroup, one workgroup per CU.  64-key tiles
+// flow through a ring of 4 LDS stages filled by bounds-checked
+// buffer-to-LDS DMA (buffer_load_dwordx4 ... lds) issued 3 tiles ahead, so
+// the fetch of a tile overlaps two tiles of compute and needs no staging
+// registers.  Keys past a block's visible length read as zero.  The loop is
+// unrolled over the ring so that every stage is a distinct LDS object; the
+// per-wave waits on the DMA are explicit vmcnt counts.
 //
-// Global loads are bounds-checked buffer loads: each thread's byte offsets
-// inside a tile are fixed, only the (scalar) tile base changes, and rows past
-// the tile's valid length read as zero.
-
-template <int D>
-struct Bf16Cfg {
-  static constexpr int TN = 64;
-  static constexpr int KS = D + 8;
-  static constexpr int VS = D + 16;
-  static constexpr int GR = D / 8;                    // 16-byte granules per row
-  static constexpr int LOADS = TN * GR / kThreads;    // per thread per tensor
-  static_assert(LOADS * kThreads == TN * GR, "tile must split evenly");
-};
+// A DMA instruction writes 64 lanes x 16 bytes contiguously, so the LDS
+// layouts are chosen for the reads (all in 16-byte slots, g = the 16-byte
+// granule of a row, r = the row = key):
+//   K: slot(r, g) = (g / 4) * 256 + (r / 16) * 64 + (g % 4) * 16 + r % 16.
+//      The QK^T A operand of 16 consecutive lanes (16 rows, one granule) is
+//      then 256 contiguous bytes, and its address is a per-lane base plus a
+//      compile-time offset.
+//   V: slot(r, g) = (g / 4) * 256 + r * 4 + g % 4.  A ds_read_b64_tr_b16 of
+//      32 lanes (4 rows x 64 contiguous bytes) is then 256 contiguous bytes.
+// Within each 16-lane group ds_read_b64_tr_b16 hands destination lane i,
+// element e the element i % 4 of source lane 4e + i / 4; a lane of group g
+// sources row base + (lane % 16) / 4 at column 16 * (g % 2) + 4 * (lane % 4)
+// and so receives, for its own column lane % 32, rows base .. base + 3: four
+// k-slots of the P.V A operand V^T.
+//
+// Software pipeline per tile i (tile i+1's keys already in LDS):
+//   S_next = K_{i+1} . Q^T   (MFMA)      -- independent of --
+//   softmax carry on S_cur = tile i (VALU),
+//   O^T += V_i^T . P_i^T     (MFMA).
 
 // Softmax/accumulator state of one wave (32 query rows, one per lane pair).
 template <int D>
@@ -215,40 +217,145 @@ struct Bf16Wave {
   float l_run;   // this lane half's part of the denominator
 };
 
-// One 64-key tile for one wave.  MASKED selects the general path: any of the
-// two 32-key sub-tiles may be skipped (run[sb] false) or need the causal /
-// segment mask; otherwise both run unmasked, straight-line.
-template <int D, bool MASKED, bool SEG>
-__device__ __forceinline__ void bf16_tile(Bf16Wave<D>& w, const bf16x8_t* qf,
-                                          const __bf16* ks, const __bf16* vs,
-                                          const int32_t* sg, int lrow, int half, int vrd,
-                                          bool run0, bool run1, bool mask0, bool mask1,
-                                          int32_t pk_tile,
-                                          int32_t lane_lim, int32_t seg_q, float scale_log2) {
-  using C = Bf16Cfg<D>;
-  constexpr int NDB = D / 32;
+template <int D>
+struct PipeCfg {
+  static constexpr int kWaves = kBlockMBf16 / 32;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int TN = 64;                 // keys per tile
+  static constexpr int GR = D / 8;              // 16-byte granules per row
+  static constexpr int SLOTS = TN * GR;         // 16-byte slots per tensor tile
+  static constexpr int ELEMS = SLOTS * 8;       // bf16 elements per tensor tile
+  static constexpr int DPW = SLOTS / 64 / kWaves;  // 1 KiB DMA per wave per tensor
+  static_assert(DPW * 64 * kWaves == SLOTS, "tile must split evenly over the waves");
+};
 
-  // S^T = K . Q^T
-  f32x16_t s[2];
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (gfx9 encoding; expcnt and lgkmcnt not waited).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
+}
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor words (base, stride 0, num_records, gfx9 word 3),
+// wave-uniform and in scalar registers.
+__device__ __forceinline__ i32x4_t rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = kRsrcWord3;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// Bounds-checked buffer-to-LDS DMA of 16 (4) bytes per lane: lane l's bytes
+// land at LDS address lds + 16 * l (4 * l); lanes whose offset is outside
+// the descriptor write zeros.  Issued as inline asm on purpose: the compiler
+// then does not track these LDS writes (its conservative tracking would add
+// waits for all outstanding DMA before unrelated LDS reads); completion is
+// enforced by the explicit vmcnt waits and barriers of the pipeline.
+__device__ __forceinline__ void dma_b128(uint32_t lds, uint32_t voff, i32x4_t rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc));
+}
+__device__ __forceinline__ void dma_b32(uint32_t lds, uint32_t voff, i32x4_t rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc));
+}
+
+// Workgroup barrier publishing the LDS tiles written by DMA.  The LDS-only
+// acquire fence keeps the compiler from reusing or hoisting LDS reads across
+// it (it does not see the DMA writes) and costs only an LDS wait.
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Per-wave view of one tile: which 32-key halves have a visible pair and
+// which need the causal or segment mask.
+struct TileFlags {
+  bool run0, run1, mask0, mask1;
+  int kloc0;
+  int32_t pk_tile;
+};
+
+template <bool SEG>
+__device__ __forceinline__ TileFlags tile_flags(const FwdParams& p, const Cursor& c,
+                                                const WaveLimits& lim, bool wave_active) {
+  TileFlags f;
+  f.kloc0 = c.kt * 64;
+  const int64_t pk = (int64_t)c.kb * p.seq_q + f.kloc0;
+  f.pk_tile = (int32_t)pk;
+  f.run0 = wave_active && pk < lim.run_lim;
+  f.run1 = wave_active && (f.kloc0 + 32 < c.klen) && pk + 32 < lim.run_lim;
+  f.mask0 = SEG || !(pk + 31 < lim.full_lim);
+  f.mask1 = SEG || !(pk + 63 < lim.full_lim);
+  return f;
+}
+
+// Issue this wave's share of the DMA of one tile into the given stage.
+template <int D, bool SEG>
+__device__ __forceinline__ void issue_tile(const FwdParams& p, const Cursor& c,
+                                           const __bf16* kbase0, const __bf16* vbase0,
+                                           const int32_t* sbase0, int64_t rs, uint32_t rs_bytes,
+                                           int wave, int lane, uint32_t k_lane, uint32_t v_lane,
+                                           __bf16* kd, __bf16* vd, int32_t* sd) {
+  using C = PipeCfg<D>;
+  const int64_t row0 = (int64_t)c.kb * p.seq_q + (int64_t)c.kt * C::TN;
+  const int nvalid = std::min(C::TN, c.klen - c.kt * C::TN);
+  const uint32_t bytes = (uint32_t)nvalid * rs_bytes;
+  const i32x4_t kr = rsrc_words(kbase0 + row0 * rs, bytes);
+  const i32x4_t vr = rsrc_words(vbase0 + row0 * rs, bytes);
+#pragma unroll
+  for (int u = 0; u < C::DPW; ++u) {
+    const int j = wave * C::DPW + u;
+    const uint32_t joff = (uint32_t)(j & 3) * 16u * rs_bytes + 64u * (uint32_t)(j >> 2);
+    dma_b128(lds_addr(kd + j * 512), k_lane + joff, kr);
+    dma_b128(lds_addr(vd + j * 512), v_lane + joff, vr);
+  }
+  if (SEG) {
+    const i32x4_t sr = rsrc_words(sbase0 + row0, (uint32_t)nvalid * 4u);
+    if (lane < 8) dma_b32(lds_addr(sd + 8 * wave), (uint32_t)(8 * wave + lane) * 4u, sr);
+  }
+}
+
+// S^T = K . Q^T for the two 32-key halves of a tile.
+template <int D>
+__device__ __forceinline__ void qk_tile(f32x16_t* s, const bf16x8_t* qf, const __bf16* kst,
+                                        int k_rd) {
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
     s[sb] = f32x16_t{};
-    if (MASKED && !(sb ? run1 : run0)) continue;
-    const __bf16* krow = ks + (32 * sb + lrow) * C::KS + 8 * half;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(krow + 16 * c);
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+          kst + k_rd + 2048 * (c >> 1) + 256 * (c & 1) + 1024 * sb);
       s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[sb], 0, 0, 0);
     }
   }
+}
 
-  // Mask and row max.  Lane (lrow, half) holds keys
-  // pk_tile + 32*sb + 8*(i/4) + 4*half + i%4 of query row lrow.
+// Mask the logits of a tile in place and return this lane's max over them.
+// MASKED: a half may be skipped (run false: all -inf) or need the causal /
+// segment mask; otherwise the tile is fully visible.
+template <bool MASKED, bool SEG>
+__device__ __forceinline__ float mask_max(f32x16_t* s, const int32_t* sg, int half,
+                                          const TileFlags& f, int32_t lane_lim, int32_t seg_q) {
   if (MASKED) {
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
-      const int32_t pkb = pk_tile + 32 * sb + 4 * half;
-      const bool r = sb ? run1 : run0, m = sb ? mask1 : mask0;
+      const int32_t pkb = f.pk_tile + 32 * sb + 4 * half;
+      const bool r = sb ? f.run1 : f.run0, m = sb ? f.mask1 : f.mask0;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int koff = 8 * (i >> 2) + (i & 3);
@@ -258,15 +365,26 @@ __device__ __forceinline__ void bf16_tile(Bf16Wave<D>& w, const bf16x8_t* qf,
       }
     }
   }
-  float mx = ninf();
+  // Independent partial maxima keep the dependency chains short.
+  float mp[4];
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb)
+  for (int k = 0; k < 4; ++k) mp[k] = fmaxf(s[k >> 1][8 * (k & 1)], s[k >> 1][8 * (k & 1) + 1]);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int i = 2; i < 8; ++i) mp[k] = fmaxf(mp[k], s[k >> 1][8 * (k & 1) + i]);
+  return fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
+}
+
+// Fold a tile's row max into the carry ("2. 数值稳定的注意力计算"): when some
+// row's max grows, rescale that row's numerator and denominator by
+// exp(prev_max - new_max).  Otherwise that factor is exactly 1 for every row
+// and nothing is done.
+template <int D>
+__device__ __forceinline__ void carry_max(Bf16Wave<D>& w, float mx, float scale_log2) {
+  constexpr int NDB = D / 32;
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   const float m_new = fmaxf(w.m_run, mx * scale_log2);
-  // Rescale only when some row's max grew: otherwise the correction
-  // exp(prev_max - new_max) is exactly 1 for every row.
   if (__builtin_amdgcn_ballot_w64(m_new > w.m_run) != 0) {
     const float alpha = m_new == ninf() ? 1.f : __builtin_amdgcn_exp2f(w.m_run - m_new);
 #pragma unroll
@@ -274,197 +392,286 @@ __device__ __forceinline__ void bf16_tile(Bf16Wave<D>& w, const bf16x8_t* qf,
     w.l_run *= alpha;
     w.m_run = m_new;
   }
-  const float m_use = MASKED && w.m_run == ninf() ? 0.f : w.m_run;
-  float rowsum = 0.f;
-#pragma unroll
-  for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][i], scale_log2, -m_use));
-      s[sb][i] = e;
-      rowsum += e;
-    }
-  }
-  w.l_run += rowsum;
+}
 
-  // O^T += V^T . P^T
+// Probabilities of a (masked, max-folded) tile and O^T += V^T . P^T.
+// Masked logits are -inf and give exactly 0.
+template <int D>
+__device__ __forceinline__ void exp_pv(Bf16Wave<D>& w, f32x16_t* s, const __bf16* vst, int v_rd,
+                                       float scale_log2) {
+  constexpr int NDB = D / 32;
+  const float m_use = w.m_run == ninf() ? 0.f : w.m_run;
+  // P in bf16 (round to nearest even) for the MFMA; the denominator sums the
+  // unrounded fp32 values.  Converting right away ends the fp32 live ranges.
+  bf16x8_t pb[4];
+  float ps[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f32x8_t e;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[q >> 1][8 * (q & 1) + i], scale_log2, -m_use));
+    ps[q] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    pb[q] = __builtin_convertvector(e, bf16x8_t);
+  }
+  w.l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
-    if (MASKED && !(sb ? run1 : run0)) continue;
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
-      const f32x8_t pf = {s[sb][8 * cc + 0], s[sb][8 * cc + 1], s[sb][8 * cc + 2],
-                          s[sb][8 * cc + 3], s[sb][8 * cc + 4], s[sb][8 * cc + 5],
-                          s[sb][8 * cc + 6], s[sb][8 * cc + 7]};
-      const bf16x8_t pb = __builtin_convertvector(pf, bf16x8_t);
-      const __bf16* vsrc = vs + vrd + (32 * sb + 16 * cc) * C::VS;
 #pragma unroll
       for (int j = 0; j < NDB; ++j) {
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vsrc + 32 * j));
-        const i16x4_t hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vsrc + 8 * C::VS + 32 * j));
+        const __bf16* src = vst + v_rd + 2048 * j + 32 * (32 * sb + 16 * cc);
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)src);
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(src + 256));
         const bf16x8_t a =
             __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        w.acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, w.acc[j], 0, 0, 0);
+        w.acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[2 * sb + cc], w.acc[j], 0, 0, 0);
       }
     }
   }
 }
 
+// Instruction order of a step: the QK^T MFMAs of tile i+1 interleaved with
+// the exponentials of tile i, then the P.V MFMAs of tile i interleaved with
+// the rest of its VALU work and tile i+1's row max.  LDS operand reads run
+// two MFMAs ahead, so their latency hides behind the MFMA in flight.
+template <int D>
+__device__ __forceinline__ void step_schedule() {
+  constexpr int kDsRead = 0x100, kMfma = 0x8, kValu = 0x2;
+  constexpr int NQK = 2 * (D / 16), NPV = 4 * (D / 32);
+  __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+#pragma unroll
+  for (int i = 0; i < NQK; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    if (i + 2 < NQK) __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kValu, 6, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kDsRead, 4, 0);
+#pragma unroll
+  for (int i = 0; i < NPV; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    if (i + 2 < NPV) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kValu, 3, 0);
+  }
+}
+
+// Everything one wave carries through the ring walk.
+template <int D>
+struct PipeState {
+  Bf16Wave<D> w;
+  f32x16_t s_cur[2];      // logits of tile i
+  Cursor c0, c1, c2, c3;  // tiles i .. i+3
+};
+
+struct PipeConst {
+  const __bf16* kbase0;
+  const __bf16* vbase0;
+  const int32_t* sbase0;
+  int64_t rs;
+  uint32_t rs_bytes;
+  int wave, lane, lrow, half, qg0;
+  bool wave_active;
+  uint32_t k_lane, v_lane;
+  int k_rd, v_rd;
+  int64_t kend;
+  int32_t seg_q;
+};
+
+// One pipeline step: tile i lives in stage PH, tile i+1 in stage PH+1, the
+// DMA for tile i+3 goes into stage PH+3 (all mod 4).  Returns whether a next
+// tile exists.
+template <int D, bool SEG, int PH>
+__device__ __forceinline__ bool pipe_step(const FwdParams& p, const PipeConst& k,
+                                          const WaveLimits& lim, const bf16x8_t* qf,
+                                          PipeState<D>& st, __bf16* const* ks,
+                                          __bf16* const* vs, int32_t* const* ss) {
+  constexpr int NPT = 2 * PipeCfg<D>::DPW + (SEG ? 1 : 0);  // DMA per wave per tile
+  constexpr int S0 = PH, S1 = (PH + 1) & 3, S3 = (PH + 3) & 3;
+  const bool have3 = st.c3.valid;
+  if (have3)
+    issue_tile<D, SEG>(p, st.c3, k.kbase0, k.vbase0, k.sbase0, k.rs, k.rs_bytes, k.wave, k.lane,
+                       k.k_lane, k.v_lane, ks[S3], vs[S3], ss[S3]);
+
+  const TileFlags f0 = tile_flags<SEG>(p, st.c0, lim, k.wave_active);
+  const bool have1 = st.c1.valid;
+  TileFlags f1{false, false, false, false, 0, 0};
+  if (have1) f1 = tile_flags<SEG>(p, st.c1, lim, k.wave_active);
+
+  // Tile i (logits in s_cur, already masked and max-folded): probabilities and
+  // P.V.  Tile i+1: logits and row max.  Both 32-key halves of both tiles
+  // are always computed, so this is one straight-line block for every step;
+  // a half without a visible pair is masked to -inf and contributes exactly 0
+  // (its keys in LDS are real keys or zeros, never undefined).
+  f32x16_t s_next[2];
+  float mx = ninf();
+  const bool any0 = f0.run0 || f0.run1, any1 = f1.run0 || f1.run1;
+  if (any0 || any1) {
+    qk_tile<D>(s_next, qf, ks[S1], k.k_rd);
+    exp_pv<D>(st.w, st.s_cur, vs[S0], k.v_rd, p.scale_log2);
+    mx = mask_max<false, false>(s_next, nullptr, k.half, f1, lim.lane_lim, k.seg_q);
+    step_schedule<D>();
+    if (SEG || !(f1.run0 && f1.run1) || f1.mask0 || f1.mask1) {
+      // Keep this a real branch: if-converted, the mask would run on every
+      // step.  An empty volatile asm cannot be speculated.
+      asm volatile("");
+      mx = mask_max<true, SEG>(s_next, ss[S1], k.half, f1, lim.lane_lim, k.seg_q);
+    }
+    if (p.run_map != nullptr && k.lane == 0) {
+      if (f0.run0) write_run_map(p, st.c0.t, k.qg0, f0.kloc0);
+      if (f0.run1) write_run_map(p, st.c0.t, k.qg0, f0.kloc0 + 32);
+    }
+  } else {
+    s_next[0] = f32x16_t{} - __builtin_inff();
+    s_next[1] = s_next[0];
+  }
+  if (k.wave_active) carry_max<D>(st.w, mx, p.scale_log2);
+
+  // Tile i+2 must have landed (for every wave) before the next step reads it.
+  if (st.c2.valid) {
+    if (have3)
+      wait_vm<NPT>();
+    else
+      wait_vm<0>();
+  }
+  stage_barrier();
+
+  st.s_cur[0] = s_next[0];
+  st.s_cur[1] = s_next[1];
+  st.c0 = st.c1;
+  st.c1 = st.c2;
+  st.c2 = st.c3;
+  if (have3) cursor_next<64>(p, st.c3, k.kend);
+  return st.c0.valid;
+}
+
 template <int D, bool SEG>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const FwdParams p) {
-  using C = Bf16Cfg<D>;
-  constexpr int TN = C::TN;
+__global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const FwdParams p) {
+  using C = PipeCfg<D>;
   constexpr int NDB = D / 32;
 
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][TN * C::KS];
-  __shared__ __attribute__((aligned(16))) __bf16 v_lds[2][TN * C::VS];
-  __shared__ int32_t seg_lds[2][SEG ? TN : 1];
+  // One LDS object per stage (K tile, V tile, then the segment ids), so that
+  // the compiler can tell the DMA into one stage from the reads of another.
+  constexpr int STAGE = 2 * C::ELEMS + (SEG ? 128 : 0);
+  __shared__ __attribute__((aligned(16))) __bf16 st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
+  __bf16* const ks[4] = {st0, st1, st2, st3};
+  __bf16* const vs[4] = {st0 + C::ELEMS, st1 + C::ELEMS, st2 + C::ELEMS, st3 + C::ELEMS};
+  int32_t* const ss[4] = {reinterpret_cast<int32_t*>(st0 + 2 * C::ELEMS),
+                          reinterpret_cast<int32_t*>(st1 + 2 * C::ELEMS),
+                          reinterpret_cast<int32_t*>(st2 + 2 * C::ELEMS),
+                          reinterpret_cast<int32_t*>(st3 + 2 * C::ELEMS)};
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int lrow = lane & 31;
-  const int half = lane >> 5;
+  PipeConst k;
+  k.lane = threadIdx.x & 63;
+  k.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  k.lrow = k.lane & 31;
+  k.half = k.lane >> 5;
 
-  const WgCoord wc = wg_coord(p);
+  const WgCoord wc = wg_coord<kBlockMBf16>(p);
   const int b = wc.b, h = wc.h, m0 = wc.m0;
-  const int qg0 = m0 + wave * 32;
-  const bool wave_active = qg0 < p.seq_q;
-  const int64_t pq_first = (int64_t)p.ring_index * p.seq_q + qg0;
-  const WaveLimits lim = wave_limits(p, pq_first, lrow);
-  const int64_t kend = wg_kend(p, m0);
-  int32_t seg_q = 0;
-  if (SEG && wave_active) seg_q = p.seg[(int64_t)b * p.seq_k + pq_first + lrow];
+  k.qg0 = m0 + k.wave * 32;
+  k.wave_active = k.qg0 < p.seq_q;
+  const int64_t pq_first = (int64_t)p.ring_index * p.seq_q + k.qg0;
+  const WaveLimits lim = wave_limits(p, pq_first, k.lrow);
+  k.kend = wg_kend<kBlockMBf16>(p, m0);
+  k.seg_q = 0;
+  if (SEG && k.wave_active) k.seg_q = p.seg[(int64_t)b * p.seq_k + pq_first + k.lrow];
 
-  const int64_t rs = (int64_t)p.heads * D;            // row stride (elements)
-  const uint32_t rs_bytes = (uint32_t)(rs * 2);
+  k.rs = (int64_t)p.heads * D;
+  k.rs_bytes = (uint32_t)(k.rs * 2);
+  k.kbase0 = static_cast<const __bf16*>(p.k) + (int64_t)b * p.seq_k * k.rs + (int64_t)h * D;
+  k.vbase0 = static_cast<const __bf16*>(p.v) + (int64_t)b * p.seq_k * k.rs + (int64_t)h * D;
+  k.sbase0 = SEG ? p.seg + (int64_t)b * p.seq_k : nullptr;
+  k.k_lane = (uint32_t)(k.lane & 15) * k.rs_bytes + 16u * (uint32_t)(k.lane >> 4);
+  k.v_lane = (uint32_t)(k.lane >> 2) * k.rs_bytes + 16u * (uint32_t)(k.lane & 3);
+  k.k_rd = 512 * (k.lrow >> 4) + 128 * k.half + 8 * (k.lrow & 15);
+  {
+    const int g = k.lane >> 4, j16 = k.lane & 15;
+    k.v_rd = 32 * (4 * (g >> 1) + (j16 >> 2)) + 16 * (g & 1) + 4 * (j16 & 3);
+  }
 
   // Q of this wave as the MFMA B operand (queries are the N dimension).
   bf16x8_t qf[D / 16];
-  if (wave_active) {
+  if (k.wave_active) {
     const __bf16* qrow = static_cast<const __bf16*>(p.q) +
-                         ((int64_t)b * p.seq_q + qg0 + lrow) * rs + (int64_t)h * D;
+                         ((int64_t)b * p.seq_q + k.qg0 + k.lrow) * k.rs + (int64_t)h * D;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
       qf[c] = __builtin_bit_cast(bf16x8_t,
-                                 *reinterpret_cast<const uint4*>(qrow + 16 * c + 8 * half));
+                                 *reinterpret_cast<const uint4*>(qrow + 16 * c + 8 * k.half));
+  }
+  // Let the Q (and segment id) loads land now: from here on the vector
+  // memory counter only tracks the K/V DMA, whose waits are explicit.
+  __builtin_amdgcn_s_waitcnt(0);
+
+  PipeState<D> st;
+#pragma unroll
+  for (int j = 0; j < NDB; ++j) st.w.acc[j] = f32x16_t{};
+  st.w.m_run = ninf();
+  st.w.l_run = 0.f;
+
+  // Prologue: tiles 0, 1, 2 in flight; tile 3's cursor ready.
+  st.c0 = Cursor{0, 0, 0, 0, 0, 0};
+  cursor_seek<64>(p, st.c0, k.kend);
+  st.c1 = st.c0;
+  if (st.c1.valid) cursor_next<64>(p, st.c1, k.kend);
+  st.c2 = st.c1;
+  if (st.c2.valid) cursor_next<64>(p, st.c2, k.kend);
+  st.c3 = st.c2;
+  if (st.c3.valid) cursor_next<64>(p, st.c3, k.kend);
+  constexpr int NPT = 2 * C::DPW + (SEG ? 1 : 0);
+  if (st.c0.valid)
+    issue_tile<D, SEG>(p, st.c0, k.kbase0, k.vbase0, k.sbase0, k.rs, k.rs_bytes, k.wave, k.lane,
+                       k.k_lane, k.v_lane, ks[0], vs[0], ss[0]);
+  if (st.c1.valid)
+    issue_tile<D, SEG>(p, st.c1, k.kbase0, k.vbase0, k.sbase0, k.rs, k.rs_bytes, k.wave, k.lane,
+                       k.k_lane, k.v_lane, ks[1], vs[1], ss[1]);
+  if (st.c2.valid)
+    issue_tile<D, SEG>(p, st.c2, k.kbase0, k.vbase0, k.sbase0, k.rs, k.rs_bytes, k.wave, k.lane,
+                       k.k_lane, k.v_lane, ks[2], vs[2], ss[2]);
+  // Tiles 0 and 1 must have landed: tile 1 is read by the first step's QK.
+  if (st.c2.valid)
+    wait_vm<NPT>();
+  else
+    wait_vm<0>();
+  stage_barrier();
+  if (st.c0.valid && k.wave_active) {
+    const TileFlags f = tile_flags<SEG>(p, st.c0, lim, k.wave_active);
+    qk_tile<D>(st.s_cur, qf, ks[0], k.k_rd);
+    const float mx = mask_max<true, SEG>(st.s_cur, ss[0], k.half, f, lim.lane_lim, k.seg_q);
+    carry_max<D>(st.w, mx, p.scale_log2);
   }
 
-  // Fixed per-thread offsets of the cooperative tile loads.
-  uint32_t goff[C::LOADS];
-  int kst[C::LOADS], vst[C::LOADS];
-#pragma unroll
-  for (int u = 0; u < C::LOADS; ++u) {
-    const int ci = tid + u * kThreads;
-    const int row = ci / C::GR, g = ci % C::GR;
-    goff[u] = (uint32_t)row * rs_bytes + (uint32_t)g * 16u;
-    kst[u] = row * C::KS + g * 8;
-    vst[u] = row * C::VS + g * 8;
-  }
-  // Source address of this lane's transposing V reads (see above).
-  const int vrd = (4 * half + ((lane & 15) >> 2)) * C::VS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
-  Bf16Wave<D> w;
-#pragma unroll
-  for (int j = 0; j < NDB; ++j) w.acc[j] = f32x16_t{};
-  w.m_run = ninf();
-  w.l_run = 0.f;
-
-  const __bf16* kbase0 = static_cast<const __bf16*>(p.k) + (int64_t)b * p.seq_k * rs + (int64_t)h * D;
-  const __bf16* vbase0 = static_cast<const __bf16*>(p.v) + (int64_t)b * p.seq_k * rs + (int64_t)h * D;
-  const int32_t* sbase0 = SEG ? p.seg + (int64_t)b * p.seq_k : nullptr;
-
-  u32x4_t kreg[C::LOADS], vreg[C::LOADS];
-  int32_t sreg = 0;
-  auto load_tile = [&](const Cursor& c) {
-    const int64_t row0 = (int64_t)c.kb * p.seq_q + (int64_t)c.kt * TN;
-    const int nvalid = std::min(TN, c.klen - c.kt * TN);
-    const uint32_t bytes = (uint32_t)nvalid * rs_bytes;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase0 + row0 * rs, bytes);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase0 + row0 * rs, bytes);
-#pragma unroll
-    for (int u = 0; u < C::LOADS; ++u) {
-      kreg[u] = __builtin_amdgcn_raw_buffer_load_b128(kr, goff[u], 0, 0);
-      vreg[u] = __builtin_amdgcn_raw_buffer_load_b128(vr, goff[u], 0, 0);
+  if (st.c0.valid) {
+    for (;;) {
+      if (!pipe_step<D, SEG, 0>(p, k, lim, qf, st, ks, vs, ss)) break;
+      if (!pipe_step<D, SEG, 1>(p, k, lim, qf, st, ks, vs, ss)) break;
+      if (!pipe_step<D, SEG, 2>(p, k, lim, qf, st, ks, vs, ss)) break;
+      if (!pipe_step<D, SEG, 3>(p, k, lim, qf, st, ks, vs, ss)) break;
     }
-    if (SEG && tid < TN) {
-      const __amdgpu_buffer_rsrc_t sr = make_rsrc(sbase0 + row0, (uint32_t)nvalid * 4u);
-      sreg = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(sr, tid * 4, 0, 0);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < C::LOADS; ++u) {
-      *reinterpret_cast<u32x4_t*>(&k_lds[buf][kst[u]]) = kreg[u];
-      *reinterpret_cast<u32x4_t*>(&v_lds[buf][vst[u]]) = vreg[u];
-    }
-    if (SEG && tid < TN) seg_lds[buf][tid] = sreg;
-  };
-
-  Cursor cur{0, 0, 0, 0, 0, 0};
-  cursor_seek<TN>(p, cur, kend);
-  if (cur.valid) {
-    load_tile(cur);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  int buf = 0;
-  while (cur.valid) {
-    Cursor nxt = cur;
-    cursor_next<TN>(p, nxt, kend);
-    if (nxt.valid) load_tile(nxt);
-
-    const int kloc0 = cur.kt * TN;
-    const int64_t pk_tile = (int64_t)cur.kb * p.seq_q + kloc0;
-    const bool run0 = wave_active && pk_tile < lim.run_lim;
-    const bool run1 = wave_active && (kloc0 + 32 < cur.klen) && pk_tile + 32 < lim.run_lim;
-    const bool mask0 = SEG || !(pk_tile + 31 < lim.full_lim);
-    const bool mask1 = SEG || !(pk_tile + 63 < lim.full_lim);
-    if (run0 || run1) {
-      const int32_t* sg = SEG ? seg_lds[buf] : nullptr;
-      if (!SEG && run0 && run1 && !mask0 && !mask1)
-        bf16_tile<D, false, false>(w, qf, k_lds[buf], v_lds[buf], sg, lrow, half, vrd, true, true,
-                                   false, false, (int32_t)pk_tile, lim.lane_lim, seg_q,
-                                   p.scale_log2);
-      else
-        bf16_tile<D, true, SEG>(w, qf, k_lds[buf], v_lds[buf], sg, lrow, half, vrd, run0, run1,
-                                mask0, mask1, (int32_t)pk_tile, lim.lane_lim, seg_q,
-                                p.scale_log2);
-      if (p.run_map != nullptr && lane == 0) {
-        if (run0) write_run_map(p, cur.t, qg0, kloc0);
-        if (run1) write_run_map(p, cur.t, qg0, kloc0 + 32);
-      }
-    }
-
-    if (nxt.valid) store_tile(buf ^ 1);
-    __syncthreads();
-    cur = nxt;
-    buf ^= 1;
   }
 
   // ---- epilogue: out = numerator / denominator, lse = ln(denominator) + max ----
-  if (!wave_active) return;
-  const float l_tot = w.l_run + __shfl_xor(w.l_run, 32);
+  if (!k.wave_active) return;
+  const float l_tot = st.w.l_run + __shfl_xor(st.w.l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const int row = qg0 + lrow;
-  __bf16* orow = static_cast<__bf16*>(p.out) + ((int64_t)b * p.seq_q + row) * rs + (int64_t)h * D;
+  const int row = k.qg0 + k.lrow;
+  __bf16* orow = static_cast<__bf16*>(p.out) + ((int64_t)b * p.seq_q + row) * k.rs + (int64_t)h * D;
 #pragma unroll
   for (int j = 0; j < NDB; ++j) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       typedef float f32x4_t __attribute__((ext_vector_type(4)));
       typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-      const f32x4_t o = {w.acc[j][4 * g] * inv, w.acc[j][4 * g + 1] * inv,
-                         w.acc[j][4 * g + 2] * inv, w.acc[j][4 * g + 3] * inv};
-      *reinterpret_cast<bf16x4_t*>(orow + 32 * j + 8 * g + 4 * half) =
+      const f32x4_t o = {st.w.acc[j][4 * g] * inv, st.w.acc[j][4 * g + 1] * inv,
+                         st.w.acc[j][4 * g + 2] * inv, st.w.acc[j][4 * g + 3] * inv};
+      *reinterpret_cast<bf16x4_t*>(orow + 32 * j + 8 * g + 4 * k.half) =
           __builtin_convertvector(o, bf16x4_t);
     }
   }
-  if (half == 0)
+  if (k.half == 0)
     p.lse[((int64_t)b * p.heads + h) * p.seq_q + row] =
-        l_tot > 0.f ? (w.m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : ninf();
+        l_tot > 0.f ? (st.w.m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : ninf();
 }
 
 // ---------------------------------------------------------------------------
@@ -492,13 +699,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(const FwdParams p)
   const int lrow = lane & 31;
   const int half = lane >> 5;
 
-  const WgCoord wc = wg_coord(p);
+  const WgCoord wc = wg_coord<kBlockMF32>(p);
   const int b = wc.b, h = wc.h, m0 = wc.m0;
   const int qg0 = m0 + wave * 32;
   const bool wave_active = qg0 < p.seq_q;
   const int64_t pq_first = (int64_t)p.ring_index * p.seq_q + qg0;
   const WaveLimits lim = wave_limits(p, pq_first, lrow);
-  const int64_t kend = wg_kend(p, m0);
+  const int64_t kend = wg_kend<kBlockMF32>(p, m0);
   const bool has_seg = p.seg != nullptr;
   int32_t seg_q = 0;
   if (has_seg && wave_active) seg_q = p.seg[(int64_t)b * p.seq_k + pq_first + lrow];
@@ -661,8 +868,9 @@ int launch_fwd(const FwdParams& p, Dtype dtype, int head_dim, int64_t run_map_by
       return 1;
     }
   }
-  const dim3 grid(p.n_wg), block(kThreads);
+  const dim3 grid(p.n_wg);
   if (dtype == Dtype::BF16) {
+    const dim3 block(PipeCfg<128>::kThreads);
     const bool seg = p.seg != nullptr;
     if (head_dim == 128) {
       if (seg)
@@ -676,6 +884,7 @@ int launch_fwd(const FwdParams& p, Dtype dtype, int head_dim, int64_t run_map_by
         hipLaunchKernelGGL((fwd_bf16_kernel<64, false>), grid, block, 0, s, p);
     }
   } else {
+    const dim3 block(kThreads);
     if (head_dim == 128)
       hipLaunchKernelGGL(fwd_f32_kernel<128>, grid, block, 0, s, p);
     else

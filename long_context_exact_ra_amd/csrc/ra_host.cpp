@@ -126,7 +126,9 @@ ra_status_t ra_blockwise_attn_fwd_ex(const void* q, const void* k, const void* v
   if (heads * head_dim > (1LL << 24))
     return fail(RA_E_UNSUPPORTED, "heads * head_dim = %lld exceeds 2^24",
                 (long long)(heads * head_dim));
-  const int64_t n_qtiles = (seq_q + ra::kBlockM - 1) / ra::kBlockM;
+  const ra::Dtype dt = dtype == RA_BF16 ? ra::Dtype::BF16 : ra::Dtype::F32;
+  const int64_t bm = ra::block_rows(dt);
+  const int64_t n_qtiles = (seq_q + bm - 1) / bm;
   const int64_t n_wg = batch * heads * n_qtiles;
   if (n_wg > kInt32Max || batch > kInt32Max)
     return fail(RA_E_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)n_wg);
@@ -158,8 +160,7 @@ ra_status_t ra_blockwise_attn_fwd_ex(const void* q, const void* k, const void* v
       run_map ? (int64_t)ring_size * (seq_q / q_chunk) * (seq_q / k_chunk) : 0;
 
   char err[256];
-  if (ra::launch_fwd(p, dtype == RA_BF16 ? ra::Dtype::BF16 : ra::Dtype::F32, (int)head_dim,
-                     map_bytes, stream, err, (int)sizeof(err)) != 0)
+  if (ra::launch_fwd(p, dt, (int)head_dim, map_bytes, stream, err, (int)sizeof(err)) != 0)
     return fail(RA_E_HIP, "%s", err);
   return RA_OK;
 }

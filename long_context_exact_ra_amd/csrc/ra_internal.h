@@ -29,11 +29,13 @@ struct FwdParams {
   float scale_log2;     // log2(e) / sqrt(head_dim)
 };
 
-// Query rows per workgroup; every dtype and head_dim uses the same tiling
-// of the query block.
-constexpr int kBlockM = 128;
-
 enum class Dtype : int { BF16 = 0, F32 = 1 };
+
+// Query rows per workgroup: 8 waves x 32 rows for bf16, 4 waves x 32 rows
+// for fp32.
+constexpr int kBlockMBf16 = 256;
+constexpr int kBlockMF32 = 128;
+inline int block_rows(Dtype d) { return d == Dtype::BF16 ? kBlockMBf16 : kBlockMF32; }
 
 // Enqueue the forward on `stream` (a hipStream_t).  Returns 0 on success,
 // otherwise writes a message into err (size errlen) and returns nonzero.
