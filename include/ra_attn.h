@@ -29,7 +29,9 @@
  * Arithmetic: logits, the running max, the denominator and the numerator
  * are float32.  bf16 inputs multiply on bf16 matrix cores with float32
  * accumulation; the probabilities are rounded to bf16 (round to nearest
- * even) before the P.V product while the denominator sums them unrounded.
+ * even), and both the P.V product and the denominator use the rounded
+ * values, so out is an exact convex combination of the rows of V (up to the
+ * float32 accumulation).
  * out is rounded to the input dtype.  A query row with no visible key gets
  * out = 0 and lse = -inf.
  *

@@ -143,24 +143,35 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Per-wave causal limits: a 32-key sub-tile starting at key position pk0
-// holds a visible pair iff pk0 < run_lim, and needs no causal mask iff
-// pk0 + 31 < full_lim; key position pk is visible from this lane's row iff
-// pk < lane_lim.
+// Per-wave causal limits as 32-bit key positions (every position is below
+// 2^31 - 1, and tiles start at multiples of 32).  For the 32-key sub-tile
+// starting at key position pk0:
+//   it holds a visible pair for some row of the wave iff pk0 < run_lim;
+//   it needs the per-element causal test iff pk0 >= mask_lim;
+// and key position pk is visible from this lane's row iff pk < lane_lim.
+// A wave without rows gets run_lim = INT32_MIN: none of its tiles run.
 struct WaveLimits {
-  int64_t run_lim, full_lim;
-  int32_t lane_lim;
+  int32_t run_lim, mask_lim, lane_lim;
 };
 
+__device__ __forceinline__ int32_t clamp_i32(int64_t x) {
+  return (int32_t)std::min<int64_t>(x, INT32_MAX);
+}
+
 __device__ __forceinline__ WaveLimits wave_limits(const FwdParams& p, int64_t pq_first,
-                                                  int lrow) {
-  WaveLimits w{INT64_MAX, INT64_MAX, p.seq_k};
+                                                  int lrow, bool wave_active) {
+  WaveLimits w{INT32_MAX, INT32_MAX, p.seq_k};
   if (p.causal > 0) {
     const int64_t c = p.causal;
-    w.run_lim = uniform64(((pq_first + 31) / c + 1) * c);
-    w.full_lim = uniform64((pq_first / c + 1) * c);
+    // First key position no row of the wave can see, and first key position
+    // that some row of the wave cannot see.
+    const int64_t run_end = ((pq_first + 31) / c + 1) * c;
+    const int64_t full_end = (pq_first / c + 1) * c;
+    w.run_lim = clamp_i32(uniform64(run_end));
+    w.mask_lim = clamp_i32(uniform64(full_end)) - 31;
     w.lane_lim = (int32_t)std::min<int64_t>(((pq_first + lrow) / c + 1) * c, p.seq_k);
   }
+  if (!wave_active) w.run_lim = INT32_MIN;
   return w;
 }
 
@@ -281,41 +292,49 @@ __device__ __forceinline__ void stage_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// A tile in flight: the global key position of its first key (its first
+// row in K and V), the end of the keys to visit in its block, its ring step
+// and block.  A tile with valid == 0 is past the end of the walk.
+struct TileInfo {
+  int32_t pk, end, t, kb, valid;
+};
+
+template <int TN>
+__device__ __forceinline__ TileInfo tile_info(const FwdParams& p, const Cursor& c) {
+  const int32_t base = c.kb * p.seq_q;
+  return TileInfo{base + c.kt * TN, base + c.klen, c.t, c.kb, c.valid};
+}
+
 // Per-wave view of one tile: which 32-key halves have a visible pair and
 // which need the causal or segment mask.
 struct TileFlags {
   bool run0, run1, mask0, mask1;
-  int kloc0;
-  int32_t pk_tile;
+  int32_t pk;
 };
 
 template <bool SEG>
-__device__ __forceinline__ TileFlags tile_flags(const FwdParams& p, const Cursor& c,
-                                                const WaveLimits& lim, bool wave_active) {
+__device__ __forceinline__ TileFlags tile_flags(const TileInfo& ti, const WaveLimits& lim) {
   TileFlags f;
-  f.kloc0 = c.kt * 64;
-  const int64_t pk = (int64_t)c.kb * p.seq_q + f.kloc0;
-  f.pk_tile = (int32_t)pk;
-  f.run0 = wave_active && pk < lim.run_lim;
-  f.run1 = wave_active && (f.kloc0 + 32 < c.klen) && pk + 32 < lim.run_lim;
-  f.mask0 = SEG || !(pk + 31 < lim.full_lim);
-  f.mask1 = SEG || !(pk + 63 < lim.full_lim);
+  f.pk = ti.pk;
+  f.run0 = ti.valid && ti.pk < lim.run_lim;
+  f.run1 = ti.valid && ti.pk + 32 < ti.end && ti.pk + 32 < lim.run_lim;
+  f.mask0 = SEG || ti.pk >= lim.mask_lim;
+  f.mask1 = SEG || ti.pk + 32 >= lim.mask_lim;
   return f;
 }
 
 // Issue this wave's share of the DMA of one tile into the given stage.
 template <int D, bool SEG>
-__device__ __forceinline__ void issue_tile(const FwdParams& p, const Cursor& c,
-                                           const __bf16* kbase0, const __bf16* vbase0,
-                                           const int32_t* sbase0, int64_t rs, uint32_t rs_bytes,
-                                           int wave, int lane, uint32_t k_lane, uint32_t v_lane,
-                                           __bf16* kd, __bf16* vd, int32_t* sd) {
+__device__ __forceinline__ void issue_tile(const TileInfo& ti, const char* kbase0,
+                                           const char* vbase0, const int32_t* sbase0,
+                                           uint32_t rs_bytes, int wave, int lane, uint32_t k_lane,
+                                           uint32_t v_lane, __bf16* kd, __bf16* vd, int32_t* sd) {
   using C = PipeCfg<D>;
-  const int64_t row0 = (int64_t)c.kb * p.seq_q + (int64_t)c.kt * C::TN;
-  const int nvalid = std::min(C::TN, c.klen - c.kt * C::TN);
+  const int nvalid = std::min(C::TN, ti.end - ti.pk);
   const uint32_t bytes = (uint32_t)nvalid * rs_bytes;
-  const i32x4_t kr = rsrc_words(kbase0 + row0 * rs, bytes);
-  const i32x4_t vr = rsrc_words(vbase0 + row0 * rs, bytes);
+  const uint64_t off = (uint64_t)(uint32_t)ti.pk * rs_bytes;
+  const i32x4_t kr = rsrc_words(kbase0 + off, bytes);
+  const i32x4_t vr = rsrc_words(vbase0 + off, bytes);
 #pragma unroll
   for (int u = 0; u < C::DPW; ++u) {
     const int j = wave * C::DPW + u;
@@ -324,7 +343,7 @@ __device__ __forceinline__ void issue_tile(const FwdParams& p, const Cursor& c,
     dma_b128(lds_addr(vd + j * 512), v_lane + joff, vr);
   }
   if (SEG) {
-    const i32x4_t sr = rsrc_words(sbase0 + row0, (uint32_t)nvalid * 4u);
+    const i32x4_t sr = rsrc_words(sbase0 + ti.pk, (uint32_t)nvalid * 4u);
     if (lane < 8) dma_b32(lds_addr(sd + 8 * wave), (uint32_t)(8 * wave + lane) * 4u, sr);
   }
 }
@@ -347,19 +366,22 @@ __device__ __forceinline__ void qk_tile(f32x16_t* s, const bf16x8_t* qf, const _
 
 // Mask the logits of a tile in place and return this lane's max over them.
 // MASKED: a half may be skipped (run false: all -inf) or need the causal /
-// segment mask; otherwise the tile is fully visible.
+// segment mask; otherwise the tile is fully visible.  Element i of a half
+// sits at key offset 8 * (i / 4) + i % 4 from the lane's first key, so the
+// causal test of a whole half reduces to one per-lane count of visible keys.
 template <bool MASKED, bool SEG>
 __device__ __forceinline__ float mask_max(f32x16_t* s, const int32_t* sg, int half,
                                           const TileFlags& f, int32_t lane_lim, int32_t seg_q) {
   if (MASKED) {
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
-      const int32_t pkb = f.pk_tile + 32 * sb + 4 * half;
       const bool r = sb ? f.run1 : f.run0, m = sb ? f.mask1 : f.mask0;
+      // Keys at offsets below nvis are causally visible from this lane's row.
+      const int32_t nvis = !r ? 0 : m ? lane_lim - (f.pk + 32 * sb + 4 * half) : 32;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int koff = 8 * (i >> 2) + (i & 3);
-        bool ok = r && (!m || pkb + koff < lane_lim);
+        bool ok = koff < nvis;
         if (SEG) ok = ok && sg[32 * sb + 4 * half + koff] == seg_q;
         s[sb][i] = ok ? s[sb][i] : ninf();
       }
@@ -376,6 +398,19 @@ __device__ __forceinline__ float mask_max(f32x16_t* s, const int32_t* sg, int ha
   return fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
 }
 
+// The two lanes holding one query row are l and l ^ 32.  Swapping the lane
+// halves of x with itself leaves both values of the pair in every lane.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Fold a tile's row max into the carry ("2. 数值稳定的注意力计算"): when some
 // row's max grows, rescale that row's numerator and denominator by
 // exp(prev_max - new_max).  Otherwise that factor is exactly 1 for every row
@@ -383,7 +418,7 @@ __device__ __forceinline__ float mask_max(f32x16_t* s, const int32_t* sg, int ha
 template <int D>
 __device__ __forceinline__ void carry_max(Bf16Wave<D>& w, float mx, float scale_log2) {
   constexpr int NDB = D / 32;
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = pair_max(mx);
   const float m_new = fmaxf(w.m_run, mx * scale_log2);
   if (__builtin_amdgcn_ballot_w64(m_new > w.m_run) != 0) {
     const float alpha = m_new == ninf() ? 1.f : __builtin_amdgcn_exp2f(w.m_run - m_new);
@@ -394,15 +429,19 @@ __device__ __forceinline__ void carry_max(Bf16Wave<D>& w, float mx, float scale_
   }
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 // Probabilities of a (masked, max-folded) tile and O^T += V^T . P^T.
-// Masked logits are -inf and give exactly 0.
+// Masked logits are -inf and give exactly 0.  P is rounded to bf16 (round
+// to nearest even) for the MFMA, and the denominator sums the same rounded
+// values, so the output is an exact convex combination of the weights the
+// numerator used.
 template <int D>
 __device__ __forceinline__ void exp_pv(Bf16Wave<D>& w, f32x16_t* s, const __bf16* vst, int v_rd,
                                        float scale_log2) {
   constexpr int NDB = D / 32;
   const float m_use = w.m_run == ninf() ? 0.f : w.m_run;
-  // P in bf16 (round to nearest even) for the MFMA; the denominator sums the
-  // unrounded fp32 values.  Converting right away ends the fp32 live ranges.
+  const bf16x2_t one2 = {(__bf16)1.f, (__bf16)1.f};
   bf16x8_t pb[4];
   float ps[4];
 #pragma unroll
@@ -411,8 +450,11 @@ __device__ __forceinline__ void exp_pv(Bf16Wave<D>& w, f32x16_t* s, const __bf16
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[q >> 1][8 * (q & 1) + i], scale_log2, -m_use));
-    ps[q] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
     pb[q] = __builtin_convertvector(e, bf16x8_t);
+    ps[q] = __builtin_amdgcn_fdot2_f32_bf16(pb[q].s01, one2, 0.f, false);
+    ps[q] = __builtin_amdgcn_fdot2_f32_bf16(pb[q].s23, one2, ps[q], false);
+    ps[q] = __builtin_amdgcn_fdot2_f32_bf16(pb[q].s45, one2, ps[q], false);
+    ps[q] = __builtin_amdgcn_fdot2_f32_bf16(pb[q].s67, one2, ps[q], false);
   }
   w.l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 #pragma unroll
@@ -460,15 +502,19 @@ __device__ __forceinline__ void step_schedule() {
 template <int D>
 struct PipeState {
   Bf16Wave<D> w;
-  f32x16_t s_cur[2];      // logits of tile i
-  Cursor c0, c1, c2, c3;  // tiles i .. i+3
+  // Logits of tiles i and i+1 in two buffers whose roles alternate from
+  // step to step (even steps: tile i in buffer 0), so no step copies them.
+  f32x16_t s[2][2];
+  // The tile held by each LDS stage; stage indices are compile-time
+  // constants in the unrolled loop, so these stay in fixed registers.
+  TileInfo ti[4];
+  Cursor ic;  // the next tile to fetch
 };
 
 struct PipeConst {
-  const __bf16* kbase0;
-  const __bf16* vbase0;
+  const char* kbase0;
+  const char* vbase0;
   const int32_t* sbase0;
-  int64_t rs;
   uint32_t rs_bytes;
   int wave, lane, lrow, half, qg0;
   bool wave_active;
@@ -477,6 +523,20 @@ struct PipeConst {
   int64_t kend;
   int32_t seg_q;
 };
+
+// Record the tile under the fetch cursor as the content of stage S, start
+// its DMA and advance the cursor.
+template <int D, bool SEG, int S>
+__device__ __forceinline__ void fetch_next(const FwdParams& p, const PipeConst& k,
+                                           PipeState<D>& st, __bf16* const* ks,
+                                           __bf16* const* vs, int32_t* const* ss) {
+  st.ti[S] = tile_info<PipeCfg<D>::TN>(p, st.ic);
+  if (st.ic.valid) {
+    issue_tile<D, SEG>(st.ti[S], k.kbase0, k.vbase0, k.sbase0, k.rs_bytes, k.wave, k.lane,
+                       k.k_lane, k.v_lane, ks[S], vs[S], ss[S]);
+    cursor_next<PipeCfg<D>::TN>(p, st.ic, k.kend);
+  }
+}
 
 // One pipeline step: tile i lives in stage PH, tile i+1 in stage PH+1, the
 // DMA for tile i+3 goes into stage PH+3 (all mod 4).  Returns whether a next
@@ -487,28 +547,24 @@ __device__ __forceinline__ bool pipe_step(const FwdParams& p, const PipeConst& k
                                           PipeState<D>& st, __bf16* const* ks,
                                           __bf16* const* vs, int32_t* const* ss) {
   constexpr int NPT = 2 * PipeCfg<D>::DPW + (SEG ? 1 : 0);  // DMA per wave per tile
-  constexpr int S0 = PH, S1 = (PH + 1) & 3, S3 = (PH + 3) & 3;
-  const bool have3 = st.c3.valid;
-  if (have3)
-    issue_tile<D, SEG>(p, st.c3, k.kbase0, k.vbase0, k.sbase0, k.rs, k.rs_bytes, k.wave, k.lane,
-                       k.k_lane, k.v_lane, ks[S3], vs[S3], ss[S3]);
+  constexpr int S0 = PH, S1 = (PH + 1) & 3, S2 = (PH + 2) & 3, S3 = (PH + 3) & 3;
+  fetch_next<D, SEG, S3>(p, k, st, ks, vs, ss);
 
-  const TileFlags f0 = tile_flags<SEG>(p, st.c0, lim, k.wave_active);
-  const bool have1 = st.c1.valid;
-  TileFlags f1{false, false, false, false, 0, 0};
-  if (have1) f1 = tile_flags<SEG>(p, st.c1, lim, k.wave_active);
+  const TileFlags f0 = tile_flags<SEG>(st.ti[S0], lim);
+  const TileFlags f1 = tile_flags<SEG>(st.ti[S1], lim);
 
   // Tile i (logits in s_cur, already masked and max-folded): probabilities and
   // P.V.  Tile i+1: logits and row max.  Both 32-key halves of both tiles
   // are always computed, so this is one straight-line block for every step;
   // a half without a visible pair is masked to -inf and contributes exactly 0
   // (its keys in LDS are real keys or zeros, never undefined).
-  f32x16_t s_next[2];
+  f32x16_t* const s_cur = st.s[PH & 1];
+  f32x16_t* const s_next = st.s[(PH + 1) & 1];
   float mx = ninf();
   const bool any0 = f0.run0 || f0.run1, any1 = f1.run0 || f1.run1;
   if (any0 || any1) {
     qk_tile<D>(s_next, qf, ks[S1], k.k_rd);
-    exp_pv<D>(st.w, st.s_cur, vs[S0], k.v_rd, p.scale_log2);
+    exp_pv<D>(st.w, s_cur, vs[S0], k.v_rd, p.scale_log2);
     mx = mask_max<false, false>(s_next, nullptr, k.half, f1, lim.lane_lim, k.seg_q);
     step_schedule<D>();
     if (SEG || !(f1.run0 && f1.run1) || f1.mask0 || f1.mask1) {
@@ -518,8 +574,10 @@ __device__ __forceinline__ bool pipe_step(const FwdParams& p, const PipeConst& k
       mx = mask_max<true, SEG>(s_next, ss[S1], k.half, f1, lim.lane_lim, k.seg_q);
     }
     if (p.run_map != nullptr && k.lane == 0) {
-      if (f0.run0) write_run_map(p, st.c0.t, k.qg0, f0.kloc0);
-      if (f0.run1) write_run_map(p, st.c0.t, k.qg0, f0.kloc0 + 32);
+      const TileInfo& t0 = st.ti[S0];
+      const int kloc0 = t0.pk - t0.kb * p.seq_q;
+      if (f0.run0) write_run_map(p, t0.t, k.qg0, kloc0);
+      if (f0.run1) write_run_map(p, t0.t, k.qg0, kloc0 + 32);
     }
   } else {
     s_next[0] = f32x16_t{} - __builtin_inff();
@@ -528,21 +586,14 @@ __device__ __forceinline__ bool pipe_step(const FwdParams& p, const PipeConst& k
   if (k.wave_active) carry_max<D>(st.w, mx, p.scale_log2);
 
   // Tile i+2 must have landed (for every wave) before the next step reads it.
-  if (st.c2.valid) {
-    if (have3)
+  if (st.ti[S2].valid) {
+    if (st.ti[S3].valid)
       wait_vm<NPT>();
     else
       wait_vm<0>();
   }
   stage_barrier();
-
-  st.s_cur[0] = s_next[0];
-  st.s_cur[1] = s_next[1];
-  st.c0 = st.c1;
-  st.c1 = st.c2;
-  st.c2 = st.c3;
-  if (have3) cursor_next<64>(p, st.c3, k.kend);
-  return st.c0.valid;
+  return st.ti[S1].valid;
 }
 
 template <int D, bool SEG>
@@ -572,15 +623,15 @@ __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const
   k.qg0 = m0 + k.wave * 32;
   k.wave_active = k.qg0 < p.seq_q;
   const int64_t pq_first = (int64_t)p.ring_index * p.seq_q + k.qg0;
-  const WaveLimits lim = wave_limits(p, pq_first, k.lrow);
+  const WaveLimits lim = wave_limits(p, pq_first, k.lrow, k.wave_active);
   k.kend = wg_kend<kBlockMBf16>(p, m0);
   k.seg_q = 0;
   if (SEG && k.wave_active) k.seg_q = p.seg[(int64_t)b * p.seq_k + pq_first + k.lrow];
 
-  k.rs = (int64_t)p.heads * D;
-  k.rs_bytes = (uint32_t)(k.rs * 2);
-  k.kbase0 = static_cast<const __bf16*>(p.k) + (int64_t)b * p.seq_k * k.rs + (int64_t)h * D;
-  k.vbase0 = static_cast<const __bf16*>(p.v) + (int64_t)b * p.seq_k * k.rs + (int64_t)h * D;
+  const int64_t rs = (int64_t)p.heads * D;
+  k.rs_bytes = (uint32_t)(rs * 2);
+  k.kbase0 = static_cast<const char*>(p.k) + ((int64_t)b * p.seq_k * rs + (int64_t)h * D) * 2;
+  k.vbase0 = static_cast<const char*>(p.v) + ((int64_t)b * p.seq_k * rs + (int64_t)h * D) * 2;
   k.sbase0 = SEG ? p.seg + (int64_t)b * p.seq_k : nullptr;
   k.k_lane = (uint32_t)(k.lane & 15) * k.rs_bytes + 16u * (uint32_t)(k.lane >> 4);
   k.v_lane = (uint32_t)(k.lane >> 2) * k.rs_bytes + 16u * (uint32_t)(k.lane & 3);
@@ -594,7 +645,7 @@ __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const
   bf16x8_t qf[D / 16];
   if (k.wave_active) {
     const __bf16* qrow = static_cast<const __bf16*>(p.q) +
-                         ((int64_t)b * p.seq_q + k.qg0 + k.lrow) * k.rs + (int64_t)h * D;
+                         ((int64_t)b * p.seq_q + k.qg0 + k.lrow) * rs + (int64_t)h * D;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
       qf[c] = __builtin_bit_cast(bf16x8_t,
@@ -610,39 +661,27 @@ __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const
   st.w.m_run = ninf();
   st.w.l_run = 0.f;
 
-  // Prologue: tiles 0, 1, 2 in flight; tile 3's cursor ready.
-  st.c0 = Cursor{0, 0, 0, 0, 0, 0};
-  cursor_seek<64>(p, st.c0, k.kend);
-  st.c1 = st.c0;
-  if (st.c1.valid) cursor_next<64>(p, st.c1, k.kend);
-  st.c2 = st.c1;
-  if (st.c2.valid) cursor_next<64>(p, st.c2, k.kend);
-  st.c3 = st.c2;
-  if (st.c3.valid) cursor_next<64>(p, st.c3, k.kend);
-  constexpr int NPT = 2 * C::DPW + (SEG ? 1 : 0);
-  if (st.c0.valid)
-    issue_tile<D, SEG>(p, st.c0, k.kbase0, k.vbase0, k.sbase0, k.rs, k.rs_bytes, k.wave, k.lane,
-                       k.k_lane, k.v_lane, ks[0], vs[0], ss[0]);
-  if (st.c1.valid)
-    issue_tile<D, SEG>(p, st.c1, k.kbase0, k.vbase0, k.sbase0, k.rs, k.rs_bytes, k.wave, k.lane,
-                       k.k_lane, k.v_lane, ks[1], vs[1], ss[1]);
-  if (st.c2.valid)
-    issue_tile<D, SEG>(p, st.c2, k.kbase0, k.vbase0, k.sbase0, k.rs, k.rs_bytes, k.wave, k.lane,
-                       k.k_lane, k.v_lane, ks[2], vs[2], ss[2]);
+  // Prologue: tiles 0, 1, 2 in flight, the cursor on tile 3.
+  st.ic = Cursor{0, 0, 0, 0, 0, 0};
+  cursor_seek<C::TN>(p, st.ic, k.kend);
+  fetch_next<D, SEG, 0>(p, k, st, ks, vs, ss);
+  fetch_next<D, SEG, 1>(p, k, st, ks, vs, ss);
+  fetch_next<D, SEG, 2>(p, k, st, ks, vs, ss);
   // Tiles 0 and 1 must have landed: tile 1 is read by the first step's QK.
-  if (st.c2.valid)
+  constexpr int NPT = 2 * C::DPW + (SEG ? 1 : 0);
+  if (st.ti[2].valid)
     wait_vm<NPT>();
   else
     wait_vm<0>();
   stage_barrier();
-  if (st.c0.valid && k.wave_active) {
-    const TileFlags f = tile_flags<SEG>(p, st.c0, lim, k.wave_active);
-    qk_tile<D>(st.s_cur, qf, ks[0], k.k_rd);
-    const float mx = mask_max<true, SEG>(st.s_cur, ss[0], k.half, f, lim.lane_lim, k.seg_q);
+  if (st.ti[0].valid && k.wave_active) {
+    const TileFlags f = tile_flags<SEG>(st.ti[0], lim);
+    qk_tile<D>(st.s[0], qf, ks[0], k.k_rd);
+    const float mx = mask_max<true, SEG>(st.s[0], ss[0], k.half, f, lim.lane_lim, k.seg_q);
     carry_max<D>(st.w, mx, p.scale_log2);
   }
 
-  if (st.c0.valid) {
+  if (st.ti[0].valid) {
     for (;;) {
       if (!pipe_step<D, SEG, 0>(p, k, lim, qf, st, ks, vs, ss)) break;
       if (!pipe_step<D, SEG, 1>(p, k, lim, qf, st, ks, vs, ss)) break;
@@ -653,10 +692,10 @@ __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const
 
   // ---- epilogue: out = numerator / denominator, lse = ln(denominator) + max ----
   if (!k.wave_active) return;
-  const float l_tot = st.w.l_run + __shfl_xor(st.w.l_run, 32);
+  const float l_tot = pair_sum(st.w.l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int row = k.qg0 + k.lrow;
-  __bf16* orow = static_cast<__bf16*>(p.out) + ((int64_t)b * p.seq_q + row) * k.rs + (int64_t)h * D;
+  __bf16* orow = static_cast<__bf16*>(p.out) + ((int64_t)b * p.seq_q + row) * rs + (int64_t)h * D;
 #pragma unroll
   for (int j = 0; j < NDB; ++j) {
 #pragma unroll
@@ -704,7 +743,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(const FwdParams p)
   const int qg0 = m0 + wave * 32;
   const bool wave_active = qg0 < p.seq_q;
   const int64_t pq_first = (int64_t)p.ring_index * p.seq_q + qg0;
-  const WaveLimits lim = wave_limits(p, pq_first, lrow);
+  const WaveLimits lim = wave_limits(p, pq_first, lrow, wave_active);
   const int64_t kend = wg_kend<kBlockMF32>(p, m0);
   const bool has_seg = p.seg != nullptr;
   int32_t seg_q = 0;
@@ -767,9 +806,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(const FwdParams p)
     if (nxt.valid) load_tile(nxt);
 
     const int kloc0 = cur.kt * TN;
-    const int64_t pk0 = (int64_t)cur.kb * p.seq_q + kloc0;
-    const bool run = wave_active && pk0 < lim.run_lim;
-    const bool mask = has_seg || !(pk0 + 31 < lim.full_lim);
+    const int32_t pk0 = cur.kb * p.seq_q + kloc0;
+    const bool run = pk0 < lim.run_lim;
+    const bool mask = has_seg || pk0 >= lim.mask_lim;
     if (run) {
       const float* ks = k_lds[buf];
       const float* vs = v_lds[buf];
@@ -781,7 +820,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(const FwdParams p)
         s = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * c], qf[c], s, 0, 0, 0);
 
       if (mask) {
-        const int32_t pkb = (int32_t)pk0 + 4 * half;
+        const int32_t pkb = pk0 + 4 * half;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int koff = 8 * (i >> 2) + (i & 3);
