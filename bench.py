@@ -2,9 +2,11 @@
 
 One step = one forward of a device's whole ring share (every KV block in
 ring order, skipping, softmax carry, normalisation, lse) through the C ABI,
-on the 7B-shaped share: batch 1, 32 heads, head_dim 128, bf16, local query
-block 32768 at ring position 15 of 16 (512K context), token causal, chunks
-2048.  Inputs are seeded Gaussian tensors already resident in HBM.
+by default on the 7B-shaped share: batch 1, 32 heads, head_dim 128, bf16,
+local query block 32768 at ring position 15 of 16 (512K context), token
+causal, chunks 2048.  ``--workload`` times another bf16 workload instead (a
+step is then one call per ring position the workload lists).  Inputs are
+seeded Gaussian tensors already resident in HBM.
 
 Prints one JSON line with the causal-adjusted TFLOP/s, the roofline of the
 kernel (MFMA bound, bf16 dense peak) and the CPU oracle timed on a bounded
@@ -14,7 +16,6 @@ sample of the same workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -28,7 +29,6 @@ if ROOT not in sys.path:
 
 WORKLOAD = "share_7b_512k"
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA
-KERNEL_SRC = os.path.join(ROOT, "long_context_exact_ra_amd", "csrc", "blockwise_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "blockwise_fwd_share_7b_512k_traffic.json")
 
 
@@ -49,28 +49,37 @@ def causal_flops(w, ring_index: int) -> float:
     return 4.0 * w.head_dim * w.heads * w.batch * n
 
 
-def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
-
-
-def measured_traffic():
+def measured_traffic(build_id: str):
     """HBM bytes per launch measured with rocprofv3 counters, valid only for
-    the kernel source they were taken on."""
+    the kernel build they were taken on (the build id the loaded library
+    reports, a hash of its device sources)."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sha256_16") != kernel_hash():
+    if t.get("kernel_sha256_16") != build_id:
         return None
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, q, k, v, ring_index: int, rows: int):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
+def cpu_baseline(w, q, k, v, seg, ring_index: int, rows: int, flops_total: float):
     """The CPU oracle, as it stands, on a bounded sample: one head and
     ``rows`` query rows of the same workload (each row over all its visible
-    keys).  Rate in the metric's unit (causal-adjusted TFLOP/s)."""
+    keys).  Rate in the metric's unit (causal-adjusted TFLOP/s); the sample
+    text also gives the oracle's time for the whole step, extrapolated
+    linearly (rows are independent)."""
     import oracle
     import torch
     head = 0
@@ -78,26 +87,30 @@ def cpu_baseline(w, q, k, v, ring_index: int, rows: int):
     kv_len = w.seq_k if not w.causal_block_size else int(
         min(w.seq_k, ((ring_index * w.seq_q + w.seq_q - 1) // w.causal_block_size + 1)
             * w.causal_block_size))
-    qh = q[:, :, head:head + 1].contiguous().cpu()
-    kh = k[:, :kv_len, head:head + 1].contiguous().cpu()
-    vh = v[:, :kv_len, head:head + 1].contiguous().cpu()
+    qh = q[:1, :, head:head + 1].contiguous().cpu()
+    kh = k[:1, :kv_len, head:head + 1].contiguous().cpu()
+    vh = v[:1, :kv_len, head:head + 1].contiguous().cpu()
+    segh = None if seg is None else seg[:1].cpu().numpy()
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover - informational only
         cores = torch.get_num_threads()
     t0 = time.perf_counter()
-    oracle.attention_fwd(qh, kh, vh, None, w.causal_block_size, w.ring_size, ring_index,
+    oracle.attention_fwd(qh, kh, vh, segh, w.causal_block_size, w.ring_size, ring_index,
                          rows=sel, kv_len=kv_len)
     dt = time.perf_counter() - t0
     pairs = int(visible_keys_per_row(w.seq_q, w.ring_size, ring_index,
                                      w.causal_block_size)[sel].sum())
     flops = 4.0 * w.head_dim * pairs
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+    rate = flops / dt
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": f"{WORKLOAD}: head 0, {rows} query rows spread over the block, "
-                      f"each over its {kv_len}-key visible range; numpy fp64; "
-                      f"{dt:.1f} s for {flops / 1e9:.1f} GFLOP"}
+            "sample": f"{w.name}: batch entry 0, head 0, {rows} query rows spread over the block of ring "
+                      f"position {ring_index}, each over its {kv_len}-key visible range; numpy "
+                      f"fp64 on {cpu_model()}; {dt:.1f} s for {flops / 1e9:.1f} GFLOP; the whole "
+                      f"step would take {flops_total / rate / 3600:.1f} h at this rate "
+                      f"(linear extrapolation)"}
 
 
 def main():
@@ -107,6 +120,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="query rows of the CPU oracle sample (0 = skip)")
+    ap.add_argument("--workload", default=WORKLOAD,
+                    choices=["small_causal", "share_7b_512k", "packed_documents", "share_65b_4m"],
+                    help="bf16 workload to time (default: the 7B-shaped share)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first; its "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate HBM byte counts")
@@ -127,10 +143,12 @@ def main():
         sys.exit(1)
     ra.load_library()
     dev = torch.device("cuda:0")
-    w = workloads.get(WORKLOAD)
+    w = workloads.get(args.workload)
     r = w.ring_indices[0]
-    print(f"[bench] generating {WORKLOAD} inputs", file=sys.stderr, flush=True)
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     q, k, v = workloads.make_qkv(w, r, device=dev)
+    qs = [q] + [workloads.make_q(w, ri, device=dev) for ri in w.ring_indices[1:]]
+    seg = workloads.make_segments(w, device=dev)
     out = torch.empty_like(q)
     lse = torch.empty((w.batch, w.heads, w.seq_q), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
@@ -144,8 +162,9 @@ def main():
         del src, dst
 
     def step():
-        ra.blockwise_attn_fwd(q, k, v, None, w.causal_block_size, w.q_chunk, w.k_chunk,
-                              w.ring_size, r, out=out, lse=lse)
+        for ri, qi in zip(w.ring_indices, qs):
+            ra.blockwise_attn_fwd(qi, k, v, seg, w.causal_block_size, w.q_chunk, w.k_chunk,
+                                  w.ring_size, ri, out=out, lse=lse)
 
     for _ in range(args.warmup):
         step()
@@ -167,9 +186,10 @@ def main():
     if not (torch.isfinite(out).all() and torch.isfinite(lse).all()):
         raise RuntimeError("non-finite output")
 
-    flops = causal_flops(w, r)
+    flops = sum(causal_flops(w, ri) for ri in w.ring_indices)
     tflops = flops / (ms * 1e-3) / 1e12
-    traffic = measured_traffic()
+    build_id = ra.version().split("+", 1)[-1]
+    traffic = measured_traffic(build_id) if w.name == WORKLOAD else None
     rec = {
         "metric": "causal-adjusted attention TFLOP/s per MI355X (% of bf16 MFMA peak in roofline.frac)",
         "value": round(tflops, 2),
@@ -182,9 +202,12 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic: seeded N(0,1) Q/K/V, bf16",
-        "config": {"workload": WORKLOAD, "batch": w.batch, "seq_q": w.seq_q,
-                   "ring_size": w.ring_size, "ring_index": r, "context": w.seq_k,
+        "data": f"synthetic: seeded Gaussian Q/K/V (std {w.std:g}), bf16"
+                + (", Geometric document lengths as segment ids" if w.segments else ""),
+        "config": {"workload": w.name, "batch": w.batch, "seq_q": w.seq_q,
+                   "ring_size": w.ring_size,
+                   "ring_index": r if len(w.ring_indices) == 1 else list(w.ring_indices),
+                   "context": w.seq_k, "segments": bool(w.segments),
                    "heads": w.heads, "head_dim": w.head_dim,
                    "causal_block_size": w.causal_block_size,
                    "q_chunk": w.q_chunk, "k_chunk": w.k_chunk,
@@ -197,7 +220,7 @@ def main():
     }
     if args.cpu_rows > 0:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, r, args.cpu_rows)
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, seg, r, args.cpu_rows, flops)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

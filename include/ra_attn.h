@@ -141,7 +141,9 @@ ra_status_t ra_blockwise_plan(int64_t causal_block_size, int64_t q_chunk,
  * stays valid until the next ra_* call on the same thread. */
 const char* ra_last_error(void);
 
-/* Library version as "major.minor.patch" (static storage). */
+/* Library version as "major.minor.patch+build" (static storage); build is
+ * the first 16 hex digits of the SHA-256 of the device sources the library
+ * was compiled from. */
 const char* ra_version(void);
 
 #ifdef __cplusplus

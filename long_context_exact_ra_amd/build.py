@@ -7,6 +7,7 @@ Packed-FP32 VALU instructions are disabled for all device code.
 
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -37,12 +38,24 @@ def _run(cmd, verbose):
     subprocess.run(cmd, check=True)
 
 
+def device_sources_sha16() -> str:
+    """First 16 hex digits of the SHA-256 over the device sources (the .hip
+    files, in name order): the build id ``ra_version()`` reports after "+"."""
+    h = hashlib.sha256()
+    for src in sorted(os.listdir(CSRC)):
+        if src.endswith(".hip"):
+            with open(os.path.join(CSRC, src), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def build(verbose: bool = True) -> str:
     """Compile every source and link ``libra_attn.so``; returns its path."""
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     os.makedirs(BUILD, exist_ok=True)
     cxx = shutil.which("g++") or "g++"
+    build_id = f'-DRA_BUILD_ID="{device_sources_sha16()}"'
     objs = []
     for src in sorted(os.listdir(CSRC)):
         path = os.path.join(CSRC, src)
@@ -50,7 +63,7 @@ def build(verbose: bool = True) -> str:
         if src.endswith(".hip"):
             _run([HIPCC, *HIP_FLAGS, "-c", path, "-o", obj], verbose)
         elif src.endswith(".cpp"):
-            _run([cxx, *CXX_FLAGS, "-c", path, "-o", obj], verbose)
+            _run([cxx, *CXX_FLAGS, build_id, "-c", path, "-o", obj], verbose)
         else:
             continue
         objs.append(obj)

@@ -70,7 +70,13 @@ extern "C" {
 
 const char* ra_last_error(void) { return g_err; }
 
-const char* ra_version(void) { return "0.1.0"; }
+// "+<id>": the first 16 hex digits of the SHA-256 of the device sources the
+// library was built from (set by the build script), so a measurement can be
+// tied to the exact kernel that produced it.
+#ifndef RA_BUILD_ID
+#define RA_BUILD_ID "unknown"
+#endif
+const char* ra_version(void) { return "0.1.0+" RA_BUILD_ID; }
 
 ra_status_t ra_blockwise_plan(int64_t causal_block_size, int64_t q_chunk, int64_t k_chunk,
                               int64_t seq_q, int32_t ring_size, int32_t ring_index,

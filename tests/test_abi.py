@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_error_string():
-    assert re.fullmatch(r"\d+\.\d+\.\d+", ra.version())
+    assert re.fullmatch(r"\d+\.\d+\.\d+\+[0-9a-f]{16}", ra.version())
     assert isinstance(ra.last_error(), str)
 
 

@@ -121,6 +121,12 @@ def make_block(shape: Sequence[int], seed: int, std: float, dtype: str,
     return x.to(_dtype(dtype))
 
 
+def make_q(w: Workload, ring_index: int, device="cpu"):
+    """Q for ring position ``ring_index`` alone (the same draw as make_qkv)."""
+    return make_block((w.batch, w.seq_q, w.heads, w.head_dim),
+                      block_seed(w.seed, "q", ring_index), w.std, w.dtype, device)
+
+
 def make_qkv(w: Workload, ring_index: int, device="cpu",
              kv_blocks: Optional[Sequence[int]] = None):
     """Q for ring position ``ring_index`` and K, V for the whole ring.
@@ -131,8 +137,7 @@ def make_qkv(w: Workload, ring_index: int, device="cpu",
     """
     torch = _torch()
     B, Lq, H, D = w.batch, w.seq_q, w.heads, w.head_dim
-    q = make_block((B, Lq, H, D), block_seed(w.seed, "q", ring_index), w.std,
-                   w.dtype, device)
+    q = make_q(w, ring_index, device)
     k = torch.empty((B, w.seq_k, H, D), dtype=_dtype(w.dtype), device=device)
     v = torch.empty_like(k)
     blocks = set(range(w.ring_size) if kv_blocks is None else kv_blocks)
