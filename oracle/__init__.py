@@ -16,3 +16,4 @@ from .attention import (  # noqa: F401
     skip_map_closed,
     visible,
 )
+from .backward import attention_bwd  # noqa: F401
