@@ -119,6 +119,51 @@ ra_status_t ra_blockwise_attn_fwd_ex(const void* q, const void* k,
                                      void* stream);
 
 /*
+ * ra_blockwise_attn_bwd -- the gradients of one ring position's share.
+ *
+ * For the forward of ra_blockwise_attn_fwd with the same q, k, v,
+ * segment_ids and masks, and an upstream gradient dout of its output,
+ * computes the gradients of sum(dout * out).  The pages pair the ring
+ * forward with a backward pass but print no backward equations; these are
+ * the exact derivatives of the attention definition ("Ring Attention with
+ * Blockwise Transformers for Near-Infinite Context", section 三, the
+ * self-attention equation): with p_ij the softmax weights of the forward,
+ *   delta_i = sum_d dout_i,d * out_i,d,
+ *   ds_ij   = p_ij * (dout_i . v_j - delta_i),
+ *   dq_i    = (1/sqrt(D)) sum_j ds_ij k_j,
+ *   dk_j    = (1/sqrt(D)) sum_i ds_ij q_i,   dv_j = sum_i p_ij dout_i.
+ *
+ *   out, lse: the forward's outputs for these inputs (layouts as above);
+ *       p_ij is recomputed from q, k and lse.
+ *   dout: [batch, seq_q, heads, head_dim] dtype.
+ *   dq: [batch, seq_q, heads, head_dim] float32, written.
+ *   dk, dv: [batch, ring_size * seq_q, heads, head_dim] float32, written:
+ *       this share's contribution to the gradients of all N key/value
+ *       blocks (in the ring, the addend this device puts into the dK/dV
+ *       blocks as they pass); keys that no local query sees get 0.
+ *   delta: [batch, heads, seq_q] float32, written (the row terms above).
+ *
+ * Arithmetic: the scores, p and ds are float32; p and ds are rounded to
+ * bf16 (round to nearest even) as operands of the bf16 matrix products,
+ * which accumulate in float32.
+ *
+ * Errors as for ra_blockwise_attn_fwd, plus RA_E_INVALID for a null out,
+ * lse, dout, dq, dk, dv or delta, and RA_E_UNSUPPORTED for RA_F32 (the
+ * backward takes bf16 inputs only).  Ownership, streams and threading as
+ * for the forward.
+ */
+ra_status_t ra_blockwise_attn_bwd(const void* q, const void* k, const void* v,
+                                  const int32_t* segment_ids,
+                                  int64_t causal_block_size, int64_t q_chunk,
+                                  int64_t k_chunk, int32_t ring_size,
+                                  int32_t ring_index, int64_t batch,
+                                  int64_t seq_q, int64_t heads,
+                                  int64_t head_dim, ra_dtype_t dtype,
+                                  const void* out, const float* lse,
+                                  const void* dout, float* dq, float* dk,
+                                  float* dv, float* delta, void* stream);
+
+/*
  * ra_blockwise_plan -- host-only: the ring order and the chunk-pair skip
  * decisions for one ring position, without touching a GPU.
  *

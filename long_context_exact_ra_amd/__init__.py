@@ -1,4 +1,5 @@
-"""Blockwise exact-attention forward of Ring Attention on MI355X (gfx950).
+"""Blockwise exact attention of Ring Attention on MI355X (gfx950): the
+forward of one device's ring share and its backward.
 
 A thin ctypes binding over the C ABI in ``include/ra_attn.h`` (library
 ``libra_attn.so`` next to this file).  It only marshals arguments: every
@@ -13,7 +14,7 @@ import ctypes
 import os
 from typing import Optional, Tuple
 
-__all__ = ["RaError", "blockwise_attn_fwd", "blockwise_plan", "last_error", "lib_path",
+__all__ = ["RaError", "blockwise_attn_fwd", "blockwise_attn_bwd", "blockwise_plan", "last_error", "lib_path",
            "load_library", "version", "RA_OK", "RA_E_INVALID", "RA_E_UNSUPPORTED",
            "RA_E_HIP", "RA_BF16", "RA_F32"]
 
@@ -52,6 +53,8 @@ def load_library():
     lib.ra_blockwise_attn_fwd.restype = ctypes.c_int
     lib.ra_blockwise_attn_fwd_ex.argtypes = fwd_args + [c_vp, c_vp]
     lib.ra_blockwise_attn_fwd_ex.restype = ctypes.c_int
+    lib.ra_blockwise_attn_bwd.argtypes = fwd_args[:14] + [c_vp] * 8
+    lib.ra_blockwise_attn_bwd.restype = ctypes.c_int
     lib.ra_blockwise_plan.argtypes = [c_i64, c_i64, c_i64, c_i64, c_i32, c_i32,
                                       c_vp, c_vp, c_vp]
     lib.ra_blockwise_plan.restype = ctypes.c_int
@@ -156,3 +159,58 @@ def blockwise_attn_fwd(q, k, v, segment_ids=None, causal_block_size: Optional[in
     else:
         _check(lib.ra_blockwise_attn_fwd(*args, sptr))
     return out, lse
+
+
+def blockwise_attn_bwd(q, k, v, out, lse, dout, segment_ids=None,
+                       causal_block_size: Optional[int] = None, q_chunk: int = 512,
+                       k_chunk: int = 512, ring_size: int = 1, ring_index: int = 0, *,
+                       dq=None, dk=None, dv=None, delta=None, stream=None):
+    """Backward of ring position ``ring_index``: returns (dq, dk, dv, delta).
+
+    q, k, v, segment_ids and the mask arguments as for blockwise_attn_fwd
+    (bfloat16 only); out and lse are that forward's outputs and dout the
+    upstream gradient of out ([B, Lq, H, D], bfloat16).  dq [B, Lq, H, D],
+    dk, dv [B, ring_size * Lq, H, D] and delta [B, H, Lq] are float32 and
+    allocated when not given; dk and dv hold this share's contribution.
+    """
+    import torch
+    lib = load_library()
+    if q.dtype != torch.bfloat16:
+        raise TypeError("the backward takes bfloat16 inputs")
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-D bfloat16 device tensor")
+    B, Lq, H, D = q.shape
+    S = ring_size * Lq
+    if tuple(k.shape) != (B, S, H, D) or k.shape != v.shape:
+        raise ValueError(f"k/v shape {tuple(k.shape)} != {(B, S, H, D)}")
+    if out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("out and dout must have q's shape")
+    if (tuple(lse.shape) != (B, H, Lq) or lse.dtype != torch.float32 or not lse.is_cuda
+            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 device tensor [B, H, Lq]")
+    seg_ptr = None
+    if segment_ids is not None:
+        if (segment_ids.dtype != torch.int32 or not segment_ids.is_cuda
+                or not segment_ids.is_contiguous() or tuple(segment_ids.shape) != (B, S)):
+            raise ValueError("segment_ids must be a contiguous int32 device tensor [B, S]")
+        seg_ptr = segment_ids.data_ptr()
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty((B, Lq, H, D), **f32) if dq is None else dq
+    dk = torch.empty((B, S, H, D), **f32) if dk is None else dk
+    dv = torch.empty((B, S, H, D), **f32) if dv is None else dv
+    delta = torch.empty((B, H, Lq), **f32) if delta is None else delta
+    for name, t, shape in (("dq", dq, (B, Lq, H, D)), ("dk", dk, (B, S, H, D)),
+                           ("dv", dv, (B, S, H, D)), ("delta", delta, (B, H, Lq))):
+        if (tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_cuda
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 device tensor {shape}")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    _check(lib.ra_blockwise_attn_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), seg_ptr, int(causal_block_size or 0),
+        q_chunk, k_chunk, ring_size, ring_index, B, Lq, H, D, RA_BF16,
+        out.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+        dv.data_ptr(), delta.data_ptr(), sptr))
+    return dq, dk, dv, delta

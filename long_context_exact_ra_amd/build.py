@@ -40,10 +40,11 @@ def _run(cmd, verbose):
 
 def device_sources_sha16() -> str:
     """First 16 hex digits of the SHA-256 over the device sources (the .hip
-    files, in name order): the build id ``ra_version()`` reports after "+"."""
+    files and the headers they include, in name order): the build id
+    ``ra_version()`` reports after "+"."""
     h = hashlib.sha256()
     for src in sorted(os.listdir(CSRC)):
-        if src.endswith(".hip"):
+        if src.endswith((".hip", ".h")):
             with open(os.path.join(CSRC, src), "rb") as f:
                 h.update(f.read())
     return h.hexdigest()[:16]

@@ -1,0 +1,606 @@
+// Backward of the blockwise exact attention for one Ring Attention device
+// share, written for gfx950 (MI355X, CDNA4), bf16 inputs.
+//
+// The pages pair the ring forward with a backward pass but print no
+// backward equations ("Ring Attention with Blockwise Transformers for
+// Near-Infinite Context", section 三, the self-attention equation; the
+// blockwise code of "从论文到代码：深入理解RingAttention的块注意力计算逻辑").
+// These kernels compute the exact derivatives of the attention definition,
+// with p_ij recomputed from the forward's lse:
+//
+//   delta_i = <dout_i, out_i>
+//   p_ij    = exp(scale <q_i, k_j> - lse_i)        (0 where j is invisible)
+//   ds_ij   = p_ij (<dout_i, v_j> - delta_i)
+//   dq_i    = scale sum_j ds_ij k_j
+//   dk_j    = scale sum_i ds_ij q_i,   dv_j = sum_i p_ij dout_i
+//
+// Three launches:
+//   bwd_delta_kernel   delta (one pass over dout and out);
+//   bwd_dq_kernel      query-stationary, like the forward: a workgroup owns
+//                      256 query rows and walks the key tiles in ring order
+//                      (block (r - t) mod N at step t), K and V tiles
+//                      arriving by buffer-to-LDS DMA through a 4-stage ring;
+//   bwd_dkdv_kernel    key-stationary: a workgroup owns 256 keys (K of each
+//                      wave in registers, V resident in LDS) and streams the
+//                      query tiles that can see them (Q, dout, segment ids,
+//                      lse and delta) through two LDS stages.
+// Both main kernels recompute the scores and dp, so a visible pair costs
+// 7 matrix products here against the 5 of the algorithm; every result is
+// written exactly once (no atomics), so dk and dv of keys no local query
+// sees come out as 0.
+//
+// MFMA orientation (v_mfma_f32_32x32x16_bf16; A[m][k] lane l row m = l % 32,
+// k-slots 8 (l / 32) .. +7; B[k][n] lane l column n = l % 32; C[m][n] lane l
+// column n = l % 32, rows 8 (i / 4) + 4 (l / 32) + i % 4):
+//   dq kernel:   S^T = K Q^T and dP^T = V dO^T (keys = M, queries = N), so
+//                a lane holds one query row and its lse and delta are
+//                per-lane scalars; dQ^T += K^T dS^T takes dS^T straight from
+//                the C registers and K^T from transposing LDS reads of the
+//                same K tile, with the same key-to-slot assignment.
+//   dkdv kernel: S = Q K^T and dP = dO V^T (queries = M, keys = N), so a
+//                lane holds one key; dV^T += dO^T P and dK^T += Q^T dS take P
+//                and dS from the C registers and dO^T, Q^T from transposing
+//                LDS reads of the Q and dO tiles.
+// All tiles use one LDS layout (16-byte slots, r = row, g = 16-byte granule
+// of the row): slot(r, g) = (g / 4) * 256 + (r / 16) * 64 + (g % 4) * 16 +
+// r % 16, read as rows by ds_read_b128 and as columns by ds_read_b64_tr_b16.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <climits>
+#include <cstdio>
+#include <type_traits>
+
+#include "ra_device.h"
+#include "ra_internal.h"
+
+namespace ra {
+namespace {
+
+constexpr int kWaves = 8;                 // waves per workgroup (both main kernels)
+constexpr int kThreadsBwd = 64 * kWaves;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Element offsets inside a 64-row tile stored in the layout above.
+// Row operand: lane l reads row 32 * blk + l % 32, columns 16 c + 8 (l / 32)
+// .. +7 (the A operand of a 16-column k-step).
+__device__ __forceinline__ int row_rd(int lane) {
+  const int lrow = lane & 31, half = lane >> 5;
+  return 512 * (lrow >> 4) + 128 * half + 8 * (lrow & 15);
+}
+__device__ __forceinline__ constexpr int row_off(int c, int blk) {
+  return 2048 * (c >> 1) + 256 * (c & 1) + 1024 * blk;
+}
+// Column operand by ds_read_b64_tr_b16: in each 16-lane group, lane j reads
+// 4 values of tile row 4 (g / 2) + j / 4 (+8 for the high half) at columns
+// 32 jb + 16 (g % 2) + 4 (j % 4); after the transpose, lane l holds for its
+// column 32 jb + l % 32 the 8 tile rows of the k-slots of its lane half.
+__device__ __forceinline__ int col_rd(int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int r0 = 4 * (g >> 1) + (j >> 2);
+  return ((2 * (g & 1) + ((j >> 1) & 1)) * 16 + r0) * 8 + 4 * (j & 1);
+}
+// jb = 32-column block, rb = 16-row block of the tile (its k-step).
+__device__ __forceinline__ constexpr int col_off(int jb, int rb) { return 2048 * jb + 512 * rb; }
+
+__device__ __forceinline__ bf16x8_t col_operand(const __bf16* tile, int rd, int jb, int rb) {
+  const __bf16* src = tile + rd + col_off(jb, rb);
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)src);
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(src + 64));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ bf16x8_t row_operand(const __bf16* tile, int rd, int c, int blk) {
+  return *reinterpret_cast<const bf16x8_t*>(tile + rd + row_off(c, blk));
+}
+
+__device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// delta_i = <dout_i, out_i>
+// ---------------------------------------------------------------------------
+
+// 16 lanes per row of D = 128 (8 for D = 64), 8 bf16 values each.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const BwdParams bp) {
+  constexpr int LPR = D / 8;  // lanes per row
+  const FwdParams& p = bp.f;
+  const int64_t rows = (int64_t)p.batch * p.seq_q * p.heads;
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR;
+  const int part = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const __bf16* o = static_cast<const __bf16*>(bp.out) + row * D + part * 8;
+    const __bf16* g = static_cast<const __bf16*>(bp.dout) + row * D + part * 8;
+    const bf16x8_t ov = *reinterpret_cast<const bf16x8_t*>(o);
+    const bf16x8_t gv = *reinterpret_cast<const bf16x8_t*>(g);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = __builtin_fmaf((float)ov[i], (float)gv[i], acc);
+  }
+#pragma unroll
+  for (int m = LPR / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m);
+  if (row < rows && part == 0) {
+    // row = (b * Lq + i) * H + h  ->  delta[b][h][i]
+    const int64_t h = row % p.heads, bi = row / p.heads;
+    const int64_t b = bi / p.seq_q, i = bi % p.seq_q;
+    bp.delta[(b * p.heads + h) * p.seq_q + i] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dq kernel (query-stationary)
+// ---------------------------------------------------------------------------
+
+template <int D, bool SEG>
+struct DqStage {
+  static constexpr int ELEMS = 64 * D;  // bf16 per 64-row tensor tile
+  static constexpr int STAGE = 2 * ELEMS + (SEG ? 128 : 0);
+  static constexpr int NPT = 2 * (64 * D / 8 / 64 / kWaves) + (SEG ? 1 : 0);  // DMA per wave
+};
+
+struct DqWave {
+  int lane, lrow, half, wave, qg0, k_rd, t_rd;
+  bool active;
+  int32_t seg_q;
+  int64_t kend;
+  const char* kbase0;
+  const char* vbase0;
+  const int32_t* sbase0;
+  uint32_t rs_bytes, k_lane;
+};
+
+// One key tile: S^T, dP^T, dS^T and dQ^T += K^T dS^T.
+template <int D, bool SEG>
+__device__ __forceinline__ void dq_tile(const FwdParams& p, const DqWave& w, const WaveLimits& lim,
+                                        const TileInfo& ti, const bf16x8_t* qf,
+                                        const bf16x8_t* dof, float lse2, float dlt,
+                                        f32x16_t* acc, const __bf16* kst, const __bf16* vst,
+                                        const int32_t* sg) {
+  constexpr int NDB = D / 32;
+  const TileFlags f = tile_flags<SEG>(ti, lim);
+  if (!(f.run0 || f.run1)) return;
+  f32x16_t s[2], dp[2];
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    s[sb] = f32x16_t{};
+    dp[sb] = f32x16_t{};
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      s[sb] = mfma(row_operand(kst, w.k_rd, c, sb), qf[c], s[sb]);
+      dp[sb] = mfma(row_operand(vst, w.k_rd, c, sb), dof[c], dp[sb]);
+    }
+  }
+  const bool masked = SEG || !(f.run0 && f.run1) || f.mask0 || f.mask1;
+  if (masked) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const bool r = sb ? f.run1 : f.run0, m = sb ? f.mask1 : f.mask0;
+      const int32_t nvis = !r ? 0 : m ? lim.lane_lim - (f.pk + 32 * sb + 4 * w.half) : 32;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int koff = 8 * (i >> 2) + (i & 3);
+        bool ok = koff < nvis;
+        if (SEG) ok = ok && sg[32 * sb + 4 * w.half + koff] == w.seg_q;
+        s[sb][i] = ok ? s[sb][i] : ninf();
+      }
+    }
+  }
+  bf16x8_t dsb[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f32x8_t d;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = 8 * (q & 1) + i;
+      const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[q >> 1][e], p.scale_log2, -lse2));
+      d[i] = pr * (dp[q >> 1][e] - dlt);
+    }
+    dsb[q] = __builtin_convertvector(d, bf16x8_t);
+  }
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int j = 0; j < NDB; ++j)
+        acc[j] = mfma(col_operand(kst, w.t_rd, j, 2 * sb + cc), dsb[2 * sb + cc], acc[j]);
+}
+
+template <int D, bool SEG>
+__global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dq_kernel(const BwdParams bp) {
+  using St = DqStage<D, SEG>;
+  constexpr int NDB = D / 32, NPT = St::NPT;
+  const FwdParams& p = bp.f;
+  __shared__ __attribute__((aligned(16))) __bf16 st0[St::STAGE], st1[St::STAGE], st2[St::STAGE],
+      st3[St::STAGE];
+  __bf16* const stg[4] = {st0, st1, st2, st3};
+
+  DqWave w;
+  w.lane = threadIdx.x & 63;
+  w.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  w.lrow = w.lane & 31;
+  w.half = w.lane >> 5;
+  const WgCoord wc = wg_coord<kBlockMBf16>(p);
+  const int b = wc.b, h = wc.h, m0 = wc.m0;
+  w.qg0 = m0 + w.wave * 32;
+  w.active = w.qg0 < p.seq_q;
+  const int64_t pq_first = (int64_t)p.ring_index * p.seq_q + w.qg0;
+  const WaveLimits lim = wave_limits(p, pq_first, w.lrow, w.active);
+  w.kend = wg_kend<kBlockMBf16>(p, m0);
+  w.seg_q = 0;
+  if (SEG && w.active) w.seg_q = p.seg[(int64_t)b * p.seq_k + pq_first + w.lrow];
+  const int64_t rs = (int64_t)p.heads * D;
+  w.rs_bytes = (uint32_t)(rs * 2);
+  w.kbase0 = static_cast<const char*>(p.k) + ((int64_t)b * p.seq_k * rs + (int64_t)h * D) * 2;
+  w.vbase0 = static_cast<const char*>(p.v) + ((int64_t)b * p.seq_k * rs + (int64_t)h * D) * 2;
+  w.sbase0 = SEG ? p.seg + (int64_t)b * p.seq_k : nullptr;
+  w.k_lane = (uint32_t)(w.lane & 15) * w.rs_bytes + 16u * (uint32_t)(w.lane >> 4);
+  w.k_rd = row_rd(w.lane);
+  w.t_rd = col_rd(w.lane);
+
+  // Q^T and dO^T of this wave as B operands; the row's lse (base 2) and delta.
+  bf16x8_t qf[D / 16], dof[D / 16];
+  float lse2 = 0.f, dlt = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    qf[c] = bf16x8_t{};
+    dof[c] = bf16x8_t{};
+  }
+  if (w.active) {
+    const int64_t roff = ((int64_t)b * p.seq_q + w.qg0 + w.lrow) * rs + (int64_t)h * D;
+    const __bf16* qrow = static_cast<const __bf16*>(p.q) + roff;
+    const __bf16* grow = static_cast<const __bf16*>(bp.dout) + roff;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      qf[c] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * c + 8 * w.half);
+      dof[c] = *reinterpret_cast<const bf16x8_t*>(grow + 16 * c + 8 * w.half);
+    }
+    const int64_t li = ((int64_t)b * p.heads + h) * p.seq_q + w.qg0 + w.lrow;
+    lse2 = bp.lse[li] * kLog2e;
+    dlt = bp.delta[li];
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  f32x16_t acc[NDB];
+#pragma unroll
+  for (int j = 0; j < NDB; ++j) acc[j] = f32x16_t{};
+
+  // Tiles 0, 1, 2 in flight; tile i is read in step i, tile i+3 is fetched
+  // into the stage of tile i-1 at the start of step i.
+  TileInfo ti[4];
+  Cursor ic{0, 0, 0, 0, 0, 0};
+  cursor_seek<64>(p, ic, w.kend);
+  auto fetch = [&](int s) {
+    ti[s] = tile_info<64>(p, ic);
+    if (ic.valid) {
+      __bf16* d = stg[s];
+      issue_tile<D, kWaves, SEG>(ti[s], w.kbase0, w.vbase0, w.sbase0, w.rs_bytes, w.wave, w.lane,
+                                 w.k_lane, w.k_lane, d, d + St::ELEMS,
+                                 reinterpret_cast<int32_t*>(d + 2 * St::ELEMS));
+      cursor_next<64>(p, ic, w.kend);
+    }
+  };
+  fetch(0);
+  fetch(1);
+  fetch(2);
+  // Tile 0 must have landed for every wave before step 0 reads it.
+  if (ti[2].valid)
+    wait_vm<2 * NPT>();
+  else if (ti[1].valid)
+    wait_vm<NPT>();
+  else
+    wait_vm<0>();
+  stage_barrier();
+
+  auto step = [&](auto PHc) -> bool {
+    constexpr int PH = decltype(PHc)::value;
+    constexpr int S0 = PH, S1 = (PH + 1) & 3;
+    fetch((PH + 3) & 3);
+    if (w.active)
+      dq_tile<D, SEG>(p, w, lim, ti[S0], qf, dof, lse2, dlt, acc, stg[S0], stg[S0] + St::ELEMS,
+                      reinterpret_cast<const int32_t*>(stg[S0] + 2 * St::ELEMS));
+    // Tile i+1 must have landed (for every wave) before the next step.
+    if (ti[S1].valid) {
+      if (ti[(PH + 3) & 3].valid)
+        wait_vm<2 * NPT>();
+      else if (ti[(PH + 2) & 3].valid)
+        wait_vm<NPT>();
+      else
+        wait_vm<0>();
+    }
+    stage_barrier();
+    return ti[S1].valid;
+  };
+  if (ti[0].valid) {
+    for (;;) {
+      if (!step(std::integral_constant<int, 0>{})) break;
+      if (!step(std::integral_constant<int, 1>{})) break;
+      if (!step(std::integral_constant<int, 2>{})) break;
+      if (!step(std::integral_constant<int, 3>{})) break;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  if (!w.active) return;
+  const float scale = p.scale_log2 / kLog2e;
+  float* drow = bp.dq + ((int64_t)b * p.seq_q + w.qg0 + w.lrow) * rs + (int64_t)h * D;
+#pragma unroll
+  for (int j = 0; j < NDB; ++j)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<float4*>(drow + 32 * j + 8 * g + 4 * w.half) =
+          make_float4(acc[j][4 * g] * scale, acc[j][4 * g + 1] * scale,
+                      acc[j][4 * g + 2] * scale, acc[j][4 * g + 3] * scale);
+}
+
+// ---------------------------------------------------------------------------
+// dk / dv kernel (key-stationary)
+// ---------------------------------------------------------------------------
+
+template <int D, bool SEG>
+struct KvLds {
+  static constexpr int ELEMS = 64 * D;                     // one 64-row tile
+  static constexpr int VRES = kBlockNBwd / 64 * ELEMS;     // resident V, 4 tiles
+  // A query stage: Q tile, dO tile, then 64 segment ids, 64 lse, 64 delta.
+  static constexpr int QSTAGE = 2 * ELEMS + 3 * 128;
+  static constexpr int NPT = 2 * (64 * D / 8 / 64 / kWaves) + (SEG ? 1 : 0);
+};
+
+// Which (batch, head, key tile) a workgroup owns: consecutive key tiles of
+// one head (which stream the same queries) share an XCD; earlier key tiles,
+// seen by more queries under a causal mask, come first.
+__device__ __forceinline__ WgCoord kv_coord(const BwdParams& bp) {
+  const int pid = blockIdx.x, n = bp.n_wg_kv;
+  const int xcd = pid & 7, idx = pid >> 3, cnt = n >> 3, rem = n & 7;
+  const int logical =
+      xcd < rem ? xcd * (cnt + 1) + idx : rem * (cnt + 1) + (xcd - rem) * cnt + idx;
+  const int kt = logical % bp.n_ktiles;
+  const int bh = logical / bp.n_ktiles;
+  return WgCoord{__builtin_amdgcn_readfirstlane(bh / bp.f.heads),
+                 __builtin_amdgcn_readfirstlane(bh % bp.f.heads),
+                 __builtin_amdgcn_readfirstlane(kt * kBlockNBwd)};
+}
+
+template <int D, bool SEG>
+__global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParams bp) {
+  using L = KvLds<D, SEG>;
+  constexpr int NDB = D / 32, NPT = L::NPT;
+  const FwdParams& p = bp.f;
+  __shared__ __attribute__((aligned(16))) __bf16 vres[L::VRES];
+  __shared__ __attribute__((aligned(16))) __bf16 qs[2 * L::QSTAGE];  // two query stages
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lrow = lane & 31, half = lane >> 5;
+  const WgCoord wc = kv_coord(bp);
+  const int b = wc.b, h = wc.h, k0 = wc.m0;
+  const int kw0 = k0 + 32 * wave;          // first key of this wave
+  const bool active = kw0 < p.seq_k;       // seq_k is a multiple of 32
+  const int key = kw0 + lrow;              // this lane's key
+  const int64_t rs = (int64_t)p.heads * D;
+  const uint32_t rs_bytes = (uint32_t)(rs * 2);
+  const uint32_t lane_off = (uint32_t)(lane & 15) * rs_bytes + 16u * (uint32_t)(lane >> 4);
+  const int r_rd = row_rd(lane), t_rd = col_rd(lane);
+  const int32_t qpos0 = p.ring_index * p.seq_q;  // global position of local row 0
+
+  // Causal threshold of this lane's key: query positions >= thr see it; the
+  // wave's smallest and largest thresholds decide which blocks run.
+  const int64_t c = p.causal;
+  int32_t thr = INT32_MIN, thr_first = INT32_MIN, thr_last = INT32_MIN;
+  if (c > 0) {
+    thr = (int32_t)(((int64_t)key / c) * c);
+    thr_first = (int32_t)uniform64(((int64_t)kw0 / c) * c);
+    thr_last = (int32_t)uniform64(((int64_t)(kw0 + 31) / c) * c);
+  }
+  const int32_t seg_k = SEG && active ? p.seg[(int64_t)b * p.seq_k + key] : 0;
+
+  // K^T of this wave as the B operand of S = Q K^T.
+  bf16x8_t kf[D / 16];
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc) kf[cc] = bf16x8_t{};
+  if (active) {
+    const __bf16* krow = static_cast<const __bf16*>(p.k) +
+                         ((int64_t)b * p.seq_k + key) * rs + (int64_t)h * D;
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc)
+      kf[cc] = *reinterpret_cast<const bf16x8_t*>(krow + 16 * cc + 8 * half);
+  }
+
+  // The workgroup's V rows, resident in LDS for the whole walk.
+  const char* vbase0 = static_cast<const char*>(p.v) + ((int64_t)b * p.seq_k * rs + (int64_t)h * D) * 2;
+  const int kend = std::min(p.seq_k, k0 + kBlockNBwd);
+#pragma unroll
+  for (int t = 0; t < kBlockNBwd / 64; ++t)
+    issue_rows<D, kWaves>(TileInfo{k0 + 64 * t, kend, 0, 0, 1}, vbase0, rs_bytes, wave, lane_off,
+                          vres + t * L::ELEMS);
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // Query rows that can see any key of the workgroup: [q_lo, Lq).
+  int q_lo = 0;
+  if (c > 0) {
+    const int64_t t0 = ((int64_t)k0 / c) * c - qpos0;
+    q_lo = t0 <= 0 ? 0 : (t0 >= p.seq_q ? p.seq_q : (int)t0);
+  }
+  q_lo &= ~63;
+  const int n_qt = (p.seq_q - q_lo + 63) / 64;
+
+  const char* qbase0 = static_cast<const char*>(p.q) + ((int64_t)b * p.seq_q * rs + (int64_t)h * D) * 2;
+  const char* gbase0 = static_cast<const char*>(bp.dout) + ((int64_t)b * p.seq_q * rs + (int64_t)h * D) * 2;
+  const int32_t* sbase0 = SEG ? p.seg + (int64_t)b * p.seq_k + qpos0 : nullptr;
+  const float* lbase = bp.lse + ((int64_t)b * p.heads + h) * p.seq_q;
+  const float* dbase = bp.delta + ((int64_t)b * p.heads + h) * p.seq_q;
+
+  auto fetch = [&](int qt, int s) {
+    const int q0 = q_lo + 64 * qt;
+    __bf16* d = qs + s * L::QSTAGE;
+    issue_tile<D, kWaves, SEG>(TileInfo{q0, p.seq_q, 0, 0, 1}, qbase0, gbase0, sbase0, rs_bytes,
+                               wave, lane, lane_off, lane_off, d, d + L::ELEMS,
+                               reinterpret_cast<int32_t*>(d + 2 * L::ELEMS));
+    const int nvalid = std::min(64, p.seq_q - q0);
+    if (wave == 0)
+      dma_b32(lds_addr(d + 2 * L::ELEMS + 128), (uint32_t)lane * 4u,
+              rsrc_words(lbase + q0, (uint32_t)nvalid * 4u));
+    if (wave == 1)
+      dma_b32(lds_addr(d + 2 * L::ELEMS + 256), (uint32_t)lane * 4u,
+              rsrc_words(dbase + q0, (uint32_t)nvalid * 4u));
+  };
+  // A wave's DMA count per query tile (waves 0 and 1 issue one more).
+  const bool extra = wave < 2;
+
+  f32x16_t dk[NDB], dv[NDB];
+#pragma unroll
+  for (int j = 0; j < NDB; ++j) {
+    dk[j] = f32x16_t{};
+    dv[j] = f32x16_t{};
+  }
+
+  if (n_qt > 0) fetch(0, 0);
+  for (int qt = 0; qt < n_qt; ++qt) {
+    const int s = qt & 1;
+    if (qt + 1 < n_qt) fetch(qt + 1, s ^ 1);
+    // This wave's share of tile qt must have landed before the barrier.
+    if (qt + 1 < n_qt) {
+      if (extra)
+        wait_vm<NPT + 1>();
+      else
+        wait_vm<NPT>();
+    } else {
+      wait_vm<0>();
+    }
+    stage_barrier();
+
+    const __bf16* qt_t = qs + s * L::QSTAGE;
+    const __bf16* gt_t = qt_t + L::ELEMS;
+    const int32_t* sg = reinterpret_cast<const int32_t*>(qt_t + 2 * L::ELEMS);
+    const float* lse_t = reinterpret_cast<const float*>(qt_t + 2 * L::ELEMS + 128);
+    const float* dlt_t = reinterpret_cast<const float*>(qt_t + 2 * L::ELEMS + 256);
+    const int q0 = q_lo + 64 * qt;
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      const int qb = q0 + 32 * qh;  // local row of the block's first query
+      // Does the block hold a visible pair, and is every pair visible?
+      const int qlast = std::min(qb + 31, p.seq_q - 1);
+      const bool rows_in = qb < p.seq_q;
+      const bool run = active && rows_in && (c == 0 || qpos0 + qlast >= thr_first);
+      const bool full = !SEG && qb + 31 < p.seq_q && (c == 0 || qpos0 + qb >= thr_last);
+      if (!run) continue;
+
+      f32x16_t sc = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+      for (int cc = 0; cc < D / 16; ++cc) {
+        const bf16x8_t vop = *reinterpret_cast<const bf16x8_t*>(
+            vres + (wave >> 1) * L::ELEMS + r_rd + row_off(cc, wave & 1));
+        sc = mfma(row_operand(qt_t, r_rd, cc, qh), kf[cc], sc);
+        dp = mfma(row_operand(gt_t, r_rd, cc, qh), vop, dp);
+      }
+      // The 16 query rows of this lane: 8 (e / 4) + 4 half + e % 4; p and
+      // ds overwrite the scores and dp in place.
+      const int32_t lo = thr == INT32_MIN ? INT32_MIN : thr - (qpos0 + qb);
+      const int32_t hi = p.seq_q - qb;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 l4 = *reinterpret_cast<const float4*>(lse_t + 32 * qh + 8 * g + 4 * half);
+        const float4 d4 = *reinterpret_cast<const float4*>(dlt_t + 32 * qh + 8 * g + 4 * half);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 4 * g + i;
+          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], p.scale_log2, -lv[i] * kLog2e));
+          if (!full) {
+            const int off = 8 * g + 4 * half + i;
+            bool ok = off >= lo && off < hi;
+            if (SEG) ok = ok && sg[32 * qh + off] == seg_k;
+            pr = ok ? pr : 0.f;
+          }
+          sc[e] = pr;
+          dp[e] = pr * (dp[e] - dvv[i]);
+        }
+      }
+      bf16x8_t pb[2], db[2];
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        f32x8_t a, d;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          a[i] = sc[8 * cc + i];
+          d[i] = dp[8 * cc + i];
+        }
+        pb[cc] = __builtin_convertvector(a, bf16x8_t);
+        db[cc] = __builtin_convertvector(d, bf16x8_t);
+      }
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int j = 0; j < NDB; ++j) {
+          dv[j] = mfma(col_operand(gt_t, t_rd, j, 2 * qh + cc), pb[cc], dv[j]);
+          dk[j] = mfma(col_operand(qt_t, t_rd, j, 2 * qh + cc), db[cc], dk[j]);
+        }
+    }
+    // Every wave is done with stage s before the next fetch overwrites it.
+    stage_barrier();
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  if (!active) return;
+  const float scale = p.scale_log2 / kLog2e;
+  const int64_t roff = ((int64_t)b * p.seq_k + key) * rs + (int64_t)h * D;
+#pragma unroll
+  for (int j = 0; j < NDB; ++j)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * j + 8 * g + 4 * half;
+      *reinterpret_cast<float4*>(bp.dk + roff + d) =
+          make_float4(dk[j][4 * g] * scale, dk[j][4 * g + 1] * scale, dk[j][4 * g + 2] * scale,
+                      dk[j][4 * g + 3] * scale);
+      *reinterpret_cast<float4*>(bp.dv + roff + d) =
+          make_float4(dv[j][4 * g], dv[j][4 * g + 1], dv[j][4 * g + 2], dv[j][4 * g + 3]);
+    }
+}
+
+}  // namespace
+
+int launch_bwd(const BwdParams& bp, int head_dim, void* stream, char* err, int errlen) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipGetLastError();  // clear a stale error from earlier work
+  (void)e;
+  const FwdParams& p = bp.f;
+  const bool seg = p.seg != nullptr;
+  const int64_t rows = (int64_t)p.batch * p.seq_q * p.heads;
+  const int64_t lanes = rows * (head_dim / 8);
+  const dim3 dgrid((unsigned)((lanes + 255) / 256));
+  if (head_dim == 128)
+    hipLaunchKernelGGL(bwd_delta_kernel<128>, dgrid, dim3(256), 0, s, bp);
+  else
+    hipLaunchKernelGGL(bwd_delta_kernel<64>, dgrid, dim3(256), 0, s, bp);
+  const dim3 block(kThreadsBwd);
+  const dim3 qgrid((unsigned)p.n_wg), kgrid((unsigned)bp.n_wg_kv);
+  if (head_dim == 128) {
+    if (seg) {
+      hipLaunchKernelGGL((bwd_dq_kernel<128, true>), qgrid, block, 0, s, bp);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<128, true>), kgrid, block, 0, s, bp);
+    } else {
+      hipLaunchKernelGGL((bwd_dq_kernel<128, false>), qgrid, block, 0, s, bp);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<128, false>), kgrid, block, 0, s, bp);
+    }
+  } else {
+    if (seg) {
+      hipLaunchKernelGGL((bwd_dq_kernel<64, true>), qgrid, block, 0, s, bp);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<64, true>), kgrid, block, 0, s, bp);
+    } else {
+      hipLaunchKernelGGL((bwd_dq_kernel<64, false>), qgrid, block, 0, s, bp);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<64, false>), kgrid, block, 0, s, bp);
+    }
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) {
+    std::snprintf(err, errlen, "backward launch failed: %s", hipGetErrorString(e));
+    return 1;
+  }
+  return 0;
+}
+
+}  // namespace ra

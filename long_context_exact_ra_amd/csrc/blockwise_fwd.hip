@@ -40,152 +40,13 @@
 #include <climits>
 #include <cstdio>
 
+#include "ra_device.h"
 #include "ra_internal.h"
 
 namespace ra {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
-
 constexpr int kThreads = 256;
-constexpr float kLn2 = 0.69314718055994530942f;
-// Buffer resource word 3 for gfx9 raw (untyped) buffer access.
-constexpr int kRsrcWord3 = 0x00020000;
-
-__device__ __forceinline__ float ninf() { return -__builtin_inff(); }
-
-// ---------------------------------------------------------------------------
-// Work decomposition shared by both kernels
-// ---------------------------------------------------------------------------
-
-// Which (batch, head, query tile) a workgroup owns.  Workgroups are
-// dispatched round-robin over the 8 XCDs; the remap puts consecutive logical
-// tiles -- the query tiles of one head, which stream the same keys and
-// values -- on the same XCD so they share its L2.  Heavier query tiles (more
-// causal work) come first.
-struct WgCoord {
-  int b, h, m0;
-};
-
-template <int BM>
-__device__ __forceinline__ WgCoord wg_coord(const FwdParams& p) {
-  const int pid = blockIdx.x, n = p.n_wg;
-  const int xcd = pid & 7, idx = pid >> 3, cnt = n >> 3, rem = n & 7;
-  const int logical =
-      xcd < rem ? xcd * (cnt + 1) + idx : rem * (cnt + 1) + (xcd - rem) * cnt + idx;
-  const int qt = p.n_qtiles - 1 - logical % p.n_qtiles;
-  const int bh = logical / p.n_qtiles;
-  // The values are workgroup-uniform; say so, so that addresses and buffer
-  // descriptors derived from them stay in scalar registers.
-  return WgCoord{__builtin_amdgcn_readfirstlane(bh / p.heads),
-                 __builtin_amdgcn_readfirstlane(bh % p.heads),
-                 __builtin_amdgcn_readfirstlane(qt * BM)};
-}
-
-// Position of the workgroup's current tile in the ring walk.
-struct Cursor {
-  int t;       // ring step
-  int kb;      // key/value block used at this step
-  int kt;      // tile index inside the block
-  int ntile;   // tiles to visit in this block
-  int klen;    // keys to visit in this block (multiple of 32)
-  int valid;   // int, not bool: no padding bytes to copy around
-};
-
-// kend: first key position no row of the workgroup can see (INT64_MAX when
-// non-causal).  The keys of block kb to visit are those before kend, rounded
-// up to whole 32-key sub-tiles.
-__device__ __forceinline__ int block_klen(const FwdParams& p, int kb, int64_t kend) {
-  const int64_t len = kend - (int64_t)kb * p.seq_q;
-  if (len <= 0) return 0;
-  if (len >= p.seq_q) return p.seq_q;
-  const int l32 = ((int)len + 31) & ~31;
-  return l32 > p.seq_q ? p.seq_q : l32;
-}
-
-template <int TN>
-__device__ __forceinline__ void cursor_seek(const FwdParams& p, Cursor& c, int64_t kend) {
-#pragma clang loop vectorize(disable) unroll(disable)
-  while (c.t < p.ring_size) {
-    // Ring order: step t uses block (r - t) mod N.
-    c.kb = p.ring_index - c.t;
-    if (c.kb < 0) c.kb += p.ring_size;
-    c.klen = block_klen(p, c.kb, kend);
-    c.ntile = (c.klen + TN - 1) / TN;
-    if (c.ntile > 0) {
-      c.valid = 1;
-      return;
-    }
-    ++c.t;
-  }
-  c.valid = 0;
-}
-
-template <int TN>
-__device__ __forceinline__ void cursor_next(const FwdParams& p, Cursor& c, int64_t kend) {
-  if (++c.kt < c.ntile) return;
-  c.kt = 0;
-  ++c.t;
-  cursor_seek<TN>(p, c, kend);
-}
-
-// A wave-uniform 64-bit value that the compiler computed in vector registers
-// (64-bit division has no scalar form), moved back to scalar registers.
-__device__ __forceinline__ int64_t uniform64(int64_t x) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)x >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
-// Per-wave causal limits as 32-bit key positions (every position is below
-// 2^31 - 1, and tiles start at multiples of 32).  For the 32-key sub-tile
-// starting at key position pk0:
-//   it holds a visible pair for some row of the wave iff pk0 < run_lim;
-//   it needs the per-element causal test iff pk0 >= mask_lim;
-// and key position pk is visible from this lane's row iff pk < lane_lim.
-// A wave without rows gets run_lim = INT32_MIN: none of its tiles run.
-struct WaveLimits {
-  int32_t run_lim, mask_lim, lane_lim;
-};
-
-__device__ __forceinline__ int32_t clamp_i32(int64_t x) {
-  return (int32_t)std::min<int64_t>(x, INT32_MAX);
-}
-
-__device__ __forceinline__ WaveLimits wave_limits(const FwdParams& p, int64_t pq_first,
-                                                  int lrow, bool wave_active) {
-  WaveLimits w{INT32_MAX, INT32_MAX, p.seq_k};
-  if (p.causal > 0) {
-    const int64_t c = p.causal;
-    // First key position no row of the wave can see, and first key position
-    // that some row of the wave cannot see.
-    const int64_t run_end = ((pq_first + 31) / c + 1) * c;
-    const int64_t full_end = (pq_first / c + 1) * c;
-    w.run_lim = clamp_i32(uniform64(run_end));
-    w.mask_lim = clamp_i32(uniform64(full_end)) - 31;
-    w.lane_lim = (int32_t)std::min<int64_t>(((pq_first + lrow) / c + 1) * c, p.seq_k);
-  }
-  if (!wave_active) w.run_lim = INT32_MIN;
-  return w;
-}
-
-template <int BM>
-__device__ __forceinline__ int64_t wg_kend(const FwdParams& p, int m0) {
-  if (p.causal == 0) return INT64_MAX;
-  const int64_t q_last = (int64_t)p.ring_index * p.seq_q + std::min(m0 + BM, p.seq_q) - 1;
-  return uniform64((q_last / p.causal + 1) * p.causal);
-}
-
-__device__ __forceinline__ void write_run_map(const FwdParams& p, int t, int qg0, int key0) {
-  const int nqc = p.seq_q / p.q_chunk, nkc = p.seq_q / p.k_chunk;
-  p.run_map[((int64_t)t * nqc + qg0 / p.q_chunk) * nkc + key0 / p.k_chunk] = 1;
-}
 
 // ---------------------------------------------------------------------------
 // bf16 kernel
@@ -240,114 +101,6 @@ struct PipeCfg {
   static_assert(DPW * 64 * kWaves == SLOTS, "tile must split evenly over the waves");
 };
 
-// s_waitcnt immediate that waits until at most n vector-memory operations of
-// this wave are outstanding (gfx9 encoding; expcnt and lgkmcnt not waited).
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
-}
-
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-
-// Raw buffer descriptor words (base, stride 0, num_records, gfx9 word 3),
-// wave-uniform and in scalar registers.
-__device__ __forceinline__ i32x4_t rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4_t r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
-  r[3] = kRsrcWord3;
-  return r;
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
-}
-
-// Bounds-checked buffer-to-LDS DMA of 16 (4) bytes per lane: lane l's bytes
-// land at LDS address lds + 16 * l (4 * l); lanes whose offset is outside
-// the descriptor write zeros.  Issued as inline asm on purpose: the compiler
-// then does not track these LDS writes (its conservative tracking would add
-// waits for all outstanding DMA before unrelated LDS reads); completion is
-// enforced by the explicit vmcnt waits and barriers of the pipeline.
-__device__ __forceinline__ void dma_b128(uint32_t lds, uint32_t voff, i32x4_t rsrc) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(voff), "s"(rsrc));
-}
-__device__ __forceinline__ void dma_b32(uint32_t lds, uint32_t voff, i32x4_t rsrc) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(voff), "s"(rsrc));
-}
-
-// Workgroup barrier publishing the LDS tiles written by DMA.  The LDS-only
-// acquire fence keeps the compiler from reusing or hoisting LDS reads across
-// it (it does not see the DMA writes) and costs only an LDS wait.
-__device__ __forceinline__ void stage_barrier() {
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// A tile in flight: the global key position of its first key (its first
-// row in K and V), the end of the keys to visit in its block, its ring step
-// and block.  A tile with valid == 0 is past the end of the walk.
-struct TileInfo {
-  int32_t pk, end, t, kb, valid;
-};
-
-template <int TN>
-__device__ __forceinline__ TileInfo tile_info(const FwdParams& p, const Cursor& c) {
-  const int32_t base = c.kb * p.seq_q;
-  return TileInfo{base + c.kt * TN, base + c.klen, c.t, c.kb, c.valid};
-}
-
-// Per-wave view of one tile: which 32-key halves have a visible pair and
-// which need the causal or segment mask.
-struct TileFlags {
-  bool run0, run1, mask0, mask1;
-  int32_t pk;
-};
-
-template <bool SEG>
-__device__ __forceinline__ TileFlags tile_flags(const TileInfo& ti, const WaveLimits& lim) {
-  TileFlags f;
-  f.pk = ti.pk;
-  f.run0 = ti.valid && ti.pk < lim.run_lim;
-  f.run1 = ti.valid && ti.pk + 32 < ti.end && ti.pk + 32 < lim.run_lim;
-  f.mask0 = SEG || ti.pk >= lim.mask_lim;
-  f.mask1 = SEG || ti.pk + 32 >= lim.mask_lim;
-  return f;
-}
-
-// Issue this wave's share of the DMA of one tile into the given stage.
-template <int D, bool SEG>
-__device__ __forceinline__ void issue_tile(const TileInfo& ti, const char* kbase0,
-                                           const char* vbase0, const int32_t* sbase0,
-                                           uint32_t rs_bytes, int wave, int lane, uint32_t k_lane,
-                                           uint32_t v_lane, __bf16* kd, __bf16* vd, int32_t* sd) {
-  using C = PipeCfg<D>;
-  const int nvalid = std::min(C::TN, ti.end - ti.pk);
-  const uint32_t bytes = (uint32_t)nvalid * rs_bytes;
-  const uint64_t off = (uint64_t)(uint32_t)ti.pk * rs_bytes;
-  const i32x4_t kr = rsrc_words(kbase0 + off, bytes);
-  const i32x4_t vr = rsrc_words(vbase0 + off, bytes);
-#pragma unroll
-  for (int u = 0; u < C::DPW; ++u) {
-    const int j = wave * C::DPW + u;
-    const uint32_t joff = (uint32_t)(j & 3) * 16u * rs_bytes + 64u * (uint32_t)(j >> 2);
-    dma_b128(lds_addr(kd + j * 512), k_lane + joff, kr);
-    dma_b128(lds_addr(vd + j * 512), v_lane + joff, vr);
-  }
-  if (SEG) {
-    const i32x4_t sr = rsrc_words(sbase0 + ti.pk, (uint32_t)nvalid * 4u);
-    if (lane < 8) dma_b32(lds_addr(sd + 8 * wave), (uint32_t)(8 * wave + lane) * 4u, sr);
-  }
-}
-
 // S^T = K . Q^T for the two 32-key halves of a tile.
 template <int D>
 __device__ __forceinline__ void qk_tile(f32x16_t* s, const bf16x8_t* qf, const __bf16* kst,
@@ -398,19 +151,6 @@ __device__ __forceinline__ float mask_max(f32x16_t* s, const int32_t* sg, int ha
   return fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
 }
 
-// The two lanes holding one query row are l and l ^ 32.  Swapping the lane
-// halves of x with itself leaves both values of the pair in every lane.
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                  false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                  false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 // Fold a tile's row max into the carry ("2. 数值稳定的注意力计算"): when some
 // row's max grows, rescale that row's numerator and denominator by
 // exp(prev_max - new_max).  Otherwise that factor is exactly 1 for every row
@@ -429,7 +169,6 @@ __device__ __forceinline__ void carry_max(Bf16Wave<D>& w, float mx, float scale_
   }
 }
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Probabilities of a (masked, max-folded) tile and O^T += V^T . P^T.
 // Masked logits are -inf and give exactly 0.  P is rounded to bf16 (round
@@ -532,8 +271,9 @@ __device__ __forceinline__ void fetch_next(const FwdParams& p, const PipeConst& 
                                            __bf16* const* vs, int32_t* const* ss) {
   st.ti[S] = tile_info<PipeCfg<D>::TN>(p, st.ic);
   if (st.ic.valid) {
-    issue_tile<D, SEG>(st.ti[S], k.kbase0, k.vbase0, k.sbase0, k.rs_bytes, k.wave, k.lane,
-                       k.k_lane, k.v_lane, ks[S], vs[S], ss[S]);
+    issue_tile<D, PipeCfg<D>::kWaves, SEG>(st.ti[S], k.kbase0, k.vbase0, k.sbase0, k.rs_bytes,
+                                           k.wave, k.lane, k.k_lane, k.v_lane, ks[S], vs[S],
+                                           ss[S]);
     cursor_next<PipeCfg<D>::TN>(p, st.ic, k.kend);
   }
 }

@@ -107,13 +107,18 @@ ra_status_t ra_blockwise_plan(int64_t causal_block_size, int64_t q_chunk, int64_
   return RA_OK;
 }
 
-ra_status_t ra_blockwise_attn_fwd_ex(const void* q, const void* k, const void* v,
-                                     const int32_t* segment_ids, int64_t causal_block_size,
-                                     int64_t q_chunk, int64_t k_chunk, int32_t ring_size,
-                                     int32_t ring_index, int64_t batch, int64_t seq_q,
-                                     int64_t heads, int64_t head_dim, ra_dtype_t dtype,
-                                     void* out, float* lse, uint8_t* run_map, void* stream) {
-  clear_error();
+}  // extern "C"
+
+namespace {
+
+// Validation and derived parameters shared by the forward and the backward.
+// Returns RA_OK with `empty` set for a valid call that has nothing to do.
+ra_status_t prepare(const void* q, const void* k, const void* v, const int32_t* segment_ids,
+                    int64_t causal_block_size, int64_t q_chunk, int64_t k_chunk,
+                    int32_t ring_size, int32_t ring_index, int64_t batch, int64_t seq_q,
+                    int64_t heads, int64_t head_dim, ra_dtype_t dtype, ra::FwdParams& p,
+                    bool& empty) {
+  empty = false;
   if (batch < 0 || heads < 0)
     return fail(RA_E_INVALID, "batch and heads must be >= 0 (got %lld, %lld)",
                 (long long)batch, (long long)heads);
@@ -126,9 +131,11 @@ ra_status_t ra_blockwise_attn_fwd_ex(const void* q, const void* k, const void* v
   if (head_dim != 64 && head_dim != 128)
     return fail(RA_E_UNSUPPORTED, "head_dim %lld is not supported (64, 128)",
                 (long long)head_dim);
-  if (batch == 0 || seq_q == 0 || heads == 0) return RA_OK;  // empty call
-  if (!q || !k || !v || !out || !lse)
-    return fail(RA_E_INVALID, "q, k, v, out and lse must be non-NULL");
+  if (batch == 0 || seq_q == 0 || heads == 0) {
+    empty = true;
+    return RA_OK;
+  }
+  if (!q || !k || !v) return fail(RA_E_INVALID, "q, k and v must be non-NULL");
   if (heads * head_dim > (1LL << 24))
     return fail(RA_E_UNSUPPORTED, "heads * head_dim = %lld exceeds 2^24",
                 (long long)(heads * head_dim));
@@ -140,14 +147,11 @@ ra_status_t ra_blockwise_attn_fwd_ex(const void* q, const void* k, const void* v
     return fail(RA_E_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)n_wg);
 
   const int64_t seq_k = seq_q * ring_size;
-  ra::FwdParams p;
+  p = ra::FwdParams{};
   p.q = q;
   p.k = k;
   p.v = v;
   p.seg = segment_ids;
-  p.out = out;
-  p.lse = lse;
-  p.run_map = run_map;
   // A causal block at least as long as the whole sequence puts every
   // position in block 0: every key is visible, exactly as without a mask.
   p.causal = causal_block_size >= seq_k ? 0 : causal_block_size;
@@ -162,11 +166,71 @@ ra_status_t ra_blockwise_attn_fwd_ex(const void* q, const void* k, const void* v
   p.n_qtiles = (int32_t)n_qtiles;
   p.n_wg = (int32_t)n_wg;
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+  return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ra_status_t ra_blockwise_attn_fwd_ex(const void* q, const void* k, const void* v,
+                                     const int32_t* segment_ids, int64_t causal_block_size,
+                                     int64_t q_chunk, int64_t k_chunk, int32_t ring_size,
+                                     int32_t ring_index, int64_t batch, int64_t seq_q,
+                                     int64_t heads, int64_t head_dim, ra_dtype_t dtype,
+                                     void* out, float* lse, uint8_t* run_map, void* stream) {
+  clear_error();
+  ra::FwdParams p;
+  bool empty = false;
+  ra_status_t st = prepare(q, k, v, segment_ids, causal_block_size, q_chunk, k_chunk, ring_size,
+                           ring_index, batch, seq_q, heads, head_dim, dtype, p, empty);
+  if (st != RA_OK || empty) return st;
+  if (!out || !lse) return fail(RA_E_INVALID, "out and lse must be non-NULL");
+  p.out = out;
+  p.lse = lse;
+  p.run_map = run_map;
   const int64_t map_bytes =
       run_map ? (int64_t)ring_size * (seq_q / q_chunk) * (seq_q / k_chunk) : 0;
-
+  const ra::Dtype dt = dtype == RA_BF16 ? ra::Dtype::BF16 : ra::Dtype::F32;
   char err[256];
   if (ra::launch_fwd(p, dt, (int)head_dim, map_bytes, stream, err, (int)sizeof(err)) != 0)
+    return fail(RA_E_HIP, "%s", err);
+  return RA_OK;
+}
+
+ra_status_t ra_blockwise_attn_bwd(const void* q, const void* k, const void* v,
+                                  const int32_t* segment_ids, int64_t causal_block_size,
+                                  int64_t q_chunk, int64_t k_chunk, int32_t ring_size,
+                                  int32_t ring_index, int64_t batch, int64_t seq_q,
+                                  int64_t heads, int64_t head_dim, ra_dtype_t dtype,
+                                  const void* out, const float* lse, const void* dout,
+                                  float* dq, float* dk, float* dv, float* delta, void* stream) {
+  clear_error();
+  ra::BwdParams bp;
+  bool empty = false;
+  ra_status_t st = prepare(q, k, v, segment_ids, causal_block_size, q_chunk, k_chunk, ring_size,
+                           ring_index, batch, seq_q, heads, head_dim, dtype, bp.f, empty);
+  if (st != RA_OK) return st;
+  if (dtype != RA_BF16)
+    return fail(RA_E_UNSUPPORTED, "the backward takes bf16 inputs only");
+  if (empty) return RA_OK;
+  if (!out || !lse || !dout || !dq || !dk || !dv || !delta)
+    return fail(RA_E_INVALID, "out, lse, dout, dq, dk, dv and delta must be non-NULL");
+  bp.out = out;
+  bp.lse = lse;
+  bp.dout = dout;
+  bp.dq = dq;
+  bp.dk = dk;
+  bp.dv = dv;
+  bp.delta = delta;
+  const int64_t n_ktiles = ((int64_t)bp.f.seq_k + ra::kBlockNBwd - 1) / ra::kBlockNBwd;
+  const int64_t n_wg_kv = batch * heads * n_ktiles;
+  if (n_wg_kv > kInt32Max)
+    return fail(RA_E_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)n_wg_kv);
+  bp.n_ktiles = (int32_t)n_ktiles;
+  bp.n_wg_kv = (int32_t)n_wg_kv;
+  char err[256];
+  if (ra::launch_bwd(bp, (int)head_dim, stream, err, (int)sizeof(err)) != 0)
     return fail(RA_E_HIP, "%s", err);
   return RA_OK;
 }

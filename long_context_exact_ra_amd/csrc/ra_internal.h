@@ -37,6 +37,29 @@ constexpr int kBlockMBf16 = 256;
 constexpr int kBlockMF32 = 128;
 inline int block_rows(Dtype d) { return d == Dtype::BF16 ? kBlockMBf16 : kBlockMF32; }
 
+// Everything the backward kernels need: the forward's parameters (q, k, v,
+// segment ids, masks and sizes; out/lse/run_map of FwdParams unused) plus
+// the forward outputs, the upstream gradient and the gradient outputs.
+struct BwdParams {
+  FwdParams f;
+  const void* out;      // [B, Lq, H, D] bf16
+  const float* lse;     // [B, H, Lq]
+  const void* dout;     // [B, Lq, H, D] bf16
+  float* dq;            // [B, Lq, H, D]
+  float* dk;            // [B, S, H, D]
+  float* dv;            // [B, S, H, D]
+  float* delta;         // [B, H, Lq]
+  int32_t n_ktiles;     // key tiles per (batch, head) of the dK/dV kernel
+  int32_t n_wg_kv;      // workgroups of the dK/dV kernel
+};
+
+// Keys per workgroup of the dK/dV kernel (8 waves x 32 keys).
+constexpr int kBlockNBwd = 256;
+
+// Enqueue the backward (bf16 inputs) on `stream`; same conventions as
+// launch_fwd.
+int launch_bwd(const BwdParams& p, int head_dim, void* stream, char* err, int errlen);
+
 // Enqueue the forward on `stream` (a hipStream_t).  Returns 0 on success,
 // otherwise writes a message into err (size errlen) and returns nonzero.
 int launch_fwd(const FwdParams& p, Dtype dtype, int head_dim, int64_t run_map_bytes,

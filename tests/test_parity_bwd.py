@@ -1,0 +1,166 @@
+"""GPU parity of the backward (dq, dk, dv, delta) against the fp64 oracle.
+
+Each case runs the library forward, then the library backward on the same
+seeded inputs and a seeded upstream gradient, and compares with
+``oracle.attention_bwd`` computed from the same (bf16-rounded) inputs.
+
+Bounds (no tolerance is given for the backward; derived from the
+arithmetic): the kernels round p and ds to bf16 (relative error <= 2^-9,
+round to nearest even) as operands of fp32-accumulating matrix products, so
+each gradient is a sum of terms with independent relative errors of that
+size; its relative L2 error is expected around 2^-9 ~ 2e-3.  The test
+requires relative L2 <= 1e-2 and max |err| <= 2e-2 * max |ref| per tensor.
+delta is a plain fp32 reduction of the kernel's own out: relative L2
+<= 1e-5 against the same sum in fp64.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_exact_ra_amd as ra
+import oracle
+import workloads
+from parity import log, to_np
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1e-2
+MAX_REL = 2e-2
+
+
+def _cmp(name, got, ref, what):
+    err = np.abs(got - ref)
+    scale = max(float(np.abs(ref).max(initial=0)), 1e-30)
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    log(f"  bwd {what} {name}: rel_l2={rel:.3e} max_err/max_ref={float(err.max(initial=0)) / scale:.3e}")
+    assert np.isfinite(got).all(), (what, name)
+    assert rel <= REL_L2, (what, name, rel)
+    assert float(err.max(initial=0)) <= MAX_REL * scale, (what, name)
+
+
+def _short_documents(B, S, seed):
+    """Segment ids of documents 1..80 tokens long (many per sequence)."""
+    rng = np.random.default_rng(seed)
+    seg = np.zeros((B, S), dtype=np.int32)
+    for b in range(B):
+        pos, doc = 0, 0
+        while pos < S:
+            n = int(rng.integers(1, 81))
+            seg[b, pos:pos + n] = doc
+            pos += n
+            doc += 1
+    return seg
+
+
+def _run(w, r, dev):
+    q, k, v = workloads.make_qkv(w, r, device=dev)
+    dout = workloads.make_dout(w, r, device=dev)
+    seg = workloads.make_segments(w, device=dev)
+    if seg is not None and w.name.startswith("edge"):
+        seg = torch.from_numpy(_short_documents(w.batch, w.seq_k, w.seed + 1)).to(dev)
+    out, lse = ra.blockwise_attn_fwd(q, k, v, seg, w.causal_block_size, w.q_chunk, w.k_chunk,
+                                     w.ring_size, r)
+    dq, dk, dv, delta = ra.blockwise_attn_bwd(q, k, v, out, lse, dout, seg, w.causal_block_size,
+                                              w.q_chunk, w.k_chunk, w.ring_size, r)
+    torch.cuda.synchronize()
+    return q, k, v, dout, seg, out, (dq, dk, dv, delta)
+
+
+def _check_delta(dout, out, delta, what):
+    ref = np.einsum("bihd,bihd->bhi", to_np(dout), to_np(out))
+    got = to_np(delta)
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    log(f"  bwd {what} delta: rel_l2={rel:.3e}")
+    assert rel <= 1e-5, (what, rel)
+
+
+def _full_case(w, r, heads=None):
+    dev = torch.device("cuda:0")
+    q, k, v, dout, seg, out, (dq, dk, dv, delta) = _run(w, r, dev)
+    what = f"{w.name} r={r}"
+    _check_delta(dout, out, delta, what)
+    hs = list(range(w.heads)) if heads is None else list(heads)
+    sl = lambda t: t[:, :, hs].contiguous().cpu()
+    rdq, rdk, rdv = oracle.attention_bwd(sl(q), sl(k), sl(v), sl(dout),
+                                         None if seg is None else seg.cpu().numpy(),
+                                         w.causal_block_size, w.ring_size, r)
+    _cmp("dq", to_np(dq[:, :, hs]), rdq, what)
+    _cmp("dk", to_np(dk[:, :, hs]), rdk, what)
+    _cmp("dv", to_np(dv[:, :, hs]), rdv, what)
+
+
+@pytest.mark.parametrize("r", [0, 3, 7])
+def test_bwd_small_causal(r):
+    _full_case(workloads.get("small_causal"), r)
+
+
+def test_bwd_packed_documents():
+    _full_case(workloads.get("packed_documents"), 5, heads=[0, 17])
+
+
+EDGE = [
+    # B, Lq, N, H, D, causal, qc, kc, segments, r
+    (1, 64, 2, 2, 128, 1, 64, 64, False, 1),
+    (2, 96, 3, 2, 64, 1, 32, 32, False, 2),
+    (1, 128, 1, 4, 128, None, 128, 128, False, 0),
+    (1, 160, 2, 2, 128, 5, 32, 32, False, 1),
+    (2, 128, 2, 2, 128, 1, 64, 64, True, 1),
+    (1, 32, 4, 1, 128, 1, 32, 32, False, 3),
+    (1, 256, 2, 2, 128, 100000, 64, 64, False, 1),
+    (1, 512, 3, 1, 128, 64, 128, 128, True, 2),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[str(c) for c in EDGE])
+def test_bwd_edge(case):
+    B, Lq, N, H, D, c, qc, kc, segs, r = case
+    w = workloads.Workload(f"edge{case}", B, Lq, N, (r,), H, D, "bf16", c, qc, kc,
+                           segments=segs, seed=4242 + Lq + D + N)
+    _full_case(w, r)
+
+
+def test_bwd_share_7b_sampled_and_invariants():
+    """The 7B-shaped share at full size: dq on sampled rows of two heads
+    against the oracle; dk and dv through invariants of the exact gradient
+    (sum_j dk_j = 0; sum_j dv_j = sum_i dout_i, each probability row summing
+    to one) on every head."""
+    w = workloads.get("share_7b_512k")
+    r = w.ring_indices[0]
+    dev = torch.device("cuda:0")
+    q, k, v, dout, seg, out, (dq, dk, dv, delta) = _run(w, r, dev)
+    what = f"{w.name} r={r}"
+    ref = torch.einsum("bihd,bihd->bhi", dout.double(), out.double())
+    rel = float((delta.double() - ref).norm() / ref.norm())
+    log(f"  bwd {what} delta: rel_l2={rel:.3e}")
+    assert rel <= 1e-5
+    rng = np.random.default_rng(77)
+    rows = np.sort(rng.choice(w.seq_q, size=48, replace=False))
+    for h in (0, 21):
+        sl = lambda t: t[:, :, h:h + 1].contiguous().cpu()
+        rdq, _, _ = oracle.attention_bwd(sl(q), sl(k), sl(v), sl(dout), None,
+                                         w.causal_block_size, w.ring_size, r, rows=rows)
+        _cmp(f"dq[h{h}, 48 rows]", to_np(dq[:, rows, h:h + 1]), rdq, what)
+    # invariants, per head, in fp64 on the device
+    sk = dk.double().sum(dim=1)                     # [B, H, D], should be 0
+    scale_k = dk.double().abs().sum(dim=1)
+    ratio = float((sk.abs() / scale_k.clamp_min(1e-30)).max())
+    log(f"  bwd {what} |sum_j dk_j| / sum_j |dk_j| max={ratio:.3e}")
+    assert ratio <= 1e-3
+    sv = dv.double().sum(dim=1)
+    so = dout.double().sum(dim=1)
+    relv = float((sv - so).norm() / so.norm())
+    log(f"  bwd {what} sum_j dv_j vs sum_i dout_i: rel_l2={relv:.3e}")
+    assert relv <= REL_L2
+    assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
+
+
+def test_bwd_rejects_fp32_and_nulls():
+    dev = torch.device("cuda:0")
+    q = torch.zeros((1, 32, 1, 128), dtype=torch.float32, device=dev)
+    with pytest.raises(TypeError):
+        ra.blockwise_attn_bwd(q, q, q, q, torch.zeros((1, 1, 32), device=dev), q)
+    lib = ra.load_library()
+    st = lib.ra_blockwise_attn_bwd(None, None, None, None, 0, 32, 32, 1, 0, 1, 32, 1, 128,
+                                   ra.RA_BF16, None, None, None, None, None, None, None, None)
+    assert st == ra.RA_E_INVALID, ra.last_error()

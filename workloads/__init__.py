@@ -20,7 +20,7 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "get", "block_seed", "document_segments",
-           "make_block", "make_qkv", "make_segments"]
+           "make_block", "make_dout", "make_q", "make_qkv", "make_segments"]
 
 
 @dataclass(frozen=True)
@@ -125,6 +125,13 @@ def make_q(w: Workload, ring_index: int, device="cpu"):
     """Q for ring position ``ring_index`` alone (the same draw as make_qkv)."""
     return make_block((w.batch, w.seq_q, w.heads, w.head_dim),
                       block_seed(w.seed, "q", ring_index), w.std, w.dtype, device)
+
+
+def make_dout(w: Workload, ring_index: int, device="cpu"):
+    """An upstream gradient of the output for ring position ``ring_index``:
+    N(0,1) drawn in fp32 with its own seed, rounded to the workload dtype."""
+    return make_block((w.batch, w.seq_q, w.heads, w.head_dim),
+                      w.seed * 7919 + 5 * 1_000_003 + ring_index, 1.0, w.dtype, device)
 
 
 def make_qkv(w: Workload, ring_index: int, device="cpu",
