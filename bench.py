@@ -5,7 +5,9 @@ ring order, skipping, softmax carry, normalisation, lse) through the C ABI,
 by default on the 7B-shaped share: batch 1, 32 heads, head_dim 128, bf16,
 local query block 32768 at ring position 15 of 16 (512K context), token
 causal, chunks 2048.  ``--workload`` times another bf16 workload instead (a
-step is then one call per ring position the workload lists).  Inputs are
+step is then one call per ring position the workload lists); ``--pass bwd``
+times the backward (dq, dk, dv of the same share, from the forward's out and
+lse and a seeded upstream gradient) instead of the forward.  Inputs are
 seeded Gaussian tensors already resident in HBM.
 
 Prints one JSON line with the causal-adjusted TFLOP/s, the roofline of the
@@ -74,7 +76,8 @@ def cpu_model() -> str:
     return "unknown CPU"
 
 
-def cpu_baseline(w, q, k, v, seg, ring_index: int, rows: int, flops_total: float):
+def cpu_baseline(w, q, k, v, seg, ring_index: int, rows: int, flops_total: float,
+                 dout=None):
     """The CPU oracle, as it stands, on a bounded sample: one head and
     ``rows`` query rows of the same workload (each row over all its visible
     keys).  Rate in the metric's unit (causal-adjusted TFLOP/s); the sample
@@ -91,22 +94,28 @@ def cpu_baseline(w, q, k, v, seg, ring_index: int, rows: int, flops_total: float
     kh = k[:1, :kv_len, head:head + 1].contiguous().cpu()
     vh = v[:1, :kv_len, head:head + 1].contiguous().cpu()
     segh = None if seg is None else seg[:1].cpu().numpy()
+    gh = None if dout is None else dout[:1, :, head:head + 1].contiguous().cpu()
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover - informational only
         cores = torch.get_num_threads()
     t0 = time.perf_counter()
-    oracle.attention_fwd(qh, kh, vh, segh, w.causal_block_size, w.ring_size, ring_index,
-                         rows=sel, kv_len=kv_len)
+    if gh is None:
+        oracle.attention_fwd(qh, kh, vh, segh, w.causal_block_size, w.ring_size, ring_index,
+                             rows=sel, kv_len=kv_len)
+    else:
+        oracle.attention_bwd(qh, kh, vh, gh, segh, w.causal_block_size, w.ring_size,
+                             ring_index, rows=sel, kv_len=kv_len)
     dt = time.perf_counter() - t0
     pairs = int(visible_keys_per_row(w.seq_q, w.ring_size, ring_index,
                                      w.causal_block_size)[sel].sum())
-    flops = 4.0 * w.head_dim * pairs
+    flops = (4.0 if gh is None else 10.0) * w.head_dim * pairs
     rate = flops / dt
     return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": f"{w.name}: batch entry 0, head 0, {rows} query rows spread over the block of ring "
+            "sample": f"{w.name}{'' if gh is None else ' backward'}: batch entry 0, head 0, "
+                      f"{rows} query rows spread over the block of ring "
                       f"position {ring_index}, each over its {kv_len}-key visible range; numpy "
                       f"fp64 on {cpu_model()}; {dt:.1f} s for {flops / 1e9:.1f} GFLOP; the whole "
                       f"step would take {flops_total / rate / 3600:.1f} h at this rate "
@@ -123,6 +132,8 @@ def main():
     ap.add_argument("--workload", default=WORKLOAD,
                     choices=["small_causal", "share_7b_512k", "packed_documents", "share_65b_4m"],
                     help="bf16 workload to time (default: the 7B-shaped share)")
+    ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd"], default="fwd",
+                    help="time the forward (default) or the backward")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first; its "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate HBM byte counts")
@@ -161,10 +172,28 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    bwd = args.pass_ == "bwd"
+    if bwd:
+        # the forward's outputs of every listed ring position, and the gradients
+        douts = [workloads.make_dout(w, ri, device=dev) for ri in w.ring_indices]
+        fw = [ra.blockwise_attn_fwd(qi, k, v, seg, w.causal_block_size, w.q_chunk, w.k_chunk,
+                                    w.ring_size, ri) for ri, qi in zip(w.ring_indices, qs)]
+        f32 = dict(dtype=torch.float32, device=dev)
+        dq = torch.empty(q.shape, **f32)
+        dk = torch.empty(k.shape, **f32)
+        dv = torch.empty(k.shape, **f32)
+        delta = torch.empty((w.batch, w.heads, w.seq_q), **f32)
+        torch.cuda.synchronize()
+
     def step():
-        for ri, qi in zip(w.ring_indices, qs):
-            ra.blockwise_attn_fwd(qi, k, v, seg, w.causal_block_size, w.q_chunk, w.k_chunk,
-                                  w.ring_size, ri, out=out, lse=lse)
+        for i, (ri, qi) in enumerate(zip(w.ring_indices, qs)):
+            if bwd:
+                ra.blockwise_attn_bwd(qi, k, v, fw[i][0], fw[i][1], douts[i], seg,
+                                      w.causal_block_size, w.q_chunk, w.k_chunk, w.ring_size,
+                                      ri, dq=dq, dk=dk, dv=dv, delta=delta)
+            else:
+                ra.blockwise_attn_fwd(qi, k, v, seg, w.causal_block_size, w.q_chunk,
+                                      w.k_chunk, w.ring_size, ri, out=out, lse=lse)
 
     for _ in range(args.warmup):
         step()
@@ -183,15 +212,20 @@ def main():
     wall = time.perf_counter() - t0
     per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
     ms = float(np.mean(per))
-    if not (torch.isfinite(out).all() and torch.isfinite(lse).all()):
+    checked = (dq, dk, dv) if bwd else (out, lse)
+    if not all(bool(torch.isfinite(t).all()) for t in checked):
         raise RuntimeError("non-finite output")
 
-    flops = sum(causal_flops(w, ri) for ri in w.ring_indices)
+    # backward: the 5 matrix products of the algorithm (S, dP, dV, dK, dQ)
+    # per visible pair against the forward's 2
+    flops = sum(causal_flops(w, ri) for ri in w.ring_indices) * (2.5 if bwd else 1.0)
     tflops = flops / (ms * 1e-3) / 1e12
     build_id = ra.version().split("+", 1)[-1]
-    traffic = measured_traffic(build_id) if w.name == WORKLOAD else None
+    traffic = measured_traffic(build_id) if (w.name == WORKLOAD and not bwd) else None
     rec = {
-        "metric": "causal-adjusted attention TFLOP/s per MI355X (% of bf16 MFMA peak in roofline.frac)",
+        "metric": ("causal-adjusted attention backward TFLOP/s per MI355X (5 matrix products "
+                   "per visible pair; % of bf16 MFMA peak in roofline.frac)") if bwd else
+                  "causal-adjusted attention TFLOP/s per MI355X (% of bf16 MFMA peak in roofline.frac)",
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -210,7 +244,7 @@ def main():
                    "context": w.seq_k, "segments": bool(w.segments),
                    "heads": w.heads, "head_dim": w.head_dim,
                    "causal_block_size": w.causal_block_size,
-                   "q_chunk": w.q_chunk, "k_chunk": w.k_chunk,
+                   "q_chunk": w.q_chunk, "k_chunk": w.k_chunk, "pass": args.pass_,
                    "flops_per_step": flops, "ms_min": round(min(per), 3),
                    "wall_s": round(wall, 3)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
@@ -220,7 +254,8 @@ def main():
     }
     if args.cpu_rows > 0:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, seg, r, args.cpu_rows, flops)
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, seg, r, args.cpu_rows, flops,
+                                           douts[0] if bwd else None)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)
