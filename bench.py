@@ -52,15 +52,19 @@ def causal_flops(w, ring_index: int) -> float:
 
 
 def measured_traffic(build_id: str):
-    """HBM bytes per launch measured with rocprofv3 counters, valid only for
-    the kernel build they were taken on (the build id the loaded library
-    reports, a hash of its device sources)."""
+    """HBM bytes per launch of the forward kernel measured with rocprofv3
+    counters, reported only when the loaded library was built from the
+    current sources (its build id, a hash of the device sources) and the
+    forward kernel's sources are those the counters were taken on."""
+    from long_context_exact_ra_amd import build as _b
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sha256_16") != build_id:
+    if build_id != _b.device_sources_sha16():
+        return None  # a stale library
+    if t.get("fwd_sources_sha16") != _b.fwd_sources_sha16():
         return None
     return t.get("hbm_bytes_per_launch")
 

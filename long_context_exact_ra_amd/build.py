@@ -50,6 +50,19 @@ def device_sources_sha16() -> str:
     return h.hexdigest()[:16]
 
 
+# The sources the forward kernel is compiled from.
+FWD_SOURCES = ("blockwise_fwd.hip", "ra_device.h", "ra_internal.h")
+
+
+def fwd_sources_sha16() -> str:
+    """First 16 hex digits of the SHA-256 over the forward kernel's sources."""
+    h = hashlib.sha256()
+    for src in FWD_SOURCES:
+        with open(os.path.join(CSRC, src), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def build(verbose: bool = True) -> str:
     """Compile every source and link ``libra_attn.so``; returns its path."""
     if not os.path.exists(HIPCC):
