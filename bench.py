@@ -7,8 +7,10 @@ local query block 32768 at ring position 15 of 16 (512K context), token
 causal, chunks 2048.  ``--workload`` times another bf16 workload instead (a
 step is then one call per ring position the workload lists); ``--pass bwd``
 times the backward (dq, dk, dv of the same share, from the forward's out and
-lse and a seeded upstream gradient) instead of the forward.  Inputs are
-seeded Gaussian tensors already resident in HBM.
+lse and a seeded upstream gradient) instead of the forward; ``--pass ffn``
+times the blockwise feedforward of the 7B-shaped share (batch 1, 32768
+tokens, hidden 4096, feedforward width 16384, chunks of 2048 rows).  Inputs
+are seeded Gaussian tensors already resident in HBM.
 
 Prints one JSON line with the causal-adjusted TFLOP/s, the roofline of the
 kernel (MFMA bound, bf16 dense peak) and the CPU oracle timed on a bounded
@@ -136,8 +138,9 @@ def main():
     ap.add_argument("--workload", default=WORKLOAD,
                     choices=["small_causal", "share_7b_512k", "packed_documents", "share_65b_4m"],
                     help="bf16 workload to time (default: the 7B-shaped share)")
-    ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd"], default="fwd",
-                    help="time the forward (default) or the backward")
+    ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd", "ffn"], default="fwd",
+                    help="time the attention forward (default), its backward, or the "
+                         "blockwise feedforward")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first; its "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate HBM byte counts")
@@ -158,6 +161,9 @@ def main():
         sys.exit(1)
     ra.load_library()
     dev = torch.device("cuda:0")
+    if args.pass_ == "ffn":
+        bench_ffn(args, dev)
+        return
     w = workloads.get(args.workload)
     r = w.ring_indices[0]
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
@@ -260,6 +266,85 @@ def main():
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v, seg, r, args.cpu_rows, flops,
                                            douts[0] if bwd else None)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+def bench_ffn(args, dev):
+    """Time the blockwise feedforward of the 7B-shaped share: one step is
+    the whole sequence, chunk by chunk, two bias-fused GEMMs per chunk."""
+    import torch
+
+    import long_context_exact_ra_amd as ra
+    import oracle
+    import workloads
+
+    w = workloads.FFN_WORKLOADS["ffn_7b_share"]
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    x, w1, b1, w2, b2 = workloads.make_ffn_inputs(w, device=dev)
+    y = torch.empty_like(x)
+    ws = torch.empty(ra.ffn_workspace_bytes(w.chunk, w.ffn), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        ra.blockwise_ffn(x, w1, b1, w2, b2, w.chunk, y=y, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms = float(np.mean(per))
+    if not bool(torch.isfinite(y).all()):
+        raise RuntimeError("non-finite output")
+    # two products of 2 * hidden * ffn flops per token
+    flops = 4.0 * w.batch * w.seq * w.hidden * w.ffn
+    tflops = flops / (ms * 1e-3) / 1e12
+    rec = {
+        "metric": "blockwise feedforward TFLOP/s per MI355X (% of bf16 MFMA peak in roofline.frac)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded Gaussian x (std 1), weights with std fan_in^-1/2, "
+                "biases std 0.1, bf16",
+        "config": {"workload": w.name, "batch": w.batch, "seq": w.seq, "hidden": w.hidden,
+                   "ffn": w.ffn, "chunk": w.chunk, "pass": "ffn", "flops_per_step": flops,
+                   "ms_min": round(min(per), 3), "wall_s": round(wall, 3)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+    if args.cpu_rows > 0:
+        # the oracle's blockwise feedforward over the whole step (every
+        # token, chunk by chunk): about ten seconds of fp64 BLAS work
+        print("[bench] timing the CPU oracle on the whole step", file=sys.stderr, flush=True)
+        xs = x.cpu()
+        ps = [t.cpu() for t in (w1, b1, w2, b2)]
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:  # pragma: no cover - informational only
+            cores = torch.get_num_threads()
+        t0 = time.perf_counter()
+        oracle.blockwise_ffn(xs, *ps, w.chunk)
+        dt = time.perf_counter() - t0
+        rate = flops / dt
+        rec["cpu_baseline"] = {
+            "value": rate / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{w.name}: the whole step ({w.seq} tokens in chunks of {w.chunk}) "
+                      f"through the fp64 blockwise feedforward (numpy on {cpu_model()}); "
+                      f"{dt:.1f} s for {flops / 1e12:.2f} TFLOP"}
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

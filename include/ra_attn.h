@@ -164,6 +164,47 @@ ra_status_t ra_blockwise_attn_bwd(const void* q, const void* k, const void* v,
                                   float* dv, float* delta, void* stream);
 
 /*
+ * ra_blockwise_ffn -- the feedforward of the Blockwise Transformer, one
+ * sequence chunk at a time.
+ *
+ *   y = max(0, x W1 + b1) W2 + b2     ("Ring Attention with Blockwise
+ *   Transformers for Near-Infinite Context", section 三, the feedforward
+ *   equation), applied to the chunks [c * chunk, (c + 1) * chunk) of every
+ *   sequence in order, so that only one chunk's hidden activations exist at
+ *   a time ("Blockwise Feedforward网络详解", sections "核心技术原理" and
+ *   "技术实现细节").
+ *
+ *   x, y:  [batch, seq, hidden] bf16, row-major, device.
+ *   w1:    [hidden, ffn] bf16;  b1: [ffn] bf16;
+ *   w2:    [ffn, hidden] bf16;  b2: [hidden] bf16 (row-major, device).
+ *   chunk_size: rows of a sequence per chunk; must divide seq.
+ *   workspace: device memory of at least
+ *       ra_blockwise_ffn_workspace_bytes(chunk_size, ffn) bytes (the bf16
+ *       hidden activations of one chunk); contents are overwritten.
+ *
+ * Arithmetic: bf16 inputs on the matrix cores with float32 accumulation;
+ * the hidden activation is rounded to bf16 (round to nearest even) between
+ * the two products; y is rounded to bf16.
+ *
+ * The products run as hipBLASLt GEMMs with fused bias / bias+ReLU
+ * epilogues; the library keeps one hipBLASLt handle per device (created on
+ * first use, never released) and the chosen algorithm per shape.
+ *
+ * Returns RA_E_INVALID for null pointers, non-positive sizes, a chunk size
+ * that does not divide seq or a workspace smaller than required;
+ * RA_E_UNSUPPORTED for RA_F32; RA_E_HIP if hipBLASLt or the runtime reports
+ * an error.  A call with batch == 0 or seq == 0 is a valid no-op.
+ */
+int64_t ra_blockwise_ffn_workspace_bytes(int64_t chunk_size, int64_t ffn_hidden);
+
+ra_status_t ra_blockwise_ffn(const void* x, const void* w1, const void* b1,
+                             const void* w2, const void* b2, int64_t batch,
+                             int64_t seq, int64_t hidden, int64_t ffn_hidden,
+                             int64_t chunk_size, ra_dtype_t dtype, void* y,
+                             void* workspace, int64_t workspace_bytes,
+                             void* stream);
+
+/*
  * ra_blockwise_plan -- host-only: the ring order and the chunk-pair skip
  * decisions for one ring position, without touching a GPU.
  *

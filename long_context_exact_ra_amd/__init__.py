@@ -1,5 +1,6 @@
 """Blockwise exact attention of Ring Attention on MI355X (gfx950): the
-forward of one device's ring share and its backward.
+forward of one device's ring share and its backward, and the blockwise
+feedforward of the Blockwise Transformer.
 
 A thin ctypes binding over the C ABI in ``include/ra_attn.h`` (library
 ``libra_attn.so`` next to this file).  It only marshals arguments: every
@@ -14,7 +15,8 @@ import ctypes
 import os
 from typing import Optional, Tuple
 
-__all__ = ["RaError", "blockwise_attn_fwd", "blockwise_attn_bwd", "blockwise_plan", "last_error", "lib_path",
+__all__ = ["RaError", "blockwise_attn_fwd", "blockwise_attn_bwd", "blockwise_ffn",
+           "ffn_workspace_bytes", "blockwise_plan", "last_error", "lib_path",
            "load_library", "version", "RA_OK", "RA_E_INVALID", "RA_E_UNSUPPORTED",
            "RA_E_HIP", "RA_BF16", "RA_F32"]
 
@@ -55,6 +57,11 @@ def load_library():
     lib.ra_blockwise_attn_fwd_ex.restype = ctypes.c_int
     lib.ra_blockwise_attn_bwd.argtypes = fwd_args[:14] + [c_vp] * 8
     lib.ra_blockwise_attn_bwd.restype = ctypes.c_int
+    lib.ra_blockwise_ffn_workspace_bytes.argtypes = [c_i64, c_i64]
+    lib.ra_blockwise_ffn_workspace_bytes.restype = c_i64
+    lib.ra_blockwise_ffn.argtypes = [c_vp] * 5 + [c_i64] * 5 + [ctypes.c_int, c_vp, c_vp,
+                                                                c_i64, c_vp]
+    lib.ra_blockwise_ffn.restype = ctypes.c_int
     lib.ra_blockwise_plan.argtypes = [c_i64, c_i64, c_i64, c_i64, c_i32, c_i32,
                                       c_vp, c_vp, c_vp]
     lib.ra_blockwise_plan.restype = ctypes.c_int
@@ -214,3 +221,49 @@ def blockwise_attn_bwd(q, k, v, out, lse, dout, segment_ids=None,
         out.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
         dv.data_ptr(), delta.data_ptr(), sptr))
     return dq, dk, dv, delta
+
+
+def ffn_workspace_bytes(chunk_size: int, ffn_hidden: int) -> int:
+    """Bytes of workspace ``blockwise_ffn`` needs (one chunk's bf16 hidden
+    activations)."""
+    return int(load_library().ra_blockwise_ffn_workspace_bytes(chunk_size, ffn_hidden))
+
+
+def blockwise_ffn(x, w1, b1, w2, b2, chunk_size: int, *, y=None, workspace=None,
+                  stream=None):
+    """y = max(0, x W1 + b1) W2 + b2 computed one sequence chunk at a time.
+
+    x [B, L, hidden], w1 [hidden, ffn], b1 [ffn], w2 [ffn, hidden], b2
+    [hidden]: contiguous bfloat16 device tensors; chunk_size divides L.  y
+    and the workspace (uint8, at least ffn_workspace_bytes(chunk_size, ffn)
+    bytes) are allocated when not given.  Returns y.
+    """
+    import torch
+    lib = load_library()
+    for name, t in (("x", x), ("w1", w1), ("b1", b1), ("w2", w2), ("b2", b2)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 device tensor")
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, seq, hidden]")
+    B, L, H = x.shape
+    Fh = w1.shape[1] if w1.dim() == 2 else -1
+    if (tuple(w1.shape) != (H, Fh) or tuple(b1.shape) != (Fh,) or tuple(w2.shape) != (Fh, H)
+            or tuple(b2.shape) != (H,)):
+        raise ValueError("weights must be w1 [hidden, ffn], b1 [ffn], w2 [ffn, hidden], b2 [hidden]")
+    if y is None:
+        y = torch.empty_like(x)
+    if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous():
+        raise ValueError("y must be contiguous with x's shape and dtype")
+    need = ffn_workspace_bytes(chunk_size, Fh) if chunk_size > 0 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    _check(lib.ra_blockwise_ffn(x.data_ptr(), w1.data_ptr(), b1.data_ptr(), w2.data_ptr(),
+                                b2.data_ptr(), B, L, H, Fh, chunk_size, RA_BF16, y.data_ptr(),
+                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                sptr))
+    return y

@@ -83,7 +83,7 @@ def build(verbose: bool = True) -> str:
         objs.append(obj)
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
-          f"-Wl,-rpath,{ROCM}/lib"], verbose)
+          f"-L{ROCM}/lib", "-lhipblaslt", f"-Wl,-rpath,{ROCM}/lib"], verbose)
     os.replace(tmp, LIB)
     return LIB
 

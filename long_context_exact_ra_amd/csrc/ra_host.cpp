@@ -235,6 +235,42 @@ ra_status_t ra_blockwise_attn_bwd(const void* q, const void* k, const void* v,
   return RA_OK;
 }
 
+int64_t ra_blockwise_ffn_workspace_bytes(int64_t chunk_size, int64_t ffn_hidden) {
+  if (chunk_size <= 0 || ffn_hidden <= 0) return 0;
+  return chunk_size * ffn_hidden * 2;
+}
+
+ra_status_t ra_blockwise_ffn(const void* x, const void* w1, const void* b1, const void* w2,
+                             const void* b2, int64_t batch, int64_t seq, int64_t hidden,
+                             int64_t ffn_hidden, int64_t chunk_size, ra_dtype_t dtype, void* y,
+                             void* workspace, int64_t workspace_bytes, void* stream) {
+  clear_error();
+  if (batch < 0 || seq < 0)
+    return fail(RA_E_INVALID, "batch and seq must be >= 0 (got %lld, %lld)", (long long)batch,
+                (long long)seq);
+  if (hidden <= 0 || ffn_hidden <= 0)
+    return fail(RA_E_INVALID, "hidden and ffn_hidden must be positive (got %lld, %lld)",
+                (long long)hidden, (long long)ffn_hidden);
+  if (chunk_size <= 0) return fail(RA_E_INVALID, "chunk_size must be positive");
+  // The sequence is cut with an exact reshape into chunks.
+  if (seq % chunk_size != 0)
+    return fail(RA_E_INVALID, "chunk_size %lld must divide seq %lld", (long long)chunk_size,
+                (long long)seq);
+  if (dtype != RA_BF16)
+    return fail(RA_E_UNSUPPORTED, "the feedforward takes bf16 inputs only");
+  if (batch == 0 || seq == 0) return RA_OK;
+  if (!x || !w1 || !b1 || !w2 || !b2 || !y || !workspace)
+    return fail(RA_E_INVALID, "x, w1, b1, w2, b2, y and workspace must be non-NULL");
+  const int64_t need = ra_blockwise_ffn_workspace_bytes(chunk_size, ffn_hidden);
+  if (workspace_bytes < need)
+    return fail(RA_E_INVALID, "workspace of %lld bytes is smaller than the %lld required",
+                (long long)workspace_bytes, (long long)need);
+  ra::FfnParams p{x, w1, b1, w2, b2, y, workspace, batch, seq, hidden, ffn_hidden, chunk_size};
+  char err[256];
+  if (ra::launch_ffn(p, stream, err, (int)sizeof(err)) != 0) return fail(RA_E_HIP, "%s", err);
+  return RA_OK;
+}
+
 ra_status_t ra_blockwise_attn_fwd(const void* q, const void* k, const void* v,
                                   const int32_t* segment_ids, int64_t causal_block_size,
                                   int64_t q_chunk, int64_t k_chunk, int32_t ring_size,

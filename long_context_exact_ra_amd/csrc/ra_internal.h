@@ -60,6 +60,21 @@ constexpr int kBlockNBwd = 256;
 // launch_fwd.
 int launch_bwd(const BwdParams& p, int head_dim, void* stream, char* err, int errlen);
 
+// The blockwise feedforward: y = max(0, x W1 + b1) W2 + b2, chunk by chunk.
+struct FfnParams {
+  const void* x;     // [batch, seq, hidden] bf16
+  const void* w1;    // [hidden, ffn] bf16
+  const void* b1;    // [ffn] bf16
+  const void* w2;    // [ffn, hidden] bf16
+  const void* b2;    // [hidden] bf16
+  void* y;           // [batch, seq, hidden] bf16
+  void* workspace;   // [chunk, ffn] bf16: one chunk's hidden activations
+  int64_t batch, seq, hidden, ffn, chunk;
+};
+
+// Enqueue the feedforward on `stream`; same conventions as launch_fwd.
+int launch_ffn(const FfnParams& p, void* stream, char* err, int errlen);
+
 // Enqueue the forward on `stream` (a hipStream_t).  Returns 0 on success,
 // otherwise writes a message into err (size errlen) and returns nonzero.
 int launch_fwd(const FwdParams& p, Dtype dtype, int head_dim, int64_t run_map_bytes,

@@ -101,3 +101,24 @@ def test_python_binding_rejects_host_tensors():
     q = torch.zeros(1, 64, 1, 64)
     with pytest.raises(ValueError):
         ra.blockwise_attn_fwd(q, q, q, None, 1, 32, 32)
+
+
+def test_ffn_validation_without_gpu():
+    """Argument errors of the feedforward are caught on the host."""
+    lib = ra.load_library()
+    assert lib.ra_blockwise_ffn_workspace_bytes(2048, 16384) == 2048 * 16384 * 2
+    assert lib.ra_blockwise_ffn_workspace_bytes(0, 16384) == 0
+    p = 1  # a non-null dummy pointer, never dereferenced on these paths
+    call = lambda **kw: lib.ra_blockwise_ffn(
+        *(kw.get(n, p) for n in ("x", "w1", "b1", "w2", "b2")),
+        kw.get("batch", 1), kw.get("seq", 64), kw.get("hidden", 64), kw.get("ffn", 128),
+        kw.get("chunk", 32), kw.get("dtype", ra.RA_BF16), kw.get("y", p), kw.get("ws", p),
+        kw.get("wsb", 1 << 20), None)
+    assert call(chunk=48) == ra.RA_E_INVALID
+    assert call(chunk=0) == ra.RA_E_INVALID
+    assert call(hidden=0) == ra.RA_E_INVALID
+    assert call(dtype=ra.RA_F32) == ra.RA_E_UNSUPPORTED
+    assert call(wsb=100) == ra.RA_E_INVALID
+    assert call(x=None) == ra.RA_E_INVALID
+    assert call(batch=0) == ra.RA_OK  # empty call: no device work
+    assert call(seq=0) == ra.RA_OK

@@ -20,7 +20,8 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "get", "block_seed", "document_segments",
-           "make_block", "make_dout", "make_q", "make_qkv", "make_segments"]
+           "make_block", "make_dout", "make_q", "make_qkv", "make_segments",
+           "FfnWorkload", "FFN_WORKLOADS", "make_ffn_inputs"]
 
 
 @dataclass(frozen=True)
@@ -168,3 +169,40 @@ def make_segments(w: Workload, device="cpu"):
     torch = _torch()
     seg = document_segments(w.batch, w.seq_k, w.seed + 3)
     return torch.from_numpy(seg).to(device)
+
+
+# ---------------------------------------------------------------------------
+# Blockwise feedforward
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class FfnWorkload:
+    """Shapes of one blockwise-feedforward call: x [batch, seq, hidden],
+    w1 [hidden, ffn], w2 [ffn, hidden], processed in chunks of ``chunk``."""
+    name: str
+    batch: int
+    seq: int
+    hidden: int
+    ffn: int
+    chunk: int
+    seed: int = 0
+
+
+FFN_WORKLOADS = {w.name: w for w in [
+    # the 7B model's width (4096) with a 4x feedforward, over the 7B share's
+    # local block of 32768 tokens, chunks of 2048
+    FfnWorkload("ffn_7b_share", 1, 32768, 4096, 16384, 2048, seed=20261206),
+    FfnWorkload("ffn_small", 2, 256, 256, 1024, 64, seed=20261207),
+]}
+
+
+def make_ffn_inputs(w: FfnWorkload, device="cpu"):
+    """x ~ N(0, 1); w1 ~ N(0, 1/hidden); w2 ~ N(0, 1/ffn); b1, b2 ~ N(0, 0.1^2);
+    each drawn in fp32 with its own seed and rounded (RNE) to bf16."""
+    H, Fh = w.hidden, w.ffn
+    x = make_block((w.batch, w.seq, H), w.seed * 31 + 1, 1.0, "bf16", device)
+    w1 = make_block((H, Fh), w.seed * 31 + 2, H ** -0.5, "bf16", device)
+    b1 = make_block((Fh,), w.seed * 31 + 3, 0.1, "bf16", device)
+    w2 = make_block((Fh, H), w.seed * 31 + 4, Fh ** -0.5, "bf16", device)
+    b2 = make_block((H,), w.seed * 31 + 5, 0.1, "bf16", device)
+    return x, w1, b1, w2, b2
