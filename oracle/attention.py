@@ -24,6 +24,11 @@ Sources (web pages; cited by title and section):
   below-or-on-diagonal test passes; causal_block_size selects the causal
   granularity).
 
+* [RA-review] section 六 "相关工作" and section 七 "局限性": causal
+  attention leaves the ring unbalanced (later devices hold more visible
+  pairs), which Striped Attention's striped partition of the sequence
+  removes; it applies to causal attention only.
+
 Readings taken where the pages are silent (each is also listed in the
 design notes of the repository):
 
@@ -38,6 +43,11 @@ design notes of the repository):
 * the carry starts at max = -inf, numerator = 0, denominator = 0, and a
   correction whose old max is -inf is 0 (the old numerator and denominator
   are 0, so any finite factor gives the same result);
+* striped placement: global position p is held by device p mod N at local
+  index p div N (device r's block holds positions r, r + N, r + 2N, ...);
+  k, v and segment ids are stored block by block in that order (storage
+  row kb * Lq + j holds position j * N + kb), and every mask is taken on
+  global positions;
 * outputs: out = numerator / denominator and the natural-log log-sum-exp
   lse = max + ln(denominator), laid out [B, H, Lq]; a query row with no
   visible key gets out = 0 and lse = -inf.
@@ -65,6 +75,8 @@ __all__ = [
     "skip_map_closed",
     "skip_map_bruteforce",
     "count_visible_pairs",
+    "striped_pair_runs",
+    "PLACEMENTS",
 ]
 
 
@@ -72,19 +84,45 @@ __all__ = [
 # Positions and the visibility mask
 # ---------------------------------------------------------------------------
 
-def query_positions(seq_q: int, ring_index: int) -> np.ndarray:
+PLACEMENTS = ("contiguous", "striped")
+
+
+def _check_placement(placement: str) -> None:
+    if placement not in PLACEMENTS:
+        raise ValueError(f"placement must be one of {PLACEMENTS}")
+
+
+def query_positions(seq_q: int, ring_index: int, ring_size: int = 1,
+                    placement: str = "contiguous") -> np.ndarray:
     """Global positions of the local query block.
 
-    [RA-review] 三 "分块注意力": the sequence Q = [Q_0 .. Q_{N-1}] is split
-    into N equal blocks and device i holds Q_i, so local row t of device i
-    sits at global position i * Lq + t.
+    Contiguous ([RA-review] 三 "分块注意力"): the sequence Q = [Q_0 ..
+    Q_{N-1}] is split into N equal blocks and device i holds Q_i, so local
+    row t of device i sits at global position i * Lq + t.
+    Striped (reading of [RA-review] 六/七): local row t of device i sits at
+    global position t * N + i.
     """
-    return ring_index * seq_q + np.arange(seq_q, dtype=np.int64)
+    _check_placement(placement)
+    t = np.arange(seq_q, dtype=np.int64)
+    if placement == "striped":
+        return t * ring_size + ring_index
+    return ring_index * seq_q + t
 
 
-def key_positions(seq_k: int) -> np.ndarray:
-    """Global positions of all keys: K = [K_0 .. K_{N-1}] in global order."""
-    return np.arange(seq_k, dtype=np.int64)
+def key_positions(seq_k: int, ring_size: int = 1,
+                  placement: str = "contiguous") -> np.ndarray:
+    """Global positions of the stored keys, in storage order.
+
+    Storage row s = kb * Lq + j holds key j of block kb: global position s
+    (contiguous: K = [K_0 .. K_{N-1}] in global order) or j * N + kb
+    (striped).
+    """
+    _check_placement(placement)
+    s = np.arange(seq_k, dtype=np.int64)
+    if placement == "striped":
+        seq_q = seq_k // ring_size
+        return (s % seq_q) * ring_size + s // seq_q
+    return s
 
 
 def _scale(head_dim: int) -> float:
@@ -155,7 +193,8 @@ def attention_fwd(q, k, v, segment_ids=None, causal_block_size=None,
                   rows: Optional[Sequence[int]] = None,
                   heads: Optional[Sequence[int]] = None,
                   kv_len: Optional[int] = None,
-                  max_scores: int = 1 << 25):
+                  max_scores: int = 1 << 25,
+                  placement: str = "contiguous"):
     """Masked softmax(Q K^T / sqrt(D)) V for one device's query block.
 
     [RA-review] 三 "核心公式" (self-attention), with the query block and
@@ -165,8 +204,12 @@ def attention_fwd(q, k, v, segment_ids=None, causal_block_size=None,
     k, v: [B, S, H, D] with S = ring_size * Lq, all blocks in global order;
           or only the first ``kv_len`` keys when the rest are provably
           causally invisible from every requested row.
-    segment_ids: [B, S] ints over the whole sequence, or None.
+    segment_ids: [B, S] ints over the whole sequence in storage order (the
+          order of the rows of k), or None.
     rows / heads: optional subsets of local query rows / heads.
+    placement: "contiguous" (the pages' blocks) or "striped" (position p on
+          device p mod N); it sets the global positions that the causal
+          mask compares.
 
     Returns (out [B, R, Hs, D], lse [B, Hs, R]) in float64 where R and Hs are
     the numbers of selected rows and heads.
@@ -187,9 +230,12 @@ def attention_fwd(q, k, v, segment_ids=None, causal_block_size=None,
         segment_ids.cpu().numpy() if hasattr(segment_ids, "cpu") else segment_ids,
         dtype=np.int64)
 
-    pq_all = query_positions(Lq, ring_index)[rows]
+    pq_all = query_positions(Lq, ring_index, ring_size, placement)[rows]
+    sq_all = ring_index * Lq + rows          # storage rows of the queries
+    if placement == "striped" and kv_len < S:
+        raise ValueError("kv_len < seq_k is only supported for contiguous placement")
     _check_kv_tail_masked(pq_all, kv_len, S, causal_block_size)
-    pk = key_positions(kv_len)
+    pk = key_positions(S, ring_size, placement)[:kv_len]
     scale = _scale(D)
 
     out = np.zeros((B, rows.shape[0], len(heads), D), dtype=np.float64)
@@ -204,7 +250,7 @@ def attention_fwd(q, k, v, segment_ids=None, causal_block_size=None,
                 pq = pq_all[r0:r0 + step]
                 s = (q[b, sel, h, :] @ K.T) * scale
                 allow = visible(pq, pk, causal_block_size,
-                                None if seg is None else seg[b, pq],
+                                None if seg is None else seg[b, sq_all[r0:r0 + step]],
                                 None if seg is None else seg[b, :kv_len])
                 s = np.where(allow, s, -np.inf)
                 m = s.max(axis=1) if kv_len > 0 else np.full(len(sel), -np.inf)
@@ -253,14 +299,27 @@ def _chunk_counts(seq_q: int, q_chunk: int, k_chunk: int):
     return seq_q // q_chunk, seq_q // k_chunk
 
 
+def striped_pair_runs(a: int, q_chunk: int, kb: int, bb: int, k_chunk: int,
+                      ring_size: int, ring_index: int, causal_block_size: int) -> bool:
+    """The same run test under striped placement: positions grow with the
+    local index inside every block, so the pair holds a visible pair iff its
+    last query (local row (a+1)*qc - 1, position ((a+1)*qc - 1) * N + r) sees
+    its first key (local row bb*kc of block kb, position bb*kc*N + kb)."""
+    last_q = ((a + 1) * q_chunk - 1) * ring_size + ring_index
+    first_k = bb * k_chunk * ring_size + kb
+    c = causal_block_size
+    return last_q // c >= first_k // c
+
+
 def skip_map_closed(causal_block_size, q_chunk: int, k_chunk: int, seq_q: int,
-                    ring_size: int, ring_index: int):
+                    ring_size: int, ring_index: int, placement: str = "contiguous"):
     """The skip decisions by the closed-form test, in ring-step order.
 
     Returns (kv_block_of_step int32 [N], run uint8 [N, Lq/qc, Lq/kc]) where
     run[t, a, b] = 1 iff query chunk a of this device runs against key chunk
     b of the block used at step t.
     """
+    _check_placement(placement)
     nq, nk = _chunk_counts(seq_q, q_chunk, k_chunk)
     order = ring_order(ring_size, ring_index)
     run = np.zeros((ring_size, nq, nk), dtype=np.uint8)
@@ -269,6 +328,9 @@ def skip_map_closed(causal_block_size, q_chunk: int, k_chunk: int, seq_q: int,
             for bb in range(nk):
                 if causal_block_size is None or causal_block_size == 0:
                     run[t, a, bb] = 1
+                elif placement == "striped":
+                    run[t, a, bb] = striped_pair_runs(a, q_chunk, kb, bb, k_chunk, ring_size,
+                                                      ring_index, int(causal_block_size))
                 else:
                     run[t, a, bb] = below_or_on_diag(
                         ring_index * nq + a, q_chunk, kb * nk + bb, k_chunk,
@@ -277,16 +339,18 @@ def skip_map_closed(causal_block_size, q_chunk: int, k_chunk: int, seq_q: int,
 
 
 def skip_map_bruteforce(causal_block_size, q_chunk: int, k_chunk: int,
-                        seq_q: int, ring_size: int, ring_index: int):
+                        seq_q: int, ring_size: int, ring_index: int,
+                        placement: str = "contiguous"):
     """The same decisions by brute force: a chunk pair runs iff any of its
     (query, key) pairs is causally visible."""
     nq, nk = _chunk_counts(seq_q, q_chunk, k_chunk)
     order = ring_order(ring_size, ring_index)
     c = None if not causal_block_size else int(causal_block_size)
-    pq = query_positions(seq_q, ring_index)
+    pq = query_positions(seq_q, ring_index, ring_size, placement)
+    pk_all = key_positions(ring_size * seq_q, ring_size, placement)
     run = np.zeros((ring_size, nq, nk), dtype=np.uint8)
     for t, kb in enumerate(order):
-        pk = kb * seq_q + np.arange(seq_q, dtype=np.int64)
+        pk = pk_all[kb * seq_q:(kb + 1) * seq_q]
         allow = _causal_visible(pq, pk, c)
         for a in range(nq):
             for bb in range(nk):
@@ -297,21 +361,24 @@ def skip_map_bruteforce(causal_block_size, q_chunk: int, k_chunk: int,
 
 def count_visible_pairs(seq_q: int, ring_size: int, ring_index: int,
                         causal_block_size, segment_ids=None, batch: int = 1,
-                        rows: Optional[Iterable[int]] = None) -> int:
+                        rows: Optional[Iterable[int]] = None,
+                        placement: str = "contiguous") -> int:
     """Number of visible (query, key) pairs for one head, summed over the
-    batch, by explicit enumeration (used to check work counts)."""
+    batch, by explicit enumeration (used to check work counts).  Segment ids
+    are in storage order."""
     c = None if not causal_block_size else int(causal_block_size)
     S = ring_size * seq_q
-    pq = query_positions(seq_q, ring_index)
-    if rows is not None:
-        pq = pq[np.asarray(list(rows), dtype=np.int64)]
-    pk = key_positions(S)
+    sel = np.arange(seq_q, dtype=np.int64) if rows is None else np.asarray(list(rows),
+                                                                           dtype=np.int64)
+    pq = query_positions(seq_q, ring_index, ring_size, placement)[sel]
+    sq = ring_index * seq_q + sel
+    pk = key_positions(S, ring_size, placement)
     total = 0
     for b in range(batch):
         seg = None if segment_ids is None else np.asarray(segment_ids)[b]
         for r0 in range(0, pq.shape[0], 256):
             p = pq[r0:r0 + 256]
-            total += int(visible(p, pk, c, None if seg is None else seg[p],
+            total += int(visible(p, pk, c, None if seg is None else seg[sq[r0:r0 + 256]],
                                  seg).sum())
     return total
 
@@ -325,7 +392,8 @@ def lazy_blockwise_fwd(q, k, v, segment_ids=None, causal_block_size=None,
                        q_chunk: Optional[int] = None,
                        k_chunk: Optional[int] = None,
                        order: Optional[Sequence[int]] = None,
-                       use_skip: bool = True):
+                       use_skip: bool = True,
+                       placement: str = "contiguous"):
     """The blockwise formulation: fold KV blocks into a running carry.
 
     [RA-review] 三 "排列不变性": attention of Q_i over all blocks equals the
@@ -341,7 +409,8 @@ def lazy_blockwise_fwd(q, k, v, segment_ids=None, causal_block_size=None,
     where w are the (masked) scaled logits of the chunk pair.  Blocks are
     visited in ``order`` (default: the ring order), key chunks of a block in
     order, and a chunk pair is skipped when the below-or-on-diagonal test
-    fails ([RA-code] "3. 因果注意力掩码支持").
+    fails ([RA-code] "3. 因果注意力掩码支持"; under striped placement the
+    same test on the pair's positions).
     """
     q = _as_f64(q)
     k = _as_f64(k)
@@ -359,7 +428,8 @@ def lazy_blockwise_fwd(q, k, v, segment_ids=None, causal_block_size=None,
     c = None if not causal_block_size else int(causal_block_size)
     seg = None if segment_ids is None else np.asarray(segment_ids, dtype=np.int64)
     scale = _scale(D)
-    pq_all = query_positions(Lq, ring_index)
+    pq_all = query_positions(Lq, ring_index, ring_size, placement)
+    pk_all = key_positions(S, ring_size, placement)
 
     out = np.zeros((B, Lq, H, D), dtype=np.float64)
     lse = np.full((B, H, Lq), -np.inf, dtype=np.float64)
@@ -369,19 +439,25 @@ def lazy_blockwise_fwd(q, k, v, segment_ids=None, causal_block_size=None,
                 rs = slice(a * qc, (a + 1) * qc)
                 Qa = q[b, rs, h, :]
                 pq = pq_all[rs]
+                sq = np.arange(ring_index * Lq + a * qc, ring_index * Lq + (a + 1) * qc)
                 prev_max = np.full(qc, -np.inf)
                 numer = np.zeros((qc, D))
                 denom = np.zeros(qc)
                 for kb in order:
                     for bb in range(nk):
-                        if use_skip and c is not None and not below_or_on_diag(
-                                ring_index * nq + a, qc, kb * nk + bb, kc, c):
-                            continue
+                        if use_skip and c is not None:
+                            runs = (striped_pair_runs(a, qc, kb, bb, kc, ring_size,
+                                                      ring_index, c)
+                                    if placement == "striped" else
+                                    below_or_on_diag(ring_index * nq + a, qc, kb * nk + bb,
+                                                     kc, c))
+                            if not runs:
+                                continue
                         ks = slice(kb * Lq + bb * kc, kb * Lq + (bb + 1) * kc)
-                        pk = key_positions(S)[ks]
+                        pk = pk_all[ks]
                         w = (Qa @ k[b, ks, h, :].T) * scale
                         allow = visible(pq, pk, c,
-                                        None if seg is None else seg[b, pq],
+                                        None if seg is None else seg[b, sq],
                                         None if seg is None else seg[b, ks])
                         w = np.where(allow, w, -np.inf)
                         new_max = np.maximum(prev_max, w.max(axis=1))

@@ -70,13 +70,16 @@ def attention_bwd(q, k, v, dout, segment_ids=None, causal_block_size=None,
                   rows: Optional[Sequence[int]] = None,
                   heads: Optional[Sequence[int]] = None,
                   kv_len: Optional[int] = None,
-                  max_scores: int = 1 << 24):
+                  max_scores: int = 1 << 24,
+                  placement: str = "contiguous"):
     """Gradients of sum(dout * out) for one device's query block.
 
     q, dout: [B, Lq, H, D] (ring position ``ring_index``); k, v: [B, S, H, D]
     with S = ring_size * Lq (or the first ``kv_len`` keys when the rest are
-    causally invisible from every requested row); segment_ids [B, S] or None.
+    causally invisible from every requested row); segment_ids [B, S] in
+    storage order (the order of the rows of k) or None.
     rows / heads: optional subsets of local query rows / heads.
+    placement: "contiguous" or "striped", as in ``attention.attention_fwd``.
 
     Returns (dq [B, R, Hs, D], dk [B, kv_len, Hs, D], dv [B, kv_len, Hs, D])
     in float64.  dq is exact for the selected rows; dk and dv hold the
@@ -102,9 +105,12 @@ def attention_bwd(q, k, v, dout, segment_ids=None, causal_block_size=None,
         segment_ids.cpu().numpy() if hasattr(segment_ids, "cpu") else segment_ids,
         dtype=np.int64)
 
-    pq_all = query_positions(Lq, ring_index)[rows]
+    pq_all = query_positions(Lq, ring_index, ring_size, placement)[rows]
+    sq_all = ring_index * Lq + rows          # storage rows of the queries
+    if placement == "striped" and kv_len < S:
+        raise ValueError("kv_len < seq_k is only supported for contiguous placement")
     _check_kv_tail_masked(pq_all, kv_len, S, causal_block_size)
-    pk = key_positions(kv_len)
+    pk = key_positions(S, ring_size, placement)[:kv_len]
     scale = _scale(D)
 
     dq = np.zeros((B, rows.shape[0], len(heads), D), dtype=np.float64)
@@ -121,7 +127,7 @@ def attention_bwd(q, k, v, dout, segment_ids=None, causal_block_size=None,
                 Q = q[b, sel, h, :]
                 dO = dout[b, sel, h, :]
                 allow = visible(pq, pk, causal_block_size,
-                                None if seg is None else seg[b, pq],
+                                None if seg is None else seg[b, sq_all[r0:r0 + step]],
                                 None if seg is None else seg[b, :kv_len])
                 s = np.where(allow, (Q @ K.T) * scale, -np.inf)
                 p, _ = _softmax_rows(s, allow)

@@ -367,7 +367,7 @@ def _mut_causal_token_level(monkeypatch):
 
 def _mut_no_ring_offset(monkeypatch):
     monkeypatch.setattr(oa, "query_positions",
-                        lambda seq_q, r: np.arange(seq_q, dtype=np.int64))
+                        lambda seq_q, r, *rest: np.arange(seq_q, dtype=np.int64))
 
 
 def _mut_segments_ignored(monkeypatch):

@@ -242,7 +242,7 @@ def _mut_segments_ignored(mp):
 
 
 def _mut_no_ring_offset(mp):
-    mp.setattr(ob, "query_positions", lambda lq, r: np.arange(lq, dtype=np.int64))
+    mp.setattr(ob, "query_positions", lambda lq, r, *rest: np.arange(lq, dtype=np.int64))
 
 
 BWD_MUTATIONS = [_mut_delta_dropped, _mut_ds_sign, _mut_ds_no_p, _mut_scale_dropped,
