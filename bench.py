@@ -36,20 +36,29 @@ PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "blockwise_fwd_share_7b_512k_traffic.json")
 
 
-def visible_keys_per_row(seq_q: int, ring_size: int, ring_index: int, causal) -> np.ndarray:
-    """Causally visible keys of each local query row (segments ignored)."""
+def visible_keys_per_row(seq_q: int, ring_size: int, ring_index: int, causal,
+                         placement: str = "contiguous") -> np.ndarray:
+    """Causally visible keys of each local query row (segments ignored).
+    Striped placement (token causal): row i sees i + 1 keys of each block
+    kb <= r and i of each block kb > r."""
     S = ring_size * seq_q
-    pq = ring_index * seq_q + np.arange(seq_q, dtype=np.int64)
+    i = np.arange(seq_q, dtype=np.int64)
     if not causal:
         return np.full(seq_q, S, dtype=np.int64)
+    if placement == "striped":
+        if int(causal) != 1:
+            raise ValueError("striped placement is token causal")
+        return ring_size * (i + 1) - (ring_size - 1 - ring_index)
     c = int(causal)
+    pq = ring_index * seq_q + i
     return np.minimum((pq // c + 1) * c, S)
 
 
 def causal_flops(w, ring_index: int) -> float:
     """F = 4 * D * H * B * sum over rows of causally visible keys: two
     GEMMs, two flops per multiply-add, per visible (query, key) pair."""
-    n = int(visible_keys_per_row(w.seq_q, w.ring_size, ring_index, w.causal_block_size).sum())
+    n = int(visible_keys_per_row(w.seq_q, w.ring_size, ring_index, w.causal_block_size,
+                                 w.placement).sum())
     return 4.0 * w.head_dim * w.heads * w.batch * n
 
 
@@ -93,7 +102,7 @@ def cpu_baseline(w, q, k, v, seg, ring_index: int, rows: int, flops_total: float
     import torch
     head = 0
     sel = np.linspace(0, w.seq_q - 1, rows).astype(np.int64)
-    kv_len = w.seq_k if not w.causal_block_size else int(
+    kv_len = w.seq_k if (not w.causal_block_size or w.placement != "contiguous") else int(
         min(w.seq_k, ((ring_index * w.seq_q + w.seq_q - 1) // w.causal_block_size + 1)
             * w.causal_block_size))
     qh = q[:1, :, head:head + 1].contiguous().cpu()
@@ -109,13 +118,13 @@ def cpu_baseline(w, q, k, v, seg, ring_index: int, rows: int, flops_total: float
     t0 = time.perf_counter()
     if gh is None:
         oracle.attention_fwd(qh, kh, vh, segh, w.causal_block_size, w.ring_size, ring_index,
-                             rows=sel, kv_len=kv_len)
+                             rows=sel, kv_len=kv_len, placement=w.placement)
     else:
         oracle.attention_bwd(qh, kh, vh, gh, segh, w.causal_block_size, w.ring_size,
-                             ring_index, rows=sel, kv_len=kv_len)
+                             ring_index, rows=sel, kv_len=kv_len, placement=w.placement)
     dt = time.perf_counter() - t0
     pairs = int(visible_keys_per_row(w.seq_q, w.ring_size, ring_index,
-                                     w.causal_block_size)[sel].sum())
+                                     w.causal_block_size, w.placement)[sel].sum())
     flops = (4.0 if gh is None else 10.0) * w.head_dim * pairs
     rate = flops / dt
     return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": int(cores),
@@ -136,8 +145,11 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="query rows of the CPU oracle sample (0 = skip)")
     ap.add_argument("--workload", default=WORKLOAD,
-                    choices=["small_causal", "share_7b_512k", "packed_documents", "share_65b_4m"],
+                    choices=["small_causal", "share_7b_512k", "packed_documents", "share_65b_4m",
+                             "small_causal_striped", "share_7b_512k_striped"],
                     help="bf16 workload to time (default: the 7B-shaped share)")
+    ap.add_argument("--ring-index", type=int, default=None,
+                    help="time this ring position instead of the workload's own list")
     ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd", "ffn"], default="fwd",
                     help="time the attention forward (default), its backward, or the "
                          "blockwise feedforward")
@@ -165,6 +177,12 @@ def main():
         bench_ffn(args, dev)
         return
     w = workloads.get(args.workload)
+    if args.ring_index is not None:
+        import dataclasses
+        if not 0 <= args.ring_index < w.ring_size:
+            print(f"--ring-index must be in [0, {w.ring_size})", file=sys.stderr)
+            sys.exit(2)
+        w = dataclasses.replace(w, ring_indices=(args.ring_index,))
     r = w.ring_indices[0]
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     q, k, v = workloads.make_qkv(w, r, device=dev)
@@ -186,6 +204,9 @@ def main():
     if bwd:
         # the forward's outputs of every listed ring position, and the gradients
         douts = [workloads.make_dout(w, ri, device=dev) for ri in w.ring_indices]
+        if w.placement != "contiguous":
+            print("--pass bwd takes contiguous placement only", file=sys.stderr)
+            sys.exit(2)
         fw = [ra.blockwise_attn_fwd(qi, k, v, seg, w.causal_block_size, w.q_chunk, w.k_chunk,
                                     w.ring_size, ri) for ri, qi in zip(w.ring_indices, qs)]
         f32 = dict(dtype=torch.float32, device=dev)
@@ -203,7 +224,8 @@ def main():
                                       ri, dq=dq, dk=dk, dv=dv, delta=delta)
             else:
                 ra.blockwise_attn_fwd(qi, k, v, seg, w.causal_block_size, w.q_chunk,
-                                      w.k_chunk, w.ring_size, ri, out=out, lse=lse)
+                                      w.k_chunk, w.ring_size, ri, out=out, lse=lse,
+                                      placement=w.placement)
 
     for _ in range(args.warmup):
         step()
@@ -255,6 +277,7 @@ def main():
                    "heads": w.heads, "head_dim": w.head_dim,
                    "causal_block_size": w.causal_block_size,
                    "q_chunk": w.q_chunk, "k_chunk": w.k_chunk, "pass": args.pass_,
+                   "placement": w.placement,
                    "flops_per_step": flops, "ms_min": round(min(per), 3),
                    "wall_s": round(wall, 3)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),

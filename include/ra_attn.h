@@ -64,6 +64,10 @@ typedef enum {
 
 typedef enum { RA_BF16 = 0, RA_F32 = 1 } ra_dtype_t;
 
+/* Which global positions a device's block holds (see
+ * ra_blockwise_attn_fwd_placed). */
+typedef enum { RA_PLACE_CONTIGUOUS = 0, RA_PLACE_STRIPED = 1 } ra_placement_t;
+
 /*
  * ra_blockwise_attn_fwd -- the forward of one ring position.
  *
@@ -117,6 +121,45 @@ ra_status_t ra_blockwise_attn_fwd_ex(const void* q, const void* k,
                                      int64_t head_dim, ra_dtype_t dtype,
                                      void* out, float* lse, uint8_t* run_map,
                                      void* stream);
+
+/*
+ * ra_blockwise_attn_fwd_placed -- the forward under a chosen placement of
+ * the sequence on the ring.
+ *
+ * The review of "Ring Attention with Blockwise Transformers for
+ * Near-Infinite Context" (sections 六 and 七) notes that causal attention
+ * leaves contiguous blocks unbalanced -- device r holds about (r + 1/2)
+ * blocks of visible pairs -- and names Striped Attention's striped
+ * partition as the fix, for causal attention only.  Reading taken here:
+ *
+ *   RA_PLACE_CONTIGUOUS: block r holds positions r*Lq .. r*Lq + Lq - 1
+ *       (ra_blockwise_attn_fwd);
+ *   RA_PLACE_STRIPED: block r holds positions r, r + N, r + 2N, ...: query
+ *       row i has position pq = i*N + r and storage row kb*Lq + j of k, v
+ *       and segment_ids holds position j*N + kb.
+ *
+ * The visibility rule is unchanged: it compares positions (causal) and the
+ * segment ids stored with the query's row (r*Lq + i) and the key's row
+ * (segment_ids stay in storage order).  Under striped placement every
+ * device holds N*Lq*(Lq+1)/2 - Lq*(N-1-r) visible pairs (token causal).
+ * Ring order, layouts, arithmetic and outputs are those of
+ * ra_blockwise_attn_fwd; run_map is that of ra_blockwise_attn_fwd_ex (a
+ * chunk pair runs iff it holds a visible pair under the placement).
+ *
+ * Errors as for ra_blockwise_attn_fwd_ex, plus RA_E_INVALID for an unknown
+ * placement and RA_E_UNSUPPORTED for RA_PLACE_STRIPED with an effective
+ * causal_block_size other than 0 or 1 (a causal block at least as long as
+ * the sequence counts as 0).
+ */
+ra_status_t ra_blockwise_attn_fwd_placed(const void* q, const void* k,
+                                         const void* v, const int32_t* segment_ids,
+                                         int64_t causal_block_size, int64_t q_chunk,
+                                         int64_t k_chunk, int32_t ring_size,
+                                         int32_t ring_index, ra_placement_t placement,
+                                         int64_t batch, int64_t seq_q, int64_t heads,
+                                         int64_t head_dim, ra_dtype_t dtype,
+                                         void* out, float* lse, uint8_t* run_map,
+                                         void* stream);
 
 /*
  * ra_blockwise_attn_bwd -- the gradients of one ring position's share.
@@ -222,6 +265,22 @@ ra_status_t ra_blockwise_plan(int64_t causal_block_size, int64_t q_chunk,
                               int32_t ring_size, int32_t ring_index,
                               int32_t* kv_block_of_step, uint8_t* run_bits,
                               int64_t* n_run_chunk_pairs);
+
+/*
+ * ra_blockwise_plan_placed -- ra_blockwise_plan under a placement (see
+ * ra_blockwise_attn_fwd_placed).  Under RA_PLACE_STRIPED the chunk pair
+ * (a, b) of the block kb used at step t runs iff its last query, position
+ * ((a+1)*q_chunk - 1)*N + r, sees its first key, position b*k_chunk*N + kb
+ * (positions grow with the local index inside a block, so this is the test
+ * for any visible pair).  Any causal_block_size is accepted here.  Returns
+ * RA_OK or RA_E_INVALID (also for an unknown placement).
+ */
+ra_status_t ra_blockwise_plan_placed(int64_t causal_block_size, int64_t q_chunk,
+                                     int64_t k_chunk, int64_t seq_q,
+                                     int32_t ring_size, int32_t ring_index,
+                                     ra_placement_t placement,
+                                     int32_t* kv_block_of_step, uint8_t* run_bits,
+                                     int64_t* n_run_chunk_pairs);
 
 /* Text of the last error on the calling thread ("" if none).  The pointer
  * stays valid until the next ra_* call on the same thread. */

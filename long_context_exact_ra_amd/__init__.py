@@ -22,6 +22,14 @@ __all__ = ["RaError", "blockwise_attn_fwd", "blockwise_attn_bwd", "blockwise_ffn
 
 RA_OK, RA_E_INVALID, RA_E_UNSUPPORTED, RA_E_HIP = 0, 1, 2, 3
 RA_BF16, RA_F32 = 0, 1
+RA_PLACE_CONTIGUOUS, RA_PLACE_STRIPED = 0, 1
+_PLACEMENTS = {"contiguous": RA_PLACE_CONTIGUOUS, "striped": RA_PLACE_STRIPED}
+
+
+def _placement(name: str) -> int:
+    if name not in _PLACEMENTS:
+        raise ValueError(f"placement must be one of {sorted(_PLACEMENTS)}")
+    return _PLACEMENTS[name]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -55,6 +63,9 @@ def load_library():
     lib.ra_blockwise_attn_fwd.restype = ctypes.c_int
     lib.ra_blockwise_attn_fwd_ex.argtypes = fwd_args + [c_vp, c_vp]
     lib.ra_blockwise_attn_fwd_ex.restype = ctypes.c_int
+    lib.ra_blockwise_attn_fwd_placed.argtypes = (fwd_args[:9] + [ctypes.c_int] + fwd_args[9:]
+                                                 + [c_vp, c_vp])
+    lib.ra_blockwise_attn_fwd_placed.restype = ctypes.c_int
     lib.ra_blockwise_attn_bwd.argtypes = fwd_args[:14] + [c_vp] * 8
     lib.ra_blockwise_attn_bwd.restype = ctypes.c_int
     lib.ra_blockwise_ffn_workspace_bytes.argtypes = [c_i64, c_i64]
@@ -65,6 +76,9 @@ def load_library():
     lib.ra_blockwise_plan.argtypes = [c_i64, c_i64, c_i64, c_i64, c_i32, c_i32,
                                       c_vp, c_vp, c_vp]
     lib.ra_blockwise_plan.restype = ctypes.c_int
+    lib.ra_blockwise_plan_placed.argtypes = [c_i64, c_i64, c_i64, c_i64, c_i32, c_i32,
+                                             ctypes.c_int, c_vp, c_vp, c_vp]
+    lib.ra_blockwise_plan_placed.restype = ctypes.c_int
     lib.ra_last_error.argtypes = []
     lib.ra_last_error.restype = ctypes.c_char_p
     lib.ra_version.argtypes = []
@@ -87,11 +101,12 @@ def _check(status: int):
 
 
 def blockwise_plan(causal_block_size: Optional[int], q_chunk: int, k_chunk: int,
-                   seq_q: int, ring_size: int, ring_index: int):
+                   seq_q: int, ring_size: int, ring_index: int,
+                   placement: str = "contiguous"):
     """Host-only ring order and chunk-pair skip decisions.
 
     Returns (kv_block_of_step int32 [N], run_bits uint8 [N, Lq/qc, Lq/kc],
-    n_run_chunk_pairs).
+    n_run_chunk_pairs).  placement: "contiguous" or "striped".
     """
     import numpy as np
     lib = load_library()
@@ -100,16 +115,17 @@ def blockwise_plan(causal_block_size: Optional[int], q_chunk: int, k_chunk: int,
     nk = seq_q // k_chunk if k_chunk > 0 else 0
     run = np.zeros((max(ring_size, 1), nq, nk), dtype=np.uint8)
     n = ctypes.c_int64(0)
-    _check(lib.ra_blockwise_plan(int(causal_block_size or 0), q_chunk, k_chunk, seq_q,
-                                 ring_size, ring_index, order.ctypes.data,
-                                 run.ctypes.data, ctypes.addressof(n)))
+    _check(lib.ra_blockwise_plan_placed(int(causal_block_size or 0), q_chunk, k_chunk, seq_q,
+                                        ring_size, ring_index, _placement(placement),
+                                        order.ctypes.data, run.ctypes.data,
+                                        ctypes.addressof(n)))
     return order, run, n.value
 
 
 def blockwise_attn_fwd(q, k, v, segment_ids=None, causal_block_size: Optional[int] = None,
                        q_chunk: int = 512, k_chunk: int = 512, ring_size: int = 1,
                        ring_index: int = 0, *, out=None, lse=None, run_map=None,
-                       stream=None) -> Tuple[object, object]:
+                       stream=None, placement: str = "contiguous") -> Tuple[object, object]:
     """Forward of ring position ``ring_index``: returns (out, lse).
 
     q: [B, Lq, H, D] and k, v: [B, ring_size * Lq, H, D], contiguous CUDA
@@ -119,7 +135,9 @@ def blockwise_attn_fwd(q, k, v, segment_ids=None, causal_block_size: Optional[in
     allocated when not given.  run_map: optional uint8 device tensor
     [ring_size, Lq / q_chunk, Lq / k_chunk] that receives the kernel's
     chunk-pair decisions.  The work is enqueued on ``stream`` (default: the
-    current torch stream).
+    current torch stream).  placement: "contiguous" (block r holds positions
+    r*Lq ..) or "striped" (block r holds positions r, r + N, ..; k, v and
+    segment_ids in that storage order; token causal or non-causal only).
     """
     import torch
     lib = load_library()
@@ -152,9 +170,11 @@ def blockwise_attn_fwd(q, k, v, segment_ids=None, causal_block_size: Optional[in
         stream = torch.cuda.current_stream(q.device)
     sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     dt = RA_BF16 if q.dtype == torch.bfloat16 else RA_F32
+    place = _placement(placement)
     args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), seg_ptr, int(causal_block_size or 0),
             q_chunk, k_chunk, ring_size, ring_index, B, Lq, H, D, dt,
             out.data_ptr(), lse.data_ptr()]
+    map_ptr = None
     if run_map is not None:
         nq = Lq // q_chunk if q_chunk else 0
         nk = Lq // k_chunk if k_chunk else 0
@@ -162,7 +182,11 @@ def blockwise_attn_fwd(q, k, v, segment_ids=None, causal_block_size: Optional[in
                 or not run_map.is_contiguous()
                 or tuple(run_map.shape) != (ring_size, nq, nk)):
             raise ValueError("run_map must be a contiguous uint8 device tensor [N, nq, nk]")
-        _check(lib.ra_blockwise_attn_fwd_ex(*args, run_map.data_ptr(), sptr))
+        map_ptr = run_map.data_ptr()
+    if place != RA_PLACE_CONTIGUOUS:
+        _check(lib.ra_blockwise_attn_fwd_placed(*args[:9], place, *args[9:], map_ptr, sptr))
+    elif map_ptr is not None:
+        _check(lib.ra_blockwise_attn_fwd_ex(*args, map_ptr, sptr))
     else:
         _check(lib.ra_blockwise_attn_fwd(*args, sptr))
     return out, lse

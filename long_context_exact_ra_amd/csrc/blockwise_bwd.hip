@@ -415,7 +415,7 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
   const int kend = std::min(p.seq_k, k0 + kBlockNBwd);
 #pragma unroll
   for (int t = 0; t < kBlockNBwd / 64; ++t)
-    issue_rows<D, kWaves>(TileInfo{k0 + 64 * t, kend, 0, 0, 1}, vbase0, rs_bytes, wave, lane_off,
+    issue_rows<D, kWaves>(TileInfo{k0 + 64 * t, kend, 0, 0, 1, 0}, vbase0, rs_bytes, wave, lane_off,
                           vres + t * L::ELEMS);
   __builtin_amdgcn_s_waitcnt(0);
 
@@ -437,7 +437,7 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
   auto fetch = [&](int qt, int s) {
     const int q0 = q_lo + 64 * qt;
     __bf16* d = qs + s * L::QSTAGE;
-    issue_tile<D, kWaves, SEG>(TileInfo{q0, p.seq_q, 0, 0, 1}, qbase0, gbase0, sbase0, rs_bytes,
+    issue_tile<D, kWaves, SEG>(TileInfo{q0, p.seq_q, 0, 0, 1, 0}, qbase0, gbase0, sbase0, rs_bytes,
                                wave, lane, lane_off, lane_off, d, d + L::ELEMS,
                                reinterpret_cast<int32_t*>(d + 2 * L::ELEMS));
     const int nvalid = std::min(64, p.seq_q - q0);

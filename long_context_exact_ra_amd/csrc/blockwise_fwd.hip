@@ -265,33 +265,33 @@ struct PipeConst {
 
 // Record the tile under the fetch cursor as the content of stage S, start
 // its DMA and advance the cursor.
-template <int D, bool SEG, int S>
+template <int D, bool SEG, bool STRIPED, int S>
 __device__ __forceinline__ void fetch_next(const FwdParams& p, const PipeConst& k,
                                            PipeState<D>& st, __bf16* const* ks,
                                            __bf16* const* vs, int32_t* const* ss) {
-  st.ti[S] = tile_info<PipeCfg<D>::TN>(p, st.ic);
+  st.ti[S] = tile_info<PipeCfg<D>::TN, STRIPED>(p, st.ic);
   if (st.ic.valid) {
     issue_tile<D, PipeCfg<D>::kWaves, SEG>(st.ti[S], k.kbase0, k.vbase0, k.sbase0, k.rs_bytes,
                                            k.wave, k.lane, k.k_lane, k.v_lane, ks[S], vs[S],
                                            ss[S]);
-    cursor_next<PipeCfg<D>::TN>(p, st.ic, k.kend);
+    cursor_next<PipeCfg<D>::TN, STRIPED>(p, st.ic, k.kend);
   }
 }
 
 // One pipeline step: tile i lives in stage PH, tile i+1 in stage PH+1, the
 // DMA for tile i+3 goes into stage PH+3 (all mod 4).  Returns whether a next
 // tile exists.
-template <int D, bool SEG, int PH>
+template <int D, bool SEG, bool STRIPED, int PH>
 __device__ __forceinline__ bool pipe_step(const FwdParams& p, const PipeConst& k,
                                           const WaveLimits& lim, const bf16x8_t* qf,
                                           PipeState<D>& st, __bf16* const* ks,
                                           __bf16* const* vs, int32_t* const* ss) {
   constexpr int NPT = 2 * PipeCfg<D>::DPW + (SEG ? 1 : 0);  // DMA per wave per tile
   constexpr int S0 = PH, S1 = (PH + 1) & 3, S2 = (PH + 2) & 3, S3 = (PH + 3) & 3;
-  fetch_next<D, SEG, S3>(p, k, st, ks, vs, ss);
+  fetch_next<D, SEG, STRIPED, S3>(p, k, st, ks, vs, ss);
 
-  const TileFlags f0 = tile_flags<SEG>(st.ti[S0], lim);
-  const TileFlags f1 = tile_flags<SEG>(st.ti[S1], lim);
+  const TileFlags f0 = tile_flags<SEG, STRIPED>(st.ti[S0], lim);
+  const TileFlags f1 = tile_flags<SEG, STRIPED>(st.ti[S1], lim);
 
   // Tile i (logits in s_cur, already masked and max-folded): probabilities and
   // P.V.  Tile i+1: logits and row max.  Both 32-key halves of both tiles
@@ -336,7 +336,7 @@ __device__ __forceinline__ bool pipe_step(const FwdParams& p, const PipeConst& k
   return st.ti[S1].valid;
 }
 
-template <int D, bool SEG>
+template <int D, bool SEG, bool STRIPED>
 __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const FwdParams p) {
   using C = PipeCfg<D>;
   constexpr int NDB = D / 32;
@@ -362,9 +362,11 @@ __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const
   const int b = wc.b, h = wc.h, m0 = wc.m0;
   k.qg0 = m0 + k.wave * 32;
   k.wave_active = k.qg0 < p.seq_q;
+  // Storage row of the wave's first query (segment ids) and its query
+  // coordinate (causal limits; the local row under striped placement).
   const int64_t pq_first = (int64_t)p.ring_index * p.seq_q + k.qg0;
-  const WaveLimits lim = wave_limits(p, pq_first, k.lrow, k.wave_active);
-  k.kend = wg_kend<kBlockMBf16>(p, m0);
+  const WaveLimits lim = wave_limits(p, STRIPED ? k.qg0 : pq_first, k.lrow, k.wave_active);
+  k.kend = wg_kend<kBlockMBf16, STRIPED>(p, m0);
   k.seg_q = 0;
   if (SEG && k.wave_active) k.seg_q = p.seg[(int64_t)b * p.seq_k + pq_first + k.lrow];
 
@@ -403,10 +405,10 @@ __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const
 
   // Prologue: tiles 0, 1, 2 in flight, the cursor on tile 3.
   st.ic = Cursor{0, 0, 0, 0, 0, 0};
-  cursor_seek<C::TN>(p, st.ic, k.kend);
-  fetch_next<D, SEG, 0>(p, k, st, ks, vs, ss);
-  fetch_next<D, SEG, 1>(p, k, st, ks, vs, ss);
-  fetch_next<D, SEG, 2>(p, k, st, ks, vs, ss);
+  cursor_seek<C::TN, STRIPED>(p, st.ic, k.kend);
+  fetch_next<D, SEG, STRIPED, 0>(p, k, st, ks, vs, ss);
+  fetch_next<D, SEG, STRIPED, 1>(p, k, st, ks, vs, ss);
+  fetch_next<D, SEG, STRIPED, 2>(p, k, st, ks, vs, ss);
   // Tiles 0 and 1 must have landed: tile 1 is read by the first step's QK.
   constexpr int NPT = 2 * C::DPW + (SEG ? 1 : 0);
   if (st.ti[2].valid)
@@ -415,7 +417,7 @@ __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const
     wait_vm<0>();
   stage_barrier();
   if (st.ti[0].valid && k.wave_active) {
-    const TileFlags f = tile_flags<SEG>(st.ti[0], lim);
+    const TileFlags f = tile_flags<SEG, STRIPED>(st.ti[0], lim);
     qk_tile<D>(st.s[0], qf, ks[0], k.k_rd);
     const float mx = mask_max<true, SEG>(st.s[0], ss[0], k.half, f, lim.lane_lim, k.seg_q);
     carry_max<D>(st.w, mx, p.scale_log2);
@@ -423,10 +425,10 @@ __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const
 
   if (st.ti[0].valid) {
     for (;;) {
-      if (!pipe_step<D, SEG, 0>(p, k, lim, qf, st, ks, vs, ss)) break;
-      if (!pipe_step<D, SEG, 1>(p, k, lim, qf, st, ks, vs, ss)) break;
-      if (!pipe_step<D, SEG, 2>(p, k, lim, qf, st, ks, vs, ss)) break;
-      if (!pipe_step<D, SEG, 3>(p, k, lim, qf, st, ks, vs, ss)) break;
+      if (!pipe_step<D, SEG, STRIPED, 0>(p, k, lim, qf, st, ks, vs, ss)) break;
+      if (!pipe_step<D, SEG, STRIPED, 1>(p, k, lim, qf, st, ks, vs, ss)) break;
+      if (!pipe_step<D, SEG, STRIPED, 2>(p, k, lim, qf, st, ks, vs, ss)) break;
+      if (!pipe_step<D, SEG, STRIPED, 3>(p, k, lim, qf, st, ks, vs, ss)) break;
     }
   }
 
@@ -461,7 +463,7 @@ __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const
 // v_mfma_f32_32x32x2_f32 (one k-slot per lane half).  The P.V A operand is
 // V^T: lane (d, half) reads V[key][d] for the key its P^T slot holds.
 
-template <int D>
+template <int D, bool STRIPED>
 __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(const FwdParams p) {
   constexpr int TN = 32;
   constexpr int KS = D + 4;
@@ -483,8 +485,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(const FwdParams p)
   const int qg0 = m0 + wave * 32;
   const bool wave_active = qg0 < p.seq_q;
   const int64_t pq_first = (int64_t)p.ring_index * p.seq_q + qg0;
-  const WaveLimits lim = wave_limits(p, pq_first, lrow, wave_active);
-  const int64_t kend = wg_kend<kBlockMF32>(p, m0);
+  const WaveLimits lim = wave_limits(p, STRIPED ? qg0 : pq_first, lrow, wave_active);
+  const int64_t kend = wg_kend<kBlockMF32, STRIPED>(p, m0);
   const bool has_seg = p.seg != nullptr;
   int32_t seg_q = 0;
   if (has_seg && wave_active) seg_q = p.seg[(int64_t)b * p.seq_k + pq_first + lrow];
@@ -532,7 +534,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(const FwdParams p)
   };
 
   Cursor cur{0, 0, 0, 0, 0, 0};
-  cursor_seek<TN>(p, cur, kend);
+  cursor_seek<TN, STRIPED>(p, cur, kend);
   if (cur.valid) {
     load_tile(cur);
     store_tile(0);
@@ -542,11 +544,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(const FwdParams p)
   int buf = 0;
   while (cur.valid) {
     Cursor nxt = cur;
-    cursor_next<TN>(p, nxt, kend);
+    cursor_next<TN, STRIPED>(p, nxt, kend);
     if (nxt.valid) load_tile(nxt);
 
     const int kloc0 = cur.kt * TN;
-    const int32_t pk0 = cur.kb * p.seq_q + kloc0;
+    const int32_t pk0 = block_vbase<STRIPED>(p, cur.kb) + kloc0;  // key coordinate
     const bool run = pk0 < lim.run_lim;
     const bool mask = has_seg || pk0 >= lim.mask_lim;
     if (run) {
@@ -630,6 +632,22 @@ __global__ void fill_u8_kernel(uint8_t* p, int64_t n) {
     p[i] = 0;
 }
 
+template <int D>
+void launch_bf16(bool seg, bool striped, dim3 grid, dim3 block, hipStream_t s,
+                 const FwdParams& p) {
+  if (seg) {
+    if (striped)
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, true, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, true, false>), grid, block, 0, s, p);
+  } else {
+    if (striped)
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, false, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, false, false>), grid, block, 0, s, p);
+  }
+}
+
 }  // namespace
 
 int launch_fwd(const FwdParams& p, Dtype dtype, int head_dim, int64_t run_map_bytes,
@@ -650,24 +668,25 @@ int launch_fwd(const FwdParams& p, Dtype dtype, int head_dim, int64_t run_map_by
   const dim3 grid(p.n_wg);
   if (dtype == Dtype::BF16) {
     const dim3 block(PipeCfg<128>::kThreads);
-    const bool seg = p.seg != nullptr;
-    if (head_dim == 128) {
-      if (seg)
-        hipLaunchKernelGGL((fwd_bf16_kernel<128, true>), grid, block, 0, s, p);
-      else
-        hipLaunchKernelGGL((fwd_bf16_kernel<128, false>), grid, block, 0, s, p);
-    } else {
-      if (seg)
-        hipLaunchKernelGGL((fwd_bf16_kernel<64, true>), grid, block, 0, s, p);
-      else
-        hipLaunchKernelGGL((fwd_bf16_kernel<64, false>), grid, block, 0, s, p);
-    }
+    const bool seg = p.seg != nullptr, str = p.striped != 0;
+    if (head_dim == 128)
+      launch_bf16<128>(seg, str, grid, block, s, p);
+    else
+      launch_bf16<64>(seg, str, grid, block, s, p);
   } else {
     const dim3 block(kThreads);
-    if (head_dim == 128)
-      hipLaunchKernelGGL(fwd_f32_kernel<128>, grid, block, 0, s, p);
-    else
-      hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, block, 0, s, p);
+    const bool str = p.striped != 0;
+    if (head_dim == 128) {
+      if (str)
+        hipLaunchKernelGGL((fwd_f32_kernel<128, true>), grid, block, 0, s, p);
+      else
+        hipLaunchKernelGGL((fwd_f32_kernel<128, false>), grid, block, 0, s, p);
+    } else {
+      if (str)
+        hipLaunchKernelGGL((fwd_f32_kernel<64, true>), grid, block, 0, s, p);
+      else
+        hipLaunchKernelGGL((fwd_f32_kernel<64, false>), grid, block, 0, s, p);
+    }
   }
   e = hipGetLastError();
   if (e != hipSuccess) {

@@ -70,25 +70,72 @@ struct Cursor {
   int valid;   // int, not bool: no padding bytes to copy around
 };
 
-// kend: first key position no row of the workgroup can see (INT64_MAX when
+// Key coordinates.  Causal tests compare a key coordinate with a limit
+// derived from the query rows.  Contiguous placement: the coordinate of key
+// j of block kb is its global position kb * Lq + j, the same as its storage
+// row.  Striped placement (position j * N + kb, token causal or none): the
+// coordinate is j + [kb > r], and query row i's limit is i + 1, because
+// j * N + kb <= i * N + r holds exactly when j + [kb > r] <= i.  Either way
+// the coordinate of block kb's first key is block_vbase and coordinates grow
+// by one per key inside a block.
+template <bool STRIPED>
+__device__ __forceinline__ int32_t block_vbase(const FwdParams& p, int kb) {
+  return STRIPED ? (kb > p.ring_index ? 1 : 0) : kb * p.seq_q;
+}
+
+// kend: first key coordinate no row of the workgroup can see (INT64_MAX when
 // non-causal).  The keys of block kb to visit are those before kend, rounded
 // up to whole 32-key sub-tiles.
+template <bool STRIPED>
 __device__ __forceinline__ int block_klen(const FwdParams& p, int kb, int64_t kend) {
-  const int64_t len = kend - (int64_t)kb * p.seq_q;
+  const int64_t len = kend - (int64_t)block_vbase<STRIPED>(p, kb);
   if (len <= 0) return 0;
   if (len >= p.seq_q) return p.seq_q;
   const int l32 = ((int)len + 31) & ~31;
   return l32 > p.seq_q ? p.seq_q : l32;
 }
 
-template <int TN>
+// The walk over the keys.  Contiguous placement: block by block in ring
+// order (step t uses block (r - t) mod N), the tiles of a block in order.
+// Striped placement: every block is a causal triangle of the same shape, so
+// the workgroups of a head, whose query tiles see different numbers of keys
+// per block, would drift apart block by block and stop sharing the key tiles
+// they stream through L2.  There the walk is tile-major instead -- tile kt
+// of every block in ring order, then tile kt + 1 -- which keeps them in
+// step until each runs out of keys.  The softmax carry does not depend on
+// the order in which keys are folded in.
+template <int TN, bool STRIPED = false>
 __device__ __forceinline__ void cursor_seek(const FwdParams& p, Cursor& c, int64_t kend) {
+  if (STRIPED) {
+    // Block r (t = 0) has the most keys to visit: if it has no tile kt,
+    // no block has.
+    const int last = block_klen<true>(p, p.ring_index, kend);
+#pragma clang loop vectorize(disable) unroll(disable)
+    while (c.kt * TN < last) {
+#pragma clang loop vectorize(disable) unroll(disable)
+      while (c.t < p.ring_size) {
+        c.kb = p.ring_index - c.t;
+        if (c.kb < 0) c.kb += p.ring_size;
+        c.klen = block_klen<true>(p, c.kb, kend);
+        c.ntile = (c.klen + TN - 1) / TN;
+        if (c.kt < c.ntile) {
+          c.valid = 1;
+          return;
+        }
+        ++c.t;
+      }
+      c.t = 0;
+      ++c.kt;
+    }
+    c.valid = 0;
+    return;
+  }
 #pragma clang loop vectorize(disable) unroll(disable)
   while (c.t < p.ring_size) {
     // Ring order: step t uses block (r - t) mod N.
     c.kb = p.ring_index - c.t;
     if (c.kb < 0) c.kb += p.ring_size;
-    c.klen = block_klen(p, c.kb, kend);
+    c.klen = block_klen<STRIPED>(p, c.kb, kend);
     c.ntile = (c.klen + TN - 1) / TN;
     if (c.ntile > 0) {
       c.valid = 1;
@@ -99,12 +146,17 @@ __device__ __forceinline__ void cursor_seek(const FwdParams& p, Cursor& c, int64
   c.valid = 0;
 }
 
-template <int TN>
+template <int TN, bool STRIPED = false>
 __device__ __forceinline__ void cursor_next(const FwdParams& p, Cursor& c, int64_t kend) {
+  if (STRIPED) {
+    ++c.t;
+    cursor_seek<TN, true>(p, c, kend);
+    return;
+  }
   if (++c.kt < c.ntile) return;
   c.kt = 0;
   ++c.t;
-  cursor_seek<TN>(p, c, kend);
+  cursor_seek<TN, STRIPED>(p, c, kend);
 }
 
 // A wave-uniform 64-bit value that the compiler computed in vector registers
@@ -115,9 +167,9 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Per-wave causal limits as 32-bit key positions (every position is below
-// 2^31 - 1, and tiles start at multiples of 32).  For the 32-key sub-tile
-// starting at key position pk0:
+// Per-wave causal limits as 32-bit key coordinates (every coordinate is
+// below 2^31 - 1, and tiles start at multiples of 32 inside a block).  For
+// the 32-key sub-tile starting at key coordinate pk0:
 //   it holds a visible pair for some row of the wave iff pk0 < run_lim;
 //   it needs the per-element causal test iff pk0 >= mask_lim;
 // and key position pk is visible from this lane's row iff pk < lane_lim.
@@ -130,6 +182,8 @@ __device__ __forceinline__ int32_t clamp_i32(int64_t x) {
   return (int32_t)std::min<int64_t>(x, INT32_MAX);
 }
 
+// pq_first: the query coordinate of the wave's first row -- its global
+// position (contiguous) or its local row (striped, token causal).
 __device__ __forceinline__ WaveLimits wave_limits(const FwdParams& p, int64_t pq_first,
                                                   int lrow, bool wave_active) {
   WaveLimits w{INT32_MAX, INT32_MAX, p.seq_k};
@@ -147,10 +201,11 @@ __device__ __forceinline__ WaveLimits wave_limits(const FwdParams& p, int64_t pq
   return w;
 }
 
-template <int BM>
+template <int BM, bool STRIPED = false>
 __device__ __forceinline__ int64_t wg_kend(const FwdParams& p, int m0) {
   if (p.causal == 0) return INT64_MAX;
-  const int64_t q_last = (int64_t)p.ring_index * p.seq_q + std::min(m0 + BM, p.seq_q) - 1;
+  const int64_t q_last =
+      (STRIPED ? 0 : (int64_t)p.ring_index * p.seq_q) + std::min(m0 + BM, p.seq_q) - 1;
   return uniform64((q_last / p.causal + 1) * p.causal);
 }
 
@@ -212,34 +267,38 @@ __device__ __forceinline__ void stage_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// A tile in flight: the global key position of its first key (its first
-// row in K and V), the end of the keys to visit in its block, its ring step
-// and block.  A tile with valid == 0 is past the end of the walk.
+// A tile in flight: the storage row of its first key in K and V, the end
+// of the rows to visit in its block, its ring step and block, and vsh = key
+// coordinate - storage row (0 for contiguous placement).  A tile with
+// valid == 0 is past the end of the walk.
 struct TileInfo {
-  int32_t pk, end, t, kb, valid;
+  int32_t pk, end, t, kb, valid, vsh;
 };
 
-template <int TN>
+template <int TN, bool STRIPED = false>
 __device__ __forceinline__ TileInfo tile_info(const FwdParams& p, const Cursor& c) {
   const int32_t base = c.kb * p.seq_q;
-  return TileInfo{base + c.kt * TN, base + c.klen, c.t, c.kb, c.valid};
+  const int32_t vsh = STRIPED ? block_vbase<true>(p, c.kb) - base : 0;
+  return TileInfo{base + c.kt * TN, base + c.klen, c.t, c.kb, c.valid, vsh};
 }
 
 // Per-wave view of one tile: which 32-key halves have a visible pair and
-// which need the causal or segment mask.
+// which need the causal or segment mask; pk is the key coordinate of the
+// tile's first key.
 struct TileFlags {
   bool run0, run1, mask0, mask1;
   int32_t pk;
 };
 
-template <bool SEG>
+template <bool SEG, bool STRIPED = false>
 __device__ __forceinline__ TileFlags tile_flags(const TileInfo& ti, const WaveLimits& lim) {
   TileFlags f;
-  f.pk = ti.pk;
-  f.run0 = ti.valid && ti.pk < lim.run_lim;
-  f.run1 = ti.valid && ti.pk + 32 < ti.end && ti.pk + 32 < lim.run_lim;
-  f.mask0 = SEG || ti.pk >= lim.mask_lim;
-  f.mask1 = SEG || ti.pk + 32 >= lim.mask_lim;
+  const int32_t pk = STRIPED ? ti.pk + ti.vsh : ti.pk;
+  f.pk = pk;
+  f.run0 = ti.valid && pk < lim.run_lim;
+  f.run1 = ti.valid && ti.pk + 32 < ti.end && pk + 32 < lim.run_lim;
+  f.mask0 = SEG || pk >= lim.mask_lim;
+  f.mask1 = SEG || pk + 32 >= lim.mask_lim;
   return f;
 }
 

@@ -78,25 +78,33 @@ const char* ra_last_error(void) { return g_err; }
 #endif
 const char* ra_version(void) { return "0.1.0+" RA_BUILD_ID; }
 
-ra_status_t ra_blockwise_plan(int64_t causal_block_size, int64_t q_chunk, int64_t k_chunk,
-                              int64_t seq_q, int32_t ring_size, int32_t ring_index,
-                              int32_t* kv_block_of_step, uint8_t* run_bits,
-                              int64_t* n_run_chunk_pairs) {
+ra_status_t ra_blockwise_plan_placed(int64_t causal_block_size, int64_t q_chunk,
+                                     int64_t k_chunk, int64_t seq_q, int32_t ring_size,
+                                     int32_t ring_index, ra_placement_t placement,
+                                     int32_t* kv_block_of_step, uint8_t* run_bits,
+                                     int64_t* n_run_chunk_pairs) {
   clear_error();
   ra_status_t st = check_ring(causal_block_size, q_chunk, k_chunk, seq_q, ring_size,
                               ring_index, false);
   if (st != RA_OK) return st;
+  if (placement != RA_PLACE_CONTIGUOUS && placement != RA_PLACE_STRIPED)
+    return fail(RA_E_INVALID, "unknown placement %d", (int)placement);
   if (kv_block_of_step == nullptr) return fail(RA_E_INVALID, "kv_block_of_step is NULL");
-  const int64_t nq = seq_q / q_chunk, nk = seq_q / k_chunk;
+  const bool striped = placement == RA_PLACE_STRIPED;
+  const int64_t nq = seq_q / q_chunk, nk = seq_q / k_chunk, N = ring_size;
   int64_t n_run = 0;
   for (int32_t t = 0; t < ring_size; ++t) {
     // Ring order: at outer step t the device uses block (index - t) mod N.
     const int32_t kb = ((ring_index - t) % ring_size + ring_size) % ring_size;
     kv_block_of_step[t] = kb;
     for (int64_t a = 0; a < nq; ++a) {
-      const int64_t last_q = (int64_t)ring_index * seq_q + (a + 1) * q_chunk - 1;
+      // Position of the chunk's last query row, (a + 1) * q_chunk - 1.
+      const int64_t i_last = (a + 1) * q_chunk - 1;
+      const int64_t last_q = striped ? i_last * N + ring_index : ring_index * seq_q + i_last;
       for (int64_t b = 0; b < nk; ++b) {
-        const int64_t first_k = (int64_t)kb * seq_q + b * k_chunk;
+        // Position of the chunk's first key, row b * k_chunk of block kb.
+        const int64_t j0 = b * k_chunk;
+        const int64_t first_k = striped ? j0 * N + kb : (int64_t)kb * seq_q + j0;
         const bool run = pair_runs(causal_block_size, last_q, first_k);
         n_run += run;
         if (run_bits) run_bits[((int64_t)t * nq + a) * nk + b] = run ? 1 : 0;
@@ -105,6 +113,15 @@ ra_status_t ra_blockwise_plan(int64_t causal_block_size, int64_t q_chunk, int64_
   }
   if (n_run_chunk_pairs) *n_run_chunk_pairs = n_run;
   return RA_OK;
+}
+
+ra_status_t ra_blockwise_plan(int64_t causal_block_size, int64_t q_chunk, int64_t k_chunk,
+                              int64_t seq_q, int32_t ring_size, int32_t ring_index,
+                              int32_t* kv_block_of_step, uint8_t* run_bits,
+                              int64_t* n_run_chunk_pairs) {
+  return ra_blockwise_plan_placed(causal_block_size, q_chunk, k_chunk, seq_q, ring_size,
+                                  ring_index, RA_PLACE_CONTIGUOUS, kv_block_of_step, run_bits,
+                                  n_run_chunk_pairs);
 }
 
 }  // extern "C"
@@ -173,13 +190,24 @@ ra_status_t prepare(const void* q, const void* k, const void* v, const int32_t* 
 
 extern "C" {
 
-ra_status_t ra_blockwise_attn_fwd_ex(const void* q, const void* k, const void* v,
-                                     const int32_t* segment_ids, int64_t causal_block_size,
-                                     int64_t q_chunk, int64_t k_chunk, int32_t ring_size,
-                                     int32_t ring_index, int64_t batch, int64_t seq_q,
-                                     int64_t heads, int64_t head_dim, ra_dtype_t dtype,
-                                     void* out, float* lse, uint8_t* run_map, void* stream) {
+ra_status_t ra_blockwise_attn_fwd_placed(const void* q, const void* k, const void* v,
+                                         const int32_t* segment_ids, int64_t causal_block_size,
+                                         int64_t q_chunk, int64_t k_chunk, int32_t ring_size,
+                                         int32_t ring_index, ra_placement_t placement,
+                                         int64_t batch, int64_t seq_q, int64_t heads,
+                                         int64_t head_dim, ra_dtype_t dtype, void* out,
+                                         float* lse, uint8_t* run_map, void* stream) {
   clear_error();
+  if (placement != RA_PLACE_CONTIGUOUS && placement != RA_PLACE_STRIPED)
+    return fail(RA_E_INVALID, "unknown placement %d", (int)placement);
+  // The kernels express striped token-causal visibility as a per-block
+  // shift of the key index (key j of block kb is visible from row i iff
+  // j + [kb > r] <= i); coarser causal blocks have no such form.
+  if (placement == RA_PLACE_STRIPED && causal_block_size > 1 &&
+      causal_block_size < seq_q * (int64_t)ring_size)
+    return fail(RA_E_UNSUPPORTED,
+                "striped placement supports causal_block_size 0 or 1 (got %lld)",
+                (long long)causal_block_size);
   ra::FwdParams p;
   bool empty = false;
   ra_status_t st = prepare(q, k, v, segment_ids, causal_block_size, q_chunk, k_chunk, ring_size,
@@ -189,6 +217,7 @@ ra_status_t ra_blockwise_attn_fwd_ex(const void* q, const void* k, const void* v
   p.out = out;
   p.lse = lse;
   p.run_map = run_map;
+  p.striped = placement == RA_PLACE_STRIPED ? 1 : 0;
   const int64_t map_bytes =
       run_map ? (int64_t)ring_size * (seq_q / q_chunk) * (seq_q / k_chunk) : 0;
   const ra::Dtype dt = dtype == RA_BF16 ? ra::Dtype::BF16 : ra::Dtype::F32;
@@ -196,6 +225,17 @@ ra_status_t ra_blockwise_attn_fwd_ex(const void* q, const void* k, const void* v
   if (ra::launch_fwd(p, dt, (int)head_dim, map_bytes, stream, err, (int)sizeof(err)) != 0)
     return fail(RA_E_HIP, "%s", err);
   return RA_OK;
+}
+
+ra_status_t ra_blockwise_attn_fwd_ex(const void* q, const void* k, const void* v,
+                                     const int32_t* segment_ids, int64_t causal_block_size,
+                                     int64_t q_chunk, int64_t k_chunk, int32_t ring_size,
+                                     int32_t ring_index, int64_t batch, int64_t seq_q,
+                                     int64_t heads, int64_t head_dim, ra_dtype_t dtype,
+                                     void* out, float* lse, uint8_t* run_map, void* stream) {
+  return ra_blockwise_attn_fwd_placed(q, k, v, segment_ids, causal_block_size, q_chunk, k_chunk,
+                                      ring_size, ring_index, RA_PLACE_CONTIGUOUS, batch, seq_q,
+                                      heads, head_dim, dtype, out, lse, run_map, stream);
 }
 
 ra_status_t ra_blockwise_attn_bwd(const void* q, const void* k, const void* v,

@@ -27,6 +27,7 @@ struct FwdParams {
   int32_t n_qtiles;     // query tiles per (batch, head)
   int32_t n_wg;         // workgroups in the grid
   float scale_log2;     // log2(e) / sqrt(head_dim)
+  int32_t striped;      // 1: striped placement (causal is then 0 or 1)
 };
 
 enum class Dtype : int { BF16 = 0, F32 = 1 };

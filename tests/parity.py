@@ -45,7 +45,8 @@ def check(out, lse, ref, ref_lse, dtype, what=""):
     return m
 
 
-def oracle_sample(q, k, v, seg, causal, ring_size, ring_index, head, rows, kv_len=None):
+def oracle_sample(q, k, v, seg, causal, ring_size, ring_index, head, rows, kv_len=None,
+                  placement="contiguous"):
     """Oracle for one head and a subset of local query rows, slicing the
     device tensors so that only that head (and only the first kv_len keys)
     crosses to the host."""
@@ -55,7 +56,7 @@ def oracle_sample(q, k, v, seg, causal, ring_size, ring_index, head, rows, kv_le
     vh = v[:, :kv_len, head:head + 1].contiguous().cpu()
     sg = None if seg is None else seg.cpu().numpy()
     out, lse = oracle.attention_fwd(qh, kh, vh, sg, causal, ring_size, ring_index,
-                                    rows=rows, kv_len=kv_len)
+                                    rows=rows, kv_len=kv_len, placement=placement)
     return out[:, :, 0, :], lse[:, 0, :]
 
 

@@ -122,3 +122,30 @@ def test_ffn_validation_without_gpu():
     assert call(x=None) == ra.RA_E_INVALID
     assert call(batch=0) == ra.RA_OK  # empty call: no device work
     assert call(seq=0) == ra.RA_OK
+
+
+def test_striped_plan_matches_oracle():
+    """The host planner's striped chunk-pair decisions equal the oracle's
+    closed form (itself pinned to brute force)."""
+    import oracle
+    for c in (1, 2, 3, None):
+        for N, Lq, qc, kc in ((4, 64, 32, 32), (3, 96, 32, 96), (16, 128, 64, 32)):
+            for r in range(N):
+                o, run, n = ra.blockwise_plan(c, qc, kc, Lq, N, r, placement="striped")
+                o2, run2 = oracle.skip_map_closed(c, qc, kc, Lq, N, r, placement="striped")
+                assert (o == o2).all() and (run == run2).all(), (c, N, Lq, r)
+                assert n == int(run2.sum())
+
+
+def test_placed_validation_without_gpu():
+    lib = ra.load_library()
+    call = lambda c, place, batch=1: lib.ra_blockwise_attn_fwd_placed(
+        None, None, None, None, c, 32, 32, 4, 1, place, batch, 32, 1, 128, ra.RA_BF16,
+        None, None, None, None)
+    assert call(2, ra.RA_PLACE_STRIPED) == ra.RA_E_UNSUPPORTED
+    assert call(1, 7) == ra.RA_E_INVALID
+    assert call(1, ra.RA_PLACE_STRIPED, batch=0) == ra.RA_OK      # empty call
+    assert call(128, ra.RA_PLACE_STRIPED, batch=0) == ra.RA_OK    # block >= sequence: non-causal
+    assert call(1, ra.RA_PLACE_STRIPED) == ra.RA_E_INVALID        # null q, k, v
+    order = (ctypes.c_int32 * 4)()
+    assert lib.ra_blockwise_plan_placed(1, 32, 32, 32, 4, 1, 9, order, None, None) == ra.RA_E_INVALID

@@ -20,7 +20,7 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "get", "block_seed", "document_segments",
-           "make_block", "make_dout", "make_q", "make_qkv", "make_segments",
+           "make_block", "make_dout", "make_q", "make_qkv", "make_segments", "to_storage_order",
            "FfnWorkload", "FFN_WORKLOADS", "make_ffn_inputs"]
 
 
@@ -41,6 +41,7 @@ class Workload:
     std: float = 1.0           # Q, K, V ~ std * N(0, 1)
     seed: int = 0
     poison_unused: bool = False  # fill KV blocks that no chunk pair reads with NaN
+    placement: str = "contiguous"  # or "striped": block r holds positions r, r + N, ...
     notes: str = field(default="", compare=False)
 
     @property
@@ -66,6 +67,13 @@ WORKLOADS = {
                  512, 512, std=0.5, seed=20261205, poison_unused=True,
                  notes="65B-shaped share: ring position 128 of 256, 4M context, "
                        "block-causal with causal_block_size 16384"),
+        # striped placement (block r holds positions r, r + N, r + 2N, ...)
+        Workload("small_causal_striped", 1, 1024, 8, tuple(range(8)), 8, 128, "bf16", 1,
+                 512, 512, seed=20261208, placement="striped",
+                 notes="small_causal's shape under striped placement"),
+        Workload("share_7b_512k_striped", 1, 32768, 16, (15,), 32, 128, "bf16", 1,
+                 2048, 2048, seed=20261209, placement="striped",
+                 notes="the 7B-shaped share under striped placement, ring position 15 of 16"),
     ]
 }
 
@@ -162,12 +170,26 @@ def make_qkv(w: Workload, ring_index: int, device="cpu",
     return q, k, v
 
 
+def to_storage_order(x: np.ndarray, ring_size: int, placement: str) -> np.ndarray:
+    """Reorder a natural-order [B, S, ...] array into the storage order of a
+    placement: unchanged for contiguous; for striped, block kb (rows kb * Lq
+    .. kb * Lq + Lq - 1) takes positions kb, kb + N, kb + 2N, ..."""
+    if placement == "contiguous":
+        return x
+    B, S = x.shape[:2]
+    y = x.reshape((B, S // ring_size, ring_size) + x.shape[2:])
+    return np.ascontiguousarray(np.swapaxes(y, 1, 2)).reshape(x.shape)
+
+
 def make_segments(w: Workload, device="cpu"):
-    """Segment ids [B, S] (int32) for workloads with packed documents, else None."""
+    """Segment ids [B, S] (int32) for workloads with packed documents, else
+    None; documents are laid out along the global positions and the ids are
+    returned in the workload's storage order."""
     if not w.segments:
         return None
     torch = _torch()
     seg = document_segments(w.batch, w.seq_k, w.seed + 3)
+    seg = to_storage_order(seg, w.ring_size, w.placement)
     return torch.from_numpy(seg).to(device)
 
 
