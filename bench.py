@@ -80,6 +80,55 @@ def measured_traffic(build_id: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def record_traffic(fetch_dir: str, write_dir: str, calib_mib: int) -> dict:
+    """Write the traffic record from two rocprofv3 --pmc runs of
+    ``bench.py --steps 1 --warmup 0 --cpu-rows 0 --calib-copy-mib M`` (one
+    with FETCH_SIZE, one with WRITE_SIZE; their output directories).  Each
+    counter of the forward dispatch is scaled by true bytes / counted bytes
+    of the plain copy of M MiB that runs first (it reads and writes M MiB).
+    Host only; the record is keyed to the build of the library in the tree."""
+    import csv
+    import glob
+
+    from long_context_exact_ra_amd import build as _b
+
+    def read(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        fwd, copy = [], []
+        for f in files:
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"]
+                if "fwd_bf16_kernel" in name:
+                    fwd.append(float(r["Counter_Value"]))
+                elif "MulFunctor<unsigned char>" in name:
+                    copy.append(float(r["Counter_Value"]))
+        if len(fwd) != 1 or len(copy) != 1:
+            raise SystemExit(f"{d}: expected one forward and one copy dispatch, "
+                             f"found {len(fwd)} and {len(copy)}")
+        return fwd[0], copy[0]
+
+    if calib_mib <= 0:
+        raise SystemExit("--record-traffic needs the --calib-copy-mib of the counter runs")
+    calib = calib_mib << 20
+    fk, fc = read(fetch_dir, "FETCH_SIZE")
+    wk, wc = read(write_dir, "WRITE_SIZE")
+    ff = round(calib / (fc * 1024), 5)
+    wf = round(calib / (wc * 1024), 5)
+    rec = {"kernel_sha256_16": _b.device_sources_sha16(), "workload": WORKLOAD,
+           "fetch_size_kib": fk, "write_size_kib": wk, "calib_copy_bytes": calib,
+           "calib_fetch_size_kib": fc, "calib_write_size_kib": wc,
+           "fetch_factor": ff, "write_factor": wf,
+           "hbm_bytes_per_launch": int(round(fk * 1024 * ff + wk * 1024 * wf)),
+           "fwd_sources_sha16": _b.fwd_sources_sha16()}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -156,7 +205,13 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first; its "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate HBM byte counts")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="host only: write the traffic record from two rocprofv3 --pmc "
+                         "output directories (FETCH_SIZE, WRITE_SIZE) and exit")
     args = ap.parse_args()
+    if args.record_traffic:
+        print(json.dumps(record_traffic(*args.record_traffic, args.calib_copy_mib)))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the ring exchange between GPUs is not part of this library)",
