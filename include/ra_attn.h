@@ -33,7 +33,8 @@
  * values, so out is an exact convex combination of the rows of V (up to the
  * float32 accumulation).
  * out is rounded to the input dtype.  A query row with no visible key gets
- * out = 0 and lse = -inf.
+ * out = 0 and lse = -inf.  q, k and v must be finite: NaN or infinite
+ * inputs give unspecified results.
  *
  * Ownership and synchronisation: all pointers except those marked "host"
  * are device pointers allocated by the caller; the library allocates no

@@ -47,6 +47,8 @@ namespace ra {
 namespace {
 
 constexpr int kThreads = 256;
+// Largest log2 of a probability weight before the running max must move.
+constexpr float kLazyMax = 8.f;
 
 // ---------------------------------------------------------------------------
 // bf16 kernel
@@ -78,7 +80,12 @@ constexpr int kThreads = 256;
 // Software pipeline per tile i (tile i+1's keys already in LDS):
 //   S_next = K_{i+1} . Q^T   (MFMA)      -- independent of --
 //   softmax carry on S_cur = tile i (VALU),
-//   O^T += V_i^T . P_i^T     (MFMA).
+//   O^T += V_i^T . P_i^T     (MFMA),
+// with the two products interleaved MFMA by MFMA (step_ilv).  On gfx950 a
+// SIMD does not run VALU work of one wave under the MFMAs of another, and
+// LDS operand reads cost issue time too, so the step is laid out to spread
+// the K reads, the (half-rate) transposing V reads and the exponentials
+// evenly between the MFMAs rather than to hide one phase behind another.
 
 // Softmax/accumulator state of one wave (32 query rows, one per lane pair).
 template <int D>
@@ -151,16 +158,20 @@ __device__ __forceinline__ float mask_max(f32x16_t* s, const int32_t* sg, int ha
   return fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
 }
 
-// Fold a tile's row max into the carry ("2. 数值稳定的注意力计算"): when some
-// row's max grows, rescale that row's numerator and denominator by
-// exp(prev_max - new_max).  Otherwise that factor is exactly 1 for every row
-// and nothing is done.
+// Fold a tile's row max into the carry ("2. 数值稳定的注意力计算"): rescale a
+// row's numerator and denominator by exp(prev_max - new_max) and move its
+// max.  The max is moved only when some row of the wave would see a weight
+// above 2^kLazyMax otherwise; until then the rows keep their previous max and
+// their weights exp(s - max) stay below 2^kLazyMax, exact in fp32 and bf16.
+// The result is the same softmax (numerator and denominator share the max,
+// and lse uses the max actually kept); rescaling becomes rare after the first
+// tiles.
 template <int D>
 __device__ __forceinline__ void carry_max(Bf16Wave<D>& w, float mx, float scale_log2) {
   constexpr int NDB = D / 32;
   mx = pair_max(mx);
   const float m_new = fmaxf(w.m_run, mx * scale_log2);
-  if (__builtin_amdgcn_ballot_w64(m_new > w.m_run) != 0) {
+  if (__builtin_amdgcn_ballot_w64(m_new > w.m_run + kLazyMax) != 0) {
     const float alpha = m_new == ninf() ? 1.f : __builtin_amdgcn_exp2f(w.m_run - m_new);
 #pragma unroll
     for (int j = 0; j < NDB; ++j) w.acc[j] *= alpha;
@@ -170,71 +181,102 @@ __device__ __forceinline__ void carry_max(Bf16Wave<D>& w, float mx, float scale_
 }
 
 
-// Probabilities of a (masked, max-folded) tile and O^T += V^T . P^T.
-// Masked logits are -inf and give exactly 0.  P is rounded to bf16 (round
-// to nearest even) for the MFMA, and the denominator sums the same rounded
-// values, so the output is an exact convex combination of the weights the
-// numerator used.
+// One step with the QK^T MFMAs of tile i+1 and the P.V MFMAs of tile i
+// interleaved one to one (slot t: QK MFMA t, P.V MFMA t), so that the K
+// reads (plain) and the V reads (transposing, half rate) are spread over
+// the whole step, and the exponentials of tile i feed the P.V MFMAs group by
+// group.  LDS operands are read two slots ahead.  Returns this lane's max
+// over tile i+1 (unmasked).
 template <int D>
-__device__ __forceinline__ void exp_pv(Bf16Wave<D>& w, f32x16_t* s, const __bf16* vst, int v_rd,
-                                       float scale_log2) {
-  constexpr int NDB = D / 32;
+__device__ __forceinline__ float step_ilv(Bf16Wave<D>& w, f32x16_t* s_cur, f32x16_t* s_next,
+                                          const bf16x8_t* qf, const __bf16* kst,
+                                          const __bf16* vst, int k_rd, int v_rd,
+                                          float scale_log2) {
+  constexpr int NDB = D / 32, NC = D / 16, N = D / 8;  // N QK and N P.V MFMAs
   const float m_use = w.m_run == ninf() ? 0.f : w.m_run;
   const bf16x2_t one2 = {(__bf16)1.f, (__bf16)1.f};
+  auto kread = [&](int t) -> bf16x8_t {
+    const int sb = t / NC, c = t % NC;
+    return *reinterpret_cast<const bf16x8_t*>(kst + k_rd + 2048 * (c >> 1) + 256 * (c & 1) +
+                                              1024 * sb);
+  };
+  auto vread = [&](int t) -> bf16x8_t {
+    const int q = t / NDB, j = t % NDB, sb = q >> 1, cc = q & 1;
+    const __bf16* src = vst + v_rd + 2048 * j + 32 * (32 * sb + 16 * cc);
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)src);
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(src + 256));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
   bf16x8_t pb[4];
   float ps[4];
+  f32x8_t e;
+  auto exp_part = [&](int q, int i0, int n) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    f32x8_t e;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[q >> 1][8 * (q & 1) + i], scale_log2, -m_use));
+    for (int i = i0; i < i0 + n; ++i)
+      e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[q >> 1][8 * (q & 1) + i], scale_log2, -m_use));
+  };
+  auto finish_pb = [&](int q) {
     pb[q] = __builtin_convertvector(e, bf16x8_t);
     ps[q] = __builtin_amdgcn_fdot2_f32_bf16(pb[q].s01, one2, 0.f, false);
     ps[q] = __builtin_amdgcn_fdot2_f32_bf16(pb[q].s23, one2, ps[q], false);
     ps[q] = __builtin_amdgcn_fdot2_f32_bf16(pb[q].s45, one2, ps[q], false);
     ps[q] = __builtin_amdgcn_fdot2_f32_bf16(pb[q].s67, one2, ps[q], false);
+  };
+  auto make_pb = [&](int q) {
+    exp_part(q, 0, 8);
+    finish_pb(q);
+  };
+  bf16x8_t ka[3], va[3];
+  ka[0] = kread(0);
+  ka[1] = kread(1);
+  va[0] = vread(0);
+  va[1] = vread(1);
+  s_next[0] = f32x16_t{};
+  s_next[1] = f32x16_t{};
+  make_pb(0);
+  float mp0 = ninf();
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < N; ++t) {
+    if (t + 2 < N) {
+      ka[(t + 2) % 3] = kread(t + 2);
+      va[(t + 2) % 3] = vread(t + 2);
+    }
+    {
+      const int sb = t / NC, c = t % NC;
+      s_next[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % 3], qf[c], s_next[sb], 0, 0, 0);
+    }
+    {
+      const int q = t / NDB, j = t % NDB;
+      w.acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t % 3], pb[q], w.acc[j], 0, 0, 0);
+    }
+    // the probabilities of the next group, a share per slot, ready before
+    // its first P.V MFMA
+    if (t / NDB + 1 < 4) {
+      constexpr int PER = 8 / NDB;
+      exp_part(t / NDB + 1, (t % NDB) * PER, PER);
+      if (t % NDB == NDB - 1) finish_pb(t / NDB + 1);
+    }
+    // the max over the first half of tile i+1, complete after QK MFMA NC-1
+    if (t == N - 2) {
+      float a = fmaxf(s_next[0][0], s_next[0][1]), b = fmaxf(s_next[0][8], s_next[0][9]);
+#pragma unroll
+      for (int i = 2; i < 8; ++i) {
+        a = fmaxf(a, s_next[0][i]);
+        b = fmaxf(b, s_next[0][8 + i]);
+      }
+      mp0 = fmaxf(a, b);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
   w.l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  float a = fmaxf(s_next[1][0], s_next[1][1]), b = fmaxf(s_next[1][8], s_next[1][9]);
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-#pragma unroll
-      for (int j = 0; j < NDB; ++j) {
-        const __bf16* src = vst + v_rd + 2048 * j + 32 * (32 * sb + 16 * cc);
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)src);
-        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(src + 256));
-        const bf16x8_t a =
-            __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        w.acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[2 * sb + cc], w.acc[j], 0, 0, 0);
-      }
-    }
+  for (int i = 2; i < 8; ++i) {
+    a = fmaxf(a, s_next[1][i]);
+    b = fmaxf(b, s_next[1][8 + i]);
   }
-}
-
-// Instruction order of a step: the QK^T MFMAs of tile i+1 interleaved with
-// the exponentials of tile i, then the P.V MFMAs of tile i interleaved with
-// the rest of its VALU work and tile i+1's row max.  LDS operand reads run
-// two MFMAs ahead, so their latency hides behind the MFMA in flight.
-template <int D>
-__device__ __forceinline__ void step_schedule() {
-  constexpr int kDsRead = 0x100, kMfma = 0x8, kValu = 0x2;
-  constexpr int NQK = 2 * (D / 16), NPV = 4 * (D / 32);
-  __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
-#pragma unroll
-  for (int i = 0; i < NQK; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-    if (i + 2 < NQK) __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kValu, 6, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(kDsRead, 4, 0);
-#pragma unroll
-  for (int i = 0; i < NPV; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-    if (i + 2 < NPV) __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(kValu, 3, 0);
-  }
+  return fmaxf(mp0, fmaxf(a, b));
 }
 
 // Everything one wave carries through the ring walk.
@@ -297,27 +339,28 @@ __device__ __forceinline__ bool pipe_step(const FwdParams& p, const PipeConst& k
   // P.V.  Tile i+1: logits and row max.  Both 32-key halves of both tiles
   // are always computed, so this is one straight-line block for every step;
   // a half without a visible pair is masked to -inf and contributes exactly 0
-  // (its keys in LDS are real keys or zeros, never undefined).
+  // (its keys in LDS are real keys or zeros, never undefined).  The debug
+  // run map is written first, so that no branch splits the block.
   f32x16_t* const s_cur = st.s[PH & 1];
   f32x16_t* const s_next = st.s[(PH + 1) & 1];
+  if (p.run_map != nullptr && k.lane == 0) {
+    const TileInfo& t0 = st.ti[S0];
+    const int kloc0 = t0.pk - t0.kb * p.seq_q;
+    if (f0.run0) write_run_map(p, t0.t, k.qg0, kloc0);
+    if (f0.run1) write_run_map(p, t0.t, k.qg0, kloc0 + 32);
+  }
   float mx = ninf();
   const bool any0 = f0.run0 || f0.run1, any1 = f1.run0 || f1.run1;
   if (any0 || any1) {
-    qk_tile<D>(s_next, qf, ks[S1], k.k_rd);
-    exp_pv<D>(st.w, s_cur, vs[S0], k.v_rd, p.scale_log2);
-    mx = mask_max<false, false>(s_next, nullptr, k.half, f1, lim.lane_lim, k.seg_q);
-    step_schedule<D>();
+    mx = step_ilv<D>(st.w, s_cur, s_next, qf, ks[S1], vs[S0], k.k_rd, k.v_rd, p.scale_log2);
     if (SEG || !(f1.run0 && f1.run1) || f1.mask0 || f1.mask1) {
       // Keep this a real branch: if-converted, the mask would run on every
-      // step.  An empty volatile asm cannot be speculated.
+      // step.  An empty volatile asm cannot be speculated.  The masked max
+      // never exceeds the unmasked one; taking the smaller of the two keeps
+      // the unmasked max used on both paths, so it stays in the block above,
+      // between the P.V MFMAs.
       asm volatile("");
-      mx = mask_max<true, SEG>(s_next, ss[S1], k.half, f1, lim.lane_lim, k.seg_q);
-    }
-    if (p.run_map != nullptr && k.lane == 0) {
-      const TileInfo& t0 = st.ti[S0];
-      const int kloc0 = t0.pk - t0.kb * p.seq_q;
-      if (f0.run0) write_run_map(p, t0.t, k.qg0, kloc0);
-      if (f0.run1) write_run_map(p, t0.t, k.qg0, kloc0 + 32);
+      mx = fminf(mx, mask_max<true, SEG>(s_next, ss[S1], k.half, f1, lim.lane_lim, k.seg_q));
     }
   } else {
     s_next[0] = f32x16_t{} - __builtin_inff();
