@@ -259,11 +259,9 @@ def main():
     if bwd:
         # the forward's outputs of every listed ring position, and the gradients
         douts = [workloads.make_dout(w, ri, device=dev) for ri in w.ring_indices]
-        if w.placement != "contiguous":
-            print("--pass bwd takes contiguous placement only", file=sys.stderr)
-            sys.exit(2)
         fw = [ra.blockwise_attn_fwd(qi, k, v, seg, w.causal_block_size, w.q_chunk, w.k_chunk,
-                                    w.ring_size, ri) for ri, qi in zip(w.ring_indices, qs)]
+                                    w.ring_size, ri, placement=w.placement)
+              for ri, qi in zip(w.ring_indices, qs)]
         f32 = dict(dtype=torch.float32, device=dev)
         dq = torch.empty(q.shape, **f32)
         dk = torch.empty(k.shape, **f32)
@@ -276,7 +274,8 @@ def main():
             if bwd:
                 ra.blockwise_attn_bwd(qi, k, v, fw[i][0], fw[i][1], douts[i], seg,
                                       w.causal_block_size, w.q_chunk, w.k_chunk, w.ring_size,
-                                      ri, dq=dq, dk=dk, dv=dv, delta=delta)
+                                      ri, dq=dq, dk=dk, dv=dv, delta=delta,
+                                      placement=w.placement)
             else:
                 ra.blockwise_attn_fwd(qi, k, v, seg, w.causal_block_size, w.q_chunk,
                                       w.k_chunk, w.ring_size, ri, out=out, lse=lse,

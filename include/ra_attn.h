@@ -208,6 +208,25 @@ ra_status_t ra_blockwise_attn_bwd(const void* q, const void* k, const void* v,
                                   float* dv, float* delta, void* stream);
 
 /*
+ * ra_blockwise_attn_bwd_placed -- ra_blockwise_attn_bwd under a placement
+ * of the sequence on the ring (see ra_blockwise_attn_fwd_placed): the
+ * gradients of that placement's forward, with segment_ids, dk and dv in
+ * storage order.  Errors as for ra_blockwise_attn_bwd, plus RA_E_INVALID for
+ * an unknown placement and RA_E_UNSUPPORTED for RA_PLACE_STRIPED with an
+ * effective causal_block_size other than 0 or 1.
+ */
+ra_status_t ra_blockwise_attn_bwd_placed(const void* q, const void* k,
+                                         const void* v, const int32_t* segment_ids,
+                                         int64_t causal_block_size, int64_t q_chunk,
+                                         int64_t k_chunk, int32_t ring_size,
+                                         int32_t ring_index, ra_placement_t placement,
+                                         int64_t batch, int64_t seq_q, int64_t heads,
+                                         int64_t head_dim, ra_dtype_t dtype,
+                                         const void* out, const float* lse,
+                                         const void* dout, float* dq, float* dk,
+                                         float* dv, float* delta, void* stream);
+
+/*
  * ra_blockwise_ffn -- the feedforward of the Blockwise Transformer, one
  * sequence chunk at a time.
  *

@@ -68,6 +68,9 @@ def load_library():
     lib.ra_blockwise_attn_fwd_placed.restype = ctypes.c_int
     lib.ra_blockwise_attn_bwd.argtypes = fwd_args[:14] + [c_vp] * 8
     lib.ra_blockwise_attn_bwd.restype = ctypes.c_int
+    lib.ra_blockwise_attn_bwd_placed.argtypes = (fwd_args[:9] + [ctypes.c_int] + fwd_args[9:14]
+                                                 + [c_vp] * 8)
+    lib.ra_blockwise_attn_bwd_placed.restype = ctypes.c_int
     lib.ra_blockwise_ffn_workspace_bytes.argtypes = [c_i64, c_i64]
     lib.ra_blockwise_ffn_workspace_bytes.restype = c_i64
     lib.ra_blockwise_ffn.argtypes = [c_vp] * 5 + [c_i64] * 5 + [ctypes.c_int, c_vp, c_vp,
@@ -195,7 +198,8 @@ def blockwise_attn_fwd(q, k, v, segment_ids=None, causal_block_size: Optional[in
 def blockwise_attn_bwd(q, k, v, out, lse, dout, segment_ids=None,
                        causal_block_size: Optional[int] = None, q_chunk: int = 512,
                        k_chunk: int = 512, ring_size: int = 1, ring_index: int = 0, *,
-                       dq=None, dk=None, dv=None, delta=None, stream=None):
+                       dq=None, dk=None, dv=None, delta=None, stream=None,
+                       placement: str = "contiguous"):
     """Backward of ring position ``ring_index``: returns (dq, dk, dv, delta).
 
     q, k, v, segment_ids and the mask arguments as for blockwise_attn_fwd
@@ -203,6 +207,8 @@ def blockwise_attn_bwd(q, k, v, out, lse, dout, segment_ids=None,
     upstream gradient of out ([B, Lq, H, D], bfloat16).  dq [B, Lq, H, D],
     dk, dv [B, ring_size * Lq, H, D] and delta [B, H, Lq] are float32 and
     allocated when not given; dk and dv hold this share's contribution.
+    placement: as for blockwise_attn_fwd (dk, dv and segment_ids in storage
+    order).
     """
     import torch
     lib = load_library()
@@ -239,9 +245,9 @@ def blockwise_attn_bwd(q, k, v, out, lse, dout, segment_ids=None,
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    _check(lib.ra_blockwise_attn_bwd(
+    _check(lib.ra_blockwise_attn_bwd_placed(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), seg_ptr, int(causal_block_size or 0),
-        q_chunk, k_chunk, ring_size, ring_index, B, Lq, H, D, RA_BF16,
+        q_chunk, k_chunk, ring_size, ring_index, _placement(placement), B, Lq, H, D, RA_BF16,
         out.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
         dv.data_ptr(), delta.data_ptr(), sptr))
     return dq, dk, dv, delta

@@ -154,14 +154,14 @@ struct DqWave {
 };
 
 // One key tile: S^T, dP^T, dS^T and dQ^T += K^T dS^T.
-template <int D, bool SEG>
+template <int D, bool SEG, bool STRIPED>
 __device__ __forceinline__ void dq_tile(const FwdParams& p, const DqWave& w, const WaveLimits& lim,
                                         const TileInfo& ti, const bf16x8_t* qf,
                                         const bf16x8_t* dof, float lse2, float dlt,
                                         f32x16_t* acc, const __bf16* kst, const __bf16* vst,
                                         const int32_t* sg) {
   constexpr int NDB = D / 32;
-  const TileFlags f = tile_flags<SEG>(ti, lim);
+  const TileFlags f = tile_flags<SEG, STRIPED>(ti, lim);
   if (!(f.run0 || f.run1)) return;
   f32x16_t s[2], dp[2];
 #pragma unroll
@@ -210,7 +210,7 @@ __device__ __forceinline__ void dq_tile(const FwdParams& p, const DqWave& w, con
         acc[j] = mfma(col_operand(kst, w.t_rd, j, 2 * sb + cc), dsb[2 * sb + cc], acc[j]);
 }
 
-template <int D, bool SEG>
+template <int D, bool SEG, bool STRIPED>
 __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dq_kernel(const BwdParams bp) {
   using St = DqStage<D, SEG>;
   constexpr int NDB = D / 32, NPT = St::NPT;
@@ -228,9 +228,11 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dq_kernel(const BwdParams 
   const int b = wc.b, h = wc.h, m0 = wc.m0;
   w.qg0 = m0 + w.wave * 32;
   w.active = w.qg0 < p.seq_q;
+  // Storage row of the wave's first query (segment ids) and its query
+  // coordinate (causal limits; the local row under striped placement).
   const int64_t pq_first = (int64_t)p.ring_index * p.seq_q + w.qg0;
-  const WaveLimits lim = wave_limits(p, pq_first, w.lrow, w.active);
-  w.kend = wg_kend<kBlockMBf16>(p, m0);
+  const WaveLimits lim = wave_limits(p, STRIPED ? w.qg0 : pq_first, w.lrow, w.active);
+  w.kend = wg_kend<kBlockMBf16, STRIPED>(p, m0);
   w.seg_q = 0;
   if (SEG && w.active) w.seg_q = p.seg[(int64_t)b * p.seq_k + pq_first + w.lrow];
   const int64_t rs = (int64_t)p.heads * D;
@@ -273,15 +275,15 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dq_kernel(const BwdParams 
   // into the stage of tile i-1 at the start of step i.
   TileInfo ti[4];
   Cursor ic{0, 0, 0, 0, 0, 0};
-  cursor_seek<64>(p, ic, w.kend);
+  cursor_seek<64, STRIPED>(p, ic, w.kend);
   auto fetch = [&](int s) {
-    ti[s] = tile_info<64>(p, ic);
+    ti[s] = tile_info<64, STRIPED>(p, ic);
     if (ic.valid) {
       __bf16* d = stg[s];
       issue_tile<D, kWaves, SEG>(ti[s], w.kbase0, w.vbase0, w.sbase0, w.rs_bytes, w.wave, w.lane,
                                  w.k_lane, w.k_lane, d, d + St::ELEMS,
                                  reinterpret_cast<int32_t*>(d + 2 * St::ELEMS));
-      cursor_next<64>(p, ic, w.kend);
+      cursor_next<64, STRIPED>(p, ic, w.kend);
     }
   };
   fetch(0);
@@ -301,7 +303,7 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dq_kernel(const BwdParams 
     constexpr int S0 = PH, S1 = (PH + 1) & 3;
     fetch((PH + 3) & 3);
     if (w.active)
-      dq_tile<D, SEG>(p, w, lim, ti[S0], qf, dof, lse2, dlt, acc, stg[S0], stg[S0] + St::ELEMS,
+      dq_tile<D, SEG, STRIPED>(p, w, lim, ti[S0], qf, dof, lse2, dlt, acc, stg[S0], stg[S0] + St::ELEMS,
                       reinterpret_cast<const int32_t*>(stg[S0] + 2 * St::ELEMS));
     // Tile i+1 must have landed (for every wave) before the next step.
     if (ti[S1].valid) {
@@ -365,7 +367,7 @@ __device__ __forceinline__ WgCoord kv_coord(const BwdParams& bp) {
                  __builtin_amdgcn_readfirstlane(kt * kBlockNBwd)};
 }
 
-template <int D, bool SEG>
+template <int D, bool SEG, bool STRIPED>
 __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParams bp) {
   using L = KvLds<D, SEG>;
   constexpr int NDB = D / 32, NPT = L::NPT;
@@ -385,13 +387,24 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
   const uint32_t rs_bytes = (uint32_t)(rs * 2);
   const uint32_t lane_off = (uint32_t)(lane & 15) * rs_bytes + 16u * (uint32_t)(lane >> 4);
   const int r_rd = row_rd(lane), t_rd = col_rd(lane);
-  const int32_t qpos0 = p.ring_index * p.seq_q;  // global position of local row 0
+  const int32_t qrow0 = p.ring_index * p.seq_q;  // storage row of local row 0
+  // Query coordinate of local row 0: its global position (contiguous), 0
+  // (striped: the coordinate is the local row itself).
+  const int32_t qpos0 = STRIPED ? 0 : qrow0;
 
-  // Causal threshold of this lane's key: query positions >= thr see it; the
-  // wave's smallest and largest thresholds decide which blocks run.
+  // Causal threshold of this lane's key: query coordinates >= thr see it;
+  // the wave's smallest and largest thresholds decide which blocks run.
+  // Striped (token causal): key j of block kb is seen from local rows
+  // i >= j + [kb > r].  The 32 keys of a wave lie in one block.
   const int64_t c = p.causal;
   int32_t thr = INT32_MIN, thr_first = INT32_MIN, thr_last = INT32_MIN;
-  if (c > 0) {
+  if (c > 0 && STRIPED) {
+    const int kb = kw0 / p.seq_q;
+    const int32_t sh = (kb > p.ring_index ? 1 : 0) - kb * p.seq_q;
+    thr = key + sh;
+    thr_first = __builtin_amdgcn_readfirstlane(kw0 + sh);
+    thr_last = __builtin_amdgcn_readfirstlane(kw0 + 31 + sh);
+  } else if (c > 0) {
     thr = (int32_t)(((int64_t)key / c) * c);
     thr_first = (int32_t)uniform64(((int64_t)kw0 / c) * c);
     thr_last = (int32_t)uniform64(((int64_t)(kw0 + 31) / c) * c);
@@ -421,7 +434,15 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
 
   // Query rows that can see any key of the workgroup: [q_lo, Lq).
   int q_lo = 0;
-  if (c > 0) {
+  if (c > 0 && STRIPED) {
+    // The smallest threshold of the workgroup's keys: that of its first
+    // key, unless its 256 keys run into the next block (whose first key's
+    // threshold is at most 1).
+    const int kb = k0 / p.seq_q;
+    const int j0 = k0 - kb * p.seq_q;
+    q_lo = j0 + kBlockNBwd <= p.seq_q ? j0 + (kb > p.ring_index ? 1 : 0) : 0;
+    q_lo = q_lo >= p.seq_q ? p.seq_q : q_lo;
+  } else if (c > 0) {
     const int64_t t0 = ((int64_t)k0 / c) * c - qpos0;
     q_lo = t0 <= 0 ? 0 : (t0 >= p.seq_q ? p.seq_q : (int)t0);
   }
@@ -430,7 +451,7 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
 
   const char* qbase0 = static_cast<const char*>(p.q) + ((int64_t)b * p.seq_q * rs + (int64_t)h * D) * 2;
   const char* gbase0 = static_cast<const char*>(bp.dout) + ((int64_t)b * p.seq_q * rs + (int64_t)h * D) * 2;
-  const int32_t* sbase0 = SEG ? p.seg + (int64_t)b * p.seq_k + qpos0 : nullptr;
+  const int32_t* sbase0 = SEG ? p.seg + (int64_t)b * p.seq_k + qrow0 : nullptr;
   const float* lbase = bp.lse + ((int64_t)b * p.heads + h) * p.seq_q;
   const float* dbase = bp.delta + ((int64_t)b * p.heads + h) * p.seq_q;
 
@@ -561,6 +582,13 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
     }
 }
 
+// The dQ and dK/dV kernels of one configuration.
+template <int D, bool SEG, bool STRIPED>
+void launch_main(dim3 qgrid, dim3 kgrid, dim3 block, hipStream_t s, const BwdParams& bp) {
+  hipLaunchKernelGGL((bwd_dq_kernel<D, SEG, STRIPED>), qgrid, block, 0, s, bp);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, SEG, STRIPED>), kgrid, block, 0, s, bp);
+}
+
 }  // namespace
 
 int launch_bwd(const BwdParams& bp, int head_dim, void* stream, char* err, int errlen) {
@@ -578,22 +606,21 @@ int launch_bwd(const BwdParams& bp, int head_dim, void* stream, char* err, int e
     hipLaunchKernelGGL(bwd_delta_kernel<64>, dgrid, dim3(256), 0, s, bp);
   const dim3 block(kThreadsBwd);
   const dim3 qgrid((unsigned)p.n_wg), kgrid((unsigned)bp.n_wg_kv);
+  const bool str = p.striped != 0;
   if (head_dim == 128) {
-    if (seg) {
-      hipLaunchKernelGGL((bwd_dq_kernel<128, true>), qgrid, block, 0, s, bp);
-      hipLaunchKernelGGL((bwd_dkdv_kernel<128, true>), kgrid, block, 0, s, bp);
-    } else {
-      hipLaunchKernelGGL((bwd_dq_kernel<128, false>), qgrid, block, 0, s, bp);
-      hipLaunchKernelGGL((bwd_dkdv_kernel<128, false>), kgrid, block, 0, s, bp);
-    }
+    if (seg)
+      str ? launch_main<128, true, true>(qgrid, kgrid, block, s, bp)
+          : launch_main<128, true, false>(qgrid, kgrid, block, s, bp);
+    else
+      str ? launch_main<128, false, true>(qgrid, kgrid, block, s, bp)
+          : launch_main<128, false, false>(qgrid, kgrid, block, s, bp);
   } else {
-    if (seg) {
-      hipLaunchKernelGGL((bwd_dq_kernel<64, true>), qgrid, block, 0, s, bp);
-      hipLaunchKernelGGL((bwd_dkdv_kernel<64, true>), kgrid, block, 0, s, bp);
-    } else {
-      hipLaunchKernelGGL((bwd_dq_kernel<64, false>), qgrid, block, 0, s, bp);
-      hipLaunchKernelGGL((bwd_dkdv_kernel<64, false>), kgrid, block, 0, s, bp);
-    }
+    if (seg)
+      str ? launch_main<64, true, true>(qgrid, kgrid, block, s, bp)
+          : launch_main<64, true, false>(qgrid, kgrid, block, s, bp);
+    else
+      str ? launch_main<64, false, true>(qgrid, kgrid, block, s, bp)
+          : launch_main<64, false, false>(qgrid, kgrid, block, s, bp);
   }
   e = hipGetLastError();
   if (e != hipSuccess) {

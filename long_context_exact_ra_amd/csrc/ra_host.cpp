@@ -238,14 +238,22 @@ ra_status_t ra_blockwise_attn_fwd_ex(const void* q, const void* k, const void* v
                                       heads, head_dim, dtype, out, lse, run_map, stream);
 }
 
-ra_status_t ra_blockwise_attn_bwd(const void* q, const void* k, const void* v,
-                                  const int32_t* segment_ids, int64_t causal_block_size,
-                                  int64_t q_chunk, int64_t k_chunk, int32_t ring_size,
-                                  int32_t ring_index, int64_t batch, int64_t seq_q,
-                                  int64_t heads, int64_t head_dim, ra_dtype_t dtype,
-                                  const void* out, const float* lse, const void* dout,
-                                  float* dq, float* dk, float* dv, float* delta, void* stream) {
+ra_status_t ra_blockwise_attn_bwd_placed(const void* q, const void* k, const void* v,
+                                         const int32_t* segment_ids, int64_t causal_block_size,
+                                         int64_t q_chunk, int64_t k_chunk, int32_t ring_size,
+                                         int32_t ring_index, ra_placement_t placement,
+                                         int64_t batch, int64_t seq_q, int64_t heads,
+                                         int64_t head_dim, ra_dtype_t dtype, const void* out,
+                                         const float* lse, const void* dout, float* dq,
+                                         float* dk, float* dv, float* delta, void* stream) {
   clear_error();
+  if (placement != RA_PLACE_CONTIGUOUS && placement != RA_PLACE_STRIPED)
+    return fail(RA_E_INVALID, "unknown placement %d", (int)placement);
+  if (placement == RA_PLACE_STRIPED && causal_block_size > 1 &&
+      causal_block_size < seq_q * (int64_t)ring_size)
+    return fail(RA_E_UNSUPPORTED,
+                "striped placement supports causal_block_size 0 or 1 (got %lld)",
+                (long long)causal_block_size);
   ra::BwdParams bp;
   bool empty = false;
   ra_status_t st = prepare(q, k, v, segment_ids, causal_block_size, q_chunk, k_chunk, ring_size,
@@ -256,6 +264,7 @@ ra_status_t ra_blockwise_attn_bwd(const void* q, const void* k, const void* v,
   if (empty) return RA_OK;
   if (!out || !lse || !dout || !dq || !dk || !dv || !delta)
     return fail(RA_E_INVALID, "out, lse, dout, dq, dk, dv and delta must be non-NULL");
+  bp.f.striped = placement == RA_PLACE_STRIPED ? 1 : 0;
   bp.out = out;
   bp.lse = lse;
   bp.dout = dout;
@@ -273,6 +282,19 @@ ra_status_t ra_blockwise_attn_bwd(const void* q, const void* k, const void* v,
   if (ra::launch_bwd(bp, (int)head_dim, stream, err, (int)sizeof(err)) != 0)
     return fail(RA_E_HIP, "%s", err);
   return RA_OK;
+}
+
+ra_status_t ra_blockwise_attn_bwd(const void* q, const void* k, const void* v,
+                                  const int32_t* segment_ids, int64_t causal_block_size,
+                                  int64_t q_chunk, int64_t k_chunk, int32_t ring_size,
+                                  int32_t ring_index, int64_t batch, int64_t seq_q,
+                                  int64_t heads, int64_t head_dim, ra_dtype_t dtype,
+                                  const void* out, const float* lse, const void* dout,
+                                  float* dq, float* dk, float* dv, float* delta, void* stream) {
+  return ra_blockwise_attn_bwd_placed(q, k, v, segment_ids, causal_block_size, q_chunk, k_chunk,
+                                      ring_size, ring_index, RA_PLACE_CONTIGUOUS, batch, seq_q,
+                                      heads, head_dim, dtype, out, lse, dout, dq, dk, dv, delta,
+                                      stream);
 }
 
 int64_t ra_blockwise_ffn_workspace_bytes(int64_t chunk_size, int64_t ffn_hidden) {

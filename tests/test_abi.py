@@ -149,3 +149,14 @@ def test_placed_validation_without_gpu():
     assert call(1, ra.RA_PLACE_STRIPED) == ra.RA_E_INVALID        # null q, k, v
     order = (ctypes.c_int32 * 4)()
     assert lib.ra_blockwise_plan_placed(1, 32, 32, 32, 4, 1, 9, order, None, None) == ra.RA_E_INVALID
+
+
+def test_bwd_placed_validation_without_gpu():
+    lib = ra.load_library()
+    call = lambda c, place, batch=1: lib.ra_blockwise_attn_bwd_placed(
+        None, None, None, None, c, 32, 32, 4, 1, place, batch, 32, 1, 128, ra.RA_BF16,
+        None, None, None, None, None, None, None, None)
+    assert call(2, ra.RA_PLACE_STRIPED) == ra.RA_E_UNSUPPORTED
+    assert call(1, 5) == ra.RA_E_INVALID
+    assert call(1, ra.RA_PLACE_STRIPED, batch=0) == ra.RA_OK
+    assert call(1, ra.RA_PLACE_STRIPED) == ra.RA_E_INVALID  # null tensors

@@ -57,12 +57,14 @@ def _run(w, r, dev):
     q, k, v = workloads.make_qkv(w, r, device=dev)
     dout = workloads.make_dout(w, r, device=dev)
     seg = workloads.make_segments(w, device=dev)
-    if seg is not None and w.name.startswith("edge"):
-        seg = torch.from_numpy(_short_documents(w.batch, w.seq_k, w.seed + 1)).to(dev)
+    if seg is not None and "edge" in w.name:
+        nat = _short_documents(w.batch, w.seq_k, w.seed + 1)
+        seg = torch.from_numpy(workloads.to_storage_order(nat, w.ring_size, w.placement)).to(dev)
     out, lse = ra.blockwise_attn_fwd(q, k, v, seg, w.causal_block_size, w.q_chunk, w.k_chunk,
-                                     w.ring_size, r)
+                                     w.ring_size, r, placement=w.placement)
     dq, dk, dv, delta = ra.blockwise_attn_bwd(q, k, v, out, lse, dout, seg, w.causal_block_size,
-                                              w.q_chunk, w.k_chunk, w.ring_size, r)
+                                              w.q_chunk, w.k_chunk, w.ring_size, r,
+                                              placement=w.placement)
     torch.cuda.synchronize()
     return q, k, v, dout, seg, out, (dq, dk, dv, delta)
 
@@ -84,7 +86,8 @@ def _full_case(w, r, heads=None):
     sl = lambda t: t[:, :, hs].contiguous().cpu()
     rdq, rdk, rdv = oracle.attention_bwd(sl(q), sl(k), sl(v), sl(dout),
                                          None if seg is None else seg.cpu().numpy(),
-                                         w.causal_block_size, w.ring_size, r)
+                                         w.causal_block_size, w.ring_size, r,
+                                         placement=w.placement)
     _cmp("dq", to_np(dq[:, :, hs]), rdq, what)
     _cmp("dk", to_np(dk[:, :, hs]), rdk, what)
     _cmp("dv", to_np(dv[:, :, hs]), rdv, what)
@@ -153,6 +156,51 @@ def test_bwd_share_7b_sampled_and_invariants():
     log(f"  bwd {what} sum_j dv_j vs sum_i dout_i: rel_l2={relv:.3e}")
     assert relv <= REL_L2
     assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
+
+
+@pytest.mark.parametrize("r", [0, 5])
+def test_bwd_small_causal_striped(r):
+    _full_case(workloads.get("small_causal_striped"), r)
+
+
+STRIPED_EDGE = [
+    # B, Lq, N, H, D, qc, kc, segments, r
+    (1, 96, 3, 2, 128, 32, 32, False, 1),   # 256-key workgroups span three blocks
+    (2, 128, 4, 2, 64, 64, 32, True, 2),
+    (1, 256, 2, 2, 128, 64, 64, True, 0),
+    (1, 32, 5, 1, 128, 32, 32, False, 4),
+]
+
+
+@pytest.mark.parametrize("case", STRIPED_EDGE, ids=[str(c) for c in STRIPED_EDGE])
+def test_bwd_striped_edge(case):
+    B, Lq, N, H, D, qc, kc, segs, r = case
+    w = workloads.Workload(f"striped_edge{case}", B, Lq, N, (r,), H, D, "bf16", 1, qc, kc,
+                           segments=segs, seed=5151 + Lq + D + N, placement="striped")
+    _full_case(w, r)
+
+
+def test_bwd_share_7b_striped_sampled():
+    """The 7B-shaped striped share at ring position 15: dq on sampled rows
+    of one head against the oracle, dk and dv through the invariants."""
+    w = workloads.get("share_7b_512k_striped")
+    r = 15
+    dev = torch.device("cuda:0")
+    q, k, v, dout, seg, out, (dq, dk, dv, delta) = _run(w, r, dev)
+    what = f"{w.name} r={r}"
+    rows = np.sort(np.random.default_rng(78).choice(w.seq_q, size=24, replace=False))
+    sl = lambda t: t[:, :, 7:8].contiguous().cpu()
+    rdq, _, _ = oracle.attention_bwd(sl(q), sl(k), sl(v), sl(dout), None, 1, w.ring_size, r,
+                                     rows=rows, placement="striped")
+    _cmp("dq[h7, 24 rows]", to_np(dq[:, rows, 7:8]), rdq, what)
+    sk = dk.double().sum(dim=1)
+    ratio = float((sk.abs() / dk.double().abs().sum(dim=1).clamp_min(1e-30)).max())
+    log(f"  bwd {what} |sum_j dk_j| / sum_j |dk_j| max={ratio:.3e}")
+    assert ratio <= 1e-3
+    relv = float((dv.double().sum(dim=1) - dout.double().sum(dim=1)).norm()
+                 / dout.double().sum(dim=1).norm())
+    log(f"  bwd {what} sum_j dv_j vs sum_i dout_i: rel_l2={relv:.3e}")
+    assert relv <= REL_L2
 
 
 def test_bwd_rejects_fp32_and_nulls():
