@@ -54,9 +54,33 @@ def visible_keys_per_row(seq_q: int, ring_size: int, ring_index: int, causal,
     return np.minimum((pq // c + 1) * c, S)
 
 
-def causal_flops(w, ring_index: int) -> float:
-    """F = 4 * D * H * B * sum over rows of causally visible keys: two
-    GEMMs, two flops per multiply-add, per visible (query, key) pair."""
+def segment_visible_keys_per_row(seg_b: np.ndarray, seq_q: int, ring_index: int) -> np.ndarray:
+    """Keys each local query row sees under token-causal masking and segment
+    ids (contiguous placement): the keys at or before the row's position with
+    the row's id, i.e. the row's rank among the positions carrying its id,
+    plus one."""
+    S = seg_b.shape[0]
+    order = np.argsort(seg_b, kind="stable")
+    ids = seg_b[order]
+    starts = np.r_[0, np.flatnonzero(np.diff(ids)) + 1]
+    first = np.repeat(starts, np.diff(np.r_[starts, S]))
+    rank = np.empty(S, dtype=np.int64)
+    rank[order] = np.arange(S) - first
+    return rank[ring_index * seq_q + np.arange(seq_q)] + 1
+
+
+def causal_flops(w, ring_index: int, seg=None) -> float:
+    """F = 4 * D * H * sum over rows of visible keys: two GEMMs, two flops
+    per multiply-add, per visible (query, key) pair.  Without segment ids
+    the pairs are the causally visible ones; with them (token causal,
+    contiguous placement) only pairs inside one segment count."""
+    if seg is not None:
+        if w.causal_block_size != 1 or w.placement != "contiguous":
+            raise ValueError("segment pair counts cover token-causal contiguous shares")
+        s_np = seg.cpu().numpy()
+        n = sum(int(segment_visible_keys_per_row(s_np[b], w.seq_q, ring_index).sum())
+                for b in range(w.batch))
+        return 4.0 * w.head_dim * w.heads * n
     n = int(visible_keys_per_row(w.seq_q, w.ring_size, ring_index, w.causal_block_size,
                                  w.placement).sum())
     return 4.0 * w.head_dim * w.heads * w.batch * n
@@ -172,8 +196,12 @@ def cpu_baseline(w, q, k, v, seg, ring_index: int, rows: int, flops_total: float
         oracle.attention_bwd(qh, kh, vh, gh, segh, w.causal_block_size, w.ring_size,
                              ring_index, rows=sel, kv_len=kv_len, placement=w.placement)
     dt = time.perf_counter() - t0
-    pairs = int(visible_keys_per_row(w.seq_q, w.ring_size, ring_index,
-                                     w.causal_block_size, w.placement)[sel].sum())
+    if seg is not None:
+        pairs = int(segment_visible_keys_per_row(seg[0].cpu().numpy(), w.seq_q,
+                                                 ring_index)[sel].sum())
+    else:
+        pairs = int(visible_keys_per_row(w.seq_q, w.ring_size, ring_index,
+                                         w.causal_block_size, w.placement)[sel].sum())
     flops = (4.0 if gh is None else 10.0) * w.head_dim * pairs
     rate = flops / dt
     return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": int(cores),
@@ -304,14 +332,15 @@ def main():
 
     # backward: the 5 matrix products of the algorithm (S, dP, dV, dK, dQ)
     # per visible pair against the forward's 2
-    flops = sum(causal_flops(w, ri) for ri in w.ring_indices) * (2.5 if bwd else 1.0)
+    flops = sum(causal_flops(w, ri, seg) for ri in w.ring_indices) * (2.5 if bwd else 1.0)
     tflops = flops / (ms * 1e-3) / 1e12
     build_id = ra.version().split("+", 1)[-1]
     traffic = measured_traffic(build_id) if (w.name == WORKLOAD and not bwd) else None
     rec = {
         "metric": ("causal-adjusted attention backward TFLOP/s per MI355X (5 matrix products "
                    "per visible pair; % of bf16 MFMA peak in roofline.frac)") if bwd else
-                  "causal-adjusted attention TFLOP/s per MI355X (% of bf16 MFMA peak in roofline.frac)",
+                  "causal-adjusted attention TFLOP/s per MI355X (% of bf16 MFMA peak in roofline.frac)"
+                  + ("; pairs visible under causal and segment masks" if seg is not None else ""),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,

@@ -109,6 +109,9 @@ ra_status_t ra_blockwise_attn_fwd(const void* q, const void* k, const void* v,
  *       holds at least one visible pair.  Parts without a visible pair are
  *       never folded in: a 64-key tile with none is skipped outright, and
  *       inside a processed tile such a part is masked to exactly zero weight.
+ *       The map records the causal decisions: segment ids never enter it
+ *       (parts whose key ids miss every id of the part's queries are also
+ *       skipped, but are recorded as the causal test decides).
  *       Intended for debugging and parity checks; it costs extra stores.
  *
  * Errors as for ra_blockwise_attn_fwd.

@@ -146,6 +146,7 @@ struct DqWave {
   int lane, lrow, half, wave, qg0, k_rd, t_rd;
   bool active;
   int32_t seg_q;
+  SegRange qseg;  // id range of the wave's queries
   int64_t kend;
   const char* kbase0;
   const char* vbase0;
@@ -161,7 +162,13 @@ __device__ __forceinline__ void dq_tile(const FwdParams& p, const DqWave& w, con
                                         f32x16_t* acc, const __bf16* kst, const __bf16* vst,
                                         const int32_t* sg) {
   constexpr int NDB = D / 32;
-  const TileFlags f = tile_flags<SEG, STRIPED>(ti, lim);
+  TileFlags f = tile_flags<SEG, STRIPED>(ti, lim);
+  if (SEG) {
+    // Halves whose key ids miss the queries' id range hold no visible pair.
+    const uint32_t ok = seg_overlap_halves(sg, w.lane, w.qseg);
+    f.run0 = f.run0 && (ok & 1u);
+    f.run1 = f.run1 && (ok & 2u);
+  }
   if (!(f.run0 || f.run1)) return;
   f32x16_t s[2], dp[2];
 #pragma unroll
@@ -235,6 +242,8 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dq_kernel(const BwdParams 
   w.kend = wg_kend<kBlockMBf16, STRIPED>(p, m0);
   w.seg_q = 0;
   if (SEG && w.active) w.seg_q = p.seg[(int64_t)b * p.seq_k + pq_first + w.lrow];
+  w.qseg = SegRange{0, 0};
+  if (SEG) w.qseg = wave_range(w.seg_q);
   const int64_t rs = (int64_t)p.heads * D;
   w.rs_bytes = (uint32_t)(rs * 2);
   w.kbase0 = static_cast<const char*>(p.k) + ((int64_t)b * p.seq_k * rs + (int64_t)h * D) * 2;
@@ -410,6 +419,7 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
     thr_last = (int32_t)uniform64(((int64_t)(kw0 + 31) / c) * c);
   }
   const int32_t seg_k = SEG && active ? p.seg[(int64_t)b * p.seq_k + key] : 0;
+  const SegRange kseg = SEG ? wave_range(seg_k) : SegRange{0, 0};  // the wave's key ids
 
   // K^T of this wave as the B operand of S = Q K^T.
   bf16x8_t kf[D / 16];
@@ -506,7 +516,12 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
       // Does the block hold a visible pair, and is every pair visible?
       const int qlast = std::min(qb + 31, p.seq_q - 1);
       const bool rows_in = qb < p.seq_q;
-      const bool run = active && rows_in && (c == 0 || qpos0 + qlast >= thr_first);
+      bool run = active && rows_in && (c == 0 || qpos0 + qlast >= thr_first);
+      if (SEG && run) {
+        // Query blocks whose ids miss the keys' id range hold no visible pair.
+        const SegRange qr = half_range(sg[32 * qh + lrow]);
+        run = __builtin_amdgcn_readfirstlane((int)(qr.hi >= kseg.lo && qr.lo <= kseg.hi)) != 0;
+      }
       const bool full = !SEG && qb + 31 < p.seq_q && (c == 0 || qpos0 + qb >= thr_last);
       if (!run) continue;
 

@@ -290,6 +290,9 @@ struct PipeState {
   // constants in the unrolled loop, so these stay in fixed registers.
   TileInfo ti[4];
   Cursor ic;  // the next tile to fetch
+  // With segment ids: per stage, which 32-key halves of its tile share an id
+  // range with the wave's queries (bit 0, bit 1).
+  uint32_t segok[4];
 };
 
 struct PipeConst {
@@ -303,6 +306,7 @@ struct PipeConst {
   int k_rd, v_rd;
   int64_t kend;
   int32_t seg_q;
+  SegRange qseg;  // id range of the wave's queries
 };
 
 // Record the tile under the fetch cursor as the content of stage S, start
@@ -332,15 +336,16 @@ __device__ __forceinline__ bool pipe_step(const FwdParams& p, const PipeConst& k
   constexpr int S0 = PH, S1 = (PH + 1) & 3, S2 = (PH + 2) & 3, S3 = (PH + 3) & 3;
   fetch_next<D, SEG, STRIPED, S3>(p, k, st, ks, vs, ss);
 
-  const TileFlags f0 = tile_flags<SEG, STRIPED>(st.ti[S0], lim);
-  const TileFlags f1 = tile_flags<SEG, STRIPED>(st.ti[S1], lim);
+  TileFlags f0 = tile_flags<SEG, STRIPED>(st.ti[S0], lim);
+  TileFlags f1 = tile_flags<SEG, STRIPED>(st.ti[S1], lim);
 
   // Tile i (logits in s_cur, already masked and max-folded): probabilities and
   // P.V.  Tile i+1: logits and row max.  Both 32-key halves of both tiles
   // are always computed, so this is one straight-line block for every step;
   // a half without a visible pair is masked to -inf and contributes exactly 0
   // (its keys in LDS are real keys or zeros, never undefined).  The debug
-  // run map is written first, so that no branch splits the block.
+  // run map (the causal decisions) is written first, so that no branch splits
+  // the block.
   f32x16_t* const s_cur = st.s[PH & 1];
   f32x16_t* const s_next = st.s[(PH + 1) & 1];
   if (p.run_map != nullptr && k.lane == 0) {
@@ -348,6 +353,15 @@ __device__ __forceinline__ bool pipe_step(const FwdParams& p, const PipeConst& k
     const int kloc0 = t0.pk - t0.kb * p.seq_q;
     if (f0.run0) write_run_map(p, t0.t, k.qg0, kloc0);
     if (f0.run1) write_run_map(p, t0.t, k.qg0, kloc0 + 32);
+  }
+  if (SEG) {
+    // Halves whose key ids miss the queries' id range hold no visible pair.
+    f0.run0 = f0.run0 && (st.segok[S0] & 1u);
+    f0.run1 = f0.run1 && (st.segok[S0] & 2u);
+    const uint32_t ok1 = seg_overlap_halves(ss[S1], k.lane, k.qseg);
+    st.segok[S1] = ok1;
+    f1.run0 = f1.run0 && (ok1 & 1u);
+    f1.run1 = f1.run1 && (ok1 & 2u);
   }
   float mx = ninf();
   const bool any0 = f0.run0 || f0.run1, any1 = f1.run0 || f1.run1;
@@ -412,6 +426,8 @@ __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const
   k.kend = wg_kend<kBlockMBf16, STRIPED>(p, m0);
   k.seg_q = 0;
   if (SEG && k.wave_active) k.seg_q = p.seg[(int64_t)b * p.seq_k + pq_first + k.lrow];
+  k.qseg = SegRange{0, 0};
+  if (SEG) k.qseg = wave_range(k.seg_q);
 
   const int64_t rs = (int64_t)p.heads * D;
   k.rs_bytes = (uint32_t)(rs * 2);
@@ -459,8 +475,13 @@ __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const
   else
     wait_vm<0>();
   stage_barrier();
+  if (SEG) st.segok[0] = seg_overlap_halves(ss[0], k.lane, k.qseg);
   if (st.ti[0].valid && k.wave_active) {
-    const TileFlags f = tile_flags<SEG, STRIPED>(st.ti[0], lim);
+    TileFlags f = tile_flags<SEG, STRIPED>(st.ti[0], lim);
+    if (SEG) {
+      f.run0 = f.run0 && (st.segok[0] & 1u);
+      f.run1 = f.run1 && (st.segok[0] & 2u);
+    }
     qk_tile<D>(st.s[0], qf, ks[0], k.k_rd);
     const float mx = mask_max<true, SEG>(st.s[0], ss[0], k.half, f, lim.lane_lim, k.seg_q);
     carry_max<D>(st.w, mx, p.scale_log2);

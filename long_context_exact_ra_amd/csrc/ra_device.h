@@ -317,6 +317,43 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 
+// Segment-id ranges.  When every key id of a tile lies outside the id range
+// of a wave's queries (or the reverse), the tile holds no visible pair
+// whatever the labelling, and skipping it changes nothing.  Packed documents
+// then cost their within-document work instead of the whole causal triangle.
+struct SegRange {
+  int32_t lo, hi;
+};
+
+// [min, max] of x over each 32-lane half of the wave (the same in every lane
+// of a half).
+__device__ __forceinline__ SegRange half_range(int32_t x) {
+  int32_t mn = x, mx = x;
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) {
+    mn = min(mn, __shfl_xor(mn, o));
+    mx = max(mx, __shfl_xor(mx, o));
+  }
+  return SegRange{mn, mx};
+}
+
+// [min, max] of x over the whole wave, wave-uniform.
+__device__ __forceinline__ SegRange wave_range(int32_t x) {
+  SegRange r = half_range(x);
+  r.lo = min(r.lo, __shfl_xor(r.lo, 32));
+  r.hi = max(r.hi, __shfl_xor(r.hi, 32));
+  return SegRange{__builtin_amdgcn_readfirstlane(r.lo), __builtin_amdgcn_readfirstlane(r.hi)};
+}
+
+// Bit h (h = 0, 1) set iff the ids of the 32 keys sg[32h .. 32h + 31] of a
+// 64-key tile in LDS overlap the range q.  Keys past the end of a block read
+// as id 0, which can only widen a range.
+__device__ __forceinline__ uint32_t seg_overlap_halves(const int32_t* sg, int lane, SegRange q) {
+  const SegRange k = half_range(sg[lane]);
+  const uint64_t b = __builtin_amdgcn_ballot_w64(k.hi >= q.lo && k.lo <= q.hi);
+  return (uint32_t)(b & 1u) | ((uint32_t)(b >> 32) & 1u) << 1;
+}
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Issue this wave's share of the DMA of one 64-row tile of two row-major
