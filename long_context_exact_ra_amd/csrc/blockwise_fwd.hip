@@ -125,26 +125,24 @@ __device__ __forceinline__ void qk_tile(f32x16_t* s, const bf16x8_t* qf, const _
 }
 
 // Mask the logits of a tile in place and return this lane's max over them.
-// MASKED: a half may be skipped (run false: all -inf) or need the causal /
-// segment mask; otherwise the tile is fully visible.  Element i of a half
-// sits at key offset 8 * (i / 4) + i % 4 from the lane's first key, so the
-// causal test of a whole half reduces to one per-lane count of visible keys.
-template <bool MASKED, bool SEG>
+// A half may be skipped (run false: all -inf) or need the causal / segment
+// mask.  Element i of a half sits at key offset 8 * (i / 4) + i % 4 from the
+// lane's first key, so the causal test of a whole half reduces to one
+// per-lane count of visible keys.
+template <bool SEG>
 __device__ __forceinline__ float mask_max(f32x16_t* s, const int32_t* sg, int half,
                                           const TileFlags& f, int32_t lane_lim, int32_t seg_q) {
-  if (MASKED) {
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const bool r = sb ? f.run1 : f.run0, m = sb ? f.mask1 : f.mask0;
-      // Keys at offsets below nvis are causally visible from this lane's row.
-      const int32_t nvis = !r ? 0 : m ? lane_lim - (f.pk + 32 * sb + 4 * half) : 32;
+  for (int sb = 0; sb < 2; ++sb) {
+    const bool r = sb ? f.run1 : f.run0, m = sb ? f.mask1 : f.mask0;
+    // Keys at offsets below nvis are causally visible from this lane's row.
+    const int32_t nvis = !r ? 0 : m ? lane_lim - (f.pk + 32 * sb + 4 * half) : 32;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int koff = 8 * (i >> 2) + (i & 3);
-        bool ok = koff < nvis;
-        if (SEG) ok = ok && sg[32 * sb + 4 * half + koff] == seg_q;
-        s[sb][i] = ok ? s[sb][i] : ninf();
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int koff = 8 * (i >> 2) + (i & 3);
+      bool ok = koff < nvis;
+      if (SEG) ok = ok && sg[32 * sb + 4 * half + koff] == seg_q;
+      s[sb][i] = ok ? s[sb][i] : ninf();
     }
   }
   // Independent partial maxima keep the dependency chains short.
@@ -374,7 +372,7 @@ __device__ __forceinline__ bool pipe_step(const FwdParams& p, const PipeConst& k
       // the unmasked max used on both paths, so it stays in the block above,
       // between the P.V MFMAs.
       asm volatile("");
-      mx = fminf(mx, mask_max<true, SEG>(s_next, ss[S1], k.half, f1, lim.lane_lim, k.seg_q));
+      mx = fminf(mx, mask_max<SEG>(s_next, ss[S1], k.half, f1, lim.lane_lim, k.seg_q));
     }
   } else {
     s_next[0] = f32x16_t{} - __builtin_inff();
@@ -483,7 +481,7 @@ __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const
       f.run1 = f.run1 && (st.segok[0] & 2u);
     }
     qk_tile<D>(st.s[0], qf, ks[0], k.k_rd);
-    const float mx = mask_max<true, SEG>(st.s[0], ss[0], k.half, f, lim.lane_lim, k.seg_q);
+    const float mx = mask_max<SEG>(st.s[0], ss[0], k.half, f, lim.lane_lim, k.seg_q);
     carry_max<D>(st.w, mx, p.scale_log2);
   }
 
