@@ -158,7 +158,7 @@ struct DqWave {
 template <int D, bool SEG, bool STRIPED>
 __device__ __forceinline__ void dq_tile(const FwdParams& p, const DqWave& w, const WaveLimits& lim,
                                         const TileInfo& ti, const bf16x8_t* qf,
-                                        const bf16x8_t* dof, float lse2, float dlt,
+                                        const bf16x8_t* dof, float lse2, const f32x16_t& ndlt,
                                         f32x16_t* acc, const __bf16* kst, const __bf16* vst,
                                         const int32_t* sg) {
   constexpr int NDB = D / 32;
@@ -170,13 +170,15 @@ __device__ __forceinline__ void dq_tile(const FwdParams& p, const DqWave& w, con
     f.run1 = f.run1 && (ok & 2u);
   }
   if (!(f.run0 || f.run1)) return;
+  // dp starts from -delta (each lane holds one query row), so the MFMAs
+  // deliver dP - delta directly.
   f32x16_t s[2], dp[2];
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
-    s[sb] = f32x16_t{};
-    dp[sb] = f32x16_t{};
+    s[sb] = mfma(row_operand(kst, w.k_rd, 0, sb), qf[0], f32x16_t{});
+    dp[sb] = mfma(row_operand(vst, w.k_rd, 0, sb), dof[0], ndlt);
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
+    for (int c = 1; c < D / 16; ++c) {
       s[sb] = mfma(row_operand(kst, w.k_rd, c, sb), qf[c], s[sb]);
       dp[sb] = mfma(row_operand(vst, w.k_rd, c, sb), dof[c], dp[sb]);
     }
@@ -204,7 +206,7 @@ __device__ __forceinline__ void dq_tile(const FwdParams& p, const DqWave& w, con
     for (int i = 0; i < 8; ++i) {
       const int e = 8 * (q & 1) + i;
       const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[q >> 1][e], p.scale_log2, -lse2));
-      d[i] = pr * (dp[q >> 1][e] - dlt);
+      d[i] = pr * dp[q >> 1][e];
     }
     dsb[q] = __builtin_convertvector(d, bf16x8_t);
   }
@@ -274,6 +276,9 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dq_kernel(const BwdParams 
     lse2 = bp.lse[li] * kLog2e;
     dlt = bp.delta[li];
   }
+  f32x16_t ndlt;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ndlt[i] = -dlt;
   __builtin_amdgcn_s_waitcnt(0);
 
   f32x16_t acc[NDB];
@@ -312,7 +317,7 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dq_kernel(const BwdParams 
     constexpr int S0 = PH, S1 = (PH + 1) & 3;
     fetch((PH + 3) & 3);
     if (w.active)
-      dq_tile<D, SEG, STRIPED>(p, w, lim, ti[S0], qf, dof, lse2, dlt, acc, stg[S0], stg[S0] + St::ELEMS,
+      dq_tile<D, SEG, STRIPED>(p, w, lim, ti[S0], qf, dof, lse2, ndlt, acc, stg[S0], stg[S0] + St::ELEMS,
                       reinterpret_cast<const int32_t*>(stg[S0] + 2 * St::ELEMS));
     // Tile i+1 must have landed (for every wave) before the next step.
     if (ti[S1].valid) {
