@@ -1,12 +1,13 @@
 """Blockwise exact attention of Ring Attention on MI355X (gfx950): the
-forward of one device's ring share and its backward, and the blockwise
-feedforward of the Blockwise Transformer.
+forward of one device's ring share and its backward (contiguous or striped
+placement of the sequence), and the blockwise feedforward of the Blockwise
+Transformer.
 
 A thin ctypes binding over the C ABI in ``include/ra_attn.h`` (library
 ``libra_attn.so`` next to this file).  It only marshals arguments: every
-step of the forward runs in the HIP kernels of the library.  PyTorch
-provides device memory and the stream.  There is no fallback: if the
-library is missing every call raises.
+step of the computation runs in the library (its HIP kernels, and hipBLASLt
+for the feedforward's GEMMs).  PyTorch provides device memory and the
+stream.  There is no fallback: if the library is missing every call raises.
 """
 
 from __future__ import annotations
@@ -18,7 +19,7 @@ from typing import Optional, Tuple
 __all__ = ["RaError", "blockwise_attn_fwd", "blockwise_attn_bwd", "blockwise_ffn",
            "ffn_workspace_bytes", "blockwise_plan", "last_error", "lib_path",
            "load_library", "version", "RA_OK", "RA_E_INVALID", "RA_E_UNSUPPORTED",
-           "RA_E_HIP", "RA_BF16", "RA_F32"]
+           "RA_E_HIP", "RA_BF16", "RA_F32", "RA_PLACE_CONTIGUOUS", "RA_PLACE_STRIPED"]
 
 RA_OK, RA_E_INVALID, RA_E_UNSUPPORTED, RA_E_HIP = 0, 1, 2, 3
 RA_BF16, RA_F32 = 0, 1
@@ -30,6 +31,7 @@ def _placement(name: str) -> int:
     if name not in _PLACEMENTS:
         raise ValueError(f"placement must be one of {sorted(_PLACEMENTS)}")
     return _PLACEMENTS[name]
+
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None

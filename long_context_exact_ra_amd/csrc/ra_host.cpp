@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/ra_attn.h: argument
-// validation, the ring-step planner and error reporting.  Plain C++; the
-// only device work is delegated to ra::launch_fwd (blockwise_fwd.hip).
+// validation, the ring-step planner and error reporting.  Plain C++; device
+// work is delegated to ra::launch_fwd (blockwise_fwd.hip), ra::launch_bwd
+// (blockwise_bwd.hip) and ra::launch_ffn (blockwise_ffn.hip).
 
 #include "ra_attn.h"
 

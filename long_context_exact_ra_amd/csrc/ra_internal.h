@@ -1,5 +1,6 @@
 // Internal interface between the host-side C ABI (ra_host.cpp, plain C++)
-// and the HIP side (blockwise_fwd.hip).  Not installed, not part of the ABI.
+// and the HIP side (blockwise_fwd.hip, blockwise_bwd.hip, blockwise_ffn.hip).
+// Not installed, not part of the ABI.
 #pragma once
 
 #include <stdint.h>
