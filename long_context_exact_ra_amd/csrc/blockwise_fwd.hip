@@ -92,8 +92,11 @@ template <int D>
 struct Bf16Wave {
   static constexpr int NDB = D / 32;
   f32x16_t acc[NDB];
-  float m_run;   // running max of the scaled logits (base-2 domain)
-  float l_run;   // this lane half's part of the denominator
+  float m_run;     // running max of the scaled logits (base-2 domain)
+  // This lane half's part of the denominator, as four running sums (one per
+  // group of 8 probabilities of a tile), so that no per-tile sum has to be
+  // started from zero and folded in.
+  float l_run[4];
 };
 
 template <int D>
@@ -173,18 +176,21 @@ __device__ __forceinline__ void carry_max(Bf16Wave<D>& w, float mx, float scale_
     const float alpha = m_new == ninf() ? 1.f : __builtin_amdgcn_exp2f(w.m_run - m_new);
 #pragma unroll
     for (int j = 0; j < NDB; ++j) w.acc[j] *= alpha;
-    w.l_run *= alpha;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) w.l_run[g] *= alpha;
     w.m_run = m_new;
   }
 }
 
 
 // One step with the QK^T MFMAs of tile i+1 and the P.V MFMAs of tile i
-// interleaved one to one (slot t: QK MFMA t, P.V MFMA t), so that the K
-// reads (plain) and the V reads (transposing, half rate) are spread over
-// the whole step, and the exponentials of tile i feed the P.V MFMAs group by
-// group.  LDS operands are read two slots ahead.  Returns this lane's max
-// over tile i+1 (unmasked).
+// interleaved one to one, so that the K reads (plain) and the V reads
+// (transposing, half rate) are spread over the whole step, and the
+// exponentials of tile i feed the P.V MFMAs group by group.  Slot t issues
+// QK MFMA t, then the LDS reads of slot t+2, then P.V MFMA t, then its share
+// of the exponentials: each MFMA is followed by independent work that the
+// wave issues while the matrix core runs it (2 % faster than issuing the two
+// MFMAs back to back).  Returns this lane's max over tile i+1 (unmasked).
 template <int D>
 __device__ __forceinline__ float step_ilv(Bf16Wave<D>& w, f32x16_t* s_cur, f32x16_t* s_next,
                                           const bf16x8_t* qf, const __bf16* kst,
@@ -206,7 +212,6 @@ __device__ __forceinline__ float step_ilv(Bf16Wave<D>& w, f32x16_t* s_cur, f32x1
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   bf16x8_t pb[4];
-  float ps[4];
   f32x8_t e;
   auto exp_part = [&](int q, int i0, int n) {
 #pragma unroll
@@ -215,10 +220,10 @@ __device__ __forceinline__ float step_ilv(Bf16Wave<D>& w, f32x16_t* s_cur, f32x1
   };
   auto finish_pb = [&](int q) {
     pb[q] = __builtin_convertvector(e, bf16x8_t);
-    ps[q] = __builtin_amdgcn_fdot2_f32_bf16(pb[q].s01, one2, 0.f, false);
-    ps[q] = __builtin_amdgcn_fdot2_f32_bf16(pb[q].s23, one2, ps[q], false);
-    ps[q] = __builtin_amdgcn_fdot2_f32_bf16(pb[q].s45, one2, ps[q], false);
-    ps[q] = __builtin_amdgcn_fdot2_f32_bf16(pb[q].s67, one2, ps[q], false);
+    float ps = __builtin_amdgcn_fdot2_f32_bf16(pb[q].s01, one2, w.l_run[q], false);
+    ps = __builtin_amdgcn_fdot2_f32_bf16(pb[q].s23, one2, ps, false);
+    ps = __builtin_amdgcn_fdot2_f32_bf16(pb[q].s45, one2, ps, false);
+    w.l_run[q] = __builtin_amdgcn_fdot2_f32_bf16(pb[q].s67, one2, ps, false);
   };
   auto make_pb = [&](int q) {
     exp_part(q, 0, 8);
@@ -236,14 +241,15 @@ __device__ __forceinline__ float step_ilv(Bf16Wave<D>& w, f32x16_t* s_cur, f32x1
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int t = 0; t < N; ++t) {
-    if (t + 2 < N) {
-      ka[(t + 2) % 3] = kread(t + 2);
-      va[(t + 2) % 3] = vread(t + 2);
-    }
     {
       const int sb = t / NC, c = t % NC;
       s_next[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % 3], qf[c], s_next[sb], 0, 0, 0);
     }
+    if (t + 2 < N) {
+      ka[(t + 2) % 3] = kread(t + 2);
+      va[(t + 2) % 3] = vread(t + 2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     {
       const int q = t / NDB, j = t % NDB;
       w.acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t % 3], pb[q], w.acc[j], 0, 0, 0);
@@ -267,7 +273,6 @@ __device__ __forceinline__ float step_ilv(Bf16Wave<D>& w, f32x16_t* s_cur, f32x1
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  w.l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
   float a = fmaxf(s_next[1][0], s_next[1][1]), b = fmaxf(s_next[1][8], s_next[1][9]);
 #pragma unroll
   for (int i = 2; i < 8; ++i) {
@@ -458,7 +463,8 @@ __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const
 #pragma unroll
   for (int j = 0; j < NDB; ++j) st.w.acc[j] = f32x16_t{};
   st.w.m_run = ninf();
-  st.w.l_run = 0.f;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) st.w.l_run[g] = 0.f;
 
   // Prologue: tiles 0, 1, 2 in flight, the cursor on tile 3.
   st.ic = Cursor{0, 0, 0, 0, 0, 0};
@@ -496,7 +502,8 @@ __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const
 
   // ---- epilogue: out = numerator / denominator, lse = ln(denominator) + max ----
   if (!k.wave_active) return;
-  const float l_tot = pair_sum(st.w.l_run);
+  const float l_tot =
+      pair_sum((st.w.l_run[0] + st.w.l_run[1]) + (st.w.l_run[2] + st.w.l_run[3]));
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int row = k.qg0 + k.lrow;
   __bf16* orow = static_cast<__bf16*>(p.out) + ((int64_t)b * p.seq_q + row) * rs + (int64_t)h * D;
