@@ -196,12 +196,9 @@ def cpu_baseline(w, q, k, v, seg, ring_index: int, rows: int, flops_total: float
         oracle.attention_bwd(qh, kh, vh, gh, segh, w.causal_block_size, w.ring_size,
                              ring_index, rows=sel, kv_len=kv_len, placement=w.placement)
     dt = time.perf_counter() - t0
-    if seg is not None:
-        pairs = int(segment_visible_keys_per_row(seg[0].cpu().numpy(), w.seq_q,
-                                                 ring_index)[sel].sum())
-    else:
-        pairs = int(visible_keys_per_row(w.seq_q, w.ring_size, ring_index,
-                                         w.causal_block_size, w.placement)[sel].sum())
+    # the same pair count as the headline: the causally visible pairs
+    pairs = int(visible_keys_per_row(w.seq_q, w.ring_size, ring_index,
+                                     w.causal_block_size, w.placement)[sel].sum())
     flops = (4.0 if gh is None else 10.0) * w.head_dim * pairs
     rate = flops / dt
     return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": int(cores),
@@ -332,15 +329,24 @@ def main():
 
     # backward: the 5 matrix products of the algorithm (S, dP, dV, dK, dQ)
     # per visible pair against the forward's 2
-    flops = sum(causal_flops(w, ri, seg) for ri in w.ring_indices) * (2.5 if bwd else 1.0)
+    # With segment ids the headline still counts the causally visible pairs;
+    # the pairs inside one segment (the work that is not masked away) are
+    # reported beside it.
+    mult = 2.5 if bwd else 1.0
+    flops = sum(causal_flops(w, ri) for ri in w.ring_indices) * mult
     tflops = flops / (ms * 1e-3) / 1e12
+    seg_adjusted = None
+    if seg is not None:
+        seg_flops = sum(causal_flops(w, ri, seg) for ri in w.ring_indices) * mult
+        seg_adjusted = {"value": round(seg_flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                        "flops_per_step": seg_flops,
+                        "pairs": "visible under the causal and the segment mask"}
     build_id = ra.version().split("+", 1)[-1]
     traffic = measured_traffic(build_id) if (w.name == WORKLOAD and not bwd) else None
     rec = {
         "metric": ("causal-adjusted attention backward TFLOP/s per MI355X (5 matrix products "
                    "per visible pair; % of bf16 MFMA peak in roofline.frac)") if bwd else
-                  "causal-adjusted attention TFLOP/s per MI355X (% of bf16 MFMA peak in roofline.frac)"
-                  + ("; pairs visible under causal and segment masks" if seg is not None else ""),
+                  "causal-adjusted attention TFLOP/s per MI355X (% of bf16 MFMA peak in roofline.frac)",
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -368,6 +374,8 @@ def main():
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
     }
+    if seg_adjusted is not None:
+        rec["segment_adjusted"] = seg_adjusted
     if args.cpu_rows > 0:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v, seg, r, args.cpu_rows, flops,
