@@ -168,6 +168,9 @@ __device__ __forceinline__ void dq_tile(const FwdParams& p, const DqWave& w, con
     const uint32_t ok = seg_overlap_halves(sg, w.lane, w.qseg);
     f.run0 = f.run0 && (ok & 1u);
     f.run1 = f.run1 && (ok & 2u);
+    // Halves whose keys and queries all carry one id need no id test.
+    f.seg0 = !(ok & 4u);
+    f.seg1 = !(ok & 8u);
   }
   if (!(f.run0 || f.run1)) return;
   // dp starts from -delta (each lane holds one query row), so the MFMAs
@@ -183,6 +186,9 @@ __device__ __forceinline__ void dq_tile(const FwdParams& p, const DqWave& w, con
       dp[sb] = mfma(row_operand(vst, w.k_rd, c, sb), dof[c], dp[sb]);
     }
   }
+  // With segment ids every tile takes the masked path (a second, unmasked
+  // path would not fit the register budget); single-id halves skip only the
+  // id compare there.
   const bool masked = SEG || !(f.run0 && f.run1) || f.mask0 || f.mask1;
   if (masked) {
 #pragma unroll
@@ -193,7 +199,7 @@ __device__ __forceinline__ void dq_tile(const FwdParams& p, const DqWave& w, con
       for (int i = 0; i < 16; ++i) {
         const int koff = 8 * (i >> 2) + (i & 3);
         bool ok = koff < nvis;
-        if (SEG) ok = ok && sg[32 * sb + 4 * w.half + koff] == w.seg_q;
+        if (SEG && (sb ? f.seg1 : f.seg0)) ok = ok && sg[32 * sb + 4 * w.half + koff] == w.seg_q;
         s[sb][i] = ok ? s[sb][i] : ninf();
       }
     }
@@ -246,6 +252,27 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dq_kernel(const BwdParams 
   if (SEG && w.active) w.seg_q = p.seg[(int64_t)b * p.seq_k + pq_first + w.lrow];
   w.qseg = SegRange{0, 0};
   if (SEG) w.qseg = wave_range(w.seg_q);
+  // Segment ids: mark the key tiles whose ids can meet the workgroup's.
+  __shared__ uint8_t smask[SEG ? kSegMaskSlots : 1];
+  __shared__ int32_t wg_ids[2 * kWaves];
+  const uint8_t* smask_p = nullptr;
+  if (SEG && p.ring_size * seg_mask_tpb(p) <= kSegMaskSlots) {
+    if (w.lane == 0) {
+      wg_ids[2 * w.wave] = w.active ? w.qseg.lo : INT32_MAX;
+      wg_ids[2 * w.wave + 1] = w.active ? w.qseg.hi : INT32_MIN;
+    }
+    __syncthreads();
+    SegRange wr{INT32_MAX, INT32_MIN};
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+      wr.lo = min(wr.lo, wg_ids[2 * i]);
+      wr.hi = max(wr.hi, wg_ids[2 * i + 1]);
+    }
+    build_seg_mask(p, p.seg + (int64_t)b * p.seq_k, wr, STRIPED ? INT64_MAX : w.kend, smask,
+                   (int)threadIdx.x, kThreadsBwd);
+    __syncthreads();
+    smask_p = smask;
+  }
   const int64_t rs = (int64_t)p.heads * D;
   w.rs_bytes = (uint32_t)(rs * 2);
   w.kbase0 = static_cast<const char*>(p.k) + ((int64_t)b * p.seq_k * rs + (int64_t)h * D) * 2;
@@ -291,6 +318,7 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dq_kernel(const BwdParams 
   Cursor ic{0, 0, 0, 0, 0, 0};
   cursor_seek<64, STRIPED>(p, ic, w.kend);
   auto fetch = [&](int s) {
+    if (SEG && smask_p != nullptr) cursor_skip_masked<64, STRIPED>(p, ic, w.kend, smask_p);
     ti[s] = tile_info<64, STRIPED>(p, ic);
     if (ic.valid) {
       __bf16* d = stg[s];
@@ -522,12 +550,16 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
       const int qlast = std::min(qb + 31, p.seq_q - 1);
       const bool rows_in = qb < p.seq_q;
       bool run = active && rows_in && (c == 0 || qpos0 + qlast >= thr_first);
+      // With segment ids: does every pair of the block carry one id?
+      bool uni = !SEG;
       if (SEG && run) {
         // Query blocks whose ids miss the keys' id range hold no visible pair.
         const SegRange qr = half_range(sg[32 * qh + lrow]);
         run = __builtin_amdgcn_readfirstlane((int)(qr.hi >= kseg.lo && qr.lo <= kseg.hi)) != 0;
+        uni = __builtin_amdgcn_readfirstlane(
+                  (int)(qr.lo == qr.hi && kseg.lo == kseg.hi && qr.lo == kseg.lo)) != 0;
       }
-      const bool full = !SEG && qb + 31 < p.seq_q && (c == 0 || qpos0 + qb >= thr_last);
+      const bool full = uni && qb + 31 < p.seq_q && (c == 0 || qpos0 + qb >= thr_last);
       if (!run) continue;
 
       f32x16_t sc = f32x16_t{}, dp = f32x16_t{};
@@ -554,7 +586,7 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
           if (!full) {
             const int off = 8 * g + 4 * half + i;
             bool ok = off >= lo && off < hi;
-            if (SEG) ok = ok && sg[32 * qh + off] == seg_k;
+            if (SEG && !uni) ok = ok && sg[32 * qh + off] == seg_k;
             pr = ok ? pr : 0.f;
           }
           sc[e] = pr;

@@ -144,7 +144,7 @@ __device__ __forceinline__ float mask_max(f32x16_t* s, const int32_t* sg, int ha
     for (int i = 0; i < 16; ++i) {
       const int koff = 8 * (i >> 2) + (i & 3);
       bool ok = koff < nvis;
-      if (SEG) ok = ok && sg[32 * sb + 4 * half + koff] == seg_q;
+      if (SEG && (sb ? f.seg1 : f.seg0)) ok = ok && sg[32 * sb + 4 * half + koff] == seg_q;
       s[sb][i] = ok ? s[sb][i] : ninf();
     }
   }
@@ -310,14 +310,20 @@ struct PipeConst {
   int64_t kend;
   int32_t seg_q;
   SegRange qseg;  // id range of the wave's queries
+  // With segment ids: the workgroup's tile mask in LDS, or nullptr (walk
+  // every causally visible tile).
+  const uint8_t* smask;
 };
 
-// Record the tile under the fetch cursor as the content of stage S, start
-// its DMA and advance the cursor.
+// Record the tile under the fetch cursor (past the tiles the segment mask
+// leaves out) as the content of stage S, start its DMA and advance the
+// cursor.
 template <int D, bool SEG, bool STRIPED, int S>
 __device__ __forceinline__ void fetch_next(const FwdParams& p, const PipeConst& k,
                                            PipeState<D>& st, __bf16* const* ks,
                                            __bf16* const* vs, int32_t* const* ss) {
+  if (SEG && k.smask != nullptr)
+    cursor_skip_masked<PipeCfg<D>::TN, STRIPED>(p, st.ic, k.kend, k.smask);
   st.ti[S] = tile_info<PipeCfg<D>::TN, STRIPED>(p, st.ic);
   if (st.ic.valid) {
     issue_tile<D, PipeCfg<D>::kWaves, SEG>(st.ti[S], k.kbase0, k.vbase0, k.sbase0, k.rs_bytes,
@@ -365,12 +371,17 @@ __device__ __forceinline__ bool pipe_step(const FwdParams& p, const PipeConst& k
     st.segok[S1] = ok1;
     f1.run0 = f1.run0 && (ok1 & 1u);
     f1.run1 = f1.run1 && (ok1 & 2u);
+    // Halves whose keys and queries all carry one id need no id test.
+    f1.seg0 = !(ok1 & 4u);
+    f1.seg1 = !(ok1 & 8u);
+    f1.mask0 = f1.mask0 || f1.seg0;
+    f1.mask1 = f1.mask1 || f1.seg1;
   }
   float mx = ninf();
   const bool any0 = f0.run0 || f0.run1, any1 = f1.run0 || f1.run1;
   if (any0 || any1) {
     mx = step_ilv<D>(st.w, s_cur, s_next, qf, ks[S1], vs[S0], k.k_rd, k.v_rd, p.scale_log2);
-    if (SEG || !(f1.run0 && f1.run1) || f1.mask0 || f1.mask1) {
+    if (!(f1.run0 && f1.run1) || f1.mask0 || f1.mask1) {
       // Keep this a real branch: if-converted, the mask would run on every
       // step.  An empty volatile asm cannot be speculated.  The masked max
       // never exceeds the unmasked one; taking the smaller of the two keeps
@@ -431,6 +442,28 @@ __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const
   if (SEG && k.wave_active) k.seg_q = p.seg[(int64_t)b * p.seq_k + pq_first + k.lrow];
   k.qseg = SegRange{0, 0};
   if (SEG) k.qseg = wave_range(k.seg_q);
+  // Segment ids: mark the tiles whose ids can meet the workgroup's (not
+  // with the debug run map, which records every causal decision).
+  __shared__ uint8_t smask[SEG ? kSegMaskSlots : 1];
+  __shared__ int32_t wg_ids[2 * C::kWaves];
+  k.smask = nullptr;
+  if (SEG && p.run_map == nullptr && p.ring_size * seg_mask_tpb(p) <= kSegMaskSlots) {
+    if (k.lane == 0) {
+      wg_ids[2 * k.wave] = k.wave_active ? k.qseg.lo : INT32_MAX;
+      wg_ids[2 * k.wave + 1] = k.wave_active ? k.qseg.hi : INT32_MIN;
+    }
+    __syncthreads();
+    SegRange wr{INT32_MAX, INT32_MIN};
+#pragma unroll
+    for (int w = 0; w < C::kWaves; ++w) {
+      wr.lo = min(wr.lo, wg_ids[2 * w]);
+      wr.hi = max(wr.hi, wg_ids[2 * w + 1]);
+    }
+    build_seg_mask(p, p.seg + (int64_t)b * p.seq_k, wr, STRIPED ? INT64_MAX : k.kend, smask,
+                   (int)threadIdx.x, C::kThreads);
+    __syncthreads();
+    k.smask = smask;
+  }
 
   const int64_t rs = (int64_t)p.heads * D;
   k.rs_bytes = (uint32_t)(rs * 2);
@@ -485,6 +518,8 @@ __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const
     if (SEG) {
       f.run0 = f.run0 && (st.segok[0] & 1u);
       f.run1 = f.run1 && (st.segok[0] & 2u);
+      f.seg0 = !(st.segok[0] & 4u);
+      f.seg1 = !(st.segok[0] & 8u);
     }
     qk_tile<D>(st.s[0], qf, ks[0], k.k_rd);
     const float mx = mask_max<SEG>(st.s[0], ss[0], k.half, f, lim.lane_lim, k.seg_q);

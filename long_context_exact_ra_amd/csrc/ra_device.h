@@ -287,6 +287,9 @@ __device__ __forceinline__ TileInfo tile_info(const FwdParams& p, const Cursor& 
 // tile's first key.
 struct TileFlags {
   bool run0, run1, mask0, mask1;
+  // With segment ids: whether a half needs the per-element id test (set by
+  // the caller from the ids in LDS; true until then).
+  bool seg0, seg1;
   int32_t pk;
 };
 
@@ -297,8 +300,9 @@ __device__ __forceinline__ TileFlags tile_flags(const TileInfo& ti, const WaveLi
   f.pk = pk;
   f.run0 = ti.valid && pk < lim.run_lim;
   f.run1 = ti.valid && ti.pk + 32 < ti.end && pk + 32 < lim.run_lim;
-  f.mask0 = SEG || pk >= lim.mask_lim;
-  f.mask1 = SEG || pk + 32 >= lim.mask_lim;
+  f.mask0 = pk >= lim.mask_lim;
+  f.mask1 = pk + 32 >= lim.mask_lim;
+  f.seg0 = f.seg1 = SEG;
   return f;
 }
 
@@ -346,12 +350,67 @@ __device__ __forceinline__ SegRange wave_range(int32_t x) {
 }
 
 // Bit h (h = 0, 1) set iff the ids of the 32 keys sg[32h .. 32h + 31] of a
-// 64-key tile in LDS overlap the range q.  Keys past the end of a block read
-// as id 0, which can only widen a range.
+// 64-key tile in LDS overlap the range q; bit 2 + h set iff those keys and
+// the queries all carry one and the same id, so that every pair of the half
+// passes the id test.  Keys past the end of a block read as id 0, which can
+// only widen a range.
 __device__ __forceinline__ uint32_t seg_overlap_halves(const int32_t* sg, int lane, SegRange q) {
   const SegRange k = half_range(sg[lane]);
   const uint64_t b = __builtin_amdgcn_ballot_w64(k.hi >= q.lo && k.lo <= q.hi);
-  return (uint32_t)(b & 1u) | ((uint32_t)(b >> 32) & 1u) << 1;
+  const uint64_t u = __builtin_amdgcn_ballot_w64(k.lo == k.hi && q.lo == q.hi && k.lo == q.lo);
+  return (uint32_t)(b & 1u) | ((uint32_t)(b >> 32) & 1u) << 1 | ((uint32_t)(u & 1u) << 2) |
+         ((uint32_t)(u >> 32) & 1u) << 3;
+}
+
+// Workgroup-level tile mask for segment ids.  Before its walk a workgroup
+// marks, for every 64-key tile slot (kb, kt) of the share (slot kb * TPB +
+// kt, TPB = tiles per block), whether the tile's key ids overlap the id
+// range of its queries; the walk then steps over unmarked tiles without
+// fetching them.  Exact for any labelling, like the per-half test: disjoint
+// ranges share no id.  The mask lives in LDS and is used only when the
+// share has at most kSegMaskSlots slots.
+constexpr int kSegMaskSlots = 8192;
+
+__device__ __forceinline__ int seg_mask_tpb(const FwdParams& p) { return (p.seq_q + 63) / 64; }
+
+// Fill mask[0 .. N * TPB) cooperatively, one slot per thread (tid of
+// nthreads), so that every id load of the workgroup is in flight at once;
+// keys past the end of a block take no part.  seg_b: the ids of one batch
+// entry in storage order.  Slots of keys at or past kend_row (the first
+// storage row no query of the workgroup can reach, for contiguous
+// placement; the whole share otherwise) are left unmarked without reading
+// their ids.
+__device__ __forceinline__ void build_seg_mask(const FwdParams& p, const int32_t* seg_b,
+                                               SegRange q, int64_t kend_row, uint8_t* mask,
+                                               int tid, int nthreads) {
+  const int tpb = seg_mask_tpb(p);
+  const int n = p.ring_size * tpb;
+  for (int t = tid; t < n; t += nthreads) {
+    const int kb = t / tpb, kt = t - kb * tpb;
+    const int64_t row0 = (int64_t)kb * p.seq_q + 64 * kt;
+    const int nk = row0 < kend_row ? min(64, p.seq_q - 64 * kt) : 0;
+    int32_t lo = INT32_MAX, hi = INT32_MIN;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+      if (j < nk) {
+        const int32_t v = seg_b[row0 + j];
+        lo = min(lo, v);
+        hi = max(hi, v);
+      }
+    }
+    mask[t] = (nk > 0 && hi >= q.lo && lo <= q.hi) ? 1 : 0;
+  }
+}
+
+// Advance the cursor past tiles the mask leaves unmarked.
+template <int TN, bool STRIPED>
+__device__ __forceinline__ void cursor_skip_masked(const FwdParams& p, Cursor& c, int64_t kend,
+                                                   const uint8_t* mask) {
+  static_assert(TN == 64, "the mask has one slot per 64-key tile");
+  const int tpb = seg_mask_tpb(p);
+#pragma clang loop vectorize(disable) unroll(disable)
+  while (c.valid && __builtin_amdgcn_readfirstlane((int)mask[c.kb * tpb + c.kt]) == 0)
+    cursor_next<TN, STRIPED>(p, c, kend);
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
