@@ -515,6 +515,62 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
   // A wave's DMA count per query tile (waves 0 and 1 issue one more).
   const bool extra = wave < 2;
 
+  // Segment ids: list the query tiles whose id range meets the id range of
+  // the workgroup's keys (exact: disjoint ranges share no id); the walk
+  // fetches only those.  Wave 0 tests 64 tiles per round, one per lane, and
+  // appends the hits in order.
+  constexpr int kQList = 2048;
+  __shared__ int16_t qlist[SEG ? kQList : 1];
+  __shared__ int32_t wg_ids[2 * kWaves + 1];
+  int n_run = n_qt;
+  bool use_list = false;
+  if (SEG && n_qt <= kQList) {
+    if (lane == 0) {
+      wg_ids[2 * wave] = active ? kseg.lo : INT32_MAX;
+      wg_ids[2 * wave + 1] = active ? kseg.hi : INT32_MIN;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      SegRange kr{INT32_MAX, INT32_MIN};
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) {
+        kr.lo = min(kr.lo, wg_ids[2 * i]);
+        kr.hi = max(kr.hi, wg_ids[2 * i + 1]);
+      }
+      int n = 0;
+      for (int t0 = 0; t0 < n_qt; t0 += 64) {
+        const int t = t0 + lane;
+        bool hit = false;
+        if (t < n_qt) {
+          const int q0 = q_lo + 64 * t;
+          const int nq = std::min(64, p.seq_q - q0);
+          int32_t lo = INT32_MAX, hi = INT32_MIN;
+#pragma unroll
+          for (int j = 0; j < 64; ++j) {
+            if (j < nq) {
+              const int32_t v = sbase0[q0 + j];
+              lo = min(lo, v);
+              hi = max(hi, v);
+            }
+          }
+          hit = hi >= kr.lo && lo <= kr.hi;
+        }
+        const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (hit) qlist[n + below] = (int16_t)t;
+        n += __builtin_popcountll(m);
+      }
+      if (lane == 0) wg_ids[2 * kWaves] = n;
+    }
+    __syncthreads();
+    n_run = __builtin_amdgcn_readfirstlane(wg_ids[2 * kWaves]);
+    use_list = true;
+  }
+  auto tile_of = [&](int i) -> int {
+    return use_list ? __builtin_amdgcn_readfirstlane((int)qlist[i]) : i;
+  };
+
   f32x16_t dk[NDB], dv[NDB];
 #pragma unroll
   for (int j = 0; j < NDB; ++j) {
@@ -522,12 +578,13 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
     dv[j] = f32x16_t{};
   }
 
-  if (n_qt > 0) fetch(0, 0);
-  for (int qt = 0; qt < n_qt; ++qt) {
-    const int s = qt & 1;
-    if (qt + 1 < n_qt) fetch(qt + 1, s ^ 1);
+  if (n_run > 0) fetch(tile_of(0), 0);
+  for (int it = 0; it < n_run; ++it) {
+    const int qt = tile_of(it);
+    const int s = it & 1;
+    if (it + 1 < n_run) fetch(tile_of(it + 1), s ^ 1);
     // This wave's share of tile qt must have landed before the barrier.
-    if (qt + 1 < n_qt) {
+    if (it + 1 < n_run) {
       if (extra)
         wait_vm<NPT + 1>();
       else
