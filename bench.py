@@ -227,6 +227,9 @@ def main():
     ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd", "ffn"], default="fwd",
                     help="time the attention forward (default), its backward, or the "
                          "blockwise feedforward")
+    ap.add_argument("--key-splits", default="auto",
+                    help="forward: key splits per query tile ('auto' = the library's count "
+                         "for this GPU, 1 for shares that fill it; an integer forces it)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first; its "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate HBM byte counts")
@@ -294,6 +297,16 @@ def main():
         delta = torch.empty((w.batch, w.heads, w.seq_q), **f32)
         torch.cuda.synchronize()
 
+    # Key splits of each ring position, and one workspace for the largest
+    # (allocated here, outside the timed region).
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    splits = [ra.fwd_key_splits(w.batch, w.seq_q, w.heads, ra.RA_BF16, w.causal_block_size,
+                                w.ring_size, ri, cus) if args.key_splits == "auto"
+              else int(args.key_splits) for ri in w.ring_indices]
+    ws_bytes = max(ra.fwd_split_workspace_bytes(w.batch, w.seq_q, w.heads, w.head_dim, n)
+                   for n in splits)
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
     def step():
         for i, (ri, qi) in enumerate(zip(w.ring_indices, qs)):
             if bwd:
@@ -304,7 +317,8 @@ def main():
             else:
                 ra.blockwise_attn_fwd(qi, k, v, seg, w.causal_block_size, w.q_chunk,
                                       w.k_chunk, w.ring_size, ri, out=out, lse=lse,
-                                      placement=w.placement)
+                                      placement=w.placement, key_splits=splits[i],
+                                      workspace=workspace)
 
     for _ in range(args.warmup):
         step()
@@ -367,6 +381,7 @@ def main():
                    "causal_block_size": w.causal_block_size,
                    "q_chunk": w.q_chunk, "k_chunk": w.k_chunk, "pass": args.pass_,
                    "placement": w.placement,
+                   "key_splits": None if bwd else (splits[0] if len(splits) == 1 else splits),
                    "flops_per_step": flops, "ms_min": round(min(per), 3),
                    "wall_s": round(wall, 3)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),

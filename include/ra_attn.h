@@ -166,6 +166,67 @@ ra_status_t ra_blockwise_attn_fwd_placed(const void* q, const void* k,
                                          void* stream);
 
 /*
+ * ra_blockwise_attn_fwd_split -- the forward with each query tile's walk
+ * over the keys cut into key_splits runs that run in parallel.
+ *
+ * A small share (few heads, a short local block) gives the forward fewer
+ * query tiles than the GPU has compute units, and each tile walks all its
+ * keys alone.  Because the softmax carry folds key blocks in any order and
+ * grouping with the same result (review of "Ring Attention with Blockwise
+ * Transformers for Near-Infinite Context", section 三 "排列不变性", and the
+ * carry of "2. 数值稳定的注意力计算"), the walk can be cut: split s folds
+ * the s-th of key_splits equal runs of the tile's walk (ring order, skips
+ * and masks unchanged) into its own max, numerator and denominator, and a
+ * second kernel folds the splits into out and lse with the same carry.
+ *
+ *   key_splits: 1 .. 64; 1 is exactly ra_blockwise_attn_fwd_placed (the
+ *       workspace may then be NULL).
+ *   workspace: device memory of at least
+ *       ra_blockwise_attn_fwd_split_workspace_bytes(...) bytes, owned by
+ *       the caller, used as scratch during the call (float32 partial
+ *       numerators [key_splits][batch][heads][seq_q][head_dim], then
+ *       [key_splits][batch][heads][seq_q][2] kept maxima and denominators);
+ *       its contents on entry do not matter.  Two calls sharing a workspace
+ *       must be ordered on one stream.
+ *   Everything else as for ra_blockwise_attn_fwd_placed, including run_map
+ *   (the union of the splits' decisions is the unsplit map).
+ *
+ * The result equals the unsplit forward up to float32 rounding of the
+ * fold (the probabilities a split rounds to bf16 are taken against its
+ * own kept max).  Errors as for ra_blockwise_attn_fwd_placed, plus
+ * RA_E_INVALID for key_splits outside [1, 64], or key_splits > 1 with a
+ * NULL workspace or one smaller than required.
+ */
+ra_status_t ra_blockwise_attn_fwd_split(const void* q, const void* k,
+                                        const void* v, const int32_t* segment_ids,
+                                        int64_t causal_block_size, int64_t q_chunk,
+                                        int64_t k_chunk, int32_t ring_size,
+                                        int32_t ring_index, ra_placement_t placement,
+                                        int64_t batch, int64_t seq_q, int64_t heads,
+                                        int64_t head_dim, ra_dtype_t dtype,
+                                        void* out, float* lse, uint8_t* run_map,
+                                        int32_t key_splits, void* workspace,
+                                        int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes ra_blockwise_attn_fwd_split needs: key_splits * batch *
+ * heads * seq_q * (head_dim + 2) * 4; 0 when key_splits <= 1 or a size is
+ * not positive.  Host-only. */
+int64_t ra_blockwise_attn_fwd_split_workspace_bytes(int64_t batch, int64_t seq_q,
+                                                     int64_t heads, int64_t head_dim,
+                                                     int32_t key_splits);
+
+/* A key split count for a share: 1 when the unsplit grid (batch * heads *
+ * ceil(seq_q / rows per workgroup) workgroups, 256 rows for RA_BF16, 128
+ * for RA_F32) already fills compute_units; otherwise as many splits as
+ * keep one workgroup per compute unit, at most one per 8 key tiles of 64
+ * keys of the longest walk, and at most 64.  Host-only; invalid arguments
+ * give 1. */
+int32_t ra_blockwise_attn_fwd_key_splits(int64_t batch, int64_t seq_q, int64_t heads,
+                                         ra_dtype_t dtype, int64_t causal_block_size,
+                                         int32_t ring_size, int32_t ring_index,
+                                         int32_t compute_units);
+
+/*
  * ra_blockwise_attn_bwd -- the gradients of one ring position's share.
  *
  * For the forward of ra_blockwise_attn_fwd with the same q, k, v,

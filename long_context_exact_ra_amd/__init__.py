@@ -17,7 +17,8 @@ import os
 from typing import Optional, Tuple
 
 __all__ = ["RaError", "blockwise_attn_fwd", "blockwise_attn_bwd", "blockwise_ffn",
-           "ffn_workspace_bytes", "blockwise_plan", "last_error", "lib_path",
+           "ffn_workspace_bytes", "fwd_split_workspace_bytes", "fwd_key_splits",
+           "blockwise_plan", "last_error", "lib_path",
            "load_library", "version", "RA_OK", "RA_E_INVALID", "RA_E_UNSUPPORTED",
            "RA_E_HIP", "RA_BF16", "RA_F32", "RA_PLACE_CONTIGUOUS", "RA_PLACE_STRIPED"]
 
@@ -68,6 +69,15 @@ def load_library():
     lib.ra_blockwise_attn_fwd_placed.argtypes = (fwd_args[:9] + [ctypes.c_int] + fwd_args[9:]
                                                  + [c_vp, c_vp])
     lib.ra_blockwise_attn_fwd_placed.restype = ctypes.c_int
+    lib.ra_blockwise_attn_fwd_split.argtypes = (fwd_args[:9] + [ctypes.c_int] + fwd_args[9:]
+                                                + [c_vp, c_i32, c_vp, c_i64, c_vp])
+    lib.ra_blockwise_attn_fwd_split.restype = ctypes.c_int
+    lib.ra_blockwise_attn_fwd_split_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_i64,
+                                                                c_i32]
+    lib.ra_blockwise_attn_fwd_split_workspace_bytes.restype = c_i64
+    lib.ra_blockwise_attn_fwd_key_splits.argtypes = [c_i64, c_i64, c_i64, ctypes.c_int, c_i64,
+                                                     c_i32, c_i32, c_i32]
+    lib.ra_blockwise_attn_fwd_key_splits.restype = c_i32
     lib.ra_blockwise_attn_bwd.argtypes = fwd_args[:14] + [c_vp] * 8
     lib.ra_blockwise_attn_bwd.restype = ctypes.c_int
     lib.ra_blockwise_attn_bwd_placed.argtypes = (fwd_args[:9] + [ctypes.c_int] + fwd_args[9:14]
@@ -127,10 +137,28 @@ def blockwise_plan(causal_block_size: Optional[int], q_chunk: int, k_chunk: int,
     return order, run, n.value
 
 
+def fwd_split_workspace_bytes(batch: int, seq_q: int, heads: int, head_dim: int,
+                              key_splits: int) -> int:
+    """Device bytes ``ra_blockwise_attn_fwd_split`` needs as workspace."""
+    return int(load_library().ra_blockwise_attn_fwd_split_workspace_bytes(
+        batch, seq_q, heads, head_dim, key_splits))
+
+
+def fwd_key_splits(batch: int, seq_q: int, heads: int, dtype: int,
+                   causal_block_size: Optional[int], ring_size: int, ring_index: int,
+                   compute_units: int) -> int:
+    """The library's key split count for a share on a GPU with
+    ``compute_units`` compute units (1 = no split)."""
+    return int(load_library().ra_blockwise_attn_fwd_key_splits(
+        batch, seq_q, heads, dtype, int(causal_block_size or 0), ring_size, ring_index,
+        compute_units))
+
+
 def blockwise_attn_fwd(q, k, v, segment_ids=None, causal_block_size: Optional[int] = None,
                        q_chunk: int = 512, k_chunk: int = 512, ring_size: int = 1,
                        ring_index: int = 0, *, out=None, lse=None, run_map=None,
-                       stream=None, placement: str = "contiguous") -> Tuple[object, object]:
+                       stream=None, placement: str = "contiguous", key_splits=1,
+                       workspace=None) -> Tuple[object, object]:
     """Forward of ring position ``ring_index``: returns (out, lse).
 
     q: [B, Lq, H, D] and k, v: [B, ring_size * Lq, H, D], contiguous CUDA
@@ -143,6 +171,12 @@ def blockwise_attn_fwd(q, k, v, segment_ids=None, causal_block_size: Optional[in
     current torch stream).  placement: "contiguous" (block r holds positions
     r*Lq ..) or "striped" (block r holds positions r, r + N, ..; k, v and
     segment_ids in that storage order; token causal or non-causal only).
+    key_splits: 1 (the walk of each query tile runs in one workgroup), an
+    integer up to 64 (``ra_blockwise_attn_fwd_split``: the walk is cut into
+    that many runs whose partial results a second kernel folds), or "auto"
+    (the library's count for this GPU's compute units).  workspace: a device
+    tensor of at least ``fwd_split_workspace_bytes`` bytes, allocated when
+    not given and the call splits.
     """
     import torch
     lib = load_library()
@@ -176,6 +210,10 @@ def blockwise_attn_fwd(q, k, v, segment_ids=None, causal_block_size: Optional[in
     sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     dt = RA_BF16 if q.dtype == torch.bfloat16 else RA_F32
     place = _placement(placement)
+    if key_splits == "auto":
+        cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+        key_splits = fwd_key_splits(B, Lq, H, dt, causal_block_size, ring_size, ring_index, cus)
+    key_splits = int(key_splits)
     args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), seg_ptr, int(causal_block_size or 0),
             q_chunk, k_chunk, ring_size, ring_index, B, Lq, H, D, dt,
             out.data_ptr(), lse.data_ptr()]
@@ -188,7 +226,16 @@ def blockwise_attn_fwd(q, k, v, segment_ids=None, causal_block_size: Optional[in
                 or tuple(run_map.shape) != (ring_size, nq, nk)):
             raise ValueError("run_map must be a contiguous uint8 device tensor [N, nq, nk]")
         map_ptr = run_map.data_ptr()
-    if place != RA_PLACE_CONTIGUOUS:
+    if key_splits != 1:
+        need = fwd_split_workspace_bytes(B, Lq, H, D, key_splits)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        ws_bytes = workspace.numel() * workspace.element_size()
+        _check(lib.ra_blockwise_attn_fwd_split(*args[:9], place, *args[9:], map_ptr, key_splits,
+                                               workspace.data_ptr(), ws_bytes, sptr))
+    elif place != RA_PLACE_CONTIGUOUS:
         _check(lib.ra_blockwise_attn_fwd_placed(*args[:9], place, *args[9:], map_ptr, sptr))
     elif map_ptr is not None:
         _check(lib.ra_blockwise_attn_fwd_ex(*args, map_ptr, sptr))

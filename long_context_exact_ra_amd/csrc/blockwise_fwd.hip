@@ -51,6 +51,75 @@ constexpr int kThreads = 256;
 constexpr float kLazyMax = 8.f;
 
 // ---------------------------------------------------------------------------
+// Key splits: partial results and their combination
+// ---------------------------------------------------------------------------
+//
+// A split's workgroup ends with the unnormalised numerator of each of its
+// rows (float32), the max it kept (base 2) and its denominator.  Folding the
+// splits is the same carry as folding blocks ("2. 数值稳定的注意力计算"): with
+// M the largest kept max, out = sum_s 2^(m_s - M) num_s / sum_s 2^(m_s - M)
+// den_s and lse = (M + log2 of that denominator) ln 2.
+
+__device__ __forceinline__ int64_t part_row(const FwdParams& p, int split, int b, int h, int row) {
+  return (((int64_t)split * p.batch + b) * p.heads + h) * p.seq_q + row;
+}
+
+// This lane's half of row `row`: acc[j][4g + e] is column 32j + 8g + 4half + e.
+template <int NDB>
+__device__ __forceinline__ void write_partial(const FwdParams& p, int split, int b, int h, int row,
+                                              int half, const f32x16_t* acc, float m_run,
+                                              float l_tot) {
+  constexpr int D = NDB * 32;
+  const int64_t pr = part_row(p, split, b, h, row);
+  float* po = p.part_o + pr * D;
+#pragma unroll
+  for (int j = 0; j < NDB; ++j)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<float4*>(po + 32 * j + 8 * g + 4 * half) =
+          make_float4(acc[j][4 * g], acc[j][4 * g + 1], acc[j][4 * g + 2], acc[j][4 * g + 3]);
+  if (half == 0) *reinterpret_cast<float2*>(p.part_ml + 2 * pr) = make_float2(m_run, l_tot);
+}
+
+// One thread per (row, 4 columns); rows in [b][h][i] order, as lse.
+template <typename T>
+__global__ void combine_splits_kernel(const FwdParams p, int head_dim) {
+  const int groups = head_dim / 4;
+  const int64_t rows = (int64_t)p.batch * p.heads * p.seq_q;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= rows * groups) return;
+  const int64_t r = tid / groups;
+  const int g = (int)(tid % groups);
+  float mmax = ninf();
+  for (int s = 0; s < p.key_splits; ++s) {
+    const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + 2 * (s * rows + r));
+    if (ml.y > 0.f) mmax = fmaxf(mmax, ml.x);
+  }
+  float den = 0.f;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < p.key_splits; ++s) {
+    const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + 2 * (s * rows + r));
+    if (!(ml.y > 0.f)) continue;
+    const float w = __builtin_amdgcn_exp2f(ml.x - mmax);
+    den += w * ml.y;
+    const float4 o = *reinterpret_cast<const float4*>(p.part_o + (s * rows + r) * head_dim + 4 * g);
+    num.x += w * o.x;
+    num.y += w * o.y;
+    num.z += w * o.z;
+    num.w += w * o.w;
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const int64_t i = r % p.seq_q, bh = r / p.seq_q;
+  const int64_t b = bh / p.heads, h = bh % p.heads;
+  T* o = static_cast<T*>(p.out) + ((b * p.seq_q + i) * p.heads + h) * head_dim + 4 * g;
+  o[0] = (T)(num.x * inv);
+  o[1] = (T)(num.y * inv);
+  o[2] = (T)(num.z * inv);
+  o[3] = (T)(num.w * inv);
+  if (g == 0) p.lse[r] = den > 0.f ? (mmax + __builtin_amdgcn_logf(den)) * kLn2 : ninf();
+}
+
+// ---------------------------------------------------------------------------
 // bf16 kernel
 // ---------------------------------------------------------------------------
 //
@@ -308,6 +377,7 @@ struct PipeConst {
   uint32_t k_lane, v_lane;
   int k_rd, v_rd;
   int64_t kend;
+  int pos_end;  // walk position where this workgroup's key split ends
   int32_t seg_q;
   SegRange qseg;  // id range of the wave's queries
   // With segment ids: the workgroup's tile mask in LDS, or nullptr (walk
@@ -324,6 +394,7 @@ __device__ __forceinline__ void fetch_next(const FwdParams& p, const PipeConst& 
                                            __bf16* const* vs, int32_t* const* ss) {
   if (SEG && k.smask != nullptr)
     cursor_skip_masked<PipeCfg<D>::TN, STRIPED>(p, st.ic, k.kend, k.smask);
+  if (st.ic.pos >= k.pos_end) st.ic.valid = 0;
   st.ti[S] = tile_info<PipeCfg<D>::TN, STRIPED>(p, st.ic);
   if (st.ic.valid) {
     issue_tile<D, PipeCfg<D>::kWaves, SEG>(st.ti[S], k.kbase0, k.vbase0, k.sbase0, k.rs_bytes,
@@ -438,6 +509,8 @@ __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const
   const int64_t pq_first = (int64_t)p.ring_index * p.seq_q + k.qg0;
   const WaveLimits lim = wave_limits(p, STRIPED ? k.qg0 : pq_first, k.lrow, k.wave_active);
   k.kend = wg_kend<kBlockMBf16, STRIPED>(p, m0);
+  const SplitRange sr = split_range<C::TN, STRIPED>(p, wc.split, k.kend);
+  k.pos_end = sr.end;
   k.seg_q = 0;
   if (SEG && k.wave_active) k.seg_q = p.seg[(int64_t)b * p.seq_k + pq_first + k.lrow];
   k.qseg = SegRange{0, 0};
@@ -500,8 +573,9 @@ __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const
   for (int g = 0; g < 4; ++g) st.w.l_run[g] = 0.f;
 
   // Prologue: tiles 0, 1, 2 in flight, the cursor on tile 3.
-  st.ic = Cursor{0, 0, 0, 0, 0, 0};
+  st.ic = Cursor{0, 0, 0, 0, 0, 0, 0};
   cursor_seek<C::TN, STRIPED>(p, st.ic, k.kend);
+  cursor_to<C::TN, STRIPED>(p, st.ic, k.kend, sr.begin);
   fetch_next<D, SEG, STRIPED, 0>(p, k, st, ks, vs, ss);
   fetch_next<D, SEG, STRIPED, 1>(p, k, st, ks, vs, ss);
   fetch_next<D, SEG, STRIPED, 2>(p, k, st, ks, vs, ss);
@@ -539,8 +613,12 @@ __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const
   if (!k.wave_active) return;
   const float l_tot =
       pair_sum((st.w.l_run[0] + st.w.l_run[1]) + (st.w.l_run[2] + st.w.l_run[3]));
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int row = k.qg0 + k.lrow;
+  if (p.part_o != nullptr) {
+    write_partial<NDB>(p, wc.split, b, h, row, k.half, st.w.acc, st.w.m_run, l_tot);
+    return;
+  }
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   __bf16* orow = static_cast<__bf16*>(p.out) + ((int64_t)b * p.seq_q + row) * rs + (int64_t)h * D;
 #pragma unroll
   for (int j = 0; j < NDB; ++j) {
@@ -637,8 +715,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(const FwdParams p)
     if (has_seg && tid < TN) seg_lds[buf][tid] = sreg;
   };
 
-  Cursor cur{0, 0, 0, 0, 0, 0};
+  const SplitRange sr = split_range<TN, STRIPED>(p, wc.split, kend);
+  Cursor cur{0, 0, 0, 0, 0, 0, 0};
   cursor_seek<TN, STRIPED>(p, cur, kend);
+  cursor_to<TN, STRIPED>(p, cur, kend, sr.begin);
+  if (cur.pos >= sr.end) cur.valid = 0;
   if (cur.valid) {
     load_tile(cur);
     store_tile(0);
@@ -649,6 +730,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(const FwdParams p)
   while (cur.valid) {
     Cursor nxt = cur;
     cursor_next<TN, STRIPED>(p, nxt, kend);
+    if (nxt.pos >= sr.end) nxt.valid = 0;
     if (nxt.valid) load_tile(nxt);
 
     const int kloc0 = cur.kt * TN;
@@ -713,8 +795,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(const FwdParams p)
 
   if (!wave_active) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int row = qg0 + lrow;
+  if (p.part_o != nullptr) {
+    write_partial<NDB>(p, wc.split, b, h, row, half, acc, m_run, l_tot);
+    return;
+  }
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   float* orow = static_cast<float*>(p.out) + ((int64_t)b * p.seq_q + row) * rs + (int64_t)h * D;
 #pragma unroll
   for (int j = 0; j < NDB; ++j) {
@@ -796,6 +882,19 @@ int launch_fwd(const FwdParams& p, Dtype dtype, int head_dim, int64_t run_map_by
   if (e != hipSuccess) {
     snprintf(err, errlen, "kernel launch failed: %s", hipGetErrorString(e));
     return 1;
+  }
+  if (p.part_o != nullptr) {
+    const int64_t threads = (int64_t)p.batch * p.heads * p.seq_q * (head_dim / 4);
+    const dim3 cgrid((unsigned)((threads + 255) / 256));
+    if (dtype == Dtype::BF16)
+      hipLaunchKernelGGL(combine_splits_kernel<__bf16>, cgrid, dim3(256), 0, s, p, head_dim);
+    else
+      hipLaunchKernelGGL(combine_splits_kernel<float>, cgrid, dim3(256), 0, s, p, head_dim);
+    e = hipGetLastError();
+    if (e != hipSuccess) {
+      snprintf(err, errlen, "split combine launch failed: %s", hipGetErrorString(e));
+      return 1;
+    }
   }
   return 0;
 }

@@ -41,8 +41,12 @@ __device__ __forceinline__ float ninf() { return -__builtin_inff(); }
 // tiles -- the query tiles of one head, which stream the same keys and
 // values -- on the same XCD so they share its L2.  Heavier query tiles (more
 // causal work) come first.
+// With key splits, split s of a query tile walks only the s-th of
+// key_splits equal runs of the tile's key walk; the splits of one head sit
+// next to each other, split-major, so that the query tiles walking the same
+// key range share an XCD.
 struct WgCoord {
-  int b, h, m0;
+  int b, h, m0, split;
 };
 
 template <int BM>
@@ -51,13 +55,15 @@ __device__ __forceinline__ WgCoord wg_coord(const FwdParams& p) {
   const int xcd = pid & 7, idx = pid >> 3, cnt = n >> 3, rem = n & 7;
   const int logical =
       xcd < rem ? xcd * (cnt + 1) + idx : rem * (cnt + 1) + (xcd - rem) * cnt + idx;
-  const int qt = p.n_qtiles - 1 - logical % p.n_qtiles;
-  const int bh = logical / p.n_qtiles;
+  const int per_bh = p.n_qtiles * p.key_splits;
+  const int bh = logical / per_bh, in_bh = logical % per_bh;
+  const int qt = p.n_qtiles - 1 - in_bh % p.n_qtiles;
   // The values are workgroup-uniform; say so, so that addresses and buffer
   // descriptors derived from them stay in scalar registers.
   return WgCoord{__builtin_amdgcn_readfirstlane(bh / p.heads),
                  __builtin_amdgcn_readfirstlane(bh % p.heads),
-                 __builtin_amdgcn_readfirstlane(qt * BM)};
+                 __builtin_amdgcn_readfirstlane(qt * BM),
+                 __builtin_amdgcn_readfirstlane(in_bh / p.n_qtiles)};
 }
 
 // Position of the workgroup's current tile in the ring walk.
@@ -68,6 +74,7 @@ struct Cursor {
   int ntile;   // tiles to visit in this block
   int klen;    // keys to visit in this block (multiple of 32)
   int valid;   // int, not bool: no padding bytes to copy around
+  int pos;     // index of the current tile in the whole walk
 };
 
 // Key coordinates.  Causal tests compare a key coordinate with a limit
@@ -148,6 +155,7 @@ __device__ __forceinline__ void cursor_seek(const FwdParams& p, Cursor& c, int64
 
 template <int TN, bool STRIPED = false>
 __device__ __forceinline__ void cursor_next(const FwdParams& p, Cursor& c, int64_t kend) {
+  ++c.pos;
   if (STRIPED) {
     ++c.t;
     cursor_seek<TN, true>(p, c, kend);
@@ -157,6 +165,32 @@ __device__ __forceinline__ void cursor_next(const FwdParams& p, Cursor& c, int64
   c.kt = 0;
   ++c.t;
   cursor_seek<TN, STRIPED>(p, c, kend);
+}
+
+// Key splits: the run [pos_begin, pos_end) of the workgroup's walk that
+// its split covers.  Counting the walk costs a scalar loop over its tiles,
+// paid only when the share is split (small grids).  Without splits the run
+// is the whole walk.
+struct SplitRange {
+  int begin, end;
+};
+
+template <int TN, bool STRIPED>
+__device__ __forceinline__ SplitRange split_range(const FwdParams& p, int split, int64_t kend) {
+  if (p.key_splits <= 1) return SplitRange{0, INT_MAX};
+  Cursor c{0, 0, 0, 0, 0, 0, 0};
+  cursor_seek<TN, STRIPED>(p, c, kend);
+#pragma clang loop vectorize(disable) unroll(disable)
+  while (c.valid) cursor_next<TN, STRIPED>(p, c, kend);
+  const int64_t n = c.pos;
+  return SplitRange{(int)(n * split / p.key_splits), (int)(n * (split + 1) / p.key_splits)};
+}
+
+// Move a freshly sought cursor to the first tile of its split.
+template <int TN, bool STRIPED>
+__device__ __forceinline__ void cursor_to(const FwdParams& p, Cursor& c, int64_t kend, int pos) {
+#pragma clang loop vectorize(disable) unroll(disable)
+  while (c.valid && c.pos < pos) cursor_next<TN, STRIPED>(p, c, kend);
 }
 
 // A wave-uniform 64-bit value that the compiler computed in vector registers

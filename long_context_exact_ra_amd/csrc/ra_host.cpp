@@ -5,6 +5,7 @@
 
 #include "ra_attn.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -184,20 +185,32 @@ ra_status_t prepare(const void* q, const void* k, const void* v, const int32_t* 
   p.n_qtiles = (int32_t)n_qtiles;
   p.n_wg = (int32_t)n_wg;
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+  p.key_splits = 1;
   return RA_OK;
+}
+
+// Largest number of key splits a call accepts.
+constexpr int32_t kMaxKeySplits = 64;
+
+int64_t split_workspace_bytes(int64_t batch, int64_t seq_q, int64_t heads, int64_t head_dim,
+                              int32_t key_splits) {
+  if (key_splits <= 1 || batch <= 0 || seq_q <= 0 || heads <= 0 || head_dim <= 0) return 0;
+  return (int64_t)key_splits * batch * heads * seq_q * (head_dim + 2) * 4;
 }
 
 }  // namespace
 
 extern "C" {
 
-ra_status_t ra_blockwise_attn_fwd_placed(const void* q, const void* k, const void* v,
-                                         const int32_t* segment_ids, int64_t causal_block_size,
-                                         int64_t q_chunk, int64_t k_chunk, int32_t ring_size,
-                                         int32_t ring_index, ra_placement_t placement,
-                                         int64_t batch, int64_t seq_q, int64_t heads,
-                                         int64_t head_dim, ra_dtype_t dtype, void* out,
-                                         float* lse, uint8_t* run_map, void* stream) {
+ra_status_t ra_blockwise_attn_fwd_split(const void* q, const void* k, const void* v,
+                                        const int32_t* segment_ids, int64_t causal_block_size,
+                                        int64_t q_chunk, int64_t k_chunk, int32_t ring_size,
+                                        int32_t ring_index, ra_placement_t placement,
+                                        int64_t batch, int64_t seq_q, int64_t heads,
+                                        int64_t head_dim, ra_dtype_t dtype, void* out,
+                                        float* lse, uint8_t* run_map, int32_t key_splits,
+                                        void* workspace, int64_t workspace_bytes,
+                                        void* stream) {
   clear_error();
   if (placement != RA_PLACE_CONTIGUOUS && placement != RA_PLACE_STRIPED)
     return fail(RA_E_INVALID, "unknown placement %d", (int)placement);
@@ -209,12 +222,28 @@ ra_status_t ra_blockwise_attn_fwd_placed(const void* q, const void* k, const voi
     return fail(RA_E_UNSUPPORTED,
                 "striped placement supports causal_block_size 0 or 1 (got %lld)",
                 (long long)causal_block_size);
+  if (key_splits < 1 || key_splits > kMaxKeySplits)
+    return fail(RA_E_INVALID, "key_splits %d outside [1, %d]", key_splits, kMaxKeySplits);
   ra::FwdParams p;
   bool empty = false;
   ra_status_t st = prepare(q, k, v, segment_ids, causal_block_size, q_chunk, k_chunk, ring_size,
                            ring_index, batch, seq_q, heads, head_dim, dtype, p, empty);
   if (st != RA_OK || empty) return st;
   if (!out || !lse) return fail(RA_E_INVALID, "out and lse must be non-NULL");
+  if (key_splits > 1) {
+    const int64_t need = split_workspace_bytes(batch, seq_q, heads, head_dim, key_splits);
+    if (!workspace) return fail(RA_E_INVALID, "key_splits %d needs a workspace", key_splits);
+    if (workspace_bytes < need)
+      return fail(RA_E_INVALID, "workspace of %lld bytes is smaller than the %lld required",
+                  (long long)workspace_bytes, (long long)need);
+    const int64_t n_wg = (int64_t)p.n_wg * key_splits;
+    if (n_wg > kInt32Max)
+      return fail(RA_E_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)n_wg);
+    p.n_wg = (int32_t)n_wg;
+    p.key_splits = key_splits;
+    p.part_o = static_cast<float*>(workspace);
+    p.part_ml = p.part_o + (int64_t)key_splits * batch * heads * seq_q * head_dim;
+  }
   p.out = out;
   p.lse = lse;
   p.run_map = run_map;
@@ -226,6 +255,48 @@ ra_status_t ra_blockwise_attn_fwd_placed(const void* q, const void* k, const voi
   if (ra::launch_fwd(p, dt, (int)head_dim, map_bytes, stream, err, (int)sizeof(err)) != 0)
     return fail(RA_E_HIP, "%s", err);
   return RA_OK;
+}
+
+int64_t ra_blockwise_attn_fwd_split_workspace_bytes(int64_t batch, int64_t seq_q, int64_t heads,
+                                                     int64_t head_dim, int32_t key_splits) {
+  return split_workspace_bytes(batch, seq_q, heads, head_dim, key_splits);
+}
+
+int32_t ra_blockwise_attn_fwd_key_splits(int64_t batch, int64_t seq_q, int64_t heads,
+                                         ra_dtype_t dtype, int64_t causal_block_size,
+                                         int32_t ring_size, int32_t ring_index,
+                                         int32_t compute_units) {
+  if (batch <= 0 || seq_q <= 0 || heads <= 0 || compute_units <= 0 || ring_size < 1 ||
+      ring_index < 0 || ring_index >= ring_size || (dtype != RA_BF16 && dtype != RA_F32))
+    return 1;
+  const int64_t bm = ra::block_rows(dtype == RA_BF16 ? ra::Dtype::BF16 : ra::Dtype::F32);
+  const int64_t n_wg = batch * heads * ((seq_q + bm - 1) / bm);
+  if (n_wg >= compute_units) return 1;
+  // Key tiles of the longest walk: every key up to the last query's causal
+  // limit (contiguous placement; an upper bound for the striped one).
+  const int64_t seq_k = seq_q * ring_size;
+  int64_t keys = seq_k;
+  if (causal_block_size > 0) {
+    const int64_t last_q = (int64_t)ring_index * seq_q + seq_q - 1;
+    keys = std::min<int64_t>((last_q / causal_block_size + 1) * causal_block_size, seq_k);
+  }
+  const int64_t tiles = (keys + 63) / 64;
+  // One workgroup per compute unit at most, and at least 8 tiles per split.
+  int64_t splits = std::min<int64_t>(compute_units / n_wg, tiles / 8);
+  splits = std::max<int64_t>(1, std::min<int64_t>(splits, kMaxKeySplits));
+  return (int32_t)splits;
+}
+
+ra_status_t ra_blockwise_attn_fwd_placed(const void* q, const void* k, const void* v,
+                                         const int32_t* segment_ids, int64_t causal_block_size,
+                                         int64_t q_chunk, int64_t k_chunk, int32_t ring_size,
+                                         int32_t ring_index, ra_placement_t placement,
+                                         int64_t batch, int64_t seq_q, int64_t heads,
+                                         int64_t head_dim, ra_dtype_t dtype, void* out,
+                                         float* lse, uint8_t* run_map, void* stream) {
+  return ra_blockwise_attn_fwd_split(q, k, v, segment_ids, causal_block_size, q_chunk, k_chunk,
+                                     ring_size, ring_index, placement, batch, seq_q, heads,
+                                     head_dim, dtype, out, lse, run_map, 1, nullptr, 0, stream);
 }
 
 ra_status_t ra_blockwise_attn_fwd_ex(const void* q, const void* k, const void* v,

@@ -29,6 +29,12 @@ struct FwdParams {
   int32_t n_wg;         // workgroups in the grid
   float scale_log2;     // log2(e) / sqrt(head_dim)
   int32_t striped;      // 1: striped placement (causal is then 0 or 1)
+  // Key splits (>= 1).  With more than one, every query tile's key walk is
+  // cut into key_splits runs, one workgroup each; they write partial
+  // results and a combine kernel folds them into out and lse.
+  int32_t key_splits;
+  float* part_o;        // [key_splits][B][H][Lq][D] unnormalised numerators
+  float* part_ml;       // [key_splits][B][H][Lq][2] (kept max, base 2; denominator)
 };
 
 enum class Dtype : int { BF16 = 0, F32 = 1 };

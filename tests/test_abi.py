@@ -160,3 +160,38 @@ def test_bwd_placed_validation_without_gpu():
     assert call(1, 5) == ra.RA_E_INVALID
     assert call(1, ra.RA_PLACE_STRIPED, batch=0) == ra.RA_OK
     assert call(1, ra.RA_PLACE_STRIPED) == ra.RA_E_INVALID  # null tensors
+
+
+def test_split_validation_without_gpu():
+    """Key-split arguments are checked on the host before any device work."""
+    lib = ra.load_library()
+    P = 0x1000  # fake device pointers: every call below fails validation first
+    call = lambda splits, ws=P, wsb=1 << 40, batch=1: lib.ra_blockwise_attn_fwd_split(
+        P, P, P, None, 1, 32, 32, 4, 1, ra.RA_PLACE_CONTIGUOUS, batch, 64, 2, 128, ra.RA_BF16,
+        P, P, None, splits, ws, wsb, None)
+    assert call(0) == ra.RA_E_INVALID
+    assert call(65) == ra.RA_E_INVALID
+    assert call(4, ws=None) == ra.RA_E_INVALID
+    need = ra.fwd_split_workspace_bytes(1, 64, 2, 128, 4)
+    assert need == 4 * 1 * 2 * 64 * 130 * 4
+    assert call(4, wsb=need - 1) == ra.RA_E_INVALID
+    assert "workspace" in ra.last_error()
+    assert call(4, batch=0) == ra.RA_OK          # empty call: nothing to do
+    assert ra.fwd_split_workspace_bytes(1, 64, 2, 128, 1) == 0
+
+
+def test_key_split_recommendation():
+    """Splits only when the grid leaves compute units idle, one workgroup per
+    compute unit at most and at least 8 key tiles per split."""
+    ks = lambda B, Lq, H, dt, c, N, r, cu=256: ra.fwd_key_splits(B, Lq, H, dt, c, N, r, cu)
+    # 7B share: 4096 workgroups of 256 rows already fill 256 compute units
+    assert ks(1, 32768, 32, ra.RA_BF16, 1, 16, 15) == 1
+    # small causal share: 32 workgroups; r = 7 walks 8192 keys = 128 tiles
+    assert ks(1, 1024, 8, ra.RA_BF16, 1, 8, 7) == 8
+    # r = 0 walks 1024 keys = 16 tiles: at most 2 splits of 8 tiles
+    assert ks(1, 1024, 8, ra.RA_BF16, 1, 8, 0) == 2
+    # fp32 workgroups hold 128 rows; non-causal walks every key
+    assert ks(1, 64, 2, ra.RA_F32, None, 4, 0) == 1     # 4 tiles: too short to split
+    assert ks(1, 1024, 2, ra.RA_F32, None, 8, 3, cu=64) == 4
+    assert ks(0, 1024, 8, ra.RA_BF16, 1, 8, 0) == 1
+    assert ks(1, 1024, 8, ra.RA_BF16, 1, 8, 8) == 1     # invalid ring index
