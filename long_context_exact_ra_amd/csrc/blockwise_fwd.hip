@@ -81,7 +81,10 @@ __device__ __forceinline__ void write_partial(const FwdParams& p, int split, int
   if (half == 0) *reinterpret_cast<float2*>(p.part_ml + 2 * pr) = make_float2(m_run, l_tot);
 }
 
-// One thread per (row, 4 columns); rows in [b][h][i] order, as lse.
+// One thread per (row, 4 columns); rows in [b][h][i] order, as lse.  The
+// splits are folded eight at a time with a running max, so that the loads
+// of eight splits are in flight together; a split without a visible key
+// (denominator 0) gets weight 0.
 template <typename T>
 __global__ void combine_splits_kernel(const FwdParams p, int head_dim) {
   const int groups = head_dim / 4;
@@ -90,23 +93,42 @@ __global__ void combine_splits_kernel(const FwdParams p, int head_dim) {
   if (tid >= rows * groups) return;
   const int64_t r = tid / groups;
   const int g = (int)(tid % groups);
-  float mmax = ninf();
-  for (int s = 0; s < p.key_splits; ++s) {
-    const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + 2 * (s * rows + r));
-    if (ml.y > 0.f) mmax = fmaxf(mmax, ml.x);
-  }
-  float den = 0.f;
+  float mmax = ninf(), den = 0.f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < p.key_splits; ++s) {
-    const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + 2 * (s * rows + r));
-    if (!(ml.y > 0.f)) continue;
-    const float w = __builtin_amdgcn_exp2f(ml.x - mmax);
-    den += w * ml.y;
-    const float4 o = *reinterpret_cast<const float4*>(p.part_o + (s * rows + r) * head_dim + 4 * g);
-    num.x += w * o.x;
-    num.y += w * o.y;
-    num.z += w * o.z;
-    num.w += w * o.w;
+  for (int s0 = 0; s0 < p.key_splits; s0 += 8) {
+    float2 ml[8];
+    float4 o[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t pr = (int64_t)(s0 + u) * rows + r;
+      if (s0 + u < p.key_splits) {
+        ml[u] = *reinterpret_cast<const float2*>(p.part_ml + 2 * pr);
+        o[u] = *reinterpret_cast<const float4*>(p.part_o + pr * head_dim + 4 * g);
+      } else {
+        ml[u] = make_float2(ninf(), 0.f);
+        o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    float cm = mmax;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) cm = ml[u].y > 0.f ? fmaxf(cm, ml[u].x) : cm;
+    // Nothing folded yet (mmax = -inf) means den and num are still 0.
+    const float sc = mmax == ninf() ? 0.f : __builtin_amdgcn_exp2f(mmax - cm);
+    den *= sc;
+    num.x *= sc;
+    num.y *= sc;
+    num.z *= sc;
+    num.w *= sc;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = ml[u].y > 0.f ? __builtin_amdgcn_exp2f(ml[u].x - cm) : 0.f;
+      den += w * ml[u].y;
+      num.x += w * o[u].x;
+      num.y += w * o[u].y;
+      num.z += w * o[u].z;
+      num.w += w * o[u].w;
+    }
+    mmax = cm;
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   const int64_t i = r % p.seq_q, bh = r / p.seq_q;

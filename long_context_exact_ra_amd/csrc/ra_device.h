@@ -167,10 +167,10 @@ __device__ __forceinline__ void cursor_next(const FwdParams& p, Cursor& c, int64
   cursor_seek<TN, STRIPED>(p, c, kend);
 }
 
-// Key splits: the run [pos_begin, pos_end) of the workgroup's walk that
-// its split covers.  Counting the walk costs a scalar loop over its tiles,
-// paid only when the share is split (small grids).  Without splits the run
-// is the whole walk.
+// Key splits: the run [begin, end) of the workgroup's walk that its split
+// covers.  The walk's length is a sum over the ring blocks (contiguous
+// placement) or a count over its tiles (striped), paid only when the share
+// is split (small grids).  Without splits the run is the whole walk.
 struct SplitRange {
   int begin, end;
 };
@@ -178,17 +178,40 @@ struct SplitRange {
 template <int TN, bool STRIPED>
 __device__ __forceinline__ SplitRange split_range(const FwdParams& p, int split, int64_t kend) {
   if (p.key_splits <= 1) return SplitRange{0, INT_MAX};
-  Cursor c{0, 0, 0, 0, 0, 0, 0};
-  cursor_seek<TN, STRIPED>(p, c, kend);
+  int64_t n = 0;
+  if (!STRIPED) {
+    // Block by block: every block contributes its whole tile count.
 #pragma clang loop vectorize(disable) unroll(disable)
-  while (c.valid) cursor_next<TN, STRIPED>(p, c, kend);
-  const int64_t n = c.pos;
+    for (int kb = 0; kb < p.ring_size; ++kb) n += (block_klen<false>(p, kb, kend) + TN - 1) / TN;
+  } else {
+    Cursor c{0, 0, 0, 0, 0, 0, 0};
+    cursor_seek<TN, true>(p, c, kend);
+#pragma clang loop vectorize(disable) unroll(disable)
+    while (c.valid) cursor_next<TN, true>(p, c, kend);
+    n = c.pos;
+  }
   return SplitRange{(int)(n * split / p.key_splits), (int)(n * (split + 1) / p.key_splits)};
 }
 
-// Move a freshly sought cursor to the first tile of its split.
+// Move a freshly sought cursor to walk position `pos` (the first tile of
+// its split).  Block by block for the contiguous walk, tile by tile for the
+// striped one.
 template <int TN, bool STRIPED>
 __device__ __forceinline__ void cursor_to(const FwdParams& p, Cursor& c, int64_t kend, int pos) {
+  if (!STRIPED) {
+#pragma clang loop vectorize(disable) unroll(disable)
+    while (c.valid && c.pos + (c.ntile - c.kt) <= pos) {
+      c.pos += c.ntile - c.kt;
+      c.kt = 0;
+      ++c.t;
+      cursor_seek<TN, false>(p, c, kend);
+    }
+    if (c.valid && c.pos < pos) {
+      c.kt += pos - c.pos;
+      c.pos = pos;
+    }
+    return;
+  }
 #pragma clang loop vectorize(disable) unroll(disable)
   while (c.valid && c.pos < pos) cursor_next<TN, STRIPED>(p, c, kend);
 }
