@@ -228,8 +228,9 @@ def main():
                     help="time the attention forward (default), its backward, or the "
                          "blockwise feedforward")
     ap.add_argument("--key-splits", default="auto",
-                    help="forward: key splits per query tile ('auto' = the library's count "
-                         "for this GPU, 1 for shares that fill it; an integer forces it)")
+                    help="key splits per query tile of the forward (and of the backward's "
+                         "dq kernel): 'auto' = the library's count for this GPU, 1 for "
+                         "shares that fill it; an integer forces it")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first; its "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate HBM byte counts")
@@ -303,8 +304,8 @@ def main():
     splits = [ra.fwd_key_splits(w.batch, w.seq_q, w.heads, ra.RA_BF16, w.causal_block_size,
                                 w.ring_size, ri, cus) if args.key_splits == "auto"
               else int(args.key_splits) for ri in w.ring_indices]
-    ws_bytes = max(ra.fwd_split_workspace_bytes(w.batch, w.seq_q, w.heads, w.head_dim, n)
-                   for n in splits)
+    ws_fn = ra.bwd_split_workspace_bytes if args.pass_ == "bwd" else ra.fwd_split_workspace_bytes
+    ws_bytes = max(ws_fn(w.batch, w.seq_q, w.heads, w.head_dim, n) for n in splits)
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
     def step():
@@ -313,7 +314,8 @@ def main():
                 ra.blockwise_attn_bwd(qi, k, v, fw[i][0], fw[i][1], douts[i], seg,
                                       w.causal_block_size, w.q_chunk, w.k_chunk, w.ring_size,
                                       ri, dq=dq, dk=dk, dv=dv, delta=delta,
-                                      placement=w.placement)
+                                      placement=w.placement, key_splits=splits[i],
+                                      workspace=workspace)
             else:
                 ra.blockwise_attn_fwd(qi, k, v, seg, w.causal_block_size, w.q_chunk,
                                       w.k_chunk, w.ring_size, ri, out=out, lse=lse,
@@ -381,7 +383,7 @@ def main():
                    "causal_block_size": w.causal_block_size,
                    "q_chunk": w.q_chunk, "k_chunk": w.k_chunk, "pass": args.pass_,
                    "placement": w.placement,
-                   "key_splits": None if bwd else (splits[0] if len(splits) == 1 else splits),
+                   "key_splits": splits[0] if len(splits) == 1 else splits,
                    "flops_per_step": flops, "ms_min": round(min(per), 3),
                    "wall_s": round(wall, 3)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),

@@ -291,6 +291,50 @@ ra_status_t ra_blockwise_attn_bwd_placed(const void* q, const void* k,
                                          float* dv, float* delta, void* stream);
 
 /*
+ * ra_blockwise_attn_bwd_split -- the backward with the query tiles' walks
+ * over the keys cut into key_splits runs, as in ra_blockwise_attn_fwd_split.
+ *
+ * dq_i is a sum over the visible keys of terms that the forward's lse and
+ * delta fix completely, so it splits over any partition of the keys: each
+ * run's workgroup writes its addend to dq into the workspace, and a last
+ * kernel adds the addends in split order (deterministic: no atomics).  dk,
+ * dv and delta are computed as by ra_blockwise_attn_bwd_placed.
+ *
+ *   key_splits: 1 .. 64; 1 is exactly ra_blockwise_attn_bwd_placed (the
+ *       workspace may then be NULL).
+ *   workspace: device memory of at least
+ *       ra_blockwise_attn_bwd_split_workspace_bytes(...) bytes, owned by
+ *       the caller (float32 [key_splits][batch][seq_q][heads][head_dim]);
+ *       its contents on entry do not matter.  Two calls sharing a workspace
+ *       must be ordered on one stream.
+ *   Everything else as for ra_blockwise_attn_bwd_placed.
+ *
+ * Errors as for ra_blockwise_attn_bwd_placed, plus RA_E_INVALID for
+ * key_splits outside [1, 64], or key_splits > 1 with a NULL workspace or
+ * one smaller than required.
+ */
+ra_status_t ra_blockwise_attn_bwd_split(const void* q, const void* k,
+                                        const void* v, const int32_t* segment_ids,
+                                        int64_t causal_block_size, int64_t q_chunk,
+                                        int64_t k_chunk, int32_t ring_size,
+                                        int32_t ring_index, ra_placement_t placement,
+                                        int64_t batch, int64_t seq_q, int64_t heads,
+                                        int64_t head_dim, ra_dtype_t dtype,
+                                        const void* out, const float* lse,
+                                        const void* dout, float* dq, float* dk,
+                                        float* dv, float* delta, int32_t key_splits,
+                                        void* workspace, int64_t workspace_bytes,
+                                        void* stream);
+
+/* Workspace bytes ra_blockwise_attn_bwd_split needs: key_splits * batch *
+ * seq_q * heads * head_dim * 4; 0 when key_splits <= 1 or a size is not
+ * positive.  Host-only.  ra_blockwise_attn_fwd_key_splits gives a split
+ * count for the backward too (its dq kernel has the forward's grid). */
+int64_t ra_blockwise_attn_bwd_split_workspace_bytes(int64_t batch, int64_t seq_q,
+                                                     int64_t heads, int64_t head_dim,
+                                                     int32_t key_splits);
+
+/*
  * ra_blockwise_ffn -- the feedforward of the Blockwise Transformer, one
  * sequence chunk at a time.
  *

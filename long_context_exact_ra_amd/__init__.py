@@ -18,6 +18,7 @@ from typing import Optional, Tuple
 
 __all__ = ["RaError", "blockwise_attn_fwd", "blockwise_attn_bwd", "blockwise_ffn",
            "ffn_workspace_bytes", "fwd_split_workspace_bytes", "fwd_key_splits",
+           "bwd_split_workspace_bytes",
            "blockwise_plan", "last_error", "lib_path",
            "load_library", "version", "RA_OK", "RA_E_INVALID", "RA_E_UNSUPPORTED",
            "RA_E_HIP", "RA_BF16", "RA_F32", "RA_PLACE_CONTIGUOUS", "RA_PLACE_STRIPED"]
@@ -83,6 +84,12 @@ def load_library():
     lib.ra_blockwise_attn_bwd_placed.argtypes = (fwd_args[:9] + [ctypes.c_int] + fwd_args[9:14]
                                                  + [c_vp] * 8)
     lib.ra_blockwise_attn_bwd_placed.restype = ctypes.c_int
+    lib.ra_blockwise_attn_bwd_split.argtypes = (fwd_args[:9] + [ctypes.c_int] + fwd_args[9:14]
+                                                + [c_vp] * 7 + [c_i32, c_vp, c_i64, c_vp])
+    lib.ra_blockwise_attn_bwd_split.restype = ctypes.c_int
+    lib.ra_blockwise_attn_bwd_split_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_i64,
+                                                                c_i32]
+    lib.ra_blockwise_attn_bwd_split_workspace_bytes.restype = c_i64
     lib.ra_blockwise_ffn_workspace_bytes.argtypes = [c_i64, c_i64]
     lib.ra_blockwise_ffn_workspace_bytes.restype = c_i64
     lib.ra_blockwise_ffn.argtypes = [c_vp] * 5 + [c_i64] * 5 + [ctypes.c_int, c_vp, c_vp,
@@ -141,6 +148,13 @@ def fwd_split_workspace_bytes(batch: int, seq_q: int, heads: int, head_dim: int,
                               key_splits: int) -> int:
     """Device bytes ``ra_blockwise_attn_fwd_split`` needs as workspace."""
     return int(load_library().ra_blockwise_attn_fwd_split_workspace_bytes(
+        batch, seq_q, heads, head_dim, key_splits))
+
+
+def bwd_split_workspace_bytes(batch: int, seq_q: int, heads: int, head_dim: int,
+                              key_splits: int) -> int:
+    """Device bytes ``ra_blockwise_attn_bwd_split`` needs as workspace."""
+    return int(load_library().ra_blockwise_attn_bwd_split_workspace_bytes(
         batch, seq_q, heads, head_dim, key_splits))
 
 
@@ -248,7 +262,7 @@ def blockwise_attn_bwd(q, k, v, out, lse, dout, segment_ids=None,
                        causal_block_size: Optional[int] = None, q_chunk: int = 512,
                        k_chunk: int = 512, ring_size: int = 1, ring_index: int = 0, *,
                        dq=None, dk=None, dv=None, delta=None, stream=None,
-                       placement: str = "contiguous"):
+                       placement: str = "contiguous", key_splits=1, workspace=None):
     """Backward of ring position ``ring_index``: returns (dq, dk, dv, delta).
 
     q, k, v, segment_ids and the mask arguments as for blockwise_attn_fwd
@@ -257,7 +271,9 @@ def blockwise_attn_bwd(q, k, v, out, lse, dout, segment_ids=None,
     dk, dv [B, ring_size * Lq, H, D] and delta [B, H, Lq] are float32 and
     allocated when not given; dk and dv hold this share's contribution.
     placement: as for blockwise_attn_fwd (dk, dv and segment_ids in storage
-    order).
+    order).  key_splits / workspace: as for blockwise_attn_fwd
+    (``ra_blockwise_attn_bwd_split``; the split applies to the dq kernel,
+    whose addends a last kernel sums).
     """
     import torch
     lib = load_library()
@@ -294,11 +310,26 @@ def blockwise_attn_bwd(q, k, v, out, lse, dout, segment_ids=None,
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    _check(lib.ra_blockwise_attn_bwd_placed(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), seg_ptr, int(causal_block_size or 0),
-        q_chunk, k_chunk, ring_size, ring_index, _placement(placement), B, Lq, H, D, RA_BF16,
-        out.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-        dv.data_ptr(), delta.data_ptr(), sptr))
+    if key_splits == "auto":
+        cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+        key_splits = fwd_key_splits(B, Lq, H, RA_BF16, causal_block_size, ring_size,
+                                    ring_index, cus)
+    key_splits = int(key_splits)
+    args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), seg_ptr, int(causal_block_size or 0),
+            q_chunk, k_chunk, ring_size, ring_index, _placement(placement), B, Lq, H, D, RA_BF16,
+            out.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+            dv.data_ptr(), delta.data_ptr()]
+    if key_splits != 1:
+        need = bwd_split_workspace_bytes(B, Lq, H, D, key_splits)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        ws_bytes = workspace.numel() * workspace.element_size()
+        _check(lib.ra_blockwise_attn_bwd_split(*args, key_splits, workspace.data_ptr(),
+                                               ws_bytes, sptr))
+    else:
+        _check(lib.ra_blockwise_attn_bwd_placed(*args, sptr))
     return dq, dk, dv, delta
 
 

@@ -24,6 +24,10 @@
 //                      wave in registers, V resident in LDS) and streams the
 //                      query tiles that can see them (Q, dout, segment ids,
 //                      lse and delta) through two LDS stages.
+// With key splits (small shares, whose query tiles leave compute units
+// idle), the dq kernel's workgroups each walk one run of the key tiles and
+// write their addend to dq into a workspace; a fourth launch,
+// bwd_dq_sum_kernel, adds them in split order.
 // Both main kernels recompute the scores and dp, so a visible pair costs
 // 7 matrix products here against the 5 of the algorithm; every result is
 // written exactly once (no atomics), so dk and dv of keys no local query
@@ -248,6 +252,8 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dq_kernel(const BwdParams 
   const int64_t pq_first = (int64_t)p.ring_index * p.seq_q + w.qg0;
   const WaveLimits lim = wave_limits(p, STRIPED ? w.qg0 : pq_first, w.lrow, w.active);
   w.kend = wg_kend<kBlockMBf16, STRIPED>(p, m0);
+  // With key splits this workgroup walks only its run of the key tiles.
+  const SplitRange sr = split_range<64, STRIPED>(p, wc.split, w.kend);
   w.seg_q = 0;
   if (SEG && w.active) w.seg_q = p.seg[(int64_t)b * p.seq_k + pq_first + w.lrow];
   w.qseg = SegRange{0, 0};
@@ -315,10 +321,12 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dq_kernel(const BwdParams 
   // Tiles 0, 1, 2 in flight; tile i is read in step i, tile i+3 is fetched
   // into the stage of tile i-1 at the start of step i.
   TileInfo ti[4];
-  Cursor ic{0, 0, 0, 0, 0, 0};
+  Cursor ic{0, 0, 0, 0, 0, 0, 0};
   cursor_seek<64, STRIPED>(p, ic, w.kend);
+  cursor_to<64, STRIPED>(p, ic, w.kend, sr.begin);
   auto fetch = [&](int s) {
     if (SEG && smask_p != nullptr) cursor_skip_masked<64, STRIPED>(p, ic, w.kend, smask_p);
+    if (ic.pos >= sr.end) ic.valid = 0;
     ti[s] = tile_info<64, STRIPED>(p, ic);
     if (ic.valid) {
       __bf16* d = stg[s];
@@ -371,7 +379,12 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dq_kernel(const BwdParams 
 
   if (!w.active) return;
   const float scale = p.scale_log2 / kLog2e;
-  float* drow = bp.dq + ((int64_t)b * p.seq_q + w.qg0 + w.lrow) * rs + (int64_t)h * D;
+  // A split writes its addend to dq into its own slice of the workspace.
+  float* const dst =
+      bp.dq_part != nullptr
+          ? bp.dq_part + (int64_t)wc.split * p.batch * p.seq_q * p.heads * D
+          : bp.dq;
+  float* drow = dst + ((int64_t)b * p.seq_q + w.qg0 + w.lrow) * rs + (int64_t)h * D;
 #pragma unroll
   for (int j = 0; j < NDB; ++j)
 #pragma unroll
@@ -692,6 +705,23 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
 }
 
 // The dQ and dK/dV kernels of one configuration.
+// dq = the sum of the splits' addends, four values per thread, in split
+// order (deterministic).
+__global__ __launch_bounds__(256) void bwd_dq_sum_kernel(const BwdParams bp, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const float4* part = reinterpret_cast<const float4*>(bp.dq_part);
+  float4 acc = part[i];
+  for (int s = 1; s < bp.f.key_splits; ++s) {
+    const float4 v = part[(int64_t)s * n4 + i];
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  reinterpret_cast<float4*>(bp.dq)[i] = acc;
+}
+
 template <int D, bool SEG, bool STRIPED>
 void launch_main(dim3 qgrid, dim3 kgrid, dim3 block, hipStream_t s, const BwdParams& bp) {
   hipLaunchKernelGGL((bwd_dq_kernel<D, SEG, STRIPED>), qgrid, block, 0, s, bp);
@@ -730,6 +760,11 @@ int launch_bwd(const BwdParams& bp, int head_dim, void* stream, char* err, int e
     else
       str ? launch_main<64, false, true>(qgrid, kgrid, block, s, bp)
           : launch_main<64, false, false>(qgrid, kgrid, block, s, bp);
+  }
+  if (bp.dq_part != nullptr) {
+    const int64_t n4 = rows * head_dim / 4;
+    hipLaunchKernelGGL(bwd_dq_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                       bp, n4);
   }
   e = hipGetLastError();
   if (e != hipSuccess) {

@@ -310,14 +310,16 @@ ra_status_t ra_blockwise_attn_fwd_ex(const void* q, const void* k, const void* v
                                       heads, head_dim, dtype, out, lse, run_map, stream);
 }
 
-ra_status_t ra_blockwise_attn_bwd_placed(const void* q, const void* k, const void* v,
-                                         const int32_t* segment_ids, int64_t causal_block_size,
-                                         int64_t q_chunk, int64_t k_chunk, int32_t ring_size,
-                                         int32_t ring_index, ra_placement_t placement,
-                                         int64_t batch, int64_t seq_q, int64_t heads,
-                                         int64_t head_dim, ra_dtype_t dtype, const void* out,
-                                         const float* lse, const void* dout, float* dq,
-                                         float* dk, float* dv, float* delta, void* stream) {
+ra_status_t ra_blockwise_attn_bwd_split(const void* q, const void* k, const void* v,
+                                        const int32_t* segment_ids, int64_t causal_block_size,
+                                        int64_t q_chunk, int64_t k_chunk, int32_t ring_size,
+                                        int32_t ring_index, ra_placement_t placement,
+                                        int64_t batch, int64_t seq_q, int64_t heads,
+                                        int64_t head_dim, ra_dtype_t dtype, const void* out,
+                                        const float* lse, const void* dout, float* dq,
+                                        float* dk, float* dv, float* delta, int32_t key_splits,
+                                        void* workspace, int64_t workspace_bytes,
+                                        void* stream) {
   clear_error();
   if (placement != RA_PLACE_CONTIGUOUS && placement != RA_PLACE_STRIPED)
     return fail(RA_E_INVALID, "unknown placement %d", (int)placement);
@@ -326,7 +328,9 @@ ra_status_t ra_blockwise_attn_bwd_placed(const void* q, const void* k, const voi
     return fail(RA_E_UNSUPPORTED,
                 "striped placement supports causal_block_size 0 or 1 (got %lld)",
                 (long long)causal_block_size);
-  ra::BwdParams bp;
+  if (key_splits < 1 || key_splits > kMaxKeySplits)
+    return fail(RA_E_INVALID, "key_splits %d outside [1, %d]", key_splits, kMaxKeySplits);
+  ra::BwdParams bp{};
   bool empty = false;
   ra_status_t st = prepare(q, k, v, segment_ids, causal_block_size, q_chunk, k_chunk, ring_size,
                            ring_index, batch, seq_q, heads, head_dim, dtype, bp.f, empty);
@@ -336,6 +340,20 @@ ra_status_t ra_blockwise_attn_bwd_placed(const void* q, const void* k, const voi
   if (empty) return RA_OK;
   if (!out || !lse || !dout || !dq || !dk || !dv || !delta)
     return fail(RA_E_INVALID, "out, lse, dout, dq, dk, dv and delta must be non-NULL");
+  if (key_splits > 1) {
+    const int64_t need = ra_blockwise_attn_bwd_split_workspace_bytes(batch, seq_q, heads,
+                                                                      head_dim, key_splits);
+    if (!workspace) return fail(RA_E_INVALID, "key_splits %d needs a workspace", key_splits);
+    if (workspace_bytes < need)
+      return fail(RA_E_INVALID, "workspace of %lld bytes is smaller than the %lld required",
+                  (long long)workspace_bytes, (long long)need);
+    const int64_t n_wg = (int64_t)bp.f.n_wg * key_splits;
+    if (n_wg > kInt32Max)
+      return fail(RA_E_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)n_wg);
+    bp.f.n_wg = (int32_t)n_wg;
+    bp.f.key_splits = key_splits;
+    bp.dq_part = static_cast<float*>(workspace);
+  }
   bp.f.striped = placement == RA_PLACE_STRIPED ? 1 : 0;
   bp.out = out;
   bp.lse = lse;
@@ -354,6 +372,26 @@ ra_status_t ra_blockwise_attn_bwd_placed(const void* q, const void* k, const voi
   if (ra::launch_bwd(bp, (int)head_dim, stream, err, (int)sizeof(err)) != 0)
     return fail(RA_E_HIP, "%s", err);
   return RA_OK;
+}
+
+int64_t ra_blockwise_attn_bwd_split_workspace_bytes(int64_t batch, int64_t seq_q, int64_t heads,
+                                                     int64_t head_dim, int32_t key_splits) {
+  if (key_splits <= 1 || batch <= 0 || seq_q <= 0 || heads <= 0 || head_dim <= 0) return 0;
+  return (int64_t)key_splits * batch * seq_q * heads * head_dim * 4;
+}
+
+ra_status_t ra_blockwise_attn_bwd_placed(const void* q, const void* k, const void* v,
+                                         const int32_t* segment_ids, int64_t causal_block_size,
+                                         int64_t q_chunk, int64_t k_chunk, int32_t ring_size,
+                                         int32_t ring_index, ra_placement_t placement,
+                                         int64_t batch, int64_t seq_q, int64_t heads,
+                                         int64_t head_dim, ra_dtype_t dtype, const void* out,
+                                         const float* lse, const void* dout, float* dq,
+                                         float* dk, float* dv, float* delta, void* stream) {
+  return ra_blockwise_attn_bwd_split(q, k, v, segment_ids, causal_block_size, q_chunk, k_chunk,
+                                     ring_size, ring_index, placement, batch, seq_q, heads,
+                                     head_dim, dtype, out, lse, dout, dq, dk, dv, delta, 1,
+                                     nullptr, 0, stream);
 }
 
 ra_status_t ra_blockwise_attn_bwd(const void* q, const void* k, const void* v,

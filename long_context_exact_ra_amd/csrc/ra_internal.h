@@ -57,6 +57,9 @@ struct BwdParams {
   float* dk;            // [B, S, H, D]
   float* dv;            // [B, S, H, D]
   float* delta;         // [B, H, Lq]
+  // With key splits (f.key_splits > 1): the splits' addends to dq,
+  // [key_splits][B, Lq, H, D]; a sum kernel writes dq.  Otherwise nullptr.
+  float* dq_part;
   int32_t n_ktiles;     // key tiles per (batch, head) of the dK/dV kernel
   int32_t n_wg_kv;      // workgroups of the dK/dV kernel
 };

@@ -195,3 +195,19 @@ def test_key_split_recommendation():
     assert ks(1, 1024, 2, ra.RA_F32, None, 8, 3, cu=64) == 4
     assert ks(0, 1024, 8, ra.RA_BF16, 1, 8, 0) == 1
     assert ks(1, 1024, 8, ra.RA_BF16, 1, 8, 8) == 1     # invalid ring index
+
+
+def test_bwd_split_validation_without_gpu():
+    lib = ra.load_library()
+    P = 0x1000
+    call = lambda splits, ws=P, wsb=1 << 40, batch=1: lib.ra_blockwise_attn_bwd_split(
+        P, P, P, None, 1, 32, 32, 4, 1, ra.RA_PLACE_CONTIGUOUS, batch, 64, 2, 128, ra.RA_BF16,
+        P, P, P, P, P, P, P, splits, ws, wsb, None)
+    assert call(0) == ra.RA_E_INVALID
+    assert call(65) == ra.RA_E_INVALID
+    assert call(3, ws=None) == ra.RA_E_INVALID
+    need = ra.bwd_split_workspace_bytes(1, 64, 2, 128, 3)
+    assert need == 3 * 64 * 2 * 128 * 4
+    assert call(3, wsb=need - 1) == ra.RA_E_INVALID
+    assert call(3, batch=0) == ra.RA_OK
+    assert ra.bwd_split_workspace_bytes(1, 64, 2, 128, 1) == 0

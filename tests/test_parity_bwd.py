@@ -53,7 +53,7 @@ def _short_documents(B, S, seed):
     return seg
 
 
-def _run(w, r, dev):
+def _run(w, r, dev, key_splits=1, workspace=None):
     q, k, v = workloads.make_qkv(w, r, device=dev)
     dout = workloads.make_dout(w, r, device=dev)
     seg = workloads.make_segments(w, device=dev)
@@ -64,7 +64,8 @@ def _run(w, r, dev):
                                      w.ring_size, r, placement=w.placement)
     dq, dk, dv, delta = ra.blockwise_attn_bwd(q, k, v, out, lse, dout, seg, w.causal_block_size,
                                               w.q_chunk, w.k_chunk, w.ring_size, r,
-                                              placement=w.placement)
+                                              placement=w.placement, key_splits=key_splits,
+                                              workspace=workspace)
     torch.cuda.synchronize()
     return q, k, v, dout, seg, out, (dq, dk, dv, delta)
 
@@ -77,10 +78,10 @@ def _check_delta(dout, out, delta, what):
     assert rel <= 1e-5, (what, rel)
 
 
-def _full_case(w, r, heads=None):
+def _full_case(w, r, heads=None, key_splits=1):
     dev = torch.device("cuda:0")
-    q, k, v, dout, seg, out, (dq, dk, dv, delta) = _run(w, r, dev)
-    what = f"{w.name} r={r}"
+    q, k, v, dout, seg, out, (dq, dk, dv, delta) = _run(w, r, dev, key_splits)
+    what = f"{w.name} r={r} splits={key_splits}"
     _check_delta(dout, out, delta, what)
     hs = list(range(w.heads)) if heads is None else list(heads)
     sl = lambda t: t[:, :, hs].contiguous().cpu()
@@ -212,3 +213,55 @@ def test_bwd_rejects_fp32_and_nulls():
     st = lib.ra_blockwise_attn_bwd(None, None, None, None, 0, 32, 32, 1, 0, 1, 32, 1, 128,
                                    ra.RA_BF16, None, None, None, None, None, None, None, None)
     assert st == ra.RA_E_INVALID, ra.last_error()
+
+
+# ---------------------------------------------------------------------------
+# key splits of the dq kernel (ra_blockwise_attn_bwd_split)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("r", [0, 7])
+def test_bwd_small_causal_split(r):
+    _full_case(workloads.get("small_causal"), r, key_splits="auto")
+
+
+def test_bwd_small_causal_striped_split():
+    _full_case(workloads.get("small_causal_striped"), 6, key_splits=5)
+
+
+SPLIT_EDGE = [
+    # B, Lq, N, H, D, causal, qc, kc, segments, r, placement, splits
+    (2, 96, 3, 2, 64, 1, 32, 32, False, 2, "contiguous", 3),
+    (1, 128, 1, 4, 128, None, 128, 128, False, 0, "contiguous", 2),
+    (2, 128, 2, 2, 128, 1, 64, 64, True, 1, "contiguous", 4),
+    (1, 512, 3, 1, 128, 64, 128, 128, True, 2, "contiguous", 7),
+    (2, 128, 4, 2, 64, 1, 64, 32, True, 2, "striped", 6),
+    (1, 32, 4, 1, 128, 1, 32, 32, False, 3, "contiguous", 64),   # splits >> tiles
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_EDGE, ids=[str(c) for c in SPLIT_EDGE])
+def test_bwd_split_edge(case):
+    B, Lq, N, H, D, c, qc, kc, segs, r, place, splits = case
+    w = workloads.Workload(f"split_edge{case}", B, Lq, N, (r,), H, D, "bf16", c, qc, kc,
+                           segments=segs, seed=6161 + Lq + D + N, placement=place)
+    _full_case(w, r, key_splits=splits)
+
+
+def test_bwd_split_workspace_and_unsplit_agree():
+    """A workspace full of NaN on entry does not matter; dk, dv and delta do
+    not depend on the split (bitwise), dq only through the order of its
+    float32 sum."""
+    w = workloads.get("small_causal")
+    r = 4
+    dev = torch.device("cuda:0")
+    splits = 8
+    nbytes = ra.bwd_split_workspace_bytes(w.batch, w.seq_q, w.heads, w.head_dim, splits)
+    assert nbytes == splits * w.batch * w.seq_q * w.heads * w.head_dim * 4
+    ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device=dev)
+    _, _, _, _, _, _, g1 = _run(w, r, dev)
+    _, _, _, _, _, _, g2 = _run(w, r, dev, key_splits=splits, workspace=ws)
+    for name, a, b in zip(("dk", "dv", "delta"), g1[1:], g2[1:]):
+        assert torch.equal(a, b), name
+    _cmp("dq split vs unsplit", to_np(g2[0]), to_np(g1[0]), "small_causal r=4")
+    rel = float((g2[0].double() - g1[0].double()).norm() / g1[0].double().norm())
+    assert rel <= 1e-5, rel
