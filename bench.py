@@ -302,7 +302,7 @@ def main():
     # (allocated here, outside the timed region).
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     splits = [ra.fwd_key_splits(w.batch, w.seq_q, w.heads, ra.RA_BF16, w.causal_block_size,
-                                w.ring_size, ri, cus) if args.key_splits == "auto"
+                                w.ring_size, ri, cus, w.placement) if args.key_splits == "auto"
               else int(args.key_splits) for ri in w.ring_indices]
     ws_fn = ra.bwd_split_workspace_bytes if args.pass_ == "bwd" else ra.fwd_split_workspace_bytes
     ws_bytes = max(ws_fn(w.batch, w.seq_q, w.heads, w.head_dim, n) for n in splits)

@@ -219,12 +219,13 @@ int64_t ra_blockwise_attn_fwd_split_workspace_bytes(int64_t batch, int64_t seq_q
  * ceil(seq_q / rows per workgroup) workgroups, 256 rows for RA_BF16, 128
  * for RA_F32) already fills compute_units; otherwise as many splits as
  * keep one workgroup per compute unit, at most one per 8 key tiles of 64
- * keys of the longest walk, and at most 64.  Host-only; invalid arguments
- * give 1. */
+ * keys of the longest walk (contiguous: the keys up to the last query's
+ * causal limit; striped or non-causal: the whole sequence), and at most
+ * 64.  Host-only; invalid arguments give 1. */
 int32_t ra_blockwise_attn_fwd_key_splits(int64_t batch, int64_t seq_q, int64_t heads,
                                          ra_dtype_t dtype, int64_t causal_block_size,
                                          int32_t ring_size, int32_t ring_index,
-                                         int32_t compute_units);
+                                         ra_placement_t placement, int32_t compute_units);
 
 /*
  * ra_blockwise_attn_bwd -- the gradients of one ring position's share.

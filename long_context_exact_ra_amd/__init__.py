@@ -77,7 +77,7 @@ def load_library():
                                                                 c_i32]
     lib.ra_blockwise_attn_fwd_split_workspace_bytes.restype = c_i64
     lib.ra_blockwise_attn_fwd_key_splits.argtypes = [c_i64, c_i64, c_i64, ctypes.c_int, c_i64,
-                                                     c_i32, c_i32, c_i32]
+                                                     c_i32, c_i32, ctypes.c_int, c_i32]
     lib.ra_blockwise_attn_fwd_key_splits.restype = c_i32
     lib.ra_blockwise_attn_bwd.argtypes = fwd_args[:14] + [c_vp] * 8
     lib.ra_blockwise_attn_bwd.restype = ctypes.c_int
@@ -160,12 +160,12 @@ def bwd_split_workspace_bytes(batch: int, seq_q: int, heads: int, head_dim: int,
 
 def fwd_key_splits(batch: int, seq_q: int, heads: int, dtype: int,
                    causal_block_size: Optional[int], ring_size: int, ring_index: int,
-                   compute_units: int) -> int:
+                   compute_units: int, placement: str = "contiguous") -> int:
     """The library's key split count for a share on a GPU with
     ``compute_units`` compute units (1 = no split)."""
     return int(load_library().ra_blockwise_attn_fwd_key_splits(
         batch, seq_q, heads, dtype, int(causal_block_size or 0), ring_size, ring_index,
-        compute_units))
+        _placement(placement), compute_units))
 
 
 def blockwise_attn_fwd(q, k, v, segment_ids=None, causal_block_size: Optional[int] = None,
@@ -226,7 +226,8 @@ def blockwise_attn_fwd(q, k, v, segment_ids=None, causal_block_size: Optional[in
     place = _placement(placement)
     if key_splits == "auto":
         cus = torch.cuda.get_device_properties(q.device).multi_processor_count
-        key_splits = fwd_key_splits(B, Lq, H, dt, causal_block_size, ring_size, ring_index, cus)
+        key_splits = fwd_key_splits(B, Lq, H, dt, causal_block_size, ring_size, ring_index, cus,
+                                    placement)
     key_splits = int(key_splits)
     args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), seg_ptr, int(causal_block_size or 0),
             q_chunk, k_chunk, ring_size, ring_index, B, Lq, H, D, dt,
@@ -313,7 +314,7 @@ def blockwise_attn_bwd(q, k, v, out, lse, dout, segment_ids=None,
     if key_splits == "auto":
         cus = torch.cuda.get_device_properties(q.device).multi_processor_count
         key_splits = fwd_key_splits(B, Lq, H, RA_BF16, causal_block_size, ring_size,
-                                    ring_index, cus)
+                                    ring_index, cus, placement)
     key_splits = int(key_splits)
     args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), seg_ptr, int(causal_block_size or 0),
             q_chunk, k_chunk, ring_size, ring_index, _placement(placement), B, Lq, H, D, RA_BF16,

@@ -175,6 +175,20 @@ struct SplitRange {
   int begin, end;
 };
 
+// Striped placement: a block's tile count depends only on whether kb > r
+// (its key coordinates start at 1 instead of 0).  Blocks kb <= r are ring
+// steps t = 0 .. r, blocks kb > r steps t = r + 1 .. N - 1.
+struct StripedCounts {
+  int lo, hi;  // tiles of each block kb <= r / kb > r
+};
+
+template <int TN>
+__device__ __forceinline__ StripedCounts striped_counts(const FwdParams& p, int64_t kend) {
+  const int kb_hi = p.ring_index + 1 < p.ring_size ? p.ring_index + 1 : p.ring_index;
+  return StripedCounts{(block_klen<true>(p, p.ring_index, kend) + TN - 1) / TN,
+                       (block_klen<true>(p, kb_hi, kend) + TN - 1) / TN};
+}
+
 template <int TN, bool STRIPED>
 __device__ __forceinline__ SplitRange split_range(const FwdParams& p, int split, int64_t kend) {
   if (p.key_splits <= 1) return SplitRange{0, INT_MAX};
@@ -184,18 +198,17 @@ __device__ __forceinline__ SplitRange split_range(const FwdParams& p, int split,
 #pragma clang loop vectorize(disable) unroll(disable)
     for (int kb = 0; kb < p.ring_size; ++kb) n += (block_klen<false>(p, kb, kend) + TN - 1) / TN;
   } else {
-    Cursor c{0, 0, 0, 0, 0, 0, 0};
-    cursor_seek<TN, true>(p, c, kend);
-#pragma clang loop vectorize(disable) unroll(disable)
-    while (c.valid) cursor_next<TN, true>(p, c, kend);
-    n = c.pos;
+    const StripedCounts sc = striped_counts<TN>(p, kend);
+    n = (int64_t)(p.ring_index + 1) * sc.lo + (int64_t)(p.ring_size - 1 - p.ring_index) * sc.hi;
   }
   return SplitRange{(int)(n * split / p.key_splits), (int)(n * (split + 1) / p.key_splits)};
 }
 
 // Move a freshly sought cursor to walk position `pos` (the first tile of
-// its split).  Block by block for the contiguous walk, tile by tile for the
-// striped one.
+// its split).  Contiguous walk: block by block.  Striped walk (tile kt of
+// every block that has one, in ring order, then kt + 1): every round below
+// the smaller tile count visits all N blocks, the rounds above it only the
+// blocks with the larger count, which are consecutive ring steps.
 template <int TN, bool STRIPED>
 __device__ __forceinline__ void cursor_to(const FwdParams& p, Cursor& c, int64_t kend, int pos) {
   if (!STRIPED) {
@@ -212,8 +225,35 @@ __device__ __forceinline__ void cursor_to(const FwdParams& p, Cursor& c, int64_t
     }
     return;
   }
-#pragma clang loop vectorize(disable) unroll(disable)
-  while (c.valid && c.pos < pos) cursor_next<TN, STRIPED>(p, c, kend);
+  if (!c.valid || pos <= c.pos) return;
+  const StripedCounts sc = striped_counts<TN>(p, kend);
+  const int n_lo = p.ring_index + 1, n_hi = p.ring_size - 1 - p.ring_index;
+  const int full = min(sc.lo, sc.hi);
+  const int64_t in_full = (int64_t)full * p.ring_size;
+  int kt, t;
+  if (pos < in_full) {
+    kt = pos / p.ring_size;
+    t = pos % p.ring_size;
+  } else {
+    // Rounds full .. max - 1 visit only the blocks with the larger count.
+    const bool lo_longer = sc.lo > sc.hi;
+    const int cnt = lo_longer ? n_lo : n_hi;
+    const int64_t rest = pos - in_full;
+    if (cnt == 0 || rest >= (int64_t)cnt * (max(sc.lo, sc.hi) - full)) {
+      c.valid = 0;
+      c.pos = pos;
+      return;
+    }
+    kt = full + (int)(rest / cnt);
+    t = (int)(rest % cnt) + (lo_longer ? 0 : n_lo);
+  }
+  c.kt = kt;
+  c.t = t;
+  c.kb = p.ring_index - t;
+  if (c.kb < 0) c.kb += p.ring_size;
+  c.klen = block_klen<true>(p, c.kb, kend);
+  c.ntile = (c.klen + TN - 1) / TN;
+  c.pos = pos;
 }
 
 // A wave-uniform 64-bit value that the compiler computed in vector registers

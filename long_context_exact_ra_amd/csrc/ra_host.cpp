@@ -265,18 +265,20 @@ int64_t ra_blockwise_attn_fwd_split_workspace_bytes(int64_t batch, int64_t seq_q
 int32_t ra_blockwise_attn_fwd_key_splits(int64_t batch, int64_t seq_q, int64_t heads,
                                          ra_dtype_t dtype, int64_t causal_block_size,
                                          int32_t ring_size, int32_t ring_index,
-                                         int32_t compute_units) {
+                                         ra_placement_t placement, int32_t compute_units) {
   if (batch <= 0 || seq_q <= 0 || heads <= 0 || compute_units <= 0 || ring_size < 1 ||
-      ring_index < 0 || ring_index >= ring_size || (dtype != RA_BF16 && dtype != RA_F32))
+      ring_index < 0 || ring_index >= ring_size || (dtype != RA_BF16 && dtype != RA_F32) ||
+      (placement != RA_PLACE_CONTIGUOUS && placement != RA_PLACE_STRIPED))
     return 1;
   const int64_t bm = ra::block_rows(dtype == RA_BF16 ? ra::Dtype::BF16 : ra::Dtype::F32);
   const int64_t n_wg = batch * heads * ((seq_q + bm - 1) / bm);
   if (n_wg >= compute_units) return 1;
   // Key tiles of the longest walk: every key up to the last query's causal
-  // limit (contiguous placement; an upper bound for the striped one).
+  // limit under contiguous placement.  Under striped placement the last
+  // query row sees all but at most N - 1 keys of the sequence.
   const int64_t seq_k = seq_q * ring_size;
   int64_t keys = seq_k;
-  if (causal_block_size > 0) {
+  if (causal_block_size > 0 && placement == RA_PLACE_CONTIGUOUS) {
     const int64_t last_q = (int64_t)ring_index * seq_q + seq_q - 1;
     keys = std::min<int64_t>((last_q / causal_block_size + 1) * causal_block_size, seq_k);
   }

@@ -183,7 +183,8 @@ def test_split_validation_without_gpu():
 def test_key_split_recommendation():
     """Splits only when the grid leaves compute units idle, one workgroup per
     compute unit at most and at least 8 key tiles per split."""
-    ks = lambda B, Lq, H, dt, c, N, r, cu=256: ra.fwd_key_splits(B, Lq, H, dt, c, N, r, cu)
+    ks = lambda B, Lq, H, dt, c, N, r, cu=256, pl="contiguous": ra.fwd_key_splits(
+        B, Lq, H, dt, c, N, r, cu, pl)
     # 7B share: 4096 workgroups of 256 rows already fill 256 compute units
     assert ks(1, 32768, 32, ra.RA_BF16, 1, 16, 15) == 1
     # small causal share: 32 workgroups; r = 7 walks 8192 keys = 128 tiles
@@ -195,6 +196,10 @@ def test_key_split_recommendation():
     assert ks(1, 1024, 2, ra.RA_F32, None, 8, 3, cu=64) == 4
     assert ks(0, 1024, 8, ra.RA_BF16, 1, 8, 0) == 1
     assert ks(1, 1024, 8, ra.RA_BF16, 1, 8, 8) == 1     # invalid ring index
+    # striped: every ring position's last query row sees about the whole
+    # sequence (8192 keys = 128 tiles), so r = 0 splits as much as r = 7
+    assert ks(1, 1024, 8, ra.RA_BF16, 1, 8, 0, pl="striped") == 8
+    assert ks(1, 1024, 8, ra.RA_BF16, 1, 8, 7, pl="striped") == 8
 
 
 def test_bwd_split_validation_without_gpu():

@@ -56,7 +56,8 @@ def test_split_workloads_all_positions(name, splits):
         if splits == "auto":
             n = ra.fwd_key_splits(w.batch, w.seq_q, w.heads, ra.RA_BF16, w.causal_block_size,
                                   w.ring_size, r,
-                                  torch.cuda.get_device_properties(DEV).multi_processor_count)
+                                  torch.cuda.get_device_properties(DEV).multi_processor_count,
+                                  w.placement)
             log(f"{name} r={r}: {n} key splits")
             assert n > 1 or r == 0
         out, lse = run_split(q, k, v, None, w, r, splits)
