@@ -36,6 +36,10 @@
  * out = 0 and lse = -inf.  q, k and v must be finite: NaN or infinite
  * inputs give unspecified results.
  *
+ * Alignment: q, k, v, out (and the backward's dout, dq, dk, dv and the
+ * split workspaces) must be 16-byte aligned; segment_ids, lse and delta
+ * 4-byte aligned.  Misaligned pointers are rejected with RA_E_INVALID.
+ *
  * Ownership and synchronisation: all pointers except those marked "host"
  * are device pointers allocated by the caller; the library allocates no
  * device memory and keeps no pointer after a call returns.  Work is enqueued

@@ -29,6 +29,12 @@ void clear_error() { g_err[0] = '\0'; }
 
 constexpr int64_t kInt32Max = 2147483647LL;
 
+// The kernels move tensor rows in 16-byte vectors (loads, buffer-to-LDS DMA,
+// stores) and ids, lse and delta as 4-byte words.
+inline bool aligned(const void* ptr, uintptr_t bytes) {
+  return (reinterpret_cast<uintptr_t>(ptr) & (bytes - 1)) == 0;
+}
+
 // Checks shared by the forward and the planner.  `kernel_chunks` adds the
 // kernels' requirement that chunks are multiples of their 32-row sub-tiles.
 ra_status_t check_ring(int64_t causal_block_size, int64_t q_chunk, int64_t k_chunk,
@@ -155,6 +161,10 @@ ra_status_t prepare(const void* q, const void* k, const void* v, const int32_t* 
     return RA_OK;
   }
   if (!q || !k || !v) return fail(RA_E_INVALID, "q, k and v must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+    return fail(RA_E_INVALID, "q, k and v must be 16-byte aligned");
+  if (segment_ids && !aligned(segment_ids, 4))
+    return fail(RA_E_INVALID, "segment_ids must be 4-byte aligned");
   if (heads * head_dim > (1LL << 24))
     return fail(RA_E_UNSUPPORTED, "heads * head_dim = %lld exceeds 2^24",
                 (long long)(heads * head_dim));
@@ -230,9 +240,12 @@ ra_status_t ra_blockwise_attn_fwd_split(const void* q, const void* k, const void
                            ring_index, batch, seq_q, heads, head_dim, dtype, p, empty);
   if (st != RA_OK || empty) return st;
   if (!out || !lse) return fail(RA_E_INVALID, "out and lse must be non-NULL");
+  if (!aligned(out, 16) || !aligned(lse, 4))
+    return fail(RA_E_INVALID, "out must be 16-byte and lse 4-byte aligned");
   if (key_splits > 1) {
     const int64_t need = split_workspace_bytes(batch, seq_q, heads, head_dim, key_splits);
     if (!workspace) return fail(RA_E_INVALID, "key_splits %d needs a workspace", key_splits);
+    if (!aligned(workspace, 16)) return fail(RA_E_INVALID, "workspace must be 16-byte aligned");
     if (workspace_bytes < need)
       return fail(RA_E_INVALID, "workspace of %lld bytes is smaller than the %lld required",
                   (long long)workspace_bytes, (long long)need);
@@ -342,10 +355,15 @@ ra_status_t ra_blockwise_attn_bwd_split(const void* q, const void* k, const void
   if (empty) return RA_OK;
   if (!out || !lse || !dout || !dq || !dk || !dv || !delta)
     return fail(RA_E_INVALID, "out, lse, dout, dq, dk, dv and delta must be non-NULL");
+  if (!aligned(out, 16) || !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) ||
+      !aligned(dv, 16) || !aligned(lse, 4) || !aligned(delta, 4))
+    return fail(RA_E_INVALID,
+                "out, dout, dq, dk and dv must be 16-byte aligned, lse and delta 4-byte");
   if (key_splits > 1) {
     const int64_t need = ra_blockwise_attn_bwd_split_workspace_bytes(batch, seq_q, heads,
                                                                       head_dim, key_splits);
     if (!workspace) return fail(RA_E_INVALID, "key_splits %d needs a workspace", key_splits);
+    if (!aligned(workspace, 16)) return fail(RA_E_INVALID, "workspace must be 16-byte aligned");
     if (workspace_bytes < need)
       return fail(RA_E_INVALID, "workspace of %lld bytes is smaller than the %lld required",
                   (long long)workspace_bytes, (long long)need);

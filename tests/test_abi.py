@@ -216,3 +216,31 @@ def test_bwd_split_validation_without_gpu():
     assert call(3, wsb=need - 1) == ra.RA_E_INVALID
     assert call(3, batch=0) == ra.RA_OK
     assert ra.bwd_split_workspace_bytes(1, 64, 2, 128, 1) == 0
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "out", "lse", "seg"])
+def test_misaligned_pointers_rejected(which):
+    """Every tensor is moved in 16-byte (ids and lse: 4-byte) units, so the
+    host rejects misaligned pointers before any device work."""
+    kw = {which: FAKE + 2}
+    if which == "seg":
+        kw["seg"] = FAKE + 2
+    st = fwd(**kw)
+    assert st == ra.RA_E_INVALID, ra.last_error()
+    assert "aligned" in ra.last_error()
+
+
+def test_misaligned_workspace_and_bwd_rejected():
+    lib = ra.load_library()
+    P = 0x1000
+    st = lib.ra_blockwise_attn_fwd_split(P, P, P, None, 1, 32, 32, 4, 1, ra.RA_PLACE_CONTIGUOUS,
+                                         1, 64, 2, 128, ra.RA_BF16, P, P, None, 4, P + 8,
+                                         1 << 40, None)
+    assert st == ra.RA_E_INVALID and "aligned" in ra.last_error()
+    for bad in range(7):   # out, lse, dout, dq, dk, dv, delta
+        ptrs = [P] * 7
+        ptrs[bad] += 2
+        st = lib.ra_blockwise_attn_bwd_split(P, P, P, None, 1, 32, 32, 4, 1,
+                                             ra.RA_PLACE_CONTIGUOUS, 1, 64, 2, 128, ra.RA_BF16,
+                                             *ptrs, 1, None, 0, None)
+        assert st == ra.RA_E_INVALID and "aligned" in ra.last_error(), bad
