@@ -14,7 +14,7 @@
 //   dq_i    = scale sum_j ds_ij k_j
 //   dk_j    = scale sum_i ds_ij q_i,   dv_j = sum_i p_ij dout_i
 //
-// Three launches:
+// Three launches (four with key splits, below):
 //   bwd_delta_kernel   delta (one pass over dout and out);
 //   bwd_dq_kernel      query-stationary, like the forward: a workgroup owns
 //                      256 query rows and walks the key tiles in ring order

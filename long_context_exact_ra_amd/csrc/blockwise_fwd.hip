@@ -22,6 +22,11 @@
 // of a wave are skipped, which is the chunk-pair skip of section
 // "3. 因果注意力掩码支持" at the kernel's own granularity.
 //
+// With key splits (shares whose query tiles alone leave compute units
+// idle), a query tile has several workgroups, each walking one run of the
+// tile's key walk and writing its partial max, numerator and denominator;
+// combine_splits_kernel folds them into out and lse with the same carry.
+//
 // MFMA operand layouts used (wave64, 32x32 output tiles):
 //   A[m][k]: lane l holds row m = l % 32, k-slots 8*(l/32) .. +7 (bf16 x16
 //            variant) or k = l / 32 (f32 x2 variant);

@@ -1,7 +1,7 @@
 // Device-side building blocks shared by the forward and backward kernels of
 // the blockwise ring-attention library (gfx950): work decomposition, the
-// ring walk, causal limits, buffer-to-LDS DMA and the per-tile visibility
-// tests.  Internal; not part of the C ABI.
+// ring walk (and its cut into key splits), causal limits, buffer-to-LDS DMA
+// and the per-tile visibility tests.  Internal; not part of the C ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -168,9 +168,10 @@ __device__ __forceinline__ void cursor_next(const FwdParams& p, Cursor& c, int64
 }
 
 // Key splits: the run [begin, end) of the workgroup's walk that its split
-// covers.  The walk's length is a sum over the ring blocks (contiguous
-// placement) or a count over its tiles (striped), paid only when the share
-// is split (small grids).  Without splits the run is the whole walk.
+// covers.  The walk's length is the sum of its blocks' tile counts (a loop
+// over the ring blocks, or a closed form under striped placement), paid only
+// when the share is split (small grids).  Without splits the run is the
+// whole walk.
 struct SplitRange {
   int begin, end;
 };
