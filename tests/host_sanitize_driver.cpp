@@ -1,0 +1,141 @@
+// Drives the host side of the C ABI (ra_host.cpp) without a GPU, for a
+// build with AddressSanitizer and UndefinedBehaviorSanitizer: the planner
+// at the shapes of every workload, argument validation, the key-split and
+// workspace helpers, and the forward / backward / feedforward entry points
+// up to the launch.  The launchers are stubs that record the parameters the
+// host derived, so that the grid sizes can be checked as well.  Fake device
+// pointers are never dereferenced.  Exit status 0 = every check passed.
+
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "ra_attn.h"
+#include "ra_internal.h"
+
+namespace ra {
+static FwdParams g_fwd;
+static BwdParams g_bwd;
+static int g_launches = 0;
+int launch_fwd(const FwdParams& p, Dtype, int, int64_t, void*, char*, int) {
+  g_fwd = p;
+  ++g_launches;
+  return 0;
+}
+int launch_bwd(const BwdParams& p, int, void*, char*, int) {
+  g_bwd = p;
+  ++g_launches;
+  return 0;
+}
+int launch_ffn(const FfnParams&, void*, char*, int) {
+  ++g_launches;
+  return 0;
+}
+}  // namespace ra
+
+static int g_fail = 0;
+#define CHECK(cond)                                                   \
+  do {                                                                \
+    if (!(cond)) {                                                    \
+      std::printf("FAILED %s:%d: %s (%s)\n", __FILE__, __LINE__, #cond, \
+                  ra_last_error());                                   \
+      ++g_fail;                                                       \
+    }                                                                 \
+  } while (0)
+
+struct Shape {
+  int64_t B, Lq, H, D;
+  int32_t N, r;
+  int64_t c, qc, kc;
+};
+
+int main() {
+  // A fake, 256-byte aligned device address.
+  char* const P = reinterpret_cast<char*>(static_cast<uintptr_t>(1) << 20);
+  // The workloads' shapes (tiny, small causal, 7B share, packed documents,
+  // 65B share) and a striped-like small one.
+  const Shape shapes[] = {{1, 64, 2, 64, 4, 0, 0, 32, 32},
+                          {1, 1024, 8, 128, 8, 7, 1, 512, 512},
+                          {1, 32768, 32, 128, 16, 15, 1, 2048, 2048},
+                          {4, 2048, 32, 128, 8, 3, 1, 512, 512},
+                          {1, 16384, 64, 128, 256, 128, 16384, 512, 512}};
+  for (const Shape& s : shapes) {
+    // Planner: exactly sized host buffers, so any overrun is caught.
+    std::vector<int32_t> order(s.N);
+    std::vector<uint8_t> run((size_t)s.N * (s.Lq / s.qc) * (s.Lq / s.kc));
+    int64_t n_run = -1;
+    for (int place = 0; place < 2; ++place) {
+      const int64_t c = place ? (s.c ? 1 : 0) : s.c;
+      CHECK(ra_blockwise_plan_placed(c, s.qc, s.kc, s.Lq, s.N, s.r, (ra_placement_t)place,
+                                     order.data(), run.data(), &n_run) == RA_OK);
+      CHECK(n_run >= 1 && n_run <= (int64_t)run.size());
+    }
+    // Forward through every entry point, unsplit and split.
+    const int64_t tiles = (s.Lq + 255) / 256;
+    for (int32_t splits : {1, 2, 8, 64}) {
+      const int64_t ws = ra_blockwise_attn_fwd_split_workspace_bytes(s.B, s.Lq, s.H, s.D, splits);
+      CHECK(ws == (splits > 1 ? (int64_t)splits * s.B * s.H * s.Lq * (s.D + 2) * 4 : 0));
+      ra::g_fwd = ra::FwdParams{};
+      CHECK(ra_blockwise_attn_fwd_split(P, P, P, nullptr, s.c, s.qc, s.kc, s.N, s.r,
+                                        RA_PLACE_CONTIGUOUS, s.B, s.Lq, s.H, s.D, RA_BF16, P,
+                                        reinterpret_cast<float*>(P), nullptr, splits,
+                                        splits > 1 ? P : nullptr, ws, nullptr) == RA_OK);
+      CHECK(ra::g_fwd.n_wg == s.B * s.H * tiles * splits);
+      CHECK(ra::g_fwd.key_splits == splits);
+      CHECK((ra::g_fwd.part_o != nullptr) == (splits > 1));
+      if (splits > 1) {
+        CHECK(reinterpret_cast<char*>(ra::g_fwd.part_ml) ==
+              P + (int64_t)splits * s.B * s.H * s.Lq * s.D * 4);
+        // one byte short
+        CHECK(ra_blockwise_attn_fwd_split(P, P, P, nullptr, s.c, s.qc, s.kc, s.N, s.r,
+                                          RA_PLACE_CONTIGUOUS, s.B, s.Lq, s.H, s.D, RA_BF16, P,
+                                          reinterpret_cast<float*>(P), nullptr, splits, P, ws - 1,
+                                          nullptr) == RA_E_INVALID);
+      }
+      const int64_t bws = ra_blockwise_attn_bwd_split_workspace_bytes(s.B, s.Lq, s.H, s.D, splits);
+      float* const F = reinterpret_cast<float*>(P);
+      CHECK(ra_blockwise_attn_bwd_split(P, P, P, nullptr, s.c, s.qc, s.kc, s.N, s.r,
+                                        RA_PLACE_CONTIGUOUS, s.B, s.Lq, s.H, s.D, RA_BF16, P, F,
+                                        P, F, F, F, F, splits, splits > 1 ? P : nullptr, bws,
+                                        nullptr) == RA_OK);
+      CHECK(ra::g_bwd.f.n_wg == s.B * s.H * tiles * splits);
+      CHECK(ra::g_bwd.n_wg_kv == s.B * s.H * ((s.N * s.Lq + 255) / 256));
+      CHECK((ra::g_bwd.dq_part != nullptr) == (splits > 1));
+    }
+    CHECK(ra_blockwise_attn_fwd(P, P, P, nullptr, s.c, s.qc, s.kc, s.N, s.r, s.B, s.Lq, s.H,
+                                s.D, RA_BF16, P, reinterpret_cast<float*>(P), nullptr) == RA_OK);
+    for (int32_t r : {0, s.N - 1})
+      for (int place = 0; place < 2; ++place) {
+        const int32_t k = ra_blockwise_attn_fwd_key_splits(s.B, s.Lq, s.H, RA_BF16, s.c, s.N, r,
+                                                           (ra_placement_t)place, 256);
+        CHECK(k >= 1 && k <= 64);
+      }
+  }
+  // Validation: each case fails on the host before any launch.
+  const int before = ra::g_launches;
+  float* const F = reinterpret_cast<float*>(P);
+  CHECK(ra_blockwise_attn_fwd(P, P, P, nullptr, 1, 32, 32, 0, 0, 1, 64, 1, 128, RA_BF16, P, F,
+                              nullptr) == RA_E_INVALID);                       // N = 0
+  CHECK(ra_blockwise_attn_fwd(P, P, P, nullptr, 1, 48, 32, 4, 0, 1, 96, 1, 128, RA_BF16, P, F,
+                              nullptr) == RA_E_UNSUPPORTED);                   // chunk % 32
+  CHECK(ra_blockwise_attn_fwd(P, P, P, nullptr, 1, 32, 32, 4, 0, 1, 64, 1, 96, RA_BF16, P, F,
+                              nullptr) == RA_E_UNSUPPORTED);                   // D = 96
+  CHECK(ra_blockwise_attn_fwd(P + 2, P, P, nullptr, 1, 32, 32, 4, 0, 1, 64, 1, 128, RA_BF16, P,
+                              F, nullptr) == RA_E_INVALID);                    // misaligned q
+  CHECK(ra_blockwise_attn_fwd_split(P, P, P, nullptr, 1, 32, 32, 4, 0, RA_PLACE_STRIPED, 1, 64, 1,
+                                    128, RA_BF16, P, F, nullptr, 0, nullptr, 0,
+                                    nullptr) == RA_E_INVALID);                 // 0 splits
+  CHECK(ra_blockwise_attn_bwd_split(P, P, P, nullptr, 1, 32, 32, 4, 0, RA_PLACE_CONTIGUOUS, 1, 64,
+                                    1, 128, RA_F32, P, F, P, F, F, F, F, 1, nullptr, 0,
+                                    nullptr) == RA_E_UNSUPPORTED);             // fp32 backward
+  CHECK(ra_blockwise_ffn(P, P, P, P, P, 1, 64, 64, 128, 48, RA_BF16, P, P, 1 << 20, nullptr) ==
+        RA_E_INVALID);                                                        // chunk 48 of 64
+  CHECK(std::strlen(ra_last_error()) > 0);
+  CHECK(ra::g_launches == before);
+  CHECK(ra_blockwise_ffn(P, P, P, P, P, 1, 64, 64, 128, 32, RA_BF16, P, P, 1 << 20, nullptr) ==
+        RA_OK);
+  CHECK(ra::g_launches == before + 1);
+  std::printf("%s: %d failure(s)\n", g_fail ? "FAILED" : "ok", g_fail);
+  return g_fail ? 1 : 0;
+}
