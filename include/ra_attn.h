@@ -222,7 +222,7 @@ int64_t ra_blockwise_attn_fwd_split_workspace_bytes(int64_t batch, int64_t seq_q
 /* A key split count for a share: 1 when the unsplit grid (batch * heads *
  * ceil(seq_q / rows per workgroup) workgroups, 256 rows for RA_BF16, 128
  * for RA_F32) already fills compute_units; otherwise as many splits as
- * keep one workgroup per compute unit, at most one per 8 key tiles of 64
+ * keep one workgroup per compute unit, at most one per 4 key tiles of 64
  * keys of the longest walk (contiguous: the keys up to the last query's
  * causal limit; striped or non-causal: the whole sequence), and at most
  * 64.  Host-only; invalid arguments give 1. */

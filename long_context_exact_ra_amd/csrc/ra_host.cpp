@@ -296,8 +296,10 @@ int32_t ra_blockwise_attn_fwd_key_splits(int64_t batch, int64_t seq_q, int64_t h
     keys = std::min<int64_t>((last_q / causal_block_size + 1) * causal_block_size, seq_k);
   }
   const int64_t tiles = (keys + 63) / 64;
-  // One workgroup per compute unit at most, and at least 8 tiles per split.
-  int64_t splits = std::min<int64_t>(compute_units / n_wg, tiles / 8);
+  // One workgroup per compute unit at most (a second round of workgroups
+  // costs more than it splits off), and at least 4 tiles per split (fewer
+  // did not pay in timings of the small causal share).
+  int64_t splits = std::min<int64_t>(compute_units / n_wg, tiles / 4);
   splits = std::max<int64_t>(1, std::min<int64_t>(splits, kMaxKeySplits));
   return (int32_t)splits;
 }

@@ -182,17 +182,20 @@ def test_split_validation_without_gpu():
 
 def test_key_split_recommendation():
     """Splits only when the grid leaves compute units idle, one workgroup per
-    compute unit at most and at least 8 key tiles per split."""
+    compute unit at most and at least 4 key tiles per split."""
     ks = lambda B, Lq, H, dt, c, N, r, cu=256, pl="contiguous": ra.fwd_key_splits(
         B, Lq, H, dt, c, N, r, cu, pl)
     # 7B share: 4096 workgroups of 256 rows already fill 256 compute units
     assert ks(1, 32768, 32, ra.RA_BF16, 1, 16, 15) == 1
     # small causal share: 32 workgroups; r = 7 walks 8192 keys = 128 tiles
     assert ks(1, 1024, 8, ra.RA_BF16, 1, 8, 7) == 8
-    # r = 0 walks 1024 keys = 16 tiles: at most 2 splits of 8 tiles
-    assert ks(1, 1024, 8, ra.RA_BF16, 1, 8, 0) == 2
+    # r = 0 walks 1024 keys = 16 tiles: at most 4 splits of 4 tiles
+    assert ks(1, 1024, 8, ra.RA_BF16, 1, 8, 0) == 4
+    assert ks(1, 1024, 8, ra.RA_BF16, 1, 8, 1) == 8
     # fp32 workgroups hold 128 rows; non-causal walks every key
     assert ks(1, 64, 2, ra.RA_F32, None, 4, 0) == 1     # 4 tiles: too short to split
+    assert ks(1, 32, 2, ra.RA_BF16, 1, 4, 3) == 1       # 128 visible keys = 2 tiles
+
     assert ks(1, 1024, 2, ra.RA_F32, None, 8, 3, cu=64) == 4
     assert ks(0, 1024, 8, ra.RA_BF16, 1, 8, 0) == 1
     assert ks(1, 1024, 8, ra.RA_BF16, 1, 8, 8) == 1     # invalid ring index
