@@ -75,6 +75,10 @@ struct Cursor {
   int klen;    // keys to visit in this block (multiple of 32)
   int valid;   // int, not bool: no padding bytes to copy around
   int pos;     // index of the current tile in the whole walk
+  // Striped placement: keys to visit in every block kb <= r and kb > r
+  // (the walk's limit is fixed, and a block's count depends only on which
+  // side of r it lies); set by cursor_seek.
+  int klen_lo, klen_hi;
 };
 
 // Key coordinates.  Causal tests compare a key coordinate with a limit
@@ -111,30 +115,35 @@ __device__ __forceinline__ int block_klen(const FwdParams& p, int kb, int64_t ke
 // of every block in ring order, then tile kt + 1 -- which keeps them in
 // step until each runs out of keys.  The softmax carry does not depend on
 // the order in which keys are folded in.
+// Striped walk: the first visited tile at or after (kt, t).  Blocks kb <= r
+// (ring steps t <= r) hold ceil(klen_lo / TN) tiles, blocks kb > r (steps
+// t > r) ceil(klen_hi / TN) <= that, so within round kt every step t <= r
+// is visited, a step t > r only while kt is below the smaller count, and the
+// walk ends with the larger count.
+template <int TN>
+__device__ __forceinline__ void striped_settle(const FwdParams& p, Cursor& c) {
+  const int n_lo = (c.klen_lo + TN - 1) / TN, n_hi = (c.klen_hi + TN - 1) / TN;
+  if (c.t >= p.ring_size || (c.t > p.ring_index && c.kt >= n_hi)) {
+    c.t = 0;
+    ++c.kt;
+  }
+  if (c.kt >= n_lo) {
+    c.valid = 0;
+    return;
+  }
+  c.kb = p.ring_index - c.t;
+  if (c.kb < 0) c.kb += p.ring_size;
+  c.klen = c.t <= p.ring_index ? c.klen_lo : c.klen_hi;
+  c.ntile = c.t <= p.ring_index ? n_lo : n_hi;
+  c.valid = 1;
+}
+
 template <int TN, bool STRIPED = false>
 __device__ __forceinline__ void cursor_seek(const FwdParams& p, Cursor& c, int64_t kend) {
   if (STRIPED) {
-    // Block r (t = 0) has the most keys to visit: if it has no tile kt,
-    // no block has.
-    const int last = block_klen<true>(p, p.ring_index, kend);
-#pragma clang loop vectorize(disable) unroll(disable)
-    while (c.kt * TN < last) {
-#pragma clang loop vectorize(disable) unroll(disable)
-      while (c.t < p.ring_size) {
-        c.kb = p.ring_index - c.t;
-        if (c.kb < 0) c.kb += p.ring_size;
-        c.klen = block_klen<true>(p, c.kb, kend);
-        c.ntile = (c.klen + TN - 1) / TN;
-        if (c.kt < c.ntile) {
-          c.valid = 1;
-          return;
-        }
-        ++c.t;
-      }
-      c.t = 0;
-      ++c.kt;
-    }
-    c.valid = 0;
+    c.klen_lo = block_klen<true>(p, p.ring_index, kend);
+    c.klen_hi = p.ring_index + 1 < p.ring_size ? block_klen<true>(p, p.ring_index + 1, kend) : 0;
+    striped_settle<TN>(p, c);
     return;
   }
 #pragma clang loop vectorize(disable) unroll(disable)
@@ -158,7 +167,7 @@ __device__ __forceinline__ void cursor_next(const FwdParams& p, Cursor& c, int64
   ++c.pos;
   if (STRIPED) {
     ++c.t;
-    cursor_seek<TN, true>(p, c, kend);
+    striped_settle<TN>(p, c);
     return;
   }
   if (++c.kt < c.ntile) return;
@@ -227,7 +236,7 @@ __device__ __forceinline__ void cursor_to(const FwdParams& p, Cursor& c, int64_t
     return;
   }
   if (!c.valid || pos <= c.pos) return;
-  const StripedCounts sc = striped_counts<TN>(p, kend);
+  const StripedCounts sc{(c.klen_lo + TN - 1) / TN, (c.klen_hi + TN - 1) / TN};
   const int n_lo = p.ring_index + 1, n_hi = p.ring_size - 1 - p.ring_index;
   const int full = min(sc.lo, sc.hi);
   const int64_t in_full = (int64_t)full * p.ring_size;
@@ -250,11 +259,8 @@ __device__ __forceinline__ void cursor_to(const FwdParams& p, Cursor& c, int64_t
   }
   c.kt = kt;
   c.t = t;
-  c.kb = p.ring_index - t;
-  if (c.kb < 0) c.kb += p.ring_size;
-  c.klen = block_klen<true>(p, c.kb, kend);
-  c.ntile = (c.klen + TN - 1) / TN;
   c.pos = pos;
+  striped_settle<TN>(p, c);
 }
 
 // A wave-uniform 64-bit value that the compiler computed in vector registers
