@@ -61,3 +61,15 @@ def test_segment_counts_never_exceed_causal():
         causal = bench.visible_keys_per_row(w.seq_q, w.ring_size, r, 1)
         within = bench.segment_visible_keys_per_row(seg, w.seq_q, r)
         assert (within <= causal).all() and (within >= 1).all()
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """One GPU only: --gpus N > 1 exits with a message before touching a GPU."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
