@@ -144,3 +144,45 @@ def test_split_rejects_bad_workspace():
     with pytest.raises(ra.RaError) as e:
         ra.blockwise_attn_fwd(q, k, v, None, 1, 512, 512, 8, 1, key_splits=65)
     assert e.value.status == ra.RA_E_INVALID
+
+
+def test_split_packed_documents_sampled():
+    """Packed documents (segment ids, 1024 query tiles) with the walk forced
+    into 3 runs: every row of one head and sampled rows of another against
+    the oracle, and the chunk map."""
+    from parity import oracle_sample, sample_rows, visible_kv_len
+    w = workloads.get("packed_documents")
+    seg = workloads.make_segments(w, device=DEV)
+    r = 5
+    q, k, v = workloads.make_qkv(w, r, device=DEV)
+    out, lse = run_split(q, k, v, seg, w, r, 3)
+    kv_len = visible_kv_len(w, r)
+    for head, nrows in ((0, w.seq_q), (21, 192)):
+        rows = np.arange(w.seq_q) if nrows == w.seq_q else sample_rows(w, 700, nrows)
+        log(f"packed_documents split=3 r={r} head={head} rows={len(rows)}")
+        ref, ref_lse = oracle_sample(q, k, v, seg, 1, w.ring_size, r, head, rows, kv_len)
+        check(to_np(out[:, rows, head]), to_np(lse[:, head, rows]), ref, ref_lse,
+              torch.bfloat16, f"packed split h={head}")
+
+
+@pytest.mark.timeout(600)
+def test_split_share_7b_sampled():
+    """The 7B-shaped share (16 blocks of 32768 keys) with each query tile's
+    walk cut into 2 runs, so that the second run seeks into the middle of
+    the ring walk: sampled rows of two heads against the oracle."""
+    from parity import oracle_sample, sample_rows
+    w = workloads.get("share_7b_512k")
+    r = w.ring_indices[0]
+    q, k, v = workloads.make_qkv(w, r, device=DEV)
+    log("share_7b_512k split=2: inputs ready")
+    out, lse = ra.blockwise_attn_fwd(q, k, v, None, 1, w.q_chunk, w.k_chunk, w.ring_size, r,
+                                     key_splits=2)
+    torch.cuda.synchronize()
+    log("share_7b_512k split=2: forward done")
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    for head in (3, 30):
+        rows = sample_rows(w, 800 + head, 24)
+        log(f"share_7b_512k split=2 head={head} rows={len(rows)}")
+        ref, ref_lse = oracle_sample(q, k, v, None, 1, w.ring_size, r, head, rows)
+        check(to_np(out[:, rows, head]), to_np(lse[:, head, rows]), ref, ref_lse,
+              torch.bfloat16, f"7b split h={head}")
