@@ -178,9 +178,13 @@ ra_status_t ra_blockwise_attn_fwd_placed(const void* q, const void* k,
  * keys alone.  Because the softmax carry folds key blocks in any order and
  * grouping with the same result (review of "Ring Attention with Blockwise
  * Transformers for Near-Infinite Context", section 三 "排列不变性", and the
- * carry of "2. 数值稳定的注意力计算"), the walk can be cut: split s folds
- * the s-th of key_splits equal runs of the tile's walk (ring order, skips
- * and masks unchanged) into its own max, numerator and denominator, and a
+ * carry of "2. 数值稳定的注意力计算"), the walk can be cut: the longest
+ * walk of the share (its last query tile's) into key_splits runs, a query
+ * tile whose walk has n of the longest walk's n_max tiles into
+ * ceil(key_splits n / n_max) runs, so that runs are about equally long.
+ * Split s of a tile folds the s-th of its equal runs (ring order, skips and
+ * masks unchanged) into its own max, numerator and denominator (the
+ * workgroups of a tile's surplus splits only mark their slot empty), and a
  * second kernel folds the splits into out and lse with the same carry.
  *
  *   key_splits: 1 .. 64; 1 is exactly ra_blockwise_attn_fwd_placed (the
@@ -222,10 +226,10 @@ int64_t ra_blockwise_attn_fwd_split_workspace_bytes(int64_t batch, int64_t seq_q
 /* A key split count for a share: 1 when the unsplit grid (batch * heads *
  * ceil(seq_q / rows per workgroup) workgroups, 256 rows for RA_BF16, 128
  * for RA_F32) already fills compute_units; otherwise as many splits as
- * keep one workgroup per compute unit, at most one per 4 key tiles of 64
- * keys of the longest walk (contiguous: the keys up to the last query's
- * causal limit; striped or non-causal: the whole sequence), and at most
- * 64.  Host-only; invalid arguments give 1. */
+ * keep the split grid at one workgroup per compute unit, at most one per 4
+ * key tiles of 64 keys of the longest walk (the share's last query tile's:
+ * its blocks' keys up to its causal limit), and at most 64.  Host-only;
+ * invalid arguments give 1. */
 int32_t ra_blockwise_attn_fwd_key_splits(int64_t batch, int64_t seq_q, int64_t heads,
                                          ra_dtype_t dtype, int64_t causal_block_size,
                                          int32_t ring_size, int32_t ring_index,

@@ -252,8 +252,24 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dq_kernel(const BwdParams 
   const int64_t pq_first = (int64_t)p.ring_index * p.seq_q + w.qg0;
   const WaveLimits lim = wave_limits(p, STRIPED ? w.qg0 : pq_first, w.lrow, w.active);
   w.kend = wg_kend<kBlockMBf16, STRIPED>(p, m0);
-  // With key splits this workgroup walks only its run of the key tiles.
-  const SplitRange sr = split_range<64, STRIPED>(p, wc.split, w.kend);
+  // With key splits this workgroup walks only its run of the key tiles; a
+  // surplus split of a short walk adds nothing to dq.
+  const SplitRange sr = split_range<64, STRIPED>(
+      p, wc.split, w.kend, wg_kend<kBlockMBf16, STRIPED>(p, (p.n_qtiles - 1) * kBlockMBf16));
+  if (sr.idle) {
+    if (w.active) {
+      float* drow = bp.dq_part + (int64_t)wc.split * p.batch * p.seq_q * p.heads * D +
+                    ((int64_t)b * p.seq_q + w.qg0 + w.lrow) * ((int64_t)p.heads * D) +
+                    (int64_t)h * D;
+#pragma unroll
+      for (int j = 0; j < NDB; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(drow + 32 * j + 8 * g + 4 * w.half) =
+              make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    return;
+  }
   w.seg_q = 0;
   if (SEG && w.active) w.seg_q = p.seg[(int64_t)b * p.seq_k + pq_first + w.lrow];
   w.qseg = SegRange{0, 0};

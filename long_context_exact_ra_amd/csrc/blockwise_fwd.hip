@@ -86,10 +86,19 @@ __device__ __forceinline__ void write_partial(const FwdParams& p, int split, int
   if (half == 0) *reinterpret_cast<float2*>(p.part_ml + 2 * pr) = make_float2(m_run, l_tot);
 }
 
+// The partial of a split that has no run (an idle workgroup): denominator 0,
+// so the combine skips the slot and never reads its numerator.
+__device__ __forceinline__ void write_empty_partial(const FwdParams& p, int split, int b, int h,
+                                                    int row) {
+  *reinterpret_cast<float2*>(p.part_ml + 2 * part_row(p, split, b, h, row)) =
+      make_float2(ninf(), 0.f);
+}
+
 // One thread per (row, 4 columns); rows in [b][h][i] order, as lse.  The
 // splits are folded eight at a time with a running max, so that the loads
 // of eight splits are in flight together; a split without a visible key
-// (denominator 0) gets weight 0.
+// (denominator 0) gets weight 0, and its numerator (unwritten if the split
+// was idle) is not used.
 template <typename T>
 __global__ void combine_splits_kernel(const FwdParams p, int head_dim) {
   const int groups = head_dim / 4;
@@ -126,7 +135,8 @@ __global__ void combine_splits_kernel(const FwdParams p, int head_dim) {
     num.w *= sc;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const float w = ml[u].y > 0.f ? __builtin_amdgcn_exp2f(ml[u].x - cm) : 0.f;
+      if (!(ml[u].y > 0.f)) continue;
+      const float w = __builtin_amdgcn_exp2f(ml[u].x - cm);
       den += w * ml[u].y;
       num.x += w * o[u].x;
       num.y += w * o[u].y;
@@ -536,7 +546,13 @@ __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const
   const int64_t pq_first = (int64_t)p.ring_index * p.seq_q + k.qg0;
   const WaveLimits lim = wave_limits(p, STRIPED ? k.qg0 : pq_first, k.lrow, k.wave_active);
   k.kend = wg_kend<kBlockMBf16, STRIPED>(p, m0);
-  const SplitRange sr = split_range<C::TN, STRIPED>(p, wc.split, k.kend);
+  const SplitRange sr = split_range<C::TN, STRIPED>(
+      p, wc.split, k.kend, wg_kend<kBlockMBf16, STRIPED>(p, (p.n_qtiles - 1) * kBlockMBf16));
+  if (sr.idle) {
+    // A surplus split of a short walk: its partial holds no key.
+    if (k.wave_active && k.half == 0) write_empty_partial(p, wc.split, b, h, k.qg0 + k.lrow);
+    return;
+  }
   k.pos_end = sr.end;
   k.seg_q = 0;
   if (SEG && k.wave_active) k.seg_q = p.seg[(int64_t)b * p.seq_k + pq_first + k.lrow];
@@ -742,7 +758,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(const FwdParams p)
     if (has_seg && tid < TN) seg_lds[buf][tid] = sreg;
   };
 
-  const SplitRange sr = split_range<TN, STRIPED>(p, wc.split, kend);
+  const SplitRange sr = split_range<TN, STRIPED>(
+      p, wc.split, kend, wg_kend<kBlockMF32, STRIPED>(p, (p.n_qtiles - 1) * kBlockMF32));
+  if (sr.idle) {
+    if (wave_active && half == 0) write_empty_partial(p, wc.split, b, h, qg0 + lrow);
+    return;
+  }
   Cursor cur{0, 0, 0, 0, 0, 0, 0};
   cursor_seek<TN, STRIPED>(p, cur, kend);
   cursor_to<TN, STRIPED>(p, cur, kend, sr.begin);

@@ -177,12 +177,17 @@ __device__ __forceinline__ void cursor_next(const FwdParams& p, Cursor& c, int64
 }
 
 // Key splits: the run [begin, end) of the workgroup's walk that its split
-// covers.  The walk's length is the sum of its blocks' tile counts (a loop
-// over the ring blocks, or a closed form under striped placement), paid only
-// when the share is split (small grids).  Without splits the run is the
-// whole walk.
+// covers.  key_splits is the number of runs of the longest walk (the last
+// query tile's: causal limits only grow with the row); a query tile whose
+// walk is shorter is cut into proportionally fewer runs, ceil(key_splits n
+// / n_max), so that every run has about the same number of tiles, and the
+// workgroups of its surplus splits are idle.  A walk's length is the sum of
+// its blocks' tile counts (a loop over the ring blocks, or a closed form
+// under striped placement), paid only when the share is split (small
+// grids).  Without splits the run is the whole walk.
 struct SplitRange {
   int begin, end;
+  int idle;  // this split has no run: the workgroup writes an empty partial
 };
 
 // Striped placement: a block's tile count depends only on whether kb > r
@@ -200,18 +205,28 @@ __device__ __forceinline__ StripedCounts striped_counts(const FwdParams& p, int6
 }
 
 template <int TN, bool STRIPED>
-__device__ __forceinline__ SplitRange split_range(const FwdParams& p, int split, int64_t kend) {
-  if (p.key_splits <= 1) return SplitRange{0, INT_MAX};
-  int64_t n = 0;
-  if (!STRIPED) {
-    // Block by block: every block contributes its whole tile count.
-#pragma clang loop vectorize(disable) unroll(disable)
-    for (int kb = 0; kb < p.ring_size; ++kb) n += (block_klen<false>(p, kb, kend) + TN - 1) / TN;
-  } else {
+__device__ __forceinline__ int64_t walk_tiles(const FwdParams& p, int64_t kend) {
+  if (STRIPED) {
     const StripedCounts sc = striped_counts<TN>(p, kend);
-    n = (int64_t)(p.ring_index + 1) * sc.lo + (int64_t)(p.ring_size - 1 - p.ring_index) * sc.hi;
+    return (int64_t)(p.ring_index + 1) * sc.lo + (int64_t)(p.ring_size - 1 - p.ring_index) * sc.hi;
   }
-  return SplitRange{(int)(n * split / p.key_splits), (int)(n * (split + 1) / p.key_splits)};
+  int64_t n = 0;
+#pragma clang loop vectorize(disable) unroll(disable)
+  for (int kb = 0; kb < p.ring_size; ++kb) n += (block_klen<false>(p, kb, kend) + TN - 1) / TN;
+  return n;
+}
+
+// kend_max: the walk limit of the share's last query tile.
+template <int TN, bool STRIPED>
+__device__ __forceinline__ SplitRange split_range(const FwdParams& p, int split, int64_t kend,
+                                                  int64_t kend_max) {
+  if (p.key_splits <= 1) return SplitRange{0, INT_MAX, 0};
+  const int64_t n = walk_tiles<TN, STRIPED>(p, kend);
+  const int64_t n_max = walk_tiles<TN, STRIPED>(p, kend_max);
+  int64_t runs = n_max > 0 ? ((int64_t)p.key_splits * n + n_max - 1) / n_max : 1;
+  runs = runs < 1 ? 1 : (runs > p.key_splits ? p.key_splits : runs);
+  if (split >= runs) return SplitRange{0, 0, 1};
+  return SplitRange{(int)(n * split / runs), (int)(n * (split + 1) / runs), 0};
 }
 
 // Move a freshly sought cursor to walk position `pos` (the first tile of

@@ -284,22 +284,38 @@ int32_t ra_blockwise_attn_fwd_key_splits(int64_t batch, int64_t seq_q, int64_t h
       (placement != RA_PLACE_CONTIGUOUS && placement != RA_PLACE_STRIPED))
     return 1;
   const int64_t bm = ra::block_rows(dtype == RA_BF16 ? ra::Dtype::BF16 : ra::Dtype::F32);
-  const int64_t n_wg = batch * heads * ((seq_q + bm - 1) / bm);
+  const int64_t n_qtiles = (seq_q + bm - 1) / bm;
+  const int64_t n_wg = batch * heads * n_qtiles;
   if (n_wg >= compute_units) return 1;
-  // Key tiles of the longest walk: every key up to the last query's causal
-  // limit under contiguous placement.  Under striped placement the last
-  // query row sees all but at most N - 1 keys of the sequence.
+  // Tiles of 64 keys in the walk of the query tile at local row m0, as the
+  // kernels walk it: every key of every block up to the tile's causal limit.
   const int64_t seq_k = seq_q * ring_size;
-  int64_t keys = seq_k;
-  if (causal_block_size > 0 && placement == RA_PLACE_CONTIGUOUS) {
-    const int64_t last_q = (int64_t)ring_index * seq_q + seq_q - 1;
-    keys = std::min<int64_t>((last_q / causal_block_size + 1) * causal_block_size, seq_k);
-  }
-  const int64_t tiles = (keys + 63) / 64;
-  // One workgroup per compute unit at most (a second round of workgroups
-  // costs more than it splits off), and at least 4 tiles per split (fewer
-  // did not pay in timings of the small causal share).
-  int64_t splits = std::min<int64_t>(compute_units / n_wg, tiles / 4);
+  const bool striped = placement == RA_PLACE_STRIPED;
+  const int64_t c = causal_block_size >= seq_k ? 0 : causal_block_size;
+  auto walk = [&](int64_t m0) -> int64_t {
+    int64_t kend = INT64_MAX;
+    if (c > 0) {
+      const int64_t q_last = (striped ? 0 : (int64_t)ring_index * seq_q) +
+                             std::min(m0 + bm, seq_q) - 1;
+      kend = (q_last / c + 1) * c;
+    }
+    int64_t n = 0;
+    for (int32_t kb = 0; kb < ring_size; ++kb) {
+      const int64_t vbase = striped ? (kb > ring_index ? 1 : 0) : (int64_t)kb * seq_q;
+      const int64_t len = kend == INT64_MAX ? seq_q : kend - vbase;
+      int64_t klen = len <= 0 ? 0 : (len >= seq_q ? seq_q : std::min<int64_t>((len + 31) & ~(int64_t)31, seq_q));
+      n += (klen + 63) / 64;
+    }
+    return n;
+  };
+  const int64_t n_max = walk((n_qtiles - 1) * bm);
+  // The kernels cut the longest walk into P runs (shorter walks into
+  // proportionally fewer, the surplus workgroups idle).  The grid, idle
+  // workgroups included, must fit one workgroup per compute unit: a second
+  // dispatch round costs more than shorter runs save (timings of the small
+  // striped share).  At least 4 tiles per run of the longest walk (fewer did
+  // not pay in timings of the small causal share).
+  int64_t splits = std::min<int64_t>(compute_units / n_wg, n_max / 4);
   splits = std::max<int64_t>(1, std::min<int64_t>(splits, kMaxKeySplits));
   return (int32_t)splits;
 }

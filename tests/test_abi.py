@@ -181,8 +181,9 @@ def test_split_validation_without_gpu():
 
 
 def test_key_split_recommendation():
-    """Splits only when the grid leaves compute units idle, one workgroup per
-    compute unit at most and at least 4 key tiles per split."""
+    """Splits only when the grid leaves compute units idle, the split grid at
+    one workgroup per compute unit at most and at least 4 key tiles per run
+    of the longest walk."""
     ks = lambda B, Lq, H, dt, c, N, r, cu=256, pl="contiguous": ra.fwd_key_splits(
         B, Lq, H, dt, c, N, r, cu, pl)
     # 7B share: 4096 workgroups of 256 rows already fill 256 compute units
@@ -199,8 +200,8 @@ def test_key_split_recommendation():
     assert ks(1, 1024, 2, ra.RA_F32, None, 8, 3, cu=64) == 4
     assert ks(0, 1024, 8, ra.RA_BF16, 1, 8, 0) == 1
     assert ks(1, 1024, 8, ra.RA_BF16, 1, 8, 8) == 1     # invalid ring index
-    # striped: every ring position's last query row sees about the whole
-    # sequence (8192 keys = 128 tiles), so r = 0 splits as much as r = 7
+    # striped: every ring position's longest walk touches every block (128
+    # tiles), so r = 0 splits as much as r = 7: 8, one workgroup per CU
     assert ks(1, 1024, 8, ra.RA_BF16, 1, 8, 0, pl="striped") == 8
     assert ks(1, 1024, 8, ra.RA_BF16, 1, 8, 7, pl="striped") == 8
 
