@@ -183,9 +183,10 @@ ra_status_t ra_blockwise_attn_fwd_placed(const void* q, const void* k,
  * tile whose walk has n of the longest walk's n_max tiles into
  * ceil(key_splits n / n_max) runs, so that runs are about equally long.
  * Split s of a tile folds the s-th of its equal runs (ring order, skips and
- * masks unchanged) into its own max, numerator and denominator (the
- * workgroups of a tile's surplus splits only mark their slot empty), and a
- * second kernel folds the splits into out and lse with the same carry.
+ * masks unchanged) into its own max, numerator and denominator, one
+ * workgroup per run (the grid holds exactly the runs; the slots of a tile's
+ * surplus splits are marked empty), and a second kernel folds the splits
+ * into out and lse with the same carry.
  *
  *   key_splits: 1 .. 64; 1 is exactly ra_blockwise_attn_fwd_placed (the
  *       workspace may then be NULL).
@@ -225,8 +226,9 @@ int64_t ra_blockwise_attn_fwd_split_workspace_bytes(int64_t batch, int64_t seq_q
 
 /* A key split count for a share: 1 when the unsplit grid (batch * heads *
  * ceil(seq_q / rows per workgroup) workgroups, 256 rows for RA_BF16, 128
- * for RA_F32) already fills compute_units; otherwise as many splits as
- * keep the split grid at one workgroup per compute unit, at most one per 4
+ * for RA_F32) already fills compute_units; otherwise the most splits whose
+ * runs (one workgroup each, over every query tile and head of the batch)
+ * fit one workgroup per compute unit, at most one per 4
  * key tiles of 64 keys of the longest walk (the share's last query tile's:
  * its blocks' keys up to its causal limit), and at most 64.  Host-only;
  * invalid arguments give 1. */

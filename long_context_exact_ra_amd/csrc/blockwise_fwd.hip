@@ -537,7 +537,9 @@ __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const
   k.lrow = k.lane & 31;
   k.half = k.lane >> 5;
 
-  const WgCoord wc = wg_coord<kBlockMBf16>(p);
+  const WgCoord wc = p.split_wgs > 0 ? wg_coord_runs<kBlockMBf16, C::TN, STRIPED>(p)
+                                     : wg_coord<kBlockMBf16>(p);
+  if (wc.split < 0) return;
   const int b = wc.b, h = wc.h, m0 = wc.m0;
   k.qg0 = m0 + k.wave * 32;
   k.wave_active = k.qg0 < p.seq_q;
@@ -659,6 +661,9 @@ __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const
   const int row = k.qg0 + k.lrow;
   if (p.part_o != nullptr) {
     write_partial<NDB>(p, wc.split, b, h, row, k.half, st.w.acc, st.w.m_run, l_tot);
+    // With an exact grid no workgroup holds the slots past this tile's runs.
+    if (p.split_wgs > 0 && wc.split == sr.runs - 1 && k.half == 0)
+      for (int u = sr.runs; u < p.key_splits; ++u) write_empty_partial(p, u, b, h, row);
     return;
   }
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -705,7 +710,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(const FwdParams p)
   const int lrow = lane & 31;
   const int half = lane >> 5;
 
-  const WgCoord wc = wg_coord<kBlockMF32>(p);
+  const WgCoord wc =
+      p.split_wgs > 0 ? wg_coord_runs<kBlockMF32, 32, STRIPED>(p) : wg_coord<kBlockMF32>(p);
+  if (wc.split < 0) return;
   const int b = wc.b, h = wc.h, m0 = wc.m0;
   const int qg0 = m0 + wave * 32;
   const bool wave_active = qg0 < p.seq_q;
@@ -846,6 +853,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(const FwdParams p)
   const int row = qg0 + lrow;
   if (p.part_o != nullptr) {
     write_partial<NDB>(p, wc.split, b, h, row, half, acc, m_run, l_tot);
+    if (p.split_wgs > 0 && wc.split == sr.runs - 1 && half == 0)
+      for (int u = sr.runs; u < p.key_splits; ++u) write_empty_partial(p, u, b, h, row);
     return;
   }
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;

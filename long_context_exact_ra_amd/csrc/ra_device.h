@@ -180,14 +180,17 @@ __device__ __forceinline__ void cursor_next(const FwdParams& p, Cursor& c, int64
 // covers.  key_splits is the number of runs of the longest walk (the last
 // query tile's: causal limits only grow with the row); a query tile whose
 // walk is shorter is cut into proportionally fewer runs, ceil(key_splits n
-// / n_max), so that every run has about the same number of tiles, and the
-// workgroups of its surplus splits are idle.  A walk's length is the sum of
+// / n_max), so that every run has about the same number of tiles; its
+// surplus splits are idle (with the exact grid of wg_coord_runs no
+// workgroup holds one, and the tile's last run marks their slots empty;
+// the backward's uniform grid keeps idle workgroups).  A walk's length is the sum of
 // its blocks' tile counts (a loop over the ring blocks, or a closed form
 // under striped placement), paid only when the share is split (small
 // grids).  Without splits the run is the whole walk.
 struct SplitRange {
   int begin, end;
   int idle;  // this split has no run: the workgroup writes an empty partial
+  int runs;  // runs of this query tile's walk
 };
 
 // Striped placement: a block's tile count depends only on whether kb > r
@@ -210,23 +213,30 @@ __device__ __forceinline__ int64_t walk_tiles(const FwdParams& p, int64_t kend) 
     const StripedCounts sc = striped_counts<TN>(p, kend);
     return (int64_t)(p.ring_index + 1) * sc.lo + (int64_t)(p.ring_size - 1 - p.ring_index) * sc.hi;
   }
-  int64_t n = 0;
-#pragma clang loop vectorize(disable) unroll(disable)
-  for (int kb = 0; kb < p.ring_size; ++kb) n += (block_klen<false>(p, kb, kend) + TN - 1) / TN;
-  return n;
+  // Contiguous: block kb starts at key kb * Lq, so the blocks before
+  // kend / Lq are whole, the next one is cut at kend and the rest are empty.
+  const int full_tiles = (p.seq_q + TN - 1) / TN;
+  if (kend >= (int64_t)p.ring_size * p.seq_q) return (int64_t)p.ring_size * full_tiles;
+  const int nfull = (int)kend / p.seq_q;  // kend < N Lq, which fits int32
+  return (int64_t)nfull * full_tiles + (block_klen<false>(p, nfull, kend) + TN - 1) / TN;
+}
+
+// Runs of a walk of n tiles when the longest walk (n_max tiles) takes
+// key_splits of them.  The host computes the same count for the grid.
+__device__ __forceinline__ int split_runs(const FwdParams& p, int64_t n, int64_t n_max) {
+  int64_t runs = n_max > 0 ? ((int64_t)p.key_splits * n + n_max - 1) / n_max : 1;
+  return (int)(runs < 1 ? 1 : (runs > p.key_splits ? p.key_splits : runs));
 }
 
 // kend_max: the walk limit of the share's last query tile.
 template <int TN, bool STRIPED>
 __device__ __forceinline__ SplitRange split_range(const FwdParams& p, int split, int64_t kend,
                                                   int64_t kend_max) {
-  if (p.key_splits <= 1) return SplitRange{0, INT_MAX, 0};
+  if (p.key_splits <= 1) return SplitRange{0, INT_MAX, 0, 1};
   const int64_t n = walk_tiles<TN, STRIPED>(p, kend);
-  const int64_t n_max = walk_tiles<TN, STRIPED>(p, kend_max);
-  int64_t runs = n_max > 0 ? ((int64_t)p.key_splits * n + n_max - 1) / n_max : 1;
-  runs = runs < 1 ? 1 : (runs > p.key_splits ? p.key_splits : runs);
-  if (split >= runs) return SplitRange{0, 0, 1};
-  return SplitRange{(int)(n * split / runs), (int)(n * (split + 1) / runs), 0};
+  const int runs = split_runs(p, n, walk_tiles<TN, STRIPED>(p, kend_max));
+  if (split >= runs) return SplitRange{0, 0, 1, runs};
+  return SplitRange{(int)(n * split / runs), (int)(n * (split + 1) / runs), 0, runs};
 }
 
 // Move a freshly sought cursor to walk position `pos` (the first tile of
@@ -326,6 +336,38 @@ __device__ __forceinline__ int64_t wg_kend(const FwdParams& p, int m0) {
   const int64_t q_last =
       (STRIPED ? 0 : (int64_t)p.ring_index * p.seq_q) + std::min(m0 + BM, p.seq_q) - 1;
   return uniform64((q_last / p.causal + 1) * p.causal);
+}
+
+// Forward with key splits: the grid holds split_wgs workgroups per (batch,
+// head), one per run of each query tile's walk (split_runs of it, heavier
+// tiles first), so that no workgroup is idle.  The host counts the same
+// runs with the same walk lengths.  A workgroup beyond the runs (which a
+// count mismatch would cause) gets split -1 and must exit without writing.
+template <int BM, int TN, bool STRIPED>
+__device__ __forceinline__ WgCoord wg_coord_runs(const FwdParams& p) {
+  const int pid = blockIdx.x, n = p.n_wg;
+  const int xcd = pid & 7, idx = pid >> 3, cnt = n >> 3, rem = n & 7;
+  const int logical =
+      xcd < rem ? xcd * (cnt + 1) + idx : rem * (cnt + 1) + (xcd - rem) * cnt + idx;
+  const int bh = __builtin_amdgcn_readfirstlane(logical / p.split_wgs);
+  const int in_bh = __builtin_amdgcn_readfirstlane(logical % p.split_wgs);
+  const int64_t n_max =
+      walk_tiles<TN, STRIPED>(p, wg_kend<BM, STRIPED>(p, (p.n_qtiles - 1) * BM));
+  int qt = -1, split = -1, first = 0;
+#pragma clang loop vectorize(disable) unroll(disable)
+  for (int t = p.n_qtiles - 1; t >= 0; --t) {
+    const int runs = split_runs(p, walk_tiles<TN, STRIPED>(p, wg_kend<BM, STRIPED>(p, t * BM)), n_max);
+    if (in_bh < first + runs) {
+      qt = t;
+      split = in_bh - first;
+      break;
+    }
+    first += runs;
+  }
+  return WgCoord{__builtin_amdgcn_readfirstlane(bh / p.heads),
+                 __builtin_amdgcn_readfirstlane(bh % p.heads),
+                 __builtin_amdgcn_readfirstlane(qt < 0 ? 0 : qt * BM),
+                 __builtin_amdgcn_readfirstlane(split)};
 }
 
 __device__ __forceinline__ void write_run_map(const FwdParams& p, int t, int qg0, int key0) {

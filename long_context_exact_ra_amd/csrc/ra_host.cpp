@@ -202,6 +202,49 @@ ra_status_t prepare(const void* q, const void* k, const void* v, const int32_t* 
 // Largest number of key splits a call accepts.
 constexpr int32_t kMaxKeySplits = 64;
 
+// Key tiles (of tn keys) in the walk of the query tile at local row m0 (bm
+// rows per tile), counted as the kernels count them: every block's keys up
+// to the tile's causal limit, rounded up to 32 (c: effective causal block
+// size, 0 = none).
+int64_t walk_tiles_host(int64_t seq_q, int32_t ring_size, int32_t ring_index, int64_t c,
+                        bool striped, int64_t m0, int64_t bm, int64_t tn) {
+  int64_t kend = INT64_MAX;
+  if (c > 0) {
+    const int64_t q_last =
+        (striped ? 0 : (int64_t)ring_index * seq_q) + std::min(m0 + bm, seq_q) - 1;
+    kend = (q_last / c + 1) * c;
+  }
+  int64_t n = 0;
+  for (int32_t kb = 0; kb < ring_size; ++kb) {
+    const int64_t vbase = striped ? (kb > ring_index ? 1 : 0) : (int64_t)kb * seq_q;
+    const int64_t len = kend == INT64_MAX ? seq_q : kend - vbase;
+    const int64_t klen =
+        len <= 0 ? 0 : (len >= seq_q ? seq_q : std::min<int64_t>((len + 31) & ~(int64_t)31, seq_q));
+    n += (klen + tn - 1) / tn;
+  }
+  return n;
+}
+
+// Runs of a walk of n tiles when the longest (n_max tiles) takes P.
+int64_t split_runs_host(int64_t P, int64_t n, int64_t n_max) {
+  const int64_t runs = n_max > 0 ? (P * n + n_max - 1) / n_max : 1;
+  return std::max<int64_t>(1, std::min<int64_t>(runs, P));
+}
+
+// Workgroups per (batch, head) of the forward with P key splits: the runs
+// of every query tile's walk.
+int64_t split_wgs_host(int64_t P, int64_t seq_q, int32_t ring_size, int32_t ring_index, int64_t c,
+                       bool striped, int64_t bm, int64_t tn) {
+  const int64_t n_qtiles = (seq_q + bm - 1) / bm;
+  const int64_t n_max =
+      walk_tiles_host(seq_q, ring_size, ring_index, c, striped, (n_qtiles - 1) * bm, bm, tn);
+  int64_t w = 0;
+  for (int64_t t = 0; t < n_qtiles; ++t)
+    w += split_runs_host(
+        P, walk_tiles_host(seq_q, ring_size, ring_index, c, striped, t * bm, bm, tn), n_max);
+  return w;
+}
+
 int64_t split_workspace_bytes(int64_t batch, int64_t seq_q, int64_t heads, int64_t head_dim,
                               int32_t key_splits) {
   if (key_splits <= 1 || batch <= 0 || seq_q <= 0 || heads <= 0 || head_dim <= 0) return 0;
@@ -249,10 +292,17 @@ ra_status_t ra_blockwise_attn_fwd_split(const void* q, const void* k, const void
     if (workspace_bytes < need)
       return fail(RA_E_INVALID, "workspace of %lld bytes is smaller than the %lld required",
                   (long long)workspace_bytes, (long long)need);
-    const int64_t n_wg = (int64_t)p.n_wg * key_splits;
-    if (n_wg > kInt32Max)
+    // One workgroup per run of every query tile's walk (heavier walks are
+    // cut into more runs), none idle.
+    const int64_t bm = ra::block_rows(dtype == RA_BF16 ? ra::Dtype::BF16 : ra::Dtype::F32);
+    const int64_t wgs = split_wgs_host(key_splits, seq_q, ring_size, ring_index, p.causal,
+                                       placement == RA_PLACE_STRIPED, bm,
+                                       dtype == RA_BF16 ? 64 : 32);
+    const int64_t n_wg = batch * heads * wgs;
+    if (n_wg > kInt32Max || wgs > kInt32Max)
       return fail(RA_E_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)n_wg);
     p.n_wg = (int32_t)n_wg;
+    p.split_wgs = (int32_t)wgs;
     p.key_splits = key_splits;
     p.part_o = static_cast<float*>(workspace);
     p.part_ml = p.part_o + (int64_t)key_splits * batch * heads * seq_q * head_dim;
@@ -287,37 +337,25 @@ int32_t ra_blockwise_attn_fwd_key_splits(int64_t batch, int64_t seq_q, int64_t h
   const int64_t n_qtiles = (seq_q + bm - 1) / bm;
   const int64_t n_wg = batch * heads * n_qtiles;
   if (n_wg >= compute_units) return 1;
-  // Tiles of 64 keys in the walk of the query tile at local row m0, as the
-  // kernels walk it: every key of every block up to the tile's causal limit.
+  // The largest P whose runs (every query tile's walk cut into runs of
+  // about the longest walk's n_max / P tiles, one workgroup each) fit one
+  // workgroup per compute unit -- a second dispatch round costs more than
+  // shorter runs save --
+  // with at least 4 tiles per run of the longest walk (fewer did not pay in
+  // timings of the small causal share).
   const int64_t seq_k = seq_q * ring_size;
   const bool striped = placement == RA_PLACE_STRIPED;
   const int64_t c = causal_block_size >= seq_k ? 0 : causal_block_size;
-  auto walk = [&](int64_t m0) -> int64_t {
-    int64_t kend = INT64_MAX;
-    if (c > 0) {
-      const int64_t q_last = (striped ? 0 : (int64_t)ring_index * seq_q) +
-                             std::min(m0 + bm, seq_q) - 1;
-      kend = (q_last / c + 1) * c;
-    }
-    int64_t n = 0;
-    for (int32_t kb = 0; kb < ring_size; ++kb) {
-      const int64_t vbase = striped ? (kb > ring_index ? 1 : 0) : (int64_t)kb * seq_q;
-      const int64_t len = kend == INT64_MAX ? seq_q : kend - vbase;
-      int64_t klen = len <= 0 ? 0 : (len >= seq_q ? seq_q : std::min<int64_t>((len + 31) & ~(int64_t)31, seq_q));
-      n += (klen + 63) / 64;
-    }
-    return n;
-  };
-  const int64_t n_max = walk((n_qtiles - 1) * bm);
-  // The kernels cut the longest walk into P runs (shorter walks into
-  // proportionally fewer, the surplus workgroups idle).  The grid, idle
-  // workgroups included, must fit one workgroup per compute unit: a second
-  // dispatch round costs more than shorter runs save (timings of the small
-  // striped share).  At least 4 tiles per run of the longest walk (fewer did
-  // not pay in timings of the small causal share).
-  int64_t splits = std::min<int64_t>(compute_units / n_wg, n_max / 4);
-  splits = std::max<int64_t>(1, std::min<int64_t>(splits, kMaxKeySplits));
-  return (int32_t)splits;
+  const int64_t tn = dtype == RA_BF16 ? 64 : 32;
+  const int64_t n_max64 =
+      walk_tiles_host(seq_q, ring_size, ring_index, c, striped, (n_qtiles - 1) * bm, bm, 64);
+  int64_t best = 1;
+  for (int64_t P = 2; P <= std::min<int64_t>(kMaxKeySplits, n_max64 / 4); ++P) {
+    const int64_t wgs = split_wgs_host(P, seq_q, ring_size, ring_index, c, striped, bm, tn);
+    if (batch * heads * wgs > compute_units) break;
+    best = P;
+  }
+  return (int32_t)best;
 }
 
 ra_status_t ra_blockwise_attn_fwd_placed(const void* q, const void* k, const void* v,

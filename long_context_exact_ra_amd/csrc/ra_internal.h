@@ -35,6 +35,9 @@ struct FwdParams {
   int32_t key_splits;
   float* part_o;        // [key_splits][B][H][Lq][D] unnormalised numerators
   float* part_ml;       // [key_splits][B][H][Lq][2] (kept max, base 2; denominator)
+  // Forward with key splits: workgroups per (batch, head), one per run of
+  // each query tile's walk (0: key_splits workgroups per query tile).
+  int32_t split_wgs;
 };
 
 enum class Dtype : int { BF16 = 0, F32 = 1 };

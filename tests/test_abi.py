@@ -201,9 +201,11 @@ def test_key_split_recommendation():
     assert ks(0, 1024, 8, ra.RA_BF16, 1, 8, 0) == 1
     assert ks(1, 1024, 8, ra.RA_BF16, 1, 8, 8) == 1     # invalid ring index
     # striped: every ring position's longest walk touches every block (128
-    # tiles), so r = 0 splits as much as r = 7: 8, one workgroup per CU
-    assert ks(1, 1024, 8, ra.RA_BF16, 1, 8, 0, pl="striped") == 8
-    assert ks(1, 1024, 8, ra.RA_BF16, 1, 8, 7, pl="striped") == 8
+    # tiles), so r = 0 splits as much as r = 7.  Runs are weighted by walk
+    # length: at 12 splits the four query tiles take 3, 6, 9 and 12 runs, 240
+    # workgroups for the 8 heads; 13 would need more than 256.
+    assert ks(1, 1024, 8, ra.RA_BF16, 1, 8, 0, pl="striped") == 12
+    assert ks(1, 1024, 8, ra.RA_BF16, 1, 8, 7, pl="striped") == 12
 
 
 def test_bwd_split_validation_without_gpu():
