@@ -98,8 +98,11 @@ __device__ __forceinline__ void write_empty_partial(const FwdParams& p, int spli
 // splits are folded eight at a time with a running max, so that the loads
 // of eight splits are in flight together; a split without a visible key
 // (denominator 0) gets weight 0, and its numerator (unwritten if the split
-// was idle) is not used.
-template <typename T>
+// was idle) is not used.  Under the exact grid a query tile's slots past
+// its run count are empty by construction, so only its runs are read (the
+// count comes from the same walk lengths as the workgroup mapping;
+// BM and TN are the forward kernel's rows per workgroup and keys per tile).
+template <typename T, int BM, int TN, bool STRIPED>
 __global__ void combine_splits_kernel(const FwdParams p, int head_dim) {
   const int groups = head_dim / 4;
   const int64_t rows = (int64_t)p.batch * p.heads * p.seq_q;
@@ -107,15 +110,22 @@ __global__ void combine_splits_kernel(const FwdParams p, int head_dim) {
   if (tid >= rows * groups) return;
   const int64_t r = tid / groups;
   const int g = (int)(tid % groups);
+  const int64_t i = r % p.seq_q, bh = r / p.seq_q;
+  int nsplit = p.key_splits;
+  if (p.split_wgs > 0) {
+    const int m0 = (int)i / BM * BM;
+    const int64_t n_max = walk_tiles<TN, STRIPED>(p, wg_kend<BM, STRIPED>(p, (p.n_qtiles - 1) * BM));
+    nsplit = split_runs(p, walk_tiles<TN, STRIPED>(p, wg_kend<BM, STRIPED>(p, m0)), n_max);
+  }
   float mmax = ninf(), den = 0.f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < p.key_splits; s0 += 8) {
+  for (int s0 = 0; s0 < nsplit; s0 += 8) {
     float2 ml[8];
     float4 o[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int64_t pr = (int64_t)(s0 + u) * rows + r;
-      if (s0 + u < p.key_splits) {
+      if (s0 + u < nsplit) {
         ml[u] = *reinterpret_cast<const float2*>(p.part_ml + 2 * pr);
         o[u] = *reinterpret_cast<const float4*>(p.part_o + pr * head_dim + 4 * g);
       } else {
@@ -146,7 +156,6 @@ __global__ void combine_splits_kernel(const FwdParams p, int head_dim) {
     mmax = cm;
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  const int64_t i = r % p.seq_q, bh = r / p.seq_q;
   const int64_t b = bh / p.heads, h = bh % p.heads;
   T* o = static_cast<T*>(p.out) + ((b * p.seq_q + i) * p.heads + h) * head_dim + 4 * g;
   o[0] = (T)(num.x * inv);
@@ -943,10 +952,22 @@ int launch_fwd(const FwdParams& p, Dtype dtype, int head_dim, int64_t run_map_by
   if (p.part_o != nullptr) {
     const int64_t threads = (int64_t)p.batch * p.heads * p.seq_q * (head_dim / 4);
     const dim3 cgrid((unsigned)((threads + 255) / 256));
-    if (dtype == Dtype::BF16)
-      hipLaunchKernelGGL(combine_splits_kernel<__bf16>, cgrid, dim3(256), 0, s, p, head_dim);
-    else
-      hipLaunchKernelGGL(combine_splits_kernel<float>, cgrid, dim3(256), 0, s, p, head_dim);
+    const bool str = p.striped != 0;
+    if (dtype == Dtype::BF16) {
+      if (str)
+        hipLaunchKernelGGL((combine_splits_kernel<__bf16, kBlockMBf16, 64, true>), cgrid,
+                           dim3(256), 0, s, p, head_dim);
+      else
+        hipLaunchKernelGGL((combine_splits_kernel<__bf16, kBlockMBf16, 64, false>), cgrid,
+                           dim3(256), 0, s, p, head_dim);
+    } else {
+      if (str)
+        hipLaunchKernelGGL((combine_splits_kernel<float, kBlockMF32, 32, true>), cgrid,
+                           dim3(256), 0, s, p, head_dim);
+      else
+        hipLaunchKernelGGL((combine_splits_kernel<float, kBlockMF32, 32, false>), cgrid,
+                           dim3(256), 0, s, p, head_dim);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) {
       snprintf(err, errlen, "split combine launch failed: %s", hipGetErrorString(e));

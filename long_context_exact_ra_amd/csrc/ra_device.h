@@ -330,12 +330,16 @@ __device__ __forceinline__ WaveLimits wave_limits(const FwdParams& p, int64_t pq
   return w;
 }
 
+// 32-bit division: the last row's coordinate is below seq_k, and a nonzero
+// causal block size is below seq_k too (a larger one means non-causal), so
+// both fit 31 bits.
 template <int BM, bool STRIPED = false>
 __device__ __forceinline__ int64_t wg_kend(const FwdParams& p, int m0) {
   if (p.causal == 0) return INT64_MAX;
-  const int64_t q_last =
-      (STRIPED ? 0 : (int64_t)p.ring_index * p.seq_q) + std::min(m0 + BM, p.seq_q) - 1;
-  return uniform64((q_last / p.causal + 1) * p.causal);
+  const uint32_t q_last =
+      (uint32_t)((STRIPED ? 0 : p.ring_index * p.seq_q) + std::min(m0 + BM, p.seq_q) - 1);
+  const uint32_t c = (uint32_t)p.causal;
+  return uniform64(((int64_t)(q_last / c) + 1) * c);
 }
 
 // Forward with key splits: the grid holds split_wgs workgroups per (batch,
