@@ -243,7 +243,11 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dq_kernel(const BwdParams 
   w.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   w.lrow = w.lane & 31;
   w.half = w.lane >> 5;
-  const WgCoord wc = wg_coord<kBlockMBf16>(p);
+  // With key splits: one workgroup per run of each query tile's walk, as in
+  // the forward (a workgroup past the runs exits).
+  const WgCoord wc = p.split_wgs > 0 ? wg_coord_runs<kBlockMBf16, 64, STRIPED>(p)
+                                     : wg_coord<kBlockMBf16>(p);
+  if (wc.split < 0) return;
   const int b = wc.b, h = wc.h, m0 = wc.m0;
   w.qg0 = m0 + w.wave * 32;
   w.active = w.qg0 < p.seq_q;
@@ -722,13 +726,32 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
 
 // The dQ and dK/dV kernels of one configuration.
 // dq = the sum of the splits' addends, four values per thread, in split
-// order (deterministic).
-__global__ __launch_bounds__(256) void bwd_dq_sum_kernel(const BwdParams bp, int64_t n4) {
+// order (deterministic).  Only the runs of the value's query tile hold an
+// addend (the dq grid has one workgroup per run); their count comes from the
+// same walk lengths as the workgroup mapping.  row4: float4s per query row
+// (heads * head_dim / 4).
+template <bool STRIPED>
+__global__ __launch_bounds__(256) void bwd_dq_sum_kernel(const BwdParams bp, int64_t n4,
+                                                         int32_t row4) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
+  const FwdParams& p = bp.f;
+  int nsplit = p.key_splits;
+  // Walks only grow with the query tile: when tile 0 (uniform arithmetic)
+  // takes all key_splits runs, every tile does.
+  const int64_t n_max = walk_tiles<64, STRIPED>(
+      p, wg_kend<kBlockMBf16, STRIPED>(p, (p.n_qtiles - 1) * kBlockMBf16));
+  if (p.split_wgs > 0 &&
+      split_runs(p, walk_tiles<64, STRIPED>(p, wg_kend<kBlockMBf16, STRIPED>(p, 0)), n_max) <
+          p.key_splits) {
+    const int q = n4 <= INT32_MAX ? (int)((uint32_t)i / (uint32_t)row4 % (uint32_t)p.seq_q)
+                                  : (int)(i / row4 % p.seq_q);
+    const int m0 = q / kBlockMBf16 * kBlockMBf16;
+    nsplit = split_runs(p, walk_tiles<64, STRIPED>(p, wg_kend<kBlockMBf16, STRIPED>(p, m0)), n_max);
+  }
   const float4* part = reinterpret_cast<const float4*>(bp.dq_part);
   float4 acc = part[i];
-  for (int s = 1; s < bp.f.key_splits; ++s) {
+  for (int s = 1; s < nsplit; ++s) {
     const float4 v = part[(int64_t)s * n4 + i];
     acc.x += v.x;
     acc.y += v.y;
@@ -779,8 +802,13 @@ int launch_bwd(const BwdParams& bp, int head_dim, void* stream, char* err, int e
   }
   if (bp.dq_part != nullptr) {
     const int64_t n4 = rows * head_dim / 4;
-    hipLaunchKernelGGL(bwd_dq_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
-                       bp, n4);
+    const int32_t row4 = bp.f.heads * head_dim / 4;
+    if (bp.f.striped)
+      hipLaunchKernelGGL(bwd_dq_sum_kernel<true>, dim3((unsigned)((n4 + 255) / 256)), dim3(256),
+                         0, s, bp, n4, row4);
+    else
+      hipLaunchKernelGGL(bwd_dq_sum_kernel<false>, dim3((unsigned)((n4 + 255) / 256)), dim3(256),
+                         0, s, bp, n4, row4);
   }
   e = hipGetLastError();
   if (e != hipSuccess) {

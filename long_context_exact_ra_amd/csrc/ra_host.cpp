@@ -423,10 +423,15 @@ ra_status_t ra_blockwise_attn_bwd_split(const void* q, const void* k, const void
     if (workspace_bytes < need)
       return fail(RA_E_INVALID, "workspace of %lld bytes is smaller than the %lld required",
                   (long long)workspace_bytes, (long long)need);
-    const int64_t n_wg = (int64_t)bp.f.n_wg * key_splits;
-    if (n_wg > kInt32Max)
+    // The dq kernel: one workgroup per run of every query tile's walk, as in
+    // the forward.
+    const int64_t wgs = split_wgs_host(key_splits, seq_q, ring_size, ring_index, bp.f.causal,
+                                       placement == RA_PLACE_STRIPED, ra::kBlockMBf16, 64);
+    const int64_t n_wg = batch * heads * wgs;
+    if (n_wg > kInt32Max || wgs > kInt32Max)
       return fail(RA_E_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)n_wg);
     bp.f.n_wg = (int32_t)n_wg;
+    bp.f.split_wgs = (int32_t)wgs;
     bp.f.key_splits = key_splits;
     bp.dq_part = static_cast<float*>(workspace);
   }

@@ -101,7 +101,8 @@ int main() {
                                         RA_PLACE_CONTIGUOUS, s.B, s.Lq, s.H, s.D, RA_BF16, P, F,
                                         P, F, F, F, F, splits, splits > 1 ? P : nullptr, bws,
                                         nullptr) == RA_OK);
-      CHECK(ra::g_bwd.f.n_wg == s.B * s.H * tiles * splits);
+      CHECK(ra::g_bwd.f.n_wg >= s.B * s.H * tiles && ra::g_bwd.f.n_wg <= s.B * s.H * tiles * splits);
+      CHECK(splits == 1 || ra::g_bwd.f.n_wg == s.B * s.H * ra::g_bwd.f.split_wgs);
       CHECK(ra::g_bwd.n_wg_kv == s.B * s.H * ((s.N * s.Lq + 255) / 256));
       CHECK((ra::g_bwd.dq_part != nullptr) == (splits > 1));
     }
