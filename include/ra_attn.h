@@ -230,8 +230,10 @@ int64_t ra_blockwise_attn_fwd_split_workspace_bytes(int64_t batch, int64_t seq_q
  * runs (one workgroup each, over every query tile and head of the batch)
  * fit one workgroup per compute unit, at most one per 4
  * key tiles of 64 keys of the longest walk (the share's last query tile's:
- * its blocks' keys up to its causal limit), and at most 64.  Host-only;
- * invalid arguments give 1. */
+ * its blocks' keys up to its causal limit), and at most 64.  The dq kernel
+ * of ra_blockwise_attn_bwd_split launches the same runs (256 query rows,
+ * 64-key tiles), so for RA_BF16 the count serves the backward as well.
+ * Host-only; invalid arguments give 1. */
 int32_t ra_blockwise_attn_fwd_key_splits(int64_t batch, int64_t seq_q, int64_t heads,
                                          ra_dtype_t dtype, int64_t causal_block_size,
                                          int32_t ring_size, int32_t ring_index,
