@@ -228,6 +228,14 @@ def test_bwd_small_causal_striped_split():
     _full_case(workloads.get("small_causal_striped"), 6, key_splits=5)
 
 
+@pytest.mark.parametrize("r", [0, 7])
+def test_bwd_small_causal_striped_auto_split(r):
+    """The count the helper picks for this share (12: the four query tiles
+    take 3, 6, 9 and 12 runs of the dq kernel's exact grid), as bench.py
+    times it."""
+    _full_case(workloads.get("small_causal_striped"), r, key_splits="auto")
+
+
 SPLIT_EDGE = [
     # B, Lq, N, H, D, causal, qc, kc, segments, r, placement, splits
     (2, 96, 3, 2, 64, 1, 32, 32, False, 2, "contiguous", 3),
