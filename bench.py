@@ -170,7 +170,8 @@ def cpu_baseline(w, q, k, v, seg, ring_index: int, rows: int, flops_total: float
     ``rows`` query rows of the same workload (each row over all its visible
     keys).  Rate in the metric's unit (causal-adjusted TFLOP/s); the sample
     text also gives the oracle's time for the whole step, extrapolated
-    linearly (rows are independent)."""
+    linearly (rows are independent).  Returns the record, the sampled rows
+    and the oracle's results on them (out and lse, or dq for the backward)."""
     import oracle
     import torch
     head = 0
@@ -190,18 +191,19 @@ def cpu_baseline(w, q, k, v, seg, ring_index: int, rows: int, flops_total: float
         cores = torch.get_num_threads()
     t0 = time.perf_counter()
     if gh is None:
-        oracle.attention_fwd(qh, kh, vh, segh, w.causal_block_size, w.ring_size, ring_index,
-                             rows=sel, kv_len=kv_len, placement=w.placement)
+        ref = oracle.attention_fwd(qh, kh, vh, segh, w.causal_block_size, w.ring_size,
+                                   ring_index, rows=sel, kv_len=kv_len, placement=w.placement)
     else:
-        oracle.attention_bwd(qh, kh, vh, gh, segh, w.causal_block_size, w.ring_size,
-                             ring_index, rows=sel, kv_len=kv_len, placement=w.placement)
+        ref = oracle.attention_bwd(qh, kh, vh, gh, segh, w.causal_block_size, w.ring_size,
+                                   ring_index, rows=sel, kv_len=kv_len,
+                                   placement=w.placement)[:1]
     dt = time.perf_counter() - t0
     # the same pair count as the headline: the causally visible pairs
     pairs = int(visible_keys_per_row(w.seq_q, w.ring_size, ring_index,
                                      w.causal_block_size, w.placement)[sel].sum())
     flops = (4.0 if gh is None else 10.0) * w.head_dim * pairs
     rate = flops / dt
-    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+    return sel, ref, {"value": rate / 1e12, "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle",
             "sample": f"{w.name}{'' if gh is None else ' backward'}: batch entry 0, head 0, "
                       f"{rows} query rows spread over the block of ring "
@@ -209,6 +211,43 @@ def cpu_baseline(w, q, k, v, seg, ring_index: int, rows: int, flops_total: float
                       f"fp64 on {cpu_model()}; {dt:.1f} s for {flops / 1e9:.1f} GFLOP; the whole "
                       f"step would take {flops_total / rate / 3600:.1f} h at this rate "
                       f"(linear extrapolation)"}
+
+
+# Parity bounds of the timed call against the oracle sample: bf16 out and
+# lse max |err| <= 2e-2, mean |err| <= 2e-3, relative L2 of out <= 1e-2 (it
+# keeps the absolute bounds from passing on long rows, where |out| ~ 1e-3);
+# backward dq: relative L2 <= 1e-2 and max |err| <= 2e-2 max |ref|.
+FWD_BOUNDS = {"max": 2e-2, "mean": 2e-3, "rel_l2": 1e-2}
+BWD_BOUNDS = {"rel_l2": 1e-2, "max_rel": 2e-2}
+
+
+def timed_call_parity(got, ref, ring_index: int, rows) -> dict:
+    """Errors of the timed call's own outputs (head 0 of batch entry 0, the
+    oracle sample's rows) against the oracle; ``got`` is (out, lse) or (dq,)."""
+    def f64(t):
+        return t.detach().float().cpu().numpy().astype(np.float64)
+
+    rec = {"ring_index": ring_index, "head": 0, "rows": int(len(rows))}
+    if len(got) == 2:
+        out, lse = f64(got[0][:1, rows, 0]), f64(got[1][:1, 0, rows])
+        ro, rl = ref[0][:, :, 0, :], ref[1][:, 0, :]
+        e, le = np.abs(out - ro), np.abs(lse - rl)
+        rec.update(out_max=float(e.max()), out_mean=float(e.mean()),
+                   out_rel_l2=float(np.linalg.norm(out - ro) / np.linalg.norm(ro)),
+                   lse_max=float(le.max()), lse_mean=float(le.mean()), bounds=FWD_BOUNDS)
+        ok = (rec["out_max"] <= FWD_BOUNDS["max"] and rec["out_mean"] <= FWD_BOUNDS["mean"]
+              and rec["out_rel_l2"] <= FWD_BOUNDS["rel_l2"]
+              and rec["lse_max"] <= FWD_BOUNDS["max"] and rec["lse_mean"] <= FWD_BOUNDS["mean"])
+    else:
+        dq, rq = f64(got[0][:1, rows, 0]), ref[0][:, :, 0, :]
+        e = np.abs(dq - rq)
+        rec.update(dq_max_rel=float(e.max() / np.abs(rq).max()),
+                   dq_rel_l2=float(np.linalg.norm(dq - rq) / np.linalg.norm(rq)),
+                   bounds=BWD_BOUNDS)
+        ok = rec["dq_rel_l2"] <= BWD_BOUNDS["rel_l2"] and rec["dq_max_rel"] <= BWD_BOUNDS["max_rel"]
+    rec["pass"] = bool(ok and all(np.isfinite(v) for v in rec.values()
+                                  if isinstance(v, float)))
+    return rec
 
 
 def main():
@@ -385,6 +424,7 @@ def main():
                    "placement": w.placement,
                    "key_splits": splits[0] if len(splits) == 1 else splits,
                    "flops_per_step": flops, "ms_min": round(min(per), 3),
+                   "ms_median": round(float(np.median(per)), 3),
                    "wall_s": round(wall, 3)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -393,13 +433,24 @@ def main():
     }
     if seg_adjusted is not None:
         rec["segment_adjusted"] = seg_adjusted
+    parity_ok = True
     if args.cpu_rows > 0:
+        # The buffers hold the last listed ring position's results: time the
+        # oracle on that position and compare it with the timed call.
+        r_last = w.ring_indices[-1]
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, seg, r, args.cpu_rows, flops,
-                                           douts[0] if bwd else None)
+        sel, ref, rec["cpu_baseline"] = cpu_baseline(w, qs[-1], k, v, seg, r_last,
+                                                     args.cpu_rows, flops,
+                                                     douts[-1] if bwd else None)
+        rec["parity"] = timed_call_parity((dq,) if bwd else (out, lse), ref, r_last, sel)
+        parity_ok = rec["parity"]["pass"]
     else:
         rec["cpu_baseline"] = None
+        rec["parity"] = None
     print(json.dumps(rec), flush=True)
+    if not parity_ok:
+        print("bench.py: the timed call's output is outside the parity bounds", file=sys.stderr)
+        sys.exit(3)
 
 
 def bench_ffn(args, dev):

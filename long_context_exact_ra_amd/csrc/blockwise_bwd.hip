@@ -737,17 +737,20 @@ __global__ __launch_bounds__(256) void bwd_dq_sum_kernel(const BwdParams bp, int
   if (i >= n4) return;
   const FwdParams& p = bp.f;
   int nsplit = p.key_splits;
+  const walk::Share sh = share_of<kBlockMBf16, 64, STRIPED>(p);
+  // Guard: the dq grid the host launched must hold exactly the runs counted
+  // here (the same functions); otherwise dq[0] is poisoned rather than
+  // summing slots that no workgroup wrote.
+  if (i == 0 && p.split_wgs > 0 && walk::split_wgs(sh, p.key_splits) != p.split_wgs) {
+    reinterpret_cast<uint32_t*>(bp.dq)[0] = 0x7fc00000u;  // NaN
+    return;
+  }
   // Walks only grow with the query tile: when tile 0 (uniform arithmetic)
   // takes all key_splits runs, every tile does.
-  const int64_t n_max = walk_tiles<64, STRIPED>(
-      p, wg_kend<kBlockMBf16, STRIPED>(p, (p.n_qtiles - 1) * kBlockMBf16));
-  if (p.split_wgs > 0 &&
-      split_runs(p, walk_tiles<64, STRIPED>(p, wg_kend<kBlockMBf16, STRIPED>(p, 0)), n_max) <
-          p.key_splits) {
+  if (p.split_wgs > 0 && walk::qtile_runs(sh, p.key_splits, 0) < p.key_splits) {
     const int q = n4 <= INT32_MAX ? (int)((uint32_t)i / (uint32_t)row4 % (uint32_t)p.seq_q)
                                   : (int)(i / row4 % p.seq_q);
-    const int m0 = q / kBlockMBf16 * kBlockMBf16;
-    nsplit = split_runs(p, walk_tiles<64, STRIPED>(p, wg_kend<kBlockMBf16, STRIPED>(p, m0)), n_max);
+    nsplit = walk::qtile_runs(sh, p.key_splits, q / kBlockMBf16);
   }
   const float4* part = reinterpret_cast<const float4*>(bp.dq_part);
   float4 acc = part[i];

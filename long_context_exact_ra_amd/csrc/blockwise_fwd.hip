@@ -113,9 +113,18 @@ __global__ void combine_splits_kernel(const FwdParams p, int head_dim) {
   const int64_t i = r % p.seq_q, bh = r / p.seq_q;
   int nsplit = p.key_splits;
   if (p.split_wgs > 0) {
-    const int m0 = (int)i / BM * BM;
-    const int64_t n_max = walk_tiles<TN, STRIPED>(p, wg_kend<BM, STRIPED>(p, (p.n_qtiles - 1) * BM));
-    nsplit = split_runs(p, walk_tiles<TN, STRIPED>(p, wg_kend<BM, STRIPED>(p, m0)), n_max);
+    const walk::Share sh = share_of<BM, TN, STRIPED>(p);
+    nsplit = walk::qtile_runs(sh, p.key_splits, (int)i / BM);
+    // Guard: the grid the host launched must hold exactly the runs counted
+    // here (the same functions, so this holds unless the parameters are
+    // inconsistent); otherwise row 0's lse is poisoned rather than folding
+    // slots that no workgroup wrote.
+    if (tid == 0 && walk::split_wgs(sh, p.key_splits) != p.split_wgs) {
+      // (the NaN bit pattern, stored as an integer: this source is built
+      // without NaN semantics)
+      reinterpret_cast<uint32_t*>(p.lse)[0] = 0x7fc00000u;
+      return;
+    }
   }
   float mmax = ninf(), den = 0.f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);

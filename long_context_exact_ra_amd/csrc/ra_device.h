@@ -11,6 +11,7 @@
 #include <climits>
 
 #include "ra_internal.h"
+#include "ra_walk.h"
 
 // Everything here has internal linkage: each kernel source that includes
 // the header gets its own inlined copy.
@@ -91,7 +92,7 @@ struct Cursor {
 // by one per key inside a block.
 template <bool STRIPED>
 __device__ __forceinline__ int32_t block_vbase(const FwdParams& p, int kb) {
-  return STRIPED ? (kb > p.ring_index ? 1 : 0) : kb * p.seq_q;
+  return walk::block_vbase(p.seq_q, p.ring_index, STRIPED, kb);
 }
 
 // kend: first key coordinate no row of the workgroup can see (INT64_MAX when
@@ -99,11 +100,7 @@ __device__ __forceinline__ int32_t block_vbase(const FwdParams& p, int kb) {
 // up to whole 32-key sub-tiles.
 template <bool STRIPED>
 __device__ __forceinline__ int block_klen(const FwdParams& p, int kb, int64_t kend) {
-  const int64_t len = kend - (int64_t)block_vbase<STRIPED>(p, kb);
-  if (len <= 0) return 0;
-  if (len >= p.seq_q) return p.seq_q;
-  const int l32 = ((int)len + 31) & ~31;
-  return l32 > p.seq_q ? p.seq_q : l32;
+  return walk::block_klen(p.seq_q, block_vbase<STRIPED>(p, kb), kend);
 }
 
 // The walk over the keys.  Contiguous placement: block by block in ring
@@ -200,32 +197,20 @@ struct StripedCounts {
   int lo, hi;  // tiles of each block kb <= r / kb > r
 };
 
-template <int TN>
-__device__ __forceinline__ StripedCounts striped_counts(const FwdParams& p, int64_t kend) {
-  const int kb_hi = p.ring_index + 1 < p.ring_size ? p.ring_index + 1 : p.ring_index;
-  return StripedCounts{(block_klen<true>(p, p.ring_index, kend) + TN - 1) / TN,
-                       (block_klen<true>(p, kb_hi, kend) + TN - 1) / TN};
-}
-
 template <int TN, bool STRIPED>
 __device__ __forceinline__ int64_t walk_tiles(const FwdParams& p, int64_t kend) {
-  if (STRIPED) {
-    const StripedCounts sc = striped_counts<TN>(p, kend);
-    return (int64_t)(p.ring_index + 1) * sc.lo + (int64_t)(p.ring_size - 1 - p.ring_index) * sc.hi;
-  }
-  // Contiguous: block kb starts at key kb * Lq, so the blocks before
-  // kend / Lq are whole, the next one is cut at kend and the rest are empty.
-  const int full_tiles = (p.seq_q + TN - 1) / TN;
-  if (kend >= (int64_t)p.ring_size * p.seq_q) return (int64_t)p.ring_size * full_tiles;
-  const int nfull = (int)kend / p.seq_q;  // kend < N Lq, which fits int32
-  return (int64_t)nfull * full_tiles + (block_klen<false>(p, nfull, kend) + TN - 1) / TN;
+  return walk::walk_tiles(p.seq_q, p.ring_size, p.ring_index, STRIPED, TN, kend);
 }
 
 // Runs of a walk of n tiles when the longest walk (n_max tiles) takes
-// key_splits of them.  The host computes the same count for the grid.
+// key_splits of them; the host sizes the grid with the same function.
 __device__ __forceinline__ int split_runs(const FwdParams& p, int64_t n, int64_t n_max) {
-  int64_t runs = n_max > 0 ? ((int64_t)p.key_splits * n + n_max - 1) / n_max : 1;
-  return (int)(runs < 1 ? 1 : (runs > p.key_splits ? p.key_splits : runs));
+  return walk::split_runs(p.key_splits, n, n_max);
+}
+
+template <int BM, int TN, bool STRIPED>
+__device__ __forceinline__ walk::Share share_of(const FwdParams& p) {
+  return walk::Share{p.seq_q, p.ring_size, p.ring_index, p.causal, STRIPED, BM, TN};
 }
 
 // kend_max: the walk limit of the share's last query tile.
@@ -330,16 +315,10 @@ __device__ __forceinline__ WaveLimits wave_limits(const FwdParams& p, int64_t pq
   return w;
 }
 
-// 32-bit division: the last row's coordinate is below seq_k, and a nonzero
-// causal block size is below seq_k too (a larger one means non-causal), so
-// both fit 31 bits.
+// The walk limit of the workgroup whose query tile starts at local row m0.
 template <int BM, bool STRIPED = false>
 __device__ __forceinline__ int64_t wg_kend(const FwdParams& p, int m0) {
-  if (p.causal == 0) return INT64_MAX;
-  const uint32_t q_last =
-      (uint32_t)((STRIPED ? 0 : p.ring_index * p.seq_q) + std::min(m0 + BM, p.seq_q) - 1);
-  const uint32_t c = (uint32_t)p.causal;
-  return uniform64(((int64_t)(q_last / c) + 1) * c);
+  return uniform64(walk::tile_kend(p.causal, p.seq_q, p.ring_index, STRIPED, m0, BM));
 }
 
 // Forward with key splits: the grid holds split_wgs workgroups per (batch,
@@ -355,12 +334,12 @@ __device__ __forceinline__ WgCoord wg_coord_runs(const FwdParams& p) {
       xcd < rem ? xcd * (cnt + 1) + idx : rem * (cnt + 1) + (xcd - rem) * cnt + idx;
   const int bh = __builtin_amdgcn_readfirstlane(logical / p.split_wgs);
   const int in_bh = __builtin_amdgcn_readfirstlane(logical % p.split_wgs);
-  const int64_t n_max =
-      walk_tiles<TN, STRIPED>(p, wg_kend<BM, STRIPED>(p, (p.n_qtiles - 1) * BM));
+  const walk::Share sh = share_of<BM, TN, STRIPED>(p);
+  const int64_t n_max = walk::qtile_walk(sh, p.n_qtiles - 1);
   int qt = -1, split = -1, first = 0;
 #pragma clang loop vectorize(disable) unroll(disable)
   for (int t = p.n_qtiles - 1; t >= 0; --t) {
-    const int runs = split_runs(p, walk_tiles<TN, STRIPED>(p, wg_kend<BM, STRIPED>(p, t * BM)), n_max);
+    const int runs = walk::split_runs(p.key_splits, walk::qtile_walk(sh, t), n_max);
     if (in_bh < first + runs) {
       qt = t;
       split = in_bh - first;

@@ -12,6 +12,7 @@
 #include <cstring>
 
 #include "ra_internal.h"
+#include "ra_walk.h"
 
 namespace {
 
@@ -202,47 +203,14 @@ ra_status_t prepare(const void* q, const void* k, const void* v, const int32_t* 
 // Largest number of key splits a call accepts.
 constexpr int32_t kMaxKeySplits = 64;
 
-// Key tiles (of tn keys) in the walk of the query tile at local row m0 (bm
-// rows per tile), counted as the kernels count them: every block's keys up
-// to the tile's causal limit, rounded up to 32 (c: effective causal block
-// size, 0 = none).
-int64_t walk_tiles_host(int64_t seq_q, int32_t ring_size, int32_t ring_index, int64_t c,
-                        bool striped, int64_t m0, int64_t bm, int64_t tn) {
-  int64_t kend = INT64_MAX;
-  if (c > 0) {
-    const int64_t q_last =
-        (striped ? 0 : (int64_t)ring_index * seq_q) + std::min(m0 + bm, seq_q) - 1;
-    kend = (q_last / c + 1) * c;
-  }
-  int64_t n = 0;
-  for (int32_t kb = 0; kb < ring_size; ++kb) {
-    const int64_t vbase = striped ? (kb > ring_index ? 1 : 0) : (int64_t)kb * seq_q;
-    const int64_t len = kend == INT64_MAX ? seq_q : kend - vbase;
-    const int64_t klen =
-        len <= 0 ? 0 : (len >= seq_q ? seq_q : std::min<int64_t>((len + 31) & ~(int64_t)31, seq_q));
-    n += (klen + tn - 1) / tn;
-  }
-  return n;
-}
-
-// Runs of a walk of n tiles when the longest (n_max tiles) takes P.
-int64_t split_runs_host(int64_t P, int64_t n, int64_t n_max) {
-  const int64_t runs = n_max > 0 ? (P * n + n_max - 1) / n_max : 1;
-  return std::max<int64_t>(1, std::min<int64_t>(runs, P));
-}
-
-// Workgroups per (batch, head) of the forward with P key splits: the runs
-// of every query tile's walk.
-int64_t split_wgs_host(int64_t P, int64_t seq_q, int32_t ring_size, int32_t ring_index, int64_t c,
+// Workgroups per (batch, head) of a launch with P key splits: the runs of
+// every query tile's walk, counted by the same functions the kernels map
+// workgroups with (ra_walk.h).  c: effective causal block size.
+int64_t split_wgs_host(int32_t P, int64_t seq_q, int32_t ring_size, int32_t ring_index, int64_t c,
                        bool striped, int64_t bm, int64_t tn) {
-  const int64_t n_qtiles = (seq_q + bm - 1) / bm;
-  const int64_t n_max =
-      walk_tiles_host(seq_q, ring_size, ring_index, c, striped, (n_qtiles - 1) * bm, bm, tn);
-  int64_t w = 0;
-  for (int64_t t = 0; t < n_qtiles; ++t)
-    w += split_runs_host(
-        P, walk_tiles_host(seq_q, ring_size, ring_index, c, striped, t * bm, bm, tn), n_max);
-  return w;
+  const ra::walk::Share sh{(int32_t)seq_q, ring_size, ring_index, c, striped, (int32_t)bm,
+                           (int32_t)tn};
+  return ra::walk::split_wgs(sh, P);
 }
 
 int64_t split_workspace_bytes(int64_t batch, int64_t seq_q, int64_t heads, int64_t head_dim,
@@ -347,10 +315,10 @@ int32_t ra_blockwise_attn_fwd_key_splits(int64_t batch, int64_t seq_q, int64_t h
   const bool striped = placement == RA_PLACE_STRIPED;
   const int64_t c = causal_block_size >= seq_k ? 0 : causal_block_size;
   const int64_t tn = dtype == RA_BF16 ? 64 : 32;
-  const int64_t n_max64 =
-      walk_tiles_host(seq_q, ring_size, ring_index, c, striped, (n_qtiles - 1) * bm, bm, 64);
+  const ra::walk::Share sh64{(int32_t)seq_q, ring_size, ring_index, c, striped, (int32_t)bm, 64};
+  const int64_t n_max64 = ra::walk::qtile_walk(sh64, (int32_t)n_qtiles - 1);
   int64_t best = 1;
-  for (int64_t P = 2; P <= std::min<int64_t>(kMaxKeySplits, n_max64 / 4); ++P) {
+  for (int32_t P = 2; P <= std::min<int64_t>(kMaxKeySplits, n_max64 / 4); ++P) {
     const int64_t wgs = split_wgs_host(P, seq_q, ring_size, ring_index, c, striped, bm, tn);
     if (batch * heads * wgs > compute_units) break;
     best = P;

@@ -293,7 +293,8 @@ def below_or_on_diag(q_chunk_global: int, q_chunk: int, k_chunk_global: int,
 
 
 def _chunk_counts(seq_q: int, q_chunk: int, k_chunk: int):
-    # [RA-code] "1. 分块处理机制": num_q = q_len // query_chunk_size.
+    # [RA-code] "1. 分块处理机制": the block is cut into seq_q / q_chunk query
+    # chunks and seq_q / k_chunk key chunks by exact integer division.
     if seq_q % q_chunk or seq_q % k_chunk:
         raise ValueError("chunk sizes must divide the block length")
     return seq_q // q_chunk, seq_q // k_chunk

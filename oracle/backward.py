@@ -71,7 +71,8 @@ def attention_bwd(q, k, v, dout, segment_ids=None, causal_block_size=None,
                   heads: Optional[Sequence[int]] = None,
                   kv_len: Optional[int] = None,
                   max_scores: int = 1 << 24,
-                  placement: str = "contiguous"):
+                  placement: str = "contiguous",
+                  keys: Optional[Sequence[int]] = None):
     """Gradients of sum(dout * out) for one device's query block.
 
     q, dout: [B, Lq, H, D] (ring position ``ring_index``); k, v: [B, S, H, D]
@@ -80,11 +81,16 @@ def attention_bwd(q, k, v, dout, segment_ids=None, causal_block_size=None,
     storage order (the order of the rows of k) or None.
     rows / heads: optional subsets of local query rows / heads.
     placement: "contiguous" or "striped", as in ``attention.attention_fwd``.
+    keys: optional subset of key storage rows (indices into the first
+    ``kv_len`` rows of k); dk and dv are then returned for those keys only,
+    in the given order.  The scores, probabilities and row terms are still
+    taken over every key of each row: a key's gradient is a sum over all
+    rows that see it, and each row's softmax runs over all its keys.
 
-    Returns (dq [B, R, Hs, D], dk [B, kv_len, Hs, D], dv [B, kv_len, Hs, D])
-    in float64.  dq is exact for the selected rows; dk and dv hold the
-    contributions of the selected rows only (the full gradient of this
-    device's share when ``rows`` is None).
+    Returns (dq [B, R, Hs, D], dk [B, K, Hs, D], dv [B, K, Hs, D]) in
+    float64, K = kv_len or len(keys).  dq is exact for the selected rows; dk
+    and dv hold the contributions of the selected rows only (the full
+    gradient of this device's share when ``rows`` is None).
     """
     q = _as_f64(q)
     k = _as_f64(k)
@@ -112,10 +118,13 @@ def attention_bwd(q, k, v, dout, segment_ids=None, causal_block_size=None,
     _check_kv_tail_masked(pq_all, kv_len, S, causal_block_size)
     pk = key_positions(S, ring_size, placement)[:kv_len]
     scale = _scale(D)
+    ksel = np.arange(kv_len) if keys is None else np.asarray(keys, dtype=np.int64)
+    if ksel.size and (ksel.min() < 0 or ksel.max() >= kv_len):
+        raise ValueError("keys must index the first kv_len key rows")
 
     dq = np.zeros((B, rows.shape[0], len(heads), D), dtype=np.float64)
-    dk = np.zeros((B, kv_len, len(heads), D), dtype=np.float64)
-    dv = np.zeros((B, kv_len, len(heads), D), dtype=np.float64)
+    dk = np.zeros((B, ksel.shape[0], len(heads), D), dtype=np.float64)
+    dv = np.zeros((B, ksel.shape[0], len(heads), D), dtype=np.float64)
     step = max(1, max_scores // max(kv_len, 1))
     for b in range(B):
         for hi, h in enumerate(heads):
@@ -135,6 +144,9 @@ def attention_bwd(q, k, v, dout, segment_ids=None, causal_block_size=None,
                 dp = dO @ V.T
                 ds = _ds_from_dp(p, dp, _row_delta(dO, out_rows))
                 dq[b, r0:r0 + step, hi, :] = (ds @ K) * scale
+                if keys is not None:
+                    ds = ds[:, ksel]
+                    p = p[:, ksel]
                 dk[b, :, hi, :] += (ds.T @ Q) * scale
                 dv[b, :, hi, :] += p.T @ dO
     return dq, dk, dv

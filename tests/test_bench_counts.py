@@ -73,3 +73,35 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
+
+
+def test_timed_call_parity_accepts_and_rejects():
+    """The bench's check of the timed call: an output equal to the oracle's
+    (up to bf16 rounding) passes; a dropped row, a zero output (which the
+    absolute bounds alone would accept at long shapes) and a shifted lse
+    fail.  CPU tensors stand in for the device buffers."""
+    import torch
+    rng = np.random.default_rng(11)
+    R, D, L = 16, 128, 64
+    rows = np.sort(rng.choice(L, R, replace=False))
+    ro = rng.standard_normal((1, R, 1, D)) * 1e-3
+    rl = 13.0 + rng.standard_normal((1, 1, R))
+    out = torch.zeros((1, L, 2, D), dtype=torch.bfloat16)
+    lse = torch.zeros((1, 2, L), dtype=torch.float32)
+    out[0, rows, 0] = torch.from_numpy(ro[0, :, 0]).to(torch.bfloat16)
+    lse[0, 0, rows] = torch.from_numpy(rl[0, 0]).float()
+    ok = bench.timed_call_parity((out, lse), (ro, rl), 15, rows)
+    assert ok["pass"] and ok["out_rel_l2"] < 1e-2
+    bad = out.clone()
+    bad[0, rows[3], 0] = 0
+    assert not bench.timed_call_parity((bad, lse), (ro, rl), 15, rows)["pass"]
+    assert not bench.timed_call_parity((torch.zeros_like(out), lse), (ro, rl), 15,
+                                       rows)["pass"]
+    assert not bench.timed_call_parity((out, lse + 0.05), (ro, rl), 15, rows)["pass"]
+    # backward: dq
+    rq = rng.standard_normal((1, R, 1, D))
+    dq = torch.zeros((1, L, 2, D), dtype=torch.float32)
+    dq[0, rows, 0] = torch.from_numpy(rq[0, :, 0]).float()
+    assert bench.timed_call_parity((dq,), (rq,), 15, rows)["pass"]
+    dq[0, rows[0], 0] *= -1
+    assert not bench.timed_call_parity((dq,), (rq,), 15, rows)["pass"]

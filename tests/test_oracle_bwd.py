@@ -178,6 +178,45 @@ def pin_bwd_row_subsets_add_up():
     _close(ga[2] + gb[2], full[2])
 
 
+def pin_bwd_key_subset_matches_autograd():
+    """keys=J returns the gradient of exactly those keys: autograd's full dk
+    and dv sliced at J, for keys from every block, out of order, one key
+    listed twice (block-causal ring share with segment ids)."""
+    B, Lq, N, H, D, r, c = 2, 8, 4, 2, 8, 2, 3
+    S = N * Lq
+    q, k, v, do = (_rand(s, 90 + i) for i, s in enumerate(
+        [(B, Lq, H, D), (B, S, H, D), (B, S, H, D), (B, Lq, H, D)]))
+    seg = np.array([[0] * 13 + [1] * 11 + [2] * 8, [4] * 20 + [7] * 12], dtype=np.int64)
+    ts = torch.from_numpy(seg)
+    mask = _causal_mask_torch(Lq, S, r, c) & (ts[:, r * Lq:(r + 1) * Lq, None] == ts[:, None, :])
+    rdq, rdk, rdv = _autograd(q, k, v, do, mask)
+    keys = [31, 0, 9, 17, 17, 24, 5, 22]
+    gq, gk, gv = oracle.attention_bwd(q, k, v, do, seg, c, N, r, keys=keys)
+    _close(gq, rdq)
+    _close(gk, rdk[:, keys])
+    _close(gv, rdv[:, keys])
+
+
+def pin_bwd_sparse_upstream():
+    """With dout zero outside a set of rows R, the share's whole gradient
+    (autograd over every row) equals the contributions of the rows in R:
+    dk and dv are those of rows=R, dq vanishes outside R."""
+    B, Lq, N, H, D, r = 1, 16, 3, 2, 8, 2
+    S = N * Lq
+    q, k, v, do = (_rand(s, 100 + i) for i, s in enumerate(
+        [(B, Lq, H, D), (B, S, H, D), (B, S, H, D), (B, Lq, H, D)]))
+    R = np.array([0, 3, 4, 11, 15])
+    sparse = np.zeros_like(do)
+    sparse[:, R] = do[:, R]
+    rdq, rdk, rdv = _autograd(q, k, v, sparse, _causal_mask_torch(Lq, S, r, 1))
+    gq, gk, gv = oracle.attention_bwd(q, k, v, sparse, None, 1, N, r, rows=R)
+    _close(gq, rdq[:, R])
+    others = np.setdiff1d(np.arange(Lq), R)
+    assert not np.any(rdq[:, others])
+    _close(gk, rdk)
+    _close(gv, rdv)
+
+
 BWD_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_bwd_")]
 
 

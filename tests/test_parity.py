@@ -101,6 +101,9 @@ def test_packed_documents_all_positions():
 
 @pytest.mark.timeout(600)
 def test_share_7b_512k_sampled():
+    """The 7B-shaped share at its real shape: sampled rows of EVERY head
+    (each XCD group of the grid holds four consecutive heads), the run map,
+    and a second launch that must agree bit for bit."""
     w = workloads.get("share_7b_512k")
     r = w.ring_indices[0]
     q, k, v = workloads.make_qkv(w, r, device=DEV)
@@ -109,16 +112,24 @@ def test_share_7b_512k_sampled():
     log("share_7b_512k: forward done")
     check_run_map(rm, w, r)
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
-    for head in (0, 15, 31):
-        rows = sample_rows(w, 200 + head, 32)
-        log(f"share_7b_512k head={head} rows={len(rows)}")
-        ref, ref_lse = oracle_sample(q, k, v, None, 1, w.ring_size, r, head, rows)
-        check(to_np(out[:, rows, head]), to_np(lse[:, head, rows]), ref, ref_lse,
-              torch.bfloat16, f"7b h={head}")
+    out2, lse2, _ = run(q, k, v, None, w, r)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2), "7B share not bitwise repeatable"
+    # one host copy of the inputs, sliced per head
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    for head in range(w.heads):
+        rows = sample_rows(w, 200 + head, 8)
+        ref, ref_lse = oracle.attention_fwd(qc[:, :, head:head + 1], kc[:, :, head:head + 1],
+                                            vc[:, :, head:head + 1], None, 1, w.ring_size, r,
+                                            rows=rows)
+        check(to_np(out[:, rows, head]), to_np(lse[:, head, rows]), ref[:, :, 0, :],
+              ref_lse[:, 0, :], torch.bfloat16, f"7b h={head} ({len(rows)} rows)")
 
 
 @pytest.mark.timeout(900)
 def test_share_65b_4m_sampled_and_poisoned():
+    """The 65B-shaped share at its real shape, with the never-read blocks
+    NaN: sampled rows of one head per XCD group of the grid (heads 8x ..
+    8x + 7 run on XCD x)."""
     w = workloads.get("share_65b_4m")
     r = w.ring_indices[0]
     order, run_bits = oracle.skip_map_closed(w.causal_block_size, w.q_chunk, w.k_chunk,
@@ -134,8 +145,8 @@ def test_share_65b_4m_sampled_and_poisoned():
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
     kv_len = visible_kv_len(w, r)
     assert kv_len == 129 * w.seq_q
-    for head in (0, 63, 29):
-        rows = sample_rows(w, 300 + head, 16)
+    for head in (0, 9, 18, 27, 36, 45, 54, 63):
+        rows = sample_rows(w, 300 + head, 8)
         log(f"share_65b_4m head={head} rows={len(rows)}")
         ref, ref_lse = oracle_sample(q, k, v, None, w.causal_block_size, w.ring_size, r,
                                      head, rows, kv_len)

@@ -159,6 +159,85 @@ def test_bwd_share_7b_sampled_and_invariants():
     assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
 
 
+def _sparse_rows(w, seed, per_tile=64, n_per_tile=2):
+    """n_per_tile seeded rows in every per_tile-row query tile of the share,
+    so that every query tile the dK/dV kernel streams holds rows of R."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for t0 in range(0, w.seq_q, per_tile):
+        n = min(per_tile, w.seq_q - t0)
+        rows.extend((t0 + rng.choice(n, size=min(n_per_tile, n), replace=False)).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def _sparse_upstream_case(w, r, heads, seed, n_per_tile):
+    """The share at full size with dout zero outside a row set R (every
+    query tile holds rows of R).  The exact gradient is then the sum of the
+    contributions of the rows in R alone (the oracle's rows=R), so dk and dv
+    can be compared element by element on EVERY key of the sampled heads --
+    every ring block, up to the last keys, whose float32 dk/dv addresses lie
+    past 2^31 bytes -- while the kernels run their full grids.  dq must
+    vanish exactly outside R on every head."""
+    dev = torch.device("cuda:0")
+    q, k, v = workloads.make_qkv(w, r, device=dev)
+    R = _sparse_rows(w, seed, n_per_tile=n_per_tile)
+    keep = torch.zeros((1, w.seq_q, 1, 1), dtype=torch.bfloat16, device=dev)
+    keep[:, torch.from_numpy(R).to(dev)] = 1
+    dout = workloads.make_dout(w, r, device=dev) * keep
+    out, lse = ra.blockwise_attn_fwd(q, k, v, None, w.causal_block_size, w.q_chunk, w.k_chunk,
+                                     w.ring_size, r, placement=w.placement)
+    dq, dk, dv, delta = ra.blockwise_attn_bwd(q, k, v, out, lse, dout, None,
+                                              w.causal_block_size, w.q_chunk, w.k_chunk,
+                                              w.ring_size, r, placement=w.placement)
+    torch.cuda.synchronize()
+    what = f"{w.name} r={r} sparse upstream ({len(R)} rows)"
+    log(f"{what}: backward done")
+    assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
+    others = torch.ones(w.seq_q, dtype=torch.bool, device=dev)
+    others[torch.from_numpy(R).to(dev)] = False
+    assert int(torch.count_nonzero(dq[:, others])) == 0, "dq nonzero outside the rows of R"
+    # invariants on every head: sum_j dk_j = 0, sum_j dv_j = sum_{i in R} dout_i
+    sk = dk.double().sum(dim=1)
+    ratio = float((sk.abs() / dk.double().abs().sum(dim=1).clamp_min(1e-30)).max())
+    assert ratio <= 1e-3, ratio
+    so = dout.double().sum(dim=1)
+    relv = float((dv.double().sum(dim=1) - so).norm() / so.norm())
+    log(f"  bwd {what}: |sum dk|/sum|dk| max={ratio:.3e}, sum dv rel_l2={relv:.3e}")
+    assert relv <= REL_L2
+    for h in heads:
+        sl = lambda t: t[:, :, h:h + 1].contiguous().cpu()
+        rdq, rdk, rdv = oracle.attention_bwd(sl(q), sl(k), sl(v), sl(dout), None,
+                                             w.causal_block_size, w.ring_size, r, rows=R,
+                                             max_scores=1 << 26, placement=w.placement)
+        _cmp(f"dq[h{h}, R]", to_np(dq[:, R, h:h + 1]), rdq, what)
+        gk, gv = to_np(dk[:, :, h:h + 1]), to_np(dv[:, :, h:h + 1])
+        _cmp(f"dk[h{h}, all {w.seq_k} keys]", gk, rdk, what)
+        _cmp(f"dv[h{h}, all {w.seq_k} keys]", gv, rdv, what)
+        # per ring block, so that a block written to the wrong place or not
+        # at all shows by name
+        for kb in range(w.ring_size):
+            ks = slice(kb * w.seq_q, (kb + 1) * w.seq_q)
+            for name, g, e in (("dk", gk, rdk), ("dv", gv, rdv)):
+                rel = float(np.linalg.norm(g[:, ks] - e[:, ks])
+                            / max(np.linalg.norm(e[:, ks]), 1e-300))
+                assert rel <= REL_L2, (what, h, name, kb, rel)
+
+
+@pytest.mark.timeout(600)
+def test_bwd_share_7b_sparse_upstream_elementwise():
+    """dk and dv of the 7B-shaped share compared element by element on all
+    524288 keys of two heads (on different XCD groups of the dK/dV grid)."""
+    w = workloads.get("share_7b_512k")
+    _sparse_upstream_case(w, w.ring_indices[0], heads=(0, 21), seed=79, n_per_tile=2)
+
+
+@pytest.mark.timeout(600)
+def test_bwd_share_7b_striped_sparse_upstream_elementwise():
+    """The same under striped placement (ring position 15), one head."""
+    w = workloads.get("share_7b_512k_striped")
+    _sparse_upstream_case(w, 15, heads=(13,), seed=80, n_per_tile=1)
+
+
 @pytest.mark.parametrize("r", [0, 5])
 def test_bwd_small_causal_striped(r):
     _full_case(workloads.get("small_causal_striped"), r)
