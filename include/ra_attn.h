@@ -42,7 +42,9 @@
  *
  * Ownership and synchronisation: all pointers except those marked "host"
  * are device pointers allocated by the caller; the library allocates no
- * device memory and keeps no pointer after a call returns.  Work is enqueued
+ * device memory and keeps no pointer after a call returns (its only device
+ * memory is the fixed scratch array of ra_blockwise_attn_fwd_split_noalloc,
+ * part of its code object).  Work is enqueued
  * on `stream` (a hipStream_t; NULL = the default stream) and the call
  * returns after the launch; the caller synchronises.  Calls are thread-safe.
  *
@@ -223,6 +225,39 @@ ra_status_t ra_blockwise_attn_fwd_split(const void* q, const void* k,
 int64_t ra_blockwise_attn_fwd_split_workspace_bytes(int64_t batch, int64_t seq_q,
                                                      int64_t heads, int64_t head_dim,
                                                      int32_t key_splits);
+
+/*
+ * ra_blockwise_attn_fwd_split_noalloc -- ra_blockwise_attn_fwd_split for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the split partials
+ * go to a scratch array that the library holds itself, so the call takes no
+ * workspace and calls no hipMalloc, hipFree or other allocating routine.
+ *
+ *   The scratch is a device array of 64 MiB (67108864 bytes) in the library's
+ *   code object: each GPU the library runs on holds one copy until the
+ *   process ends.  Its device address is looked up on the first call on each
+ *   device (the current device; `stream` must belong to it).  Calls whose
+ *   partials, ra_blockwise_attn_fwd_split_workspace_bytes(batch, seq_q,
+ *   heads, head_dim, key_splits) bytes, exceed 64 MiB return
+ *   RA_E_UNSUPPORTED before any GPU work.  Nothing in the scratch has to
+ *   start at zero (every slot a call reads is written by that call first).
+ *   All calls on one GPU share its scratch: calls that may overlap on one
+ *   GPU (on different streams, or from several threads without ordering)
+ *   race; order them on one stream.
+ *
+ * Arguments, results and other errors as for ra_blockwise_attn_fwd_split
+ * without the workspace; RA_E_HIP also when the scratch's address cannot be
+ * obtained.
+ */
+ra_status_t ra_blockwise_attn_fwd_split_noalloc(const void* q, const void* k,
+                                                const void* v, const int32_t* segment_ids,
+                                                int64_t causal_block_size, int64_t q_chunk,
+                                                int64_t k_chunk, int32_t ring_size,
+                                                int32_t ring_index, ra_placement_t placement,
+                                                int64_t batch, int64_t seq_q, int64_t heads,
+                                                int64_t head_dim, ra_dtype_t dtype,
+                                                void* out, float* lse, uint8_t* run_map,
+                                                int32_t key_splits, void* stream);
 
 /* A key split count for a share: 1 when the unsplit grid (batch * heads *
  * ceil(seq_q / rows per workgroup) workgroups, 256 rows for RA_BF16, 128

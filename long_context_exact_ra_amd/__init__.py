@@ -73,6 +73,9 @@ def load_library():
     lib.ra_blockwise_attn_fwd_split.argtypes = (fwd_args[:9] + [ctypes.c_int] + fwd_args[9:]
                                                 + [c_vp, c_i32, c_vp, c_i64, c_vp])
     lib.ra_blockwise_attn_fwd_split.restype = ctypes.c_int
+    lib.ra_blockwise_attn_fwd_split_noalloc.argtypes = (fwd_args[:9] + [ctypes.c_int]
+                                                        + fwd_args[9:] + [c_vp, c_i32, c_vp])
+    lib.ra_blockwise_attn_fwd_split_noalloc.restype = ctypes.c_int
     lib.ra_blockwise_attn_fwd_split_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_i64,
                                                                 c_i32]
     lib.ra_blockwise_attn_fwd_split_workspace_bytes.restype = c_i64
@@ -190,7 +193,10 @@ def blockwise_attn_fwd(q, k, v, segment_ids=None, causal_block_size: Optional[in
     that many runs whose partial results a second kernel folds), or "auto"
     (the library's count for this GPU's compute units).  workspace: a device
     tensor of at least ``fwd_split_workspace_bytes`` bytes, allocated when
-    not given and the call splits.
+    not given and the call splits; or the string "scratch"
+    (``ra_blockwise_attn_fwd_split_noalloc``: the partials go to the
+    library's own 64 MiB scratch and the library allocates nothing; pass out
+    and lse to allocate nothing here either).
     """
     import torch
     lib = load_library()
@@ -241,7 +247,12 @@ def blockwise_attn_fwd(q, k, v, segment_ids=None, causal_block_size: Optional[in
                 or tuple(run_map.shape) != (ring_size, nq, nk)):
             raise ValueError("run_map must be a contiguous uint8 device tensor [N, nq, nk]")
         map_ptr = run_map.data_ptr()
-    if key_splits != 1:
+    if isinstance(workspace, str):
+        if workspace != "scratch":
+            raise ValueError('workspace must be a device tensor, None or "scratch"')
+        _check(lib.ra_blockwise_attn_fwd_split_noalloc(*args[:9], place, *args[9:], map_ptr,
+                                                       key_splits, sptr))
+    elif key_splits != 1:
         need = fwd_split_workspace_bytes(B, Lq, H, D, key_splits)
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

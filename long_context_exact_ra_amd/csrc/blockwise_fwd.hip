@@ -44,6 +44,7 @@
 #include <algorithm>
 #include <climits>
 #include <cstdio>
+#include <mutex>
 
 #include "ra_device.h"
 #include "ra_internal.h"
@@ -914,6 +915,39 @@ void launch_bf16(bool seg, bool striped, dim3 grid, dim3 block, hipStream_t s,
 }
 
 }  // namespace
+
+// Scratch of ra_blockwise_attn_fwd_split_noalloc (the split partials of
+// callers that cannot allocate).  In host code `scratch` names a host-side
+// stand-in, not device memory: kernels only ever get the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) char scratch[kFwdScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+}  // namespace
+
+int fwd_scratch(void** ptr, char* err, int errlen) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= 64) {
+    snprintf(err, errlen, "no usable current device (%s, device %d)", hipGetErrorString(e), dev);
+    return 1;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      snprintf(err, errlen, "hipGetSymbolAddress of the scratch array failed on device %d: %s",
+               dev, hipGetErrorString(e));
+      return 1;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return 0;
+}
 
 int launch_fwd(const FwdParams& p, Dtype dtype, int head_dim, int64_t run_map_bytes,
                void* stream, char* err, int errlen) {

@@ -293,6 +293,31 @@ int64_t ra_blockwise_attn_fwd_split_workspace_bytes(int64_t batch, int64_t seq_q
   return split_workspace_bytes(batch, seq_q, heads, head_dim, key_splits);
 }
 
+ra_status_t ra_blockwise_attn_fwd_split_noalloc(
+    const void* q, const void* k, const void* v, const int32_t* segment_ids,
+    int64_t causal_block_size, int64_t q_chunk, int64_t k_chunk, int32_t ring_size,
+    int32_t ring_index, ra_placement_t placement, int64_t batch, int64_t seq_q, int64_t heads,
+    int64_t head_dim, ra_dtype_t dtype, void* out, float* lse, uint8_t* run_map,
+    int32_t key_splits, void* stream) {
+  clear_error();
+  // The partials live in the library's fixed scratch; larger calls are
+  // refused before anything touches the GPU.
+  const int64_t need = split_workspace_bytes(batch, seq_q, heads, head_dim, key_splits);
+  if (need > ra::kFwdScratchBytes)
+    return fail(RA_E_UNSUPPORTED,
+                "key_splits %d over batch %lld x heads %lld x seq_q %lld needs %lld bytes of "
+                "split partials; the no-allocation forward's scratch holds %lld",
+                key_splits, (long long)batch, (long long)heads, (long long)seq_q,
+                (long long)need, (long long)ra::kFwdScratchBytes);
+  void* scratch = nullptr;
+  char err[256];
+  if (ra::fwd_scratch(&scratch, err, (int)sizeof(err)) != 0) return fail(RA_E_HIP, "%s", err);
+  return ra_blockwise_attn_fwd_split(q, k, v, segment_ids, causal_block_size, q_chunk, k_chunk,
+                                     ring_size, ring_index, placement, batch, seq_q, heads,
+                                     head_dim, dtype, out, lse, run_map, key_splits, scratch,
+                                     ra::kFwdScratchBytes, stream);
+}
+
 int32_t ra_blockwise_attn_fwd_key_splits(int64_t batch, int64_t seq_q, int64_t heads,
                                          ra_dtype_t dtype, int64_t causal_block_size,
                                          int32_t ring_size, int32_t ring_index,

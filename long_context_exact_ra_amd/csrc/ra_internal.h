@@ -89,6 +89,15 @@ struct FfnParams {
 // Enqueue the feedforward on `stream`; same conventions as launch_fwd.
 int launch_ffn(const FfnParams& p, void* stream, char* err, int errlen);
 
+// The no-allocation forward's scratch: a file-scope device array of the
+// forward's source, one copy per GPU, held until the process ends.
+constexpr int64_t kFwdScratchBytes = 64LL << 20;
+
+// Device address of the current device's scratch array (looked up once per
+// device with hipGetSymbolAddress, then cached).  Returns 0 on success,
+// otherwise writes a message into err and returns nonzero.
+int fwd_scratch(void** ptr, char* err, int errlen);
+
 // Enqueue the forward on `stream` (a hipStream_t).  Returns 0 on success,
 // otherwise writes a message into err (size errlen) and returns nonzero.
 int launch_fwd(const FwdParams& p, Dtype dtype, int head_dim, int64_t run_map_bytes,

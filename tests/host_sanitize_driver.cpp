@@ -32,6 +32,10 @@ int launch_ffn(const FfnParams&, void*, char*, int) {
   ++g_launches;
   return 0;
 }
+int fwd_scratch(void** ptr, char*, int) {
+  *ptr = reinterpret_cast<void*>(static_cast<uintptr_t>(1) << 24);
+  return 0;
+}
 }  // namespace ra
 
 static int g_fail = 0;
@@ -94,6 +98,20 @@ int main() {
                                           RA_PLACE_CONTIGUOUS, s.B, s.Lq, s.H, s.D, RA_BF16, P,
                                           reinterpret_cast<float*>(P), nullptr, splits, P, ws - 1,
                                           nullptr) == RA_E_INVALID);
+      }
+      // The no-allocation forward: its own scratch when the partials fit
+      // 64 MiB, a refusal otherwise.
+      ra::g_fwd = ra::FwdParams{};
+      const ra_status_t na = ra_blockwise_attn_fwd_split_noalloc(
+          P, P, P, nullptr, s.c, s.qc, s.kc, s.N, s.r, RA_PLACE_CONTIGUOUS, s.B, s.Lq, s.H, s.D,
+          RA_BF16, P, reinterpret_cast<float*>(P), nullptr, splits, nullptr);
+      if (ws <= ra::kFwdScratchBytes) {
+        CHECK(na == RA_OK);
+        CHECK(ra::g_fwd.key_splits == splits);
+        CHECK(splits == 1 || ra::g_fwd.part_o == reinterpret_cast<float*>(
+                                 static_cast<uintptr_t>(1) << 24));
+      } else {
+        CHECK(na == RA_E_UNSUPPORTED);
       }
       const int64_t bws = ra_blockwise_attn_bwd_split_workspace_bytes(s.B, s.Lq, s.H, s.D, splits);
       float* const F = reinterpret_cast<float*>(P);

@@ -250,3 +250,24 @@ def test_misaligned_workspace_and_bwd_rejected():
                                              ra.RA_PLACE_CONTIGUOUS, 1, 64, 2, 128, ra.RA_BF16,
                                              *ptrs, 1, None, 0, None)
         assert st == ra.RA_E_INVALID and "aligned" in ra.last_error(), bad
+
+
+def test_noalloc_refuses_partials_beyond_its_scratch():
+    """ra_blockwise_attn_fwd_split_noalloc refuses, before any HIP call, a
+    call whose split partials exceed its 64 MiB scratch (the 7B-shaped share
+    with 2 key splits needs 1.09 GB), and says how much it would need."""
+    lib = ra.load_library()
+    P = 0x1000
+    st = lib.ra_blockwise_attn_fwd_split_noalloc(P, P, P, None, 1, 2048, 2048, 16, 15,
+                                                 ra.RA_PLACE_CONTIGUOUS, 1, 32768, 32, 128,
+                                                 ra.RA_BF16, P, P, None, 2, None)
+    assert st == ra.RA_E_UNSUPPORTED
+    msg = ra.last_error()
+    assert "1090519040 bytes" in msg and "67108864" in msg, msg
+    # just past the limit: 2 splits x 64528 rows x (128 + 2) x 4 bytes
+    assert ra.fwd_split_workspace_bytes(1, 64528, 1, 128, 2) == 67109120 > (64 << 20)
+    assert ra.fwd_split_workspace_bytes(1, 64527, 1, 128, 2) <= (64 << 20)
+    st = lib.ra_blockwise_attn_fwd_split_noalloc(P, P, P, None, 1, 32, 32, 1, 0,
+                                                 ra.RA_PLACE_CONTIGUOUS, 1, 64528, 1, 128,
+                                                 ra.RA_BF16, P, P, None, 2, None)
+    assert st == ra.RA_E_UNSUPPORTED
