@@ -311,16 +311,25 @@ __device__ __forceinline__ void carry_max(Bf16Wave<D>& w, float mx, float scale_
 // One step with the QK^T MFMAs of tile i+1 and the P.V MFMAs of tile i
 // interleaved one to one, so that the K reads (plain) and the V reads
 // (transposing, half rate) are spread over the whole step, and the
-// exponentials of tile i feed the P.V MFMAs group by group.  Slot t issues
-// QK MFMA t, then the LDS reads of slot t+2, then P.V MFMA t, then its share
-// of the exponentials: each MFMA is followed by independent work that the
-// wave issues while the matrix core runs it (2 % faster than issuing the two
-// MFMAs back to back).  Returns this lane's max over tile i+1 (unmasked).
-template <int D>
+// exponentials of tile i feed the P.V MFMAs group by group.  QK MFMA 0 is
+// issued first, with the first group's exponentials behind it; then slot t
+// issues QK MFMA t+1, the LDS reads of the K operand three and the V
+// operand two MFMAs ahead, P.V MFMA t and its share of the exponentials, so
+// that each MFMA is followed by independent work that the wave issues while
+// the matrix core runs it.  The row max of each half of tile i+1 is taken
+// as soon as its QK MFMAs are in flight.  `mid` runs at slot 2: the caller
+// issues the next tile's DMA there, so that its scalar work (cursor,
+// descriptors) runs beside the matrix cores instead of delaying the first
+// MFMAs of both waves of a SIMD after the barrier (2.9-3.8 % faster on the
+// 7B-shaped share than issuing it at the start of the step; slots 0, 1, 3
+// and 5 were measured slower).  The running sums and maxima are pinned with
+// empty asm so that the compiler does not sink them behind the last MFMA.
+// Returns this lane's max over tile i+1 (unmasked).
+template <int D, typename Mid>
 __device__ __forceinline__ float step_ilv(Bf16Wave<D>& w, f32x16_t* s_cur, f32x16_t* s_next,
                                           const bf16x8_t* qf, const __bf16* kst,
                                           const __bf16* vst, int k_rd, int v_rd,
-                                          float scale_log2) {
+                                          float scale_log2, Mid&& mid) {
   constexpr int NDB = D / 32, NC = D / 16, N = D / 8;  // N QK and N P.V MFMAs
   const float m_use = w.m_run == ninf() ? 0.f : w.m_run;
   const bf16x2_t one2 = {(__bf16)1.f, (__bf16)1.f};
@@ -349,6 +358,9 @@ __device__ __forceinline__ float step_ilv(Bf16Wave<D>& w, f32x16_t* s_cur, f32x1
     ps = __builtin_amdgcn_fdot2_f32_bf16(pb[q].s23, one2, ps, false);
     ps = __builtin_amdgcn_fdot2_f32_bf16(pb[q].s45, one2, ps, false);
     w.l_run[q] = __builtin_amdgcn_fdot2_f32_bf16(pb[q].s67, one2, ps, false);
+    // keep the sum in its slot: unpinned, it is sunk past the mask branch,
+    // behind the last MFMA
+    asm volatile("" : "+v"(w.l_run[q]));
   };
   auto make_pb = [&](int q) {
     exp_part(q, 0, 8);
@@ -361,19 +373,21 @@ __device__ __forceinline__ float step_ilv(Bf16Wave<D>& w, f32x16_t* s_cur, f32x1
   va[1] = vread(1);
   s_next[0] = f32x16_t{};
   s_next[1] = f32x16_t{};
+  // QK MFMA 0 first: the first group's exponentials run behind it.
+  s_next[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[0], s_next[0], 0, 0, 0);
+  ka[2] = kread(2);
   make_pb(0);
-  float mp0 = ninf();
+  float mp0 = ninf(), mp1 = ninf();
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int t = 0; t < N; ++t) {
-    {
-      const int sb = t / NC, c = t % NC;
-      s_next[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % 3], qf[c], s_next[sb], 0, 0, 0);
+    // QK MFMA t+1 leads P.V MFMA t by one slot
+    if (t + 1 < N) {
+      const int u = t + 1, sb = u / NC, c = u % NC;
+      s_next[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[u % 3], qf[c], s_next[sb], 0, 0, 0);
     }
-    if (t + 2 < N) {
-      ka[(t + 2) % 3] = kread(t + 2);
-      va[(t + 2) % 3] = vread(t + 2);
-    }
+    if (t + 3 < N) ka[(t + 3) % 3] = kread(t + 3);
+    if (t + 2 < N) va[(t + 2) % 3] = vread(t + 2);
     __builtin_amdgcn_sched_barrier(0);
     {
       const int q = t / NDB, j = t % NDB;
@@ -386,8 +400,13 @@ __device__ __forceinline__ float step_ilv(Bf16Wave<D>& w, f32x16_t* s_cur, f32x1
       exp_part(t / NDB + 1, (t % NDB) * PER, PER);
       if (t % NDB == NDB - 1) finish_pb(t / NDB + 1);
     }
+    if (t == 2) {
+      __builtin_amdgcn_sched_barrier(0);
+      mid();
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // the max over the first half of tile i+1, complete after QK MFMA NC-1
-    if (t == N - 2) {
+    if (t == N - 3) {
       float a = fmaxf(s_next[0][0], s_next[0][1]), b = fmaxf(s_next[0][8], s_next[0][9]);
 #pragma unroll
       for (int i = 2; i < 8; ++i) {
@@ -395,16 +414,22 @@ __device__ __forceinline__ float step_ilv(Bf16Wave<D>& w, f32x16_t* s_cur, f32x1
         b = fmaxf(b, s_next[0][8 + i]);
       }
       mp0 = fmaxf(a, b);
+      asm volatile("" : "+v"(mp0));
+    }
+    // and over the second half, behind the last P.V MFMA
+    if (t == N - 1) {
+      float a = fmaxf(s_next[1][0], s_next[1][1]), b = fmaxf(s_next[1][8], s_next[1][9]);
+#pragma unroll
+      for (int i = 2; i < 8; ++i) {
+        a = fmaxf(a, s_next[1][i]);
+        b = fmaxf(b, s_next[1][8 + i]);
+      }
+      mp1 = fmaxf(a, b);
+      asm volatile("" : "+v"(mp1));
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  float a = fmaxf(s_next[1][0], s_next[1][1]), b = fmaxf(s_next[1][8], s_next[1][9]);
-#pragma unroll
-  for (int i = 2; i < 8; ++i) {
-    a = fmaxf(a, s_next[1][i]);
-    b = fmaxf(b, s_next[1][8 + i]);
-  }
-  return fmaxf(mp0, fmaxf(a, b));
+  return fmaxf(mp0, mp1);
 }
 
 // Everything one wave carries through the ring walk.
@@ -470,7 +495,10 @@ __device__ __forceinline__ bool pipe_step(const FwdParams& p, const PipeConst& k
                                           __bf16* const* vs, int32_t* const* ss) {
   constexpr int NPT = 2 * PipeCfg<D>::DPW + (SEG ? 1 : 0);  // DMA per wave per tile
   constexpr int S0 = PH, S1 = (PH + 1) & 3, S2 = (PH + 2) & 3, S3 = (PH + 3) & 3;
-  fetch_next<D, SEG, STRIPED, S3>(p, k, st, ks, vs, ss);
+  // The DMA of tile i+3 into stage S3 (read last in step i-1, before the
+  // barrier that ended it) is issued inside the MFMA block, where its
+  // scalar work runs beside the matrix cores.
+  auto fetch = [&]() { fetch_next<D, SEG, STRIPED, S3>(p, k, st, ks, vs, ss); };
 
   TileFlags f0 = tile_flags<SEG, STRIPED>(st.ti[S0], lim);
   TileFlags f1 = tile_flags<SEG, STRIPED>(st.ti[S1], lim);
@@ -507,7 +535,8 @@ __device__ __forceinline__ bool pipe_step(const FwdParams& p, const PipeConst& k
   float mx = ninf();
   const bool any0 = f0.run0 || f0.run1, any1 = f1.run0 || f1.run1;
   if (any0 || any1) {
-    mx = step_ilv<D>(st.w, s_cur, s_next, qf, ks[S1], vs[S0], k.k_rd, k.v_rd, p.scale_log2);
+    mx = step_ilv<D>(st.w, s_cur, s_next, qf, ks[S1], vs[S0], k.k_rd, k.v_rd, p.scale_log2,
+                     fetch);
     if (!(f1.run0 && f1.run1) || f1.mask0 || f1.mask1) {
       // Keep this a real branch: if-converted, the mask would run on every
       // step.  An empty volatile asm cannot be speculated.  The masked max
@@ -518,6 +547,7 @@ __device__ __forceinline__ bool pipe_step(const FwdParams& p, const PipeConst& k
       mx = fminf(mx, mask_max<SEG>(s_next, ss[S1], k.half, f1, lim.lane_lim, k.seg_q));
     }
   } else {
+    fetch();
     s_next[0] = f32x16_t{} - __builtin_inff();
     s_next[1] = s_next[0];
   }
