@@ -493,6 +493,31 @@ def bench_ffn(args, dev):
     # two products of 2 * hidden * ffn flops per token
     flops = 4.0 * w.batch * w.seq * w.hidden * w.ffn
     tflops = flops / (ms * 1e-3) / 1e12
+
+    # Context only: the same chunked feedforward through torch's addmm
+    # (hipBLASLt GEMMs with a bias epilogue, the ReLU a separate kernel),
+    # timed the same way.  Not the library's number.
+    xs = x.view(w.batch * w.seq, w.hidden)
+    hbuf = torch.empty((w.chunk, w.ffn), dtype=x.dtype, device=dev)
+    ybuf = torch.empty_like(xs)
+
+    def torch_step():
+        for r0 in range(0, w.batch * w.seq, w.chunk):
+            torch.addmm(b1, xs[r0:r0 + w.chunk], w1, out=hbuf)
+            torch.relu_(hbuf)
+            torch.addmm(b2, hbuf, w2, out=ybuf[r0:r0 + w.chunk])
+
+    for _ in range(args.warmup):
+        torch_step()
+    torch.cuda.synchronize()
+    tev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    tev[0].record(stream)
+    for i in range(args.steps):
+        torch_step()
+        tev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t_ms = float(np.mean([tev[i].elapsed_time(tev[i + 1]) for i in range(args.steps)]))
+    d_vs_torch = float((ybuf.view_as(y).float() - y.float()).abs().max())
     rec = {
         "metric": "blockwise feedforward TFLOP/s per MI355X (% of bf16 MFMA peak in roofline.frac)",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -506,6 +531,10 @@ def bench_ffn(args, dev):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": None},
+        "hipblaslt_context": {"ms_per_step": round(t_ms, 3),
+                              "value": round(flops / (t_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                              "what": "torch addmm (hipBLASLt, bias epilogue) + relu_ per chunk",
+                              "max_abs_diff_vs_library": d_vs_torch},
     }
     if args.cpu_rows > 0:
         # the oracle's blockwise feedforward over the whole step (every

@@ -402,17 +402,19 @@ int64_t ra_blockwise_attn_bwd_split_workspace_bytes(int64_t batch, int64_t seq_q
  *       hidden activations of one chunk); contents are overwritten.
  *
  * Arithmetic: bf16 inputs on the matrix cores with float32 accumulation;
- * the hidden activation is rounded to bf16 (round to nearest even) between
- * the two products; y is rounded to bf16.
+ * each bias is added in float32; the hidden activation is rounded to bf16
+ * (round to nearest even) after the ReLU, between the two products; y is
+ * rounded to bf16.  Both products run in the library's own GEMM kernel
+ * with the bias (and ReLU) fused into its epilogue.
  *
- * The products run as hipBLASLt GEMMs with fused bias / bias+ReLU
- * epilogues; the library keeps one hipBLASLt handle per device (created on
- * first use, never released) and the chosen algorithm per shape.
+ * Alignment: x, w1, w2, y and the workspace 16-byte, b1 and b2 8-byte.
  *
- * Returns RA_E_INVALID for null pointers, non-positive sizes, a chunk size
- * that does not divide seq or a workspace smaller than required;
- * RA_E_UNSUPPORTED for RA_F32; RA_E_HIP if hipBLASLt or the runtime reports
- * an error.  A call with batch == 0 or seq == 0 is a valid no-op.
+ * Returns RA_E_INVALID for null or misaligned pointers, non-positive sizes,
+ * a chunk size that does not divide seq or a workspace smaller than
+ * required; RA_E_UNSUPPORTED for RA_F32, for hidden or ffn_hidden not a
+ * multiple of 8, or an operand (w1, w2, one chunk of x, y or of the hidden
+ * activations) of more than 4 GiB; RA_E_HIP if a launch fails.  A call with
+ * batch == 0 or seq == 0 is a valid no-op.
  */
 int64_t ra_blockwise_ffn_workspace_bytes(int64_t chunk_size, int64_t ffn_hidden);
 

@@ -5,8 +5,7 @@ Transformer.
 
 A thin ctypes binding over the C ABI in ``include/ra_attn.h`` (library
 ``libra_attn.so`` next to this file).  It only marshals arguments: every
-step of the computation runs in the library (its HIP kernels, and hipBLASLt
-for the feedforward's GEMMs).  PyTorch provides device memory and the
+step of the computation runs in the library's own HIP kernels.  PyTorch provides device memory and the
 stream.  There is no fallback: if the library is missing every call raises.
 """
 

@@ -93,8 +93,7 @@ def build(verbose: bool = True) -> str:
             continue
         objs.append(obj)
     tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
-          f"-L{ROCM}/lib", "-lhipblaslt", f"-Wl,-rpath,{ROCM}/lib"], verbose)
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     return LIB
 

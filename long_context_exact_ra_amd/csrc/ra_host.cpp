@@ -504,9 +504,21 @@ ra_status_t ra_blockwise_ffn(const void* x, const void* w1, const void* b1, cons
                 (long long)seq);
   if (dtype != RA_BF16)
     return fail(RA_E_UNSUPPORTED, "the feedforward takes bf16 inputs only");
+  // The GEMM kernel moves rows in 16-byte vectors and addresses each operand
+  // with 32-bit byte offsets.
+  if (hidden % 8 != 0 || ffn_hidden % 8 != 0)
+    return fail(RA_E_UNSUPPORTED, "hidden %lld and ffn_hidden %lld must be multiples of 8",
+                (long long)hidden, (long long)ffn_hidden);
+  if (hidden * ffn_hidden * 2 > 4294967295LL || chunk_size * hidden * 2 > 4294967295LL ||
+      chunk_size * ffn_hidden * 2 > 4294967295LL)
+    return fail(RA_E_UNSUPPORTED, "an operand of the feedforward exceeds 4 GiB");
   if (batch == 0 || seq == 0) return RA_OK;
   if (!x || !w1 || !b1 || !w2 || !b2 || !y || !workspace)
     return fail(RA_E_INVALID, "x, w1, b1, w2, b2, y and workspace must be non-NULL");
+  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(y, 16) ||
+      !aligned(workspace, 16) || !aligned(b1, 8) || !aligned(b2, 8))
+    return fail(RA_E_INVALID,
+                "x, w1, w2, y and workspace must be 16-byte aligned, b1 and b2 8-byte aligned");
   const int64_t need = ra_blockwise_ffn_workspace_bytes(chunk_size, ffn_hidden);
   if (workspace_bytes < need)
     return fail(RA_E_INVALID, "workspace of %lld bytes is smaller than the %lld required",

@@ -271,3 +271,22 @@ def test_noalloc_refuses_partials_beyond_its_scratch():
                                                  ra.RA_PLACE_CONTIGUOUS, 1, 64528, 1, 128,
                                                  ra.RA_BF16, P, P, None, 2, None)
     assert st == ra.RA_E_UNSUPPORTED
+
+
+def test_ffn_host_validation():
+    """The feedforward's own GEMM needs hidden and ffn_hidden multiples of 8
+    and aligned operands; both are refused on the host, before any HIP call."""
+    lib = ra.load_library()
+    P = 0x1000
+    ws = ra.ffn_workspace_bytes(64, 256)
+    st = lib.ra_blockwise_ffn(P, P, P, P, P, 1, 64, 60, 256, 64, ra.RA_BF16, P, P, ws, None)
+    assert st == ra.RA_E_UNSUPPORTED and "multiples of 8" in ra.last_error()
+    st = lib.ra_blockwise_ffn(P, P, P, P, P, 1, 64, 64, 252, 64, ra.RA_BF16, P, P,
+                              ra.ffn_workspace_bytes(64, 252), None)
+    assert st == ra.RA_E_UNSUPPORTED
+    st = lib.ra_blockwise_ffn(P + 8, P, P, P, P, 1, 64, 64, 256, 64, ra.RA_BF16, P, P, ws, None)
+    assert st == ra.RA_E_INVALID and "aligned" in ra.last_error()
+    st = lib.ra_blockwise_ffn(P, P, P + 2, P, P, 1, 64, 64, 256, 64, ra.RA_BF16, P, P, ws, None)
+    assert st == ra.RA_E_INVALID
+    st = lib.ra_blockwise_ffn(P, P, P, P, P, 1, 64, 64, 256, 64, ra.RA_F32, P, P, ws, None)
+    assert st == ra.RA_E_UNSUPPORTED
