@@ -437,6 +437,7 @@ def main():
                      "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4),
                      "traffic": traffic},
+        "library_build": build_id,
     }
     if seg_adjusted is not None:
         rec["segment_adjusted"] = seg_adjusted
@@ -542,6 +543,7 @@ def bench_ffn(args, dev):
                               "value": round(flops / (t_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
                               "what": "torch addmm (hipBLASLt, bias epilogue) + relu_ per chunk",
                               "max_abs_diff_vs_library": d_vs_torch},
+        "library_build": ra.version().split("+", 1)[-1],
     }
     if args.cpu_rows > 0:
         # the oracle's blockwise feedforward over the whole step (every

@@ -61,7 +61,7 @@ def device_sources_sha16() -> str:
 
 
 # The sources the forward kernel is compiled from.
-FWD_SOURCES = ("blockwise_fwd.hip", "ra_device.h", "ra_internal.h")
+FWD_SOURCES = ("blockwise_fwd.hip", "ra_device.h", "ra_internal.h", "ra_walk.h")
 
 
 def fwd_sources_sha16() -> str:

@@ -47,7 +47,14 @@
 //                LDS reads of the Q and dO tiles.
 // All tiles use one LDS layout (16-byte slots, r = row, g = 16-byte granule
 // of the row): slot(r, g) = (g / 4) * 256 + (r / 16) * 64 + (g % 4) * 16 +
-// r % 16, read as rows by ds_read_b128 and as columns by ds_read_b64_tr_b16.
+// ((r % 16) ^ (4 * (g % 4))), read as rows by ds_read_b128 and as columns by
+// ds_read_b64_tr_b16.  LDS has 64 four-byte banks, so 16 consecutive slots
+// (256 bytes) cover every bank once.  A row read (16 lanes: 16 rows, one
+// granule) and a column read (32 lanes: 4 rows x 4 granules of a quad) each
+// touch 16 slots that differ modulo 16, so neither has bank conflicts; the
+// XOR of the row's bits 2-3 with the granule is what makes the column read
+// conflict-free (without it, the 4 rows of a column read hit the same 4 of
+// the 16 bank groups four times each).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -67,13 +74,23 @@ constexpr int kWaves = 8;                 // waves per workgroup (both main kern
 constexpr int kThreadsBwd = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 
+// The DMA fills 64 consecutive slots per instruction (16 rows x one granule
+// quad); lane l's byte offset in the tensor puts the row and granule that
+// belong in slot l there.
+__device__ __forceinline__ uint32_t tile_lane_off(int lane, uint32_t rs_bytes) {
+  return (uint32_t)((lane & 15) ^ (4 * (lane >> 4))) * rs_bytes + 16u * (uint32_t)(lane >> 4);
+}
+
 // Element offsets inside a 64-row tile stored in the layout above.
 // Row operand: lane l reads row 32 * blk + l % 32, columns 16 c + 8 (l / 32)
-// .. +7 (the A operand of a 16-column k-step).
+// .. +7 (the A operand of a 16-column k-step).  row_rd is the lane's offset
+// for even c; odd c moves the granule by 2 within its quad, which flips the
+// swizzle's bit 3 of the row: offset ^ 64.
 __device__ __forceinline__ int row_rd(int lane) {
   const int lrow = lane & 31, half = lane >> 5;
-  return 512 * (lrow >> 4) + 128 * half + 8 * (lrow & 15);
+  return 512 * (lrow >> 4) + 128 * half + 8 * ((lrow & 15) ^ (4 * half));
 }
+__device__ __forceinline__ constexpr int row_rd_c(int rd, int c) { return (c & 1) ? (rd ^ 64) : rd; }
 __device__ __forceinline__ constexpr int row_off(int c, int blk) {
   return 2048 * (c >> 1) + 256 * (c & 1) + 1024 * blk;
 }
@@ -81,23 +98,24 @@ __device__ __forceinline__ constexpr int row_off(int c, int blk) {
 // 4 values of tile row 4 (g / 2) + j / 4 (+8 for the high half) at columns
 // 32 jb + 16 (g % 2) + 4 (j % 4); after the transpose, lane l holds for its
 // column 32 jb + l % 32 the 8 tile rows of the k-slots of its lane half.
+// Rows + 8 flip the swizzled row's bit 3: the high half reads at offset ^ 64.
 __device__ __forceinline__ int col_rd(int lane) {
   const int g = lane >> 4, j = lane & 15;
-  const int r0 = 4 * (g >> 1) + (j >> 2);
-  return ((2 * (g & 1) + ((j >> 1) & 1)) * 16 + r0) * 8 + 4 * (j & 1);
+  const int r0 = 4 * (g >> 1) + (j >> 2), q = 2 * (g & 1) + ((j >> 1) & 1);
+  return (q * 16 + (r0 ^ (4 * q))) * 8 + 4 * (j & 1);
 }
 // jb = 32-column block, rb = 16-row block of the tile (its k-step).
 __device__ __forceinline__ constexpr int col_off(int jb, int rb) { return 2048 * jb + 512 * rb; }
 
 __device__ __forceinline__ bf16x8_t col_operand(const __bf16* tile, int rd, int jb, int rb) {
-  const __bf16* src = tile + rd + col_off(jb, rb);
-  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)src);
-  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(src + 64));
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tile + rd + col_off(jb, rb)));
+  const i16x4_t hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tile + (rd ^ 64) + col_off(jb, rb)));
   return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 __device__ __forceinline__ bf16x8_t row_operand(const __bf16* tile, int rd, int c, int blk) {
-  return *reinterpret_cast<const bf16x8_t*>(tile + rd + row_off(c, blk));
+  return *reinterpret_cast<const bf16x8_t*>(tile + row_rd_c(rd, c) + row_off(c, blk));
 }
 
 __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
@@ -304,7 +322,7 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dq_kernel(const BwdParams 
   w.kbase0 = static_cast<const char*>(p.k) + ((int64_t)b * p.seq_k * rs + (int64_t)h * D) * 2;
   w.vbase0 = static_cast<const char*>(p.v) + ((int64_t)b * p.seq_k * rs + (int64_t)h * D) * 2;
   w.sbase0 = SEG ? p.seg + (int64_t)b * p.seq_k : nullptr;
-  w.k_lane = (uint32_t)(w.lane & 15) * w.rs_bytes + 16u * (uint32_t)(w.lane >> 4);
+  w.k_lane = tile_lane_off(w.lane, w.rs_bytes);
   w.k_rd = row_rd(w.lane);
   w.t_rd = col_rd(w.lane);
 
@@ -460,7 +478,7 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
   const int key = kw0 + lrow;              // this lane's key
   const int64_t rs = (int64_t)p.heads * D;
   const uint32_t rs_bytes = (uint32_t)(rs * 2);
-  const uint32_t lane_off = (uint32_t)(lane & 15) * rs_bytes + 16u * (uint32_t)(lane >> 4);
+  const uint32_t lane_off = tile_lane_off(lane, rs_bytes);
   const int r_rd = row_rd(lane), t_rd = col_rd(lane);
   const int32_t qrow0 = p.ring_index * p.seq_q;  // storage row of local row 0
   // Query coordinate of local row 0: its global position (contiguous), 0
@@ -656,7 +674,7 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
 #pragma unroll
       for (int cc = 0; cc < D / 16; ++cc) {
         const bf16x8_t vop = *reinterpret_cast<const bf16x8_t*>(
-            vres + (wave >> 1) * L::ELEMS + r_rd + row_off(cc, wave & 1));
+            vres + (wave >> 1) * L::ELEMS + row_rd_c(r_rd, cc) + row_off(cc, wave & 1));
         sc = mfma(row_operand(qt_t, r_rd, cc, qh), kf[cc], sc);
         dp = mfma(row_operand(gt_t, r_rd, cc, qh), vop, dp);
       }
