@@ -152,14 +152,19 @@ ra_status_t ra_blockwise_attn_fwd_ex(const void* q, const void* k,
  * segment ids stored with the query's row (r*Lq + i) and the key's row
  * (segment_ids stay in storage order).  Under striped placement every
  * device holds N*Lq*(Lq+1)/2 - Lq*(N-1-r) visible pairs (token causal).
- * Ring order, layouts, arithmetic and outputs are those of
+ * Striped placement serves the causal blocks c that divide N (the mask is
+ * then token causal between local indices, with the keys of blocks kb >=
+ * (floor(r/c) + 1) c counted one index later) and those that are multiples
+ * of N (block causal with blocks of c/N local indices); other c have no
+ * such form.  Layouts, arithmetic and outputs are those of
  * ra_blockwise_attn_fwd; run_map is that of ra_blockwise_attn_fwd_ex (a
- * chunk pair runs iff it holds a visible pair under the placement).
+ * chunk pair runs iff it holds a visible pair under the placement; its
+ * first index is the ring step (r - kb) mod N).
  *
  * Errors as for ra_blockwise_attn_fwd_ex, plus RA_E_INVALID for an unknown
  * placement and RA_E_UNSUPPORTED for RA_PLACE_STRIPED with an effective
- * causal_block_size other than 0 or 1 (a causal block at least as long as
- * the sequence counts as 0).
+ * causal_block_size c > 0 that neither divides ring_size nor is a multiple
+ * of it (a causal block at least as long as the sequence counts as 0).
  */
 ra_status_t ra_blockwise_attn_fwd_placed(const void* q, const void* k,
                                          const void* v, const int32_t* segment_ids,
@@ -325,7 +330,8 @@ ra_status_t ra_blockwise_attn_bwd(const void* q, const void* k, const void* v,
  * gradients of that placement's forward, with segment_ids, dk and dv in
  * storage order.  Errors as for ra_blockwise_attn_bwd, plus RA_E_INVALID for
  * an unknown placement and RA_E_UNSUPPORTED for RA_PLACE_STRIPED with an
- * effective causal_block_size other than 0 or 1.
+ * effective causal_block_size that neither divides ring_size nor is a
+ * multiple of it (as for ra_blockwise_attn_fwd_placed).
  */
 ra_status_t ra_blockwise_attn_bwd_placed(const void* q, const void* k,
                                          const void* v, const int32_t* segment_ids,

@@ -487,16 +487,19 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
 
   // Causal threshold of this lane's key: query coordinates >= thr see it;
   // the wave's smallest and largest thresholds decide which blocks run.
-  // Striped (token causal): key j of block kb is seen from local rows
-  // i >= j + [kb > r].  The 32 keys of a wave lie in one block.
+  // Striped: key j of block kb has coordinate j + [kb >= stripe_hi] and is
+  // seen from local rows i with floor(i / c) >= floor(coordinate / c) (c in
+  // coordinates; c = 1: i >= j + [kb > r]).  The 32 keys of a wave lie in
+  // one block.
   const int64_t c = p.causal;
   int32_t thr = INT32_MIN, thr_first = INT32_MIN, thr_last = INT32_MIN;
   if (c > 0 && STRIPED) {
     const int kb = kw0 / p.seq_q;
-    const int32_t sh = (kb > p.ring_index ? 1 : 0) - kb * p.seq_q;
-    thr = key + sh;
-    thr_first = __builtin_amdgcn_readfirstlane(kw0 + sh);
-    thr_last = __builtin_amdgcn_readfirstlane(kw0 + 31 + sh);
+    const int32_t sh = (kb >= p.stripe_hi ? 1 : 0) - kb * p.seq_q;
+    const int32_t cc = (int32_t)c;
+    thr = (key + sh) / cc * cc;
+    thr_first = __builtin_amdgcn_readfirstlane((kw0 + sh) / cc * cc);
+    thr_last = __builtin_amdgcn_readfirstlane((kw0 + 31 + sh) / cc * cc);
   } else if (c > 0) {
     thr = (int32_t)(((int64_t)key / c) * c);
     thr_first = (int32_t)uniform64(((int64_t)kw0 / c) * c);
@@ -534,7 +537,8 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
     // threshold is at most 1).
     const int kb = k0 / p.seq_q;
     const int j0 = k0 - kb * p.seq_q;
-    q_lo = j0 + kBlockNBwd <= p.seq_q ? j0 + (kb > p.ring_index ? 1 : 0) : 0;
+    const int32_t cc = (int32_t)c;
+    q_lo = j0 + kBlockNBwd <= p.seq_q ? (j0 + (kb >= p.stripe_hi ? 1 : 0)) / cc * cc : 0;
     q_lo = q_lo >= p.seq_q ? p.seq_q : q_lo;
   } else if (c > 0) {
     const int64_t t0 = ((int64_t)k0 / c) * c - qpos0;

@@ -32,12 +32,15 @@
 //     granule: 8 consecutive k of each row) is 256 contiguous bytes, one
 //     ds_read_b128.
 //   W stage, 32 rows k x BN / 8 granules, row-major with the granules of row
-//     k permuted: slot k * BN / 8 + j holds granule j ^ 2 (k % 4).  A DMA
+//     k permuted: slot k * BN / 8 + j holds granule j ^ 4 (k % 4).  A DMA
 //     instruction fetches whole rows (64 lanes, BN / 8 per row); two
 //     ds_read_b64_tr_b16 (gfx950's transposing LDS read) give each lane 8
 //     consecutive k of its own column n, the W^T operand, with no transpose
-//     in registers, and the permutation puts the four rows one transposing
-//     read touches in different LDS banks.
+//     in registers.  Half a wave of one transposing read touches 4 rows x 4
+//     granules of a quad; a row is a multiple of 256 bytes (the 64 four-byte
+//     banks), so without the permutation the 4 rows would hit the same 4 of
+//     the 16 bank groups; XORing the granule's quad bits with the row puts
+//     them in 4 different quads, every bank once.
 // Both operands assign the 16 k of an MFMA step to the k-slots the same
 // way (lane half h takes k = 8 h .. 8 h + 7), so the contraction is exact.
 // Workgroups are numbered so that consecutive tiles of one column block
@@ -111,14 +114,14 @@ __device__ __forceinline__ void gemm_fetch(const GemmArgs& a, int m0, int n0, in
     dma_b128(lds_addr(st + i * 512), off, xr);
   }
   // W: whole rows of the stage tile per instruction (BN / 8 lanes per row);
-  // slot k * (BN / 8) + j of the stage holds granule j ^ 2 (k % 4) of row k.
+  // slot k * (BN / 8) + j of the stage holds granule j ^ 4 (k % 4) of row k.
   constexpr int GPR = BN / 8;          // granules per row
   constexpr int RPI = 64 / GPR;        // rows per DMA instruction
 #pragma unroll
   for (int u = 0; u < C::W_DMA; ++u) {
     const int i = wave * C::W_DMA + u;
     const int k = RPI * i + lane / GPR;
-    const int g = (lane % GPR) ^ (2 * (k & 3));
+    const int g = (lane % GPR) ^ (4 * (k & 3));
     const uint32_t off = (uint32_t)k * (uint32_t)a.n * 2u + (uint32_t)(n0 + 8 * g) * 2u;
     dma_b128(lds_addr(st + C::X_ELEMS + i * 512), off, wr);
   }
@@ -143,7 +146,7 @@ __device__ __forceinline__ void gemm_fetch_one(const GemmArgs& a, int m0, int n0
     constexpr int GPR = BN / 8, RPI = 64 / GPR;
     const int i = wave * C::W_DMA + (u - C::X_DMA);
     const int k = RPI * i + lane / GPR;
-    const int g = (lane % GPR) ^ (2 * (k & 3));
+    const int g = (lane % GPR) ^ (4 * (k & 3));
     const uint32_t off = (uint32_t)k * (uint32_t)a.n * 2u + (uint32_t)(n0 + 8 * g) * 2u;
     dma_b128(lds_addr(st + C::X_ELEMS + i * 512), off, wr);
   }
@@ -167,14 +170,15 @@ struct Operands {
 };
 
 template <int BM, int BN>
-__device__ __forceinline__ void read_operands(Operands<BM, BN>& o, const __bf16* st, int w_rd0,
-                                              int w_rd1, int x_rd, int ks) {
+__device__ __forceinline__ void read_operands(Operands<BM, BN>& o, const __bf16* st,
+                                              const int (&w_rd)[GemmCfg<BM, BN>::NB], int x_rd,
+                                              int ks) {
   using C = GemmCfg<BM, BN>;
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb) {
-    // rows ks*16 .. of the swizzled row-major W stage; the lane's granule
-    // depends on the parity of nb (w_rd0 / w_rd1), the rest is a constant
-    const __bf16* src = st + ((nb & 1) ? w_rd1 : w_rd0) + (nb >> 1) * 64 + ks * 16 * BN;
+    // rows ks*16 .. of the swizzled row-major W stage (the lane's base
+    // w_rd[nb] holds its row and swizzled granule; the rest is a constant)
+    const __bf16* src = st + w_rd[nb] + ks * 16 * BN;
     const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)src);
     const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(src + 4 * BN));
     o.w[nb] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -246,14 +250,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bias_kernel(const GemmAr
   // W: lane reads row kr = 8 (g16 / 2) + j16 / 4 (+ ks * 16, + 4 for the
   // second read; kr % 4 = j16 / 4 either way) at column wn + 32 nb + 16 (g16
   // % 2) + 4 (j16 % 4): granule gc = (wn + 32 nb) / 8 + 2 (g16 % 2) + (j16 %
-  // 4) / 2, stored at slot kr * BN / 8 + (gc ^ 2 (kr % 4)).  The low three
-  // bits of gc hold nb % 2 in bit 2, so two bases cover every nb.
-  const int kr = 8 * (g16 >> 1) + (j16 >> 2), sw = 2 * (j16 >> 2);
-  auto w_base = [&](int nbpar) {
-    const int gc = wn / 8 + 4 * nbpar + 2 * (g16 & 1) + ((j16 & 3) >> 1);
-    return C::X_ELEMS + kr * BN + (gc ^ sw) * 8 + 4 * (j16 & 1);
-  };
-  const int w_rd0 = w_base(0), w_rd1 = w_base(1);
+  // 4) / 2, stored at slot kr * BN / 8 + (gc ^ 4 (kr % 4)).  The XOR
+  // touches the bits of gc that nb sets, so each nb has its own base.
+  const int kr = 8 * (g16 >> 1) + (j16 >> 2), sw = 4 * (j16 >> 2);
+  int w_rd[C::NB];
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb) {
+    const int gc = wn / 8 + 4 * nb + 2 * (g16 & 1) + ((j16 & 3) >> 1);
+    w_rd[nb] = C::X_ELEMS + kr * BN + (gc ^ sw) * 8 + 4 * (j16 & 1);
+  }
 
   f32x16_t acc[C::NB * C::MB];
 #pragma unroll
@@ -277,7 +282,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bias_kernel(const GemmAr
   }
   stage_barrier();
   Operands<BM, BN> op0, op1;
-  read_operands<BM, BN>(op0, lds, w_rd0, w_rd1, x_rd, 0);
+  read_operands<BM, BN>(op0, lds, w_rd, x_rd, 0);
 
   // Every stage but the last; the loop body has no branch around the
   // barrier, so the compiler's LDS waits stay exact (LDS reads complete in
@@ -288,7 +293,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bias_kernel(const GemmAr
   for (int kt = 0; kt + 1 < nk; ++kt) {
     const int nxt = cur == kStages - 1 ? 0 : cur + 1;
     const int prv = cur == 0 ? kStages - 1 : cur - 1;  // stage of kt - 1 = kt + 4
-    read_operands<BM, BN>(op1, lds + cur * C::STAGE, w_rd0, w_rd1, x_rd, 1);
+    read_operands<BM, BN>(op1, lds + cur * C::STAGE, w_rd, x_rd, 1);
     mma_step<BM, BN>(acc, op0);
     // Stage kt + 1 must have landed (stages kt + 1 .. kt + 3, as far as
     // issued, are in flight here).
@@ -302,7 +307,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bias_kernel(const GemmAr
         wait_vm<0>();
     }
     stage_barrier();
-    read_operands<BM, BN>(op0, lds + nxt * C::STAGE, w_rd0, w_rd1, x_rd, 0);
+    read_operands<BM, BN>(op0, lds + nxt * C::STAGE, w_rd, x_rd, 0);
     // the DMA of stage kt + 4, spread over the MFMAs
     const bool dma = kt + 4 < nk;
     __bf16* const dst = lds + prv * C::STAGE;
@@ -315,7 +320,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bias_kernel(const GemmAr
     });
     cur = nxt;
   }
-  read_operands<BM, BN>(op1, lds + cur * C::STAGE, w_rd0, w_rd1, x_rd, 1);
+  read_operands<BM, BN>(op1, lds + cur * C::STAGE, w_rd, x_rd, 1);
   mma_step<BM, BN>(acc, op0);
   mma_step<BM, BN>(acc, op1);
 

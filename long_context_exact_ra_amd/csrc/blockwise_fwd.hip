@@ -515,8 +515,8 @@ __device__ __forceinline__ bool pipe_step(const FwdParams& p, const PipeConst& k
   if (p.run_map != nullptr && k.lane == 0) {
     const TileInfo& t0 = st.ti[S0];
     const int kloc0 = t0.pk - t0.kb * p.seq_q;
-    if (f0.run0) write_run_map(p, t0.t, k.qg0, kloc0);
-    if (f0.run1) write_run_map(p, t0.t, k.qg0, kloc0 + 32);
+    if (f0.run0) write_run_map(p, t0.kb, k.qg0, kloc0);
+    if (f0.run1) write_run_map(p, t0.kb, k.qg0, kloc0 + 32);
   }
   if (SEG) {
     // Halves whose key ids miss the queries' id range hold no visible pair.
@@ -888,7 +888,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(const FwdParams p)
         for (int j = 0; j < NDB; ++j)
           acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[32 * j + lrow], s[i], acc[j], 0, 0, 0);
       }
-      if (p.run_map != nullptr && lane == 0) write_run_map(p, cur.t, qg0, kloc0);
+      if (p.run_map != nullptr && lane == 0) write_run_map(p, cur.kb, qg0, kloc0);
     }
 
     if (nxt.valid) store_tile(buf ^ 1);

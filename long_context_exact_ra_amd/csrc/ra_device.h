@@ -85,14 +85,15 @@ struct Cursor {
 // Key coordinates.  Causal tests compare a key coordinate with a limit
 // derived from the query rows.  Contiguous placement: the coordinate of key
 // j of block kb is its global position kb * Lq + j, the same as its storage
-// row.  Striped placement (position j * N + kb, token causal or none): the
-// coordinate is j + [kb > r], and query row i's limit is i + 1, because
-// j * N + kb <= i * N + r holds exactly when j + [kb > r] <= i.  Either way
-// the coordinate of block kb's first key is block_vbase and coordinates grow
-// by one per key inside a block.
+// row.  Striped placement (position j * N + kb): the coordinate is j + [kb
+// >= stripe_hi] and query row i's is i, with p.causal the causal block in
+// coordinates (walk::striped_causal: token causal when the mask's block
+// divides N, j + [kb > r] <= i for c = 1; block causal on the local indices
+// when N divides it).  Either way the coordinate of block kb's first key is
+// block_vbase and coordinates grow by one per key inside a block.
 template <bool STRIPED>
 __device__ __forceinline__ int32_t block_vbase(const FwdParams& p, int kb) {
-  return walk::block_vbase(p.seq_q, p.ring_index, STRIPED, kb);
+  return walk::block_vbase(p.seq_q, p.stripe_hi, STRIPED, kb);
 }
 
 // kend: first key coordinate no row of the workgroup can see (INT64_MAX when
@@ -112,15 +113,19 @@ __device__ __forceinline__ int block_klen(const FwdParams& p, int kb, int64_t ke
 // of every block in ring order, then tile kt + 1 -- which keeps them in
 // step until each runs out of keys.  The softmax carry does not depend on
 // the order in which keys are folded in.
-// Striped walk: the first visited tile at or after (kt, t).  Blocks kb <= r
-// (ring steps t <= r) hold ceil(klen_lo / TN) tiles, blocks kb > r (steps
-// t > r) ceil(klen_hi / TN) <= that, so within round kt every step t <= r
-// is visited, a step t > r only while kt is below the smaller count, and the
-// walk ends with the larger count.
+// Striped walk: the first visited tile at or after (kt, t).  The steps of a
+// round visit the blocks kb < stripe_hi first (steps t < stripe_hi: blocks
+// r, r - 1, .., 0, then stripe_hi - 1, .., r + 1), then the shifted ones
+// (N - 1 down to stripe_hi); with stripe_hi = r + 1 (token causal, no mask)
+// this is the ring order, step t using block (r - t) mod N.  Unshifted
+// blocks hold ceil(klen_lo / TN) tiles, shifted ones ceil(klen_hi / TN) <=
+// that, so within round kt every step t < stripe_hi is visited, a later
+// step only while kt is below the smaller count, and the walk ends with the
+// larger count.
 template <int TN>
 __device__ __forceinline__ void striped_settle(const FwdParams& p, Cursor& c) {
   const int n_lo = (c.klen_lo + TN - 1) / TN, n_hi = (c.klen_hi + TN - 1) / TN;
-  if (c.t >= p.ring_size || (c.t > p.ring_index && c.kt >= n_hi)) {
+  if (c.t >= p.ring_size || (c.t >= p.stripe_hi && c.kt >= n_hi)) {
     c.t = 0;
     ++c.kt;
   }
@@ -128,18 +133,22 @@ __device__ __forceinline__ void striped_settle(const FwdParams& p, Cursor& c) {
     c.valid = 0;
     return;
   }
-  c.kb = p.ring_index - c.t;
-  if (c.kb < 0) c.kb += p.ring_size;
-  c.klen = c.t <= p.ring_index ? c.klen_lo : c.klen_hi;
-  c.ntile = c.t <= p.ring_index ? n_lo : n_hi;
+  if (c.t < p.stripe_hi) {
+    c.kb = p.ring_index - c.t;
+    if (c.kb < 0) c.kb += p.stripe_hi;
+  } else {
+    c.kb = p.ring_size - 1 + p.stripe_hi - c.t;
+  }
+  c.klen = c.t < p.stripe_hi ? c.klen_lo : c.klen_hi;
+  c.ntile = c.t < p.stripe_hi ? n_lo : n_hi;
   c.valid = 1;
 }
 
 template <int TN, bool STRIPED = false>
 __device__ __forceinline__ void cursor_seek(const FwdParams& p, Cursor& c, int64_t kend) {
   if (STRIPED) {
-    c.klen_lo = block_klen<true>(p, p.ring_index, kend);
-    c.klen_hi = p.ring_index + 1 < p.ring_size ? block_klen<true>(p, p.ring_index + 1, kend) : 0;
+    c.klen_lo = block_klen<true>(p, 0, kend);
+    c.klen_hi = p.stripe_hi < p.ring_size ? block_klen<true>(p, p.stripe_hi, kend) : 0;
     striped_settle<TN>(p, c);
     return;
   }
@@ -199,7 +208,7 @@ struct StripedCounts {
 
 template <int TN, bool STRIPED>
 __device__ __forceinline__ int64_t walk_tiles(const FwdParams& p, int64_t kend) {
-  return walk::walk_tiles(p.seq_q, p.ring_size, p.ring_index, STRIPED, TN, kend);
+  return walk::walk_tiles(p.seq_q, p.ring_size, p.stripe_hi, STRIPED, TN, kend);
 }
 
 // Runs of a walk of n tiles when the longest walk (n_max tiles) takes
@@ -210,7 +219,7 @@ __device__ __forceinline__ int split_runs(const FwdParams& p, int64_t n, int64_t
 
 template <int BM, int TN, bool STRIPED>
 __device__ __forceinline__ walk::Share share_of(const FwdParams& p) {
-  return walk::Share{p.seq_q, p.ring_size, p.ring_index, p.causal, STRIPED, BM, TN};
+  return walk::Share{p.seq_q, p.ring_size, p.ring_index, p.causal, STRIPED, BM, TN, p.stripe_hi};
 }
 
 // kend_max: the walk limit of the share's last query tile.
@@ -247,7 +256,7 @@ __device__ __forceinline__ void cursor_to(const FwdParams& p, Cursor& c, int64_t
   }
   if (!c.valid || pos <= c.pos) return;
   const StripedCounts sc{(c.klen_lo + TN - 1) / TN, (c.klen_hi + TN - 1) / TN};
-  const int n_lo = p.ring_index + 1, n_hi = p.ring_size - 1 - p.ring_index;
+  const int n_lo = p.stripe_hi, n_hi = p.ring_size - p.stripe_hi;
   const int full = min(sc.lo, sc.hi);
   const int64_t in_full = (int64_t)full * p.ring_size;
   int kt, t;
@@ -353,8 +362,11 @@ __device__ __forceinline__ WgCoord wg_coord_runs(const FwdParams& p) {
                  __builtin_amdgcn_readfirstlane(split)};
 }
 
-__device__ __forceinline__ void write_run_map(const FwdParams& p, int t, int qg0, int key0) {
+// Debug run map, in ring-step order: block kb arrives at step (r - kb) mod N
+// (the walk itself may visit the blocks in another order).
+__device__ __forceinline__ void write_run_map(const FwdParams& p, int kb, int qg0, int key0) {
   const int nqc = p.seq_q / p.q_chunk, nkc = p.seq_q / p.k_chunk;
+  const int t = p.ring_index - kb + (kb > p.ring_index ? p.ring_size : 0);
   p.run_map[((int64_t)t * nqc + qg0 / p.q_chunk) * nkc + key0 / p.k_chunk] = 1;
 }
 

@@ -141,10 +141,12 @@ namespace {
 // Returns RA_OK with `empty` set for a valid call that has nothing to do.
 ra_status_t prepare(const void* q, const void* k, const void* v, const int32_t* segment_ids,
                     int64_t causal_block_size, int64_t q_chunk, int64_t k_chunk,
-                    int32_t ring_size, int32_t ring_index, int64_t batch, int64_t seq_q,
-                    int64_t heads, int64_t head_dim, ra_dtype_t dtype, ra::FwdParams& p,
-                    bool& empty) {
+                    int32_t ring_size, int32_t ring_index, ra_placement_t placement,
+                    int64_t batch, int64_t seq_q, int64_t heads, int64_t head_dim,
+                    ra_dtype_t dtype, ra::FwdParams& p, bool& empty) {
   empty = false;
+  if (placement != RA_PLACE_CONTIGUOUS && placement != RA_PLACE_STRIPED)
+    return fail(RA_E_INVALID, "unknown placement %d", (int)placement);
   if (batch < 0 || heads < 0)
     return fail(RA_E_INVALID, "batch and heads must be >= 0 (got %lld, %lld)",
                 (long long)batch, (long long)heads);
@@ -152,6 +154,20 @@ ra_status_t prepare(const void* q, const void* k, const void* v, const int32_t* 
   ra_status_t st = check_ring(causal_block_size, q_chunk, k_chunk, seq_q, ring_size,
                               ring_index, true);
   if (st != RA_OK) return st;
+  // A causal block at least as long as the whole sequence puts every
+  // position in block 0: every key is visible, exactly as without a mask.
+  const int64_t seq_k = seq_q * ring_size;
+  const int64_t causal = causal_block_size >= seq_k ? 0 : causal_block_size;
+  // Striped placement: the kernels test visibility on key coordinates
+  // (walk::striped_causal), which exist when the causal block divides the
+  // ring size or is a multiple of it.
+  const ra::walk::StripedCausal sc = ra::walk::striped_causal(causal, ring_size, ring_index);
+  const bool striped = placement == RA_PLACE_STRIPED;
+  if (striped && !sc.ok)
+    return fail(RA_E_UNSUPPORTED,
+                "striped placement supports a causal_block_size that divides ring_size or is a "
+                "multiple of it (got %lld with ring_size %d)",
+                (long long)causal_block_size, ring_size);
   if (dtype != RA_BF16 && dtype != RA_F32)
     return fail(RA_E_UNSUPPORTED, "dtype %d is not supported (RA_BF16, RA_F32)", (int)dtype);
   if (head_dim != 64 && head_dim != 128)
@@ -176,15 +192,14 @@ ra_status_t prepare(const void* q, const void* k, const void* v, const int32_t* 
   if (n_wg > kInt32Max || batch > kInt32Max)
     return fail(RA_E_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)n_wg);
 
-  const int64_t seq_k = seq_q * ring_size;
   p = ra::FwdParams{};
   p.q = q;
   p.k = k;
   p.v = v;
   p.seg = segment_ids;
-  // A causal block at least as long as the whole sequence puts every
-  // position in block 0: every key is visible, exactly as without a mask.
-  p.causal = causal_block_size >= seq_k ? 0 : causal_block_size;
+  p.causal = striped ? sc.causal : causal;
+  p.striped = striped ? 1 : 0;
+  p.stripe_hi = striped ? sc.stripe_hi : ring_index + 1;
   p.seq_q = (int32_t)seq_q;
   p.seq_k = (int32_t)seq_k;
   p.q_chunk = (int32_t)q_chunk;
@@ -203,14 +218,18 @@ ra_status_t prepare(const void* q, const void* k, const void* v, const int32_t* 
 // Largest number of key splits a call accepts.
 constexpr int32_t kMaxKeySplits = 64;
 
+// The walk terms of a prepared call (the kernels build the same from the
+// parameters they receive).
+ra::walk::Share share_of(const ra::FwdParams& p, int64_t bm, int64_t tn) {
+  return ra::walk::Share{p.seq_q,      p.ring_size, p.ring_index, p.causal,    p.striped != 0,
+                         (int32_t)bm, (int32_t)tn, p.stripe_hi};
+}
+
 // Workgroups per (batch, head) of a launch with P key splits: the runs of
 // every query tile's walk, counted by the same functions the kernels map
-// workgroups with (ra_walk.h).  c: effective causal block size.
-int64_t split_wgs_host(int32_t P, int64_t seq_q, int32_t ring_size, int32_t ring_index, int64_t c,
-                       bool striped, int64_t bm, int64_t tn) {
-  const ra::walk::Share sh{(int32_t)seq_q, ring_size, ring_index, c, striped, (int32_t)bm,
-                           (int32_t)tn};
-  return ra::walk::split_wgs(sh, P);
+// workgroups with (ra_walk.h).
+int64_t split_wgs_host(int32_t P, const ra::FwdParams& p, int64_t bm, int64_t tn) {
+  return ra::walk::split_wgs(share_of(p, bm, tn), P);
 }
 
 int64_t split_workspace_bytes(int64_t batch, int64_t seq_q, int64_t heads, int64_t head_dim,
@@ -233,22 +252,12 @@ ra_status_t ra_blockwise_attn_fwd_split(const void* q, const void* k, const void
                                         void* workspace, int64_t workspace_bytes,
                                         void* stream) {
   clear_error();
-  if (placement != RA_PLACE_CONTIGUOUS && placement != RA_PLACE_STRIPED)
-    return fail(RA_E_INVALID, "unknown placement %d", (int)placement);
-  // The kernels express striped token-causal visibility as a per-block
-  // shift of the key index (key j of block kb is visible from row i iff
-  // j + [kb > r] <= i); coarser causal blocks have no such form.
-  if (placement == RA_PLACE_STRIPED && causal_block_size > 1 &&
-      causal_block_size < seq_q * (int64_t)ring_size)
-    return fail(RA_E_UNSUPPORTED,
-                "striped placement supports causal_block_size 0 or 1 (got %lld)",
-                (long long)causal_block_size);
   if (key_splits < 1 || key_splits > kMaxKeySplits)
     return fail(RA_E_INVALID, "key_splits %d outside [1, %d]", key_splits, kMaxKeySplits);
   ra::FwdParams p;
   bool empty = false;
   ra_status_t st = prepare(q, k, v, segment_ids, causal_block_size, q_chunk, k_chunk, ring_size,
-                           ring_index, batch, seq_q, heads, head_dim, dtype, p, empty);
+                           ring_index, placement, batch, seq_q, heads, head_dim, dtype, p, empty);
   if (st != RA_OK || empty) return st;
   if (!out || !lse) return fail(RA_E_INVALID, "out and lse must be non-NULL");
   if (!aligned(out, 16) || !aligned(lse, 4))
@@ -263,9 +272,7 @@ ra_status_t ra_blockwise_attn_fwd_split(const void* q, const void* k, const void
     // One workgroup per run of every query tile's walk (heavier walks are
     // cut into more runs), none idle.
     const int64_t bm = ra::block_rows(dtype == RA_BF16 ? ra::Dtype::BF16 : ra::Dtype::F32);
-    const int64_t wgs = split_wgs_host(key_splits, seq_q, ring_size, ring_index, p.causal,
-                                       placement == RA_PLACE_STRIPED, bm,
-                                       dtype == RA_BF16 ? 64 : 32);
+    const int64_t wgs = split_wgs_host(key_splits, p, bm, dtype == RA_BF16 ? 64 : 32);
     const int64_t n_wg = batch * heads * wgs;
     if (n_wg > kInt32Max || wgs > kInt32Max)
       return fail(RA_E_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)n_wg);
@@ -278,7 +285,6 @@ ra_status_t ra_blockwise_attn_fwd_split(const void* q, const void* k, const void
   p.out = out;
   p.lse = lse;
   p.run_map = run_map;
-  p.striped = placement == RA_PLACE_STRIPED ? 1 : 0;
   const int64_t map_bytes =
       run_map ? (int64_t)ring_size * (seq_q / q_chunk) * (seq_q / k_chunk) : 0;
   const ra::Dtype dt = dtype == RA_BF16 ? ra::Dtype::BF16 : ra::Dtype::F32;
@@ -339,12 +345,20 @@ int32_t ra_blockwise_attn_fwd_key_splits(int64_t batch, int64_t seq_q, int64_t h
   const int64_t seq_k = seq_q * ring_size;
   const bool striped = placement == RA_PLACE_STRIPED;
   const int64_t c = causal_block_size >= seq_k ? 0 : causal_block_size;
+  const ra::walk::StripedCausal sc = ra::walk::striped_causal(c, ring_size, ring_index);
+  if (striped && !sc.ok) return 1;  // such calls are refused anyway
+  ra::FwdParams p{};
+  p.seq_q = (int32_t)seq_q;
+  p.ring_size = ring_size;
+  p.ring_index = ring_index;
+  p.causal = striped ? sc.causal : c;
+  p.striped = striped ? 1 : 0;
+  p.stripe_hi = striped ? sc.stripe_hi : ring_index + 1;
   const int64_t tn = dtype == RA_BF16 ? 64 : 32;
-  const ra::walk::Share sh64{(int32_t)seq_q, ring_size, ring_index, c, striped, (int32_t)bm, 64};
-  const int64_t n_max64 = ra::walk::qtile_walk(sh64, (int32_t)n_qtiles - 1);
+  const int64_t n_max64 = ra::walk::qtile_walk(share_of(p, bm, 64), (int32_t)n_qtiles - 1);
   int64_t best = 1;
   for (int32_t P = 2; P <= std::min<int64_t>(kMaxKeySplits, n_max64 / 4); ++P) {
-    const int64_t wgs = split_wgs_host(P, seq_q, ring_size, ring_index, c, striped, bm, tn);
+    const int64_t wgs = split_wgs_host(P, p, bm, tn);
     if (batch * heads * wgs > compute_units) break;
     best = P;
   }
@@ -385,19 +399,13 @@ ra_status_t ra_blockwise_attn_bwd_split(const void* q, const void* k, const void
                                         void* workspace, int64_t workspace_bytes,
                                         void* stream) {
   clear_error();
-  if (placement != RA_PLACE_CONTIGUOUS && placement != RA_PLACE_STRIPED)
-    return fail(RA_E_INVALID, "unknown placement %d", (int)placement);
-  if (placement == RA_PLACE_STRIPED && causal_block_size > 1 &&
-      causal_block_size < seq_q * (int64_t)ring_size)
-    return fail(RA_E_UNSUPPORTED,
-                "striped placement supports causal_block_size 0 or 1 (got %lld)",
-                (long long)causal_block_size);
   if (key_splits < 1 || key_splits > kMaxKeySplits)
     return fail(RA_E_INVALID, "key_splits %d outside [1, %d]", key_splits, kMaxKeySplits);
   ra::BwdParams bp{};
   bool empty = false;
   ra_status_t st = prepare(q, k, v, segment_ids, causal_block_size, q_chunk, k_chunk, ring_size,
-                           ring_index, batch, seq_q, heads, head_dim, dtype, bp.f, empty);
+                           ring_index, placement, batch, seq_q, heads, head_dim, dtype, bp.f,
+                           empty);
   if (st != RA_OK) return st;
   if (dtype != RA_BF16)
     return fail(RA_E_UNSUPPORTED, "the backward takes bf16 inputs only");
@@ -418,8 +426,7 @@ ra_status_t ra_blockwise_attn_bwd_split(const void* q, const void* k, const void
                   (long long)workspace_bytes, (long long)need);
     // The dq kernel: one workgroup per run of every query tile's walk, as in
     // the forward.
-    const int64_t wgs = split_wgs_host(key_splits, seq_q, ring_size, ring_index, bp.f.causal,
-                                       placement == RA_PLACE_STRIPED, ra::kBlockMBf16, 64);
+    const int64_t wgs = split_wgs_host(key_splits, bp.f, ra::kBlockMBf16, 64);
     const int64_t n_wg = batch * heads * wgs;
     if (n_wg > kInt32Max || wgs > kInt32Max)
       return fail(RA_E_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)n_wg);
@@ -428,7 +435,6 @@ ra_status_t ra_blockwise_attn_bwd_split(const void* q, const void* k, const void
     bp.f.key_splits = key_splits;
     bp.dq_part = static_cast<float*>(workspace);
   }
-  bp.f.striped = placement == RA_PLACE_STRIPED ? 1 : 0;
   bp.out = out;
   bp.lse = lse;
   bp.dout = dout;

@@ -28,7 +28,10 @@ struct FwdParams {
   int32_t n_qtiles;     // query tiles per (batch, head)
   int32_t n_wg;         // workgroups in the grid
   float scale_log2;     // log2(e) / sqrt(head_dim)
-  int32_t striped;      // 1: striped placement (causal is then 0 or 1)
+  int32_t striped;      // 1: striped placement (causal is then in key coordinates)
+  // Striped placement: blocks kb >= stripe_hi have key coordinates from 1
+  // (walk::striped_causal); the host sets it for contiguous calls too.
+  int32_t stripe_hi;
   // Key splits (>= 1).  With more than one, every query tile's key walk is
   // cut into key_splits runs, one workgroup each; they write partial
   // results and a combine kernel folds them into out and lse.

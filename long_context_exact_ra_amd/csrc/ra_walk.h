@@ -11,8 +11,12 @@
 // every key/value block, the keys up to its causal limit, rounded up to whole
 // 32-key sub-tiles, in tiles of tn keys ("3. 因果注意力掩码支持" skips the
 // rest).  Key coordinates: contiguous placement, key j of block kb has
-// coordinate kb * Lq + j; striped placement (token causal), j + [kb > r],
-// with query row i's limit i + 1.
+// coordinate kb * Lq + j and query row i has coordinate r * Lq + i.  Striped
+// placement (query row i of device r at position i * N + r, key j of block
+// kb at j * N + kb): query row i has coordinate i and key j of block kb has
+// coordinate j + [kb >= stripe_hi], with the causal block c' below
+// (striped_causal), so that floor(i N + r, c) >= floor(j N + kb, c) holds
+// exactly when floor(i / c') >= floor((j + [kb >= stripe_hi]) / c').
 #pragma once
 
 #include <stdint.h>
@@ -21,6 +25,34 @@ namespace ra {
 namespace walk {
 
 constexpr int64_t kNoLimit = INT64_MAX;
+
+// Striped placement with causal block c (0 < c < N Lq), in coordinates.
+//  * c divides N: floor((i N + r) / c) = i N / c + floor(r / c), so key j of
+//    block kb is visible from row i iff i > j, or i = j and floor(kb / c) <=
+//    floor(r / c): token causal (c' = 1) on the coordinates i and j + [kb >=
+//    stripe_hi] with stripe_hi = (floor(r / c) + 1) c.  c = 1 gives the
+//    token-causal rule j + [kb > r] <= i.
+//  * N divides c: floor((i N + r) / c) = floor(i / (c / N)) because r < N,
+//    and the same for keys: block causal with c' = c / N on the local
+//    indices, the same in every block (stripe_hi = N: no shift).
+//  * Any other c mixes the two and has no such form: not supported.
+// c = 0 (no mask): c' = 0, and the shift of blocks kb > r is kept (it only
+// orders the walk).
+struct StripedCausal {
+  int64_t causal;     // c' (0: no mask)
+  int32_t stripe_hi;  // blocks kb >= stripe_hi have coordinates from 1
+  bool ok;            // c is 0, divides N or is a multiple of N
+};
+
+constexpr StripedCausal striped_causal(int64_t c, int32_t ring_size, int32_t ring_index) {
+  if (c <= 0) return StripedCausal{0, ring_index + 1, true};
+  if (c <= ring_size) {
+    if (ring_size % c != 0) return StripedCausal{0, 0, false};
+    return StripedCausal{1, (int32_t)((ring_index / c + 1) * c), true};
+  }
+  if (c % ring_size != 0) return StripedCausal{0, 0, false};
+  return StripedCausal{c / ring_size, ring_size, true};
+}
 
 // First key coordinate no row of the query tile [m0, m0 + bm) can see
 // (kNoLimit when non-causal; c is the effective causal block size, below
@@ -35,9 +67,9 @@ constexpr int64_t tile_kend(int64_t c, int32_t seq_q, int32_t ring_index, bool s
   return ((int64_t)(q_last / cc) + 1) * cc;
 }
 
-// Coordinate of block kb's first key.
-constexpr int32_t block_vbase(int32_t seq_q, int32_t ring_index, bool striped, int32_t kb) {
-  return striped ? (kb > ring_index ? 1 : 0) : kb * seq_q;
+// Coordinate of block kb's first key (stripe_hi: striped placement only).
+constexpr int32_t block_vbase(int32_t seq_q, int32_t stripe_hi, bool striped, int32_t kb) {
+  return striped ? (kb >= stripe_hi ? 1 : 0) : kb * seq_q;
 }
 
 // Keys of a block (first key at coordinate vbase) before kend, rounded up
@@ -54,14 +86,14 @@ constexpr int32_t ceil_div(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
 // Tiles of tn keys in the walk up to kend, in closed form.  Contiguous:
 // the blocks before kend / Lq are whole, the next one is cut at kend, the
-// rest are empty.  Striped: blocks kb <= r (r + 1 of them) and kb > r
-// (N - 1 - r) each have one count.
-constexpr int64_t walk_tiles(int32_t seq_q, int32_t ring_size, int32_t ring_index, bool striped,
+// rest are empty.  Striped: blocks kb < stripe_hi (stripe_hi of them) and
+// kb >= stripe_hi (N - stripe_hi) each have one count.
+constexpr int64_t walk_tiles(int32_t seq_q, int32_t ring_size, int32_t stripe_hi, bool striped,
                              int32_t tn, int64_t kend) {
   if (striped) {
     const int32_t lo = ceil_div(block_klen(seq_q, 0, kend), tn);
     const int32_t hi = ceil_div(block_klen(seq_q, 1, kend), tn);
-    return (int64_t)(ring_index + 1) * lo + (int64_t)(ring_size - 1 - ring_index) * hi;
+    return (int64_t)stripe_hi * lo + (int64_t)(ring_size - stripe_hi) * hi;
   }
   const int32_t full = ceil_div(seq_q, tn);
   if (kend >= (int64_t)ring_size * seq_q) return (int64_t)ring_size * full;
@@ -81,15 +113,16 @@ constexpr int32_t split_runs(int32_t P, int64_t n, int64_t n_max) {
 // Everything the run count of one query tile depends on.
 struct Share {
   int32_t seq_q, ring_size, ring_index;
-  int64_t causal;  // effective causal block size, 0 = none
+  int64_t causal;  // effective causal block size (striped: c' in coordinates), 0 = none
   bool striped;
-  int32_t bm, tn;  // rows per query tile, keys per key tile
+  int32_t bm, tn;     // rows per query tile, keys per key tile
+  int32_t stripe_hi;  // striped placement: the first shifted block
 };
 
 constexpr int32_t n_qtiles(const Share& s) { return ceil_div(s.seq_q, s.bm); }
 
 constexpr int64_t qtile_walk(const Share& s, int32_t qt) {
-  return walk_tiles(s.seq_q, s.ring_size, s.ring_index, s.striped, s.tn,
+  return walk_tiles(s.seq_q, s.ring_size, s.stripe_hi, s.striped, s.tn,
                     tile_kend(s.causal, s.seq_q, s.ring_index, s.striped, qt * s.bm, s.bm));
 }
 

@@ -142,7 +142,15 @@ def test_placed_validation_without_gpu():
     call = lambda c, place, batch=1: lib.ra_blockwise_attn_fwd_placed(
         None, None, None, None, c, 32, 32, 4, 1, place, batch, 32, 1, 128, ra.RA_BF16,
         None, None, None, None)
-    assert call(2, ra.RA_PLACE_STRIPED) == ra.RA_E_UNSUPPORTED
+    # N = 4: causal blocks that divide 4 or are multiples of it are served,
+    # others have no form on key coordinates and are refused, even when
+    # empty; accepted masks get as far as the null tensors.
+    for c in (3, 6, 10):
+        assert call(c, ra.RA_PLACE_STRIPED) == ra.RA_E_UNSUPPORTED
+        assert "divides ring_size" in ra.last_error()
+        assert call(c, ra.RA_PLACE_STRIPED, batch=0) == ra.RA_E_UNSUPPORTED
+    for c in (2, 4, 8, 12):
+        assert call(c, ra.RA_PLACE_STRIPED) == ra.RA_E_INVALID
     assert call(1, 7) == ra.RA_E_INVALID
     assert call(1, ra.RA_PLACE_STRIPED, batch=0) == ra.RA_OK      # empty call
     assert call(128, ra.RA_PLACE_STRIPED, batch=0) == ra.RA_OK    # block >= sequence: non-causal
@@ -156,7 +164,9 @@ def test_bwd_placed_validation_without_gpu():
     call = lambda c, place, batch=1: lib.ra_blockwise_attn_bwd_placed(
         None, None, None, None, c, 32, 32, 4, 1, place, batch, 32, 1, 128, ra.RA_BF16,
         None, None, None, None, None, None, None, None)
-    assert call(2, ra.RA_PLACE_STRIPED) == ra.RA_E_UNSUPPORTED
+    assert call(3, ra.RA_PLACE_STRIPED) == ra.RA_E_UNSUPPORTED
+    assert call(2, ra.RA_PLACE_STRIPED) == ra.RA_E_INVALID  # served; null tensors
+    assert call(8, ra.RA_PLACE_STRIPED) == ra.RA_E_INVALID
     assert call(1, 5) == ra.RA_E_INVALID
     assert call(1, ra.RA_PLACE_STRIPED, batch=0) == ra.RA_OK
     assert call(1, ra.RA_PLACE_STRIPED) == ra.RA_E_INVALID  # null tensors
@@ -206,6 +216,12 @@ def test_key_split_recommendation():
     # workgroups for the 8 heads; 13 would need more than 256.
     assert ks(1, 1024, 8, ra.RA_BF16, 1, 8, 0, pl="striped") == 12
     assert ks(1, 1024, 8, ra.RA_BF16, 1, 8, 7, pl="striped") == 12
+    # striped with a causal block of 2 positions on 8 devices: token causal
+    # on coordinates, ring position 0 shifts blocks 2..7 (stripe_hi 2), the
+    # same walk lengths as c = 1 at position 1; a block of 3 is refused
+    assert ks(1, 1024, 8, ra.RA_BF16, 2, 8, 0, pl="striped") == \
+        ks(1, 1024, 8, ra.RA_BF16, 1, 8, 1, pl="striped")
+    assert ks(1, 1024, 8, ra.RA_BF16, 3, 8, 0, pl="striped") == 1
 
 
 def test_bwd_split_validation_without_gpu():

@@ -152,15 +152,12 @@ def pin_striped_lazy_any_order():
         np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
 
 
-def pin_striped_backward_stitching():
-    """Striped backward: each device's dq rows and its dk/dv addends, summed
-    over devices and put back in natural order, equal torch float64
-    autograd through SDPA on the whole sequence."""
-    B, N, Lq, H, D = 1, 3, 8, 2, 8
+def _striped_backward_case(N, Lq, c, seed):
+    B, H, D = 1, 2, 8
     S = N * Lq
-    q, k, v, g = (_rand((B, S, H, D), s) for s in (600, 601, 602, 603))
+    q, k, v, g = (_rand((B, S, H, D), seed + i) for i in range(4))
     tq, tk, tv = (torch.from_numpy(x).permute(0, 2, 1, 3).requires_grad_() for x in (q, k, v))
-    mask = torch.tril(torch.ones(S, S, dtype=torch.bool))
+    mask = _block_causal_mask(S, c)
     o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask)
     o.backward(torch.from_numpy(g).permute(0, 2, 1, 3))
     rq, rk, rv = (t.grad.permute(0, 2, 1, 3).numpy() for t in (tq, tk, tv))
@@ -169,13 +166,24 @@ def pin_striped_backward_stitching():
     dv_sum = np.zeros_like(vs)
     for r in range(N):
         sl = slice(r * Lq, (r + 1) * Lq)
-        dq, dk, dv = ob.attention_bwd(qs[:, sl], ks, vs, gs[:, sl], None, 1, N, r,
+        dq, dk, dv = ob.attention_bwd(qs[:, sl], ks, vs, gs[:, sl], None, c, N, r,
                                       placement="striped")
         np.testing.assert_allclose(dq, rq[:, r::N], rtol=0, atol=1e-12)
         dk_sum += dk
         dv_sum += dv
     np.testing.assert_allclose(dk_sum, _to_striped(rk, N), rtol=0, atol=1e-12)
     np.testing.assert_allclose(dv_sum, _to_striped(rv, N), rtol=0, atol=1e-12)
+
+
+def pin_striped_backward_stitching():
+    """Striped backward: each device's dq rows and its dk/dv addends, summed
+    over devices and put back in natural order, equal torch float64
+    autograd through SDPA on the whole sequence: token causal, a causal
+    block dividing N, one that is a multiple of N, and one that is neither."""
+    _striped_backward_case(3, 8, 1, 600)
+    _striped_backward_case(4, 8, 2, 610)
+    _striped_backward_case(3, 8, 6, 620)
+    _striped_backward_case(4, 6, 3, 630)
 
 
 STRIPED_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -260,6 +260,26 @@ def test_bwd_striped_edge(case):
     _full_case(w, r)
 
 
+STRIPED_BLOCK_EDGE = [
+    # B, Lq, N, H, D, causal, qc, kc, segments, r: the causal block divides
+    # N (token causal on shifted coordinates) or is a multiple of it (block
+    # causal on the local rows)
+    (1, 128, 4, 2, 128, 2, 32, 32, False, 1),
+    (1, 96, 8, 2, 64, 4, 32, 32, False, 5),
+    (2, 128, 4, 2, 128, 8, 64, 32, True, 2),
+    (1, 160, 2, 2, 128, 6, 32, 32, False, 1),
+    (1, 288, 3, 2, 128, 96, 32, 32, False, 2),  # 256-key workgroups span blocks
+]
+
+
+@pytest.mark.parametrize("case", STRIPED_BLOCK_EDGE, ids=[str(c) for c in STRIPED_BLOCK_EDGE])
+def test_bwd_striped_block_causal(case):
+    B, Lq, N, H, D, c, qc, kc, segs, r = case
+    w = workloads.Workload(f"striped_block{case}", B, Lq, N, (r,), H, D, "bf16", c, qc, kc,
+                           segments=segs, seed=5252 + Lq + D + N + c, placement="striped")
+    _full_case(w, r)
+
+
 def test_bwd_share_7b_striped_sampled():
     """The 7B-shaped striped share at ring position 15: dq on sampled rows
     of one head against the oracle, dk and dv through the invariants."""
@@ -322,6 +342,8 @@ SPLIT_EDGE = [
     (2, 128, 2, 2, 128, 1, 64, 64, True, 1, "contiguous", 4),
     (1, 512, 3, 1, 128, 64, 128, 128, True, 2, "contiguous", 7),
     (2, 128, 4, 2, 64, 1, 64, 32, True, 2, "striped", 6),
+    (1, 256, 4, 2, 128, 2, 64, 64, False, 1, "striped", 5),
+    (2, 128, 2, 2, 128, 8, 64, 32, True, 1, "striped", 3),
     (1, 32, 4, 1, 128, 1, 32, 32, False, 3, "contiguous", 64),   # splits >> tiles
 ]
 

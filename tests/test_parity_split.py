@@ -110,6 +110,8 @@ SPLIT_EDGE = [
     (2, 64, 3, 3, 64, "f32", 5, 32, 32, True, "contiguous", 3),
     (1, 32, 1, 1, 128, "bf16", 1, 32, 32, False, "contiguous", 64),   # splits >> tiles
     (1, 64, 4, 2, 64, "f32", None, 32, 32, False, "striped", 64),
+    (1, 256, 4, 2, 128, "bf16", 2, 64, 64, False, "striped", 5),
+    (2, 128, 2, 2, 128, "bf16", 8, 64, 64, True, "striped", 4),
 ]
 
 

@@ -62,6 +62,16 @@ EDGE = [
     (1, 64, 4, 2, 64, "f32", 1, 32, 32, False, 2),
     (1, 96, 3, 2, 128, "f32", 1, 32, 32, True, 0),
     (1, 160, 2, 2, 128, "bf16", 100000, 32, 32, False, 1),
+    # block causal: c divides N (token causal on shifted coordinates) ...
+    (1, 128, 4, 2, 128, "bf16", 2, 32, 32, False, 1),
+    (1, 128, 4, 2, 128, "bf16", 2, 64, 32, True, 3),
+    (1, 96, 8, 2, 64, "bf16", 4, 32, 32, False, 5),
+    (1, 64, 4, 2, 64, "f32", 4, 32, 32, False, 2),
+    # ... or is a multiple of N (block causal on the local rows)
+    (2, 128, 4, 2, 128, "bf16", 8, 64, 32, True, 2),
+    (1, 160, 2, 2, 128, "bf16", 6, 32, 32, False, 1),
+    (1, 96, 3, 2, 64, "bf16", 96, 32, 32, False, 1),
+    (1, 96, 3, 2, 128, "f32", 12, 32, 32, False, 0),
 ]
 
 
@@ -121,9 +131,12 @@ def test_share_7b_striped_sampled():
         torch.cuda.empty_cache()
 
 
-def test_striped_rejects_block_causal():
+def test_striped_rejects_block_causal_without_coordinates():
+    """A causal block that neither divides the ring size nor is a multiple
+    of it has no form on key coordinates: refused before any launch."""
     q = torch.zeros((1, 64, 1, 128), dtype=torch.bfloat16, device=DEV)
-    k = torch.zeros((1, 128, 1, 128), dtype=torch.bfloat16, device=DEV)
-    with pytest.raises(ra.RaError) as e:
-        ra.blockwise_attn_fwd(q, k, k, None, 2, 32, 32, 2, 1, placement=STRIPED)
-    assert e.value.status == ra.RA_E_UNSUPPORTED
+    k = torch.zeros((1, 256, 1, 128), dtype=torch.bfloat16, device=DEV)
+    for c in (3, 6, 10):
+        with pytest.raises(ra.RaError) as e:
+            ra.blockwise_attn_fwd(q, k, k, None, c, 32, 32, 4, 1, placement=STRIPED)
+        assert e.value.status == ra.RA_E_UNSUPPORTED

@@ -66,19 +66,27 @@ int main() {
         for (int striped = 0; striped < 2; ++striped) {
           const int64_t S = (int64_t)Lq * N;
           std::vector<int64_t> cs = {0, 1};
-          if (!striped)
-            for (int64_t c : std::vector<int64_t>{2, 5, 37, 64, 100, (int64_t)Lq, 3 * (int64_t)Lq / 2, S - 1, S,
-                              2 * S})
-              cs.push_back(c);
-          else
-            cs.push_back(S);  // a causal block covering the sequence
+          for (int64_t c : std::vector<int64_t>{2, 3, 4, 5, 8, 10, 37, 64, 100, (int64_t)Lq,
+                                                3 * (int64_t)Lq / 2, 2 * (int64_t)N, 4 * (int64_t)N,
+                                                (int64_t)Lq * N / 2, S - 1, S, 2 * S})
+            cs.push_back(c);
           for (int64_t c_raw : cs) {
             // the host passes c >= S as "no mask"
-            const int64_t c = c_raw >= S ? 0 : c_raw;
+            const int64_t c0 = c_raw >= S ? 0 : c_raw;
+            // Striped placement: the causal block in key coordinates, for
+            // the blocks that have one (c divides N or is a multiple of it).
+            const w::StripedCausal sc = w::striped_causal(c0, N, r);
+            const bool supported = c0 == 0 || N % c0 == 0 || c0 % N == 0;
+            CHECK(!striped || sc.ok == supported, "striped_causal ok N %d c %lld", N,
+                  (long long)c0);
+            if (striped && !sc.ok) continue;
+            const int64_t c = striped ? sc.causal : c0;
+            const int32_t shi = striped ? sc.stripe_hi : r + 1;
+            CHECK(shi > r && shi <= N, "stripe_hi %d r %d N %d", shi, r, N);
             for (int32_t bm : {128, 256})
               for (int32_t tn : {32, 64}) {
                 ++configs;
-                const w::Share sh{Lq, N, r, c, striped != 0, bm, tn};
+                const w::Share sh{Lq, N, r, c, striped != 0, bm, tn, shi};
                 const int32_t nq = w::n_qtiles(sh);
                 CHECK(nq == (Lq + bm - 1) / bm, "n_qtiles");
                 std::vector<int64_t> walks(nq);
@@ -90,7 +98,7 @@ int main() {
                   for (int32_t kb = 0; kb < N; ++kb) {
                     const int64_t bf = brute_klen(Lq, N, r, striped != 0, c_raw, last_row, kb);
                     const int32_t got =
-                        w::block_klen(Lq, w::block_vbase(Lq, r, striped != 0, kb), kend);
+                        w::block_klen(Lq, w::block_vbase(Lq, shi, striped != 0, kb), kend);
                     CHECK(got == bf, "Lq %d N %d r %d striped %d c %lld bm %d qt %d kb %d: %d vs %lld",
                           Lq, N, r, striped, (long long)c_raw, bm, qt, kb, got, (long long)bf);
                     n_bf += (bf + tn - 1) / tn;
@@ -99,7 +107,7 @@ int main() {
                   CHECK(walks[qt] == n_bf, "walk Lq %d N %d r %d striped %d c %lld bm %d tn %d qt %d: %lld vs %lld",
                         Lq, N, r, striped, (long long)c_raw, bm, tn, qt, (long long)walks[qt],
                         (long long)n_bf);
-                  CHECK(walks[qt] == w::walk_tiles(Lq, N, r, striped != 0, tn, kend), "walk");
+                  CHECK(walks[qt] == w::walk_tiles(Lq, N, shi, striped != 0, tn, kend), "walk");
                 }
                 for (int32_t P = 1; P <= 64; P = P < 16 ? P + 1 : P * 2) {
                   int32_t prev = 0;
