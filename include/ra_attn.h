@@ -271,8 +271,10 @@ ra_status_t ra_blockwise_attn_fwd_split_noalloc(const void* q, const void* k,
  * fit one workgroup per compute unit, at most one per 4
  * key tiles of 64 keys of the longest walk (the share's last query tile's:
  * its blocks' keys up to its causal limit), and at most 64.  The dq kernel
- * of ra_blockwise_attn_bwd_split launches the same runs (256 query rows,
- * 64-key tiles), so for RA_BF16 the count serves the backward as well.
+ * of ra_blockwise_attn_bwd_split launches the same runs (the forward's
+ * query rows per workgroup and key tiles of the dtype: 256 rows and 64
+ * keys for RA_BF16, 128 and 32 for RA_F32), so the count serves the
+ * backward as well.
  * Host-only; invalid arguments give 1. */
 int32_t ra_blockwise_attn_fwd_key_splits(int64_t batch, int64_t seq_q, int64_t heads,
                                          ra_dtype_t dtype, int64_t causal_block_size,
@@ -304,13 +306,13 @@ int32_t ra_blockwise_attn_fwd_key_splits(int64_t batch, int64_t seq_q, int64_t h
  *       blocks as they pass); keys that no local query sees get 0.
  *   delta: [batch, heads, seq_q] float32, written (the row terms above).
  *
- * Arithmetic: the scores, p and ds are float32; p and ds are rounded to
- * bf16 (round to nearest even) as operands of the bf16 matrix products,
- * which accumulate in float32.
+ * Arithmetic: the scores, p and ds are float32.  RA_BF16: p and ds are
+ * rounded to bf16 (round to nearest even) as operands of the bf16 matrix
+ * products, which accumulate in float32.  RA_F32: every operand stays
+ * float32 (float32 matrix products).
  *
  * Errors as for ra_blockwise_attn_fwd, plus RA_E_INVALID for a null out,
- * lse, dout, dq, dk, dv or delta, and RA_E_UNSUPPORTED for RA_F32 (the
- * backward takes bf16 inputs only).  Ownership, streams and threading as
+ * lse, dout, dq, dk, dv or delta.  Ownership, streams and threading as
  * for the forward.
  */
 ra_status_t ra_blockwise_attn_bwd(const void* q, const void* k, const void* v,

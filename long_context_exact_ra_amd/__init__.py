@@ -277,8 +277,8 @@ def blockwise_attn_bwd(q, k, v, out, lse, dout, segment_ids=None,
     """Backward of ring position ``ring_index``: returns (dq, dk, dv, delta).
 
     q, k, v, segment_ids and the mask arguments as for blockwise_attn_fwd
-    (bfloat16 only); out and lse are that forward's outputs and dout the
-    upstream gradient of out ([B, Lq, H, D], bfloat16).  dq [B, Lq, H, D],
+    (bfloat16 or float32); out and lse are that forward's outputs and dout
+    the upstream gradient of out ([B, Lq, H, D], q's dtype).  dq [B, Lq, H, D],
     dk, dv [B, ring_size * Lq, H, D] and delta [B, H, Lq] are float32 and
     allocated when not given; dk and dv hold this share's contribution.
     placement: as for blockwise_attn_fwd (dk, dv and segment_ids in storage
@@ -288,11 +288,12 @@ def blockwise_attn_bwd(q, k, v, out, lse, dout, segment_ids=None,
     """
     import torch
     lib = load_library()
-    if q.dtype != torch.bfloat16:
-        raise TypeError("the backward takes bfloat16 inputs")
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("the backward takes bfloat16 or float32 inputs")
+    dt = RA_BF16 if q.dtype == torch.bfloat16 else RA_F32
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
-        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
-            raise ValueError(f"{name} must be a contiguous 4-D bfloat16 device tensor")
+        if t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-D device tensor of q's dtype")
     B, Lq, H, D = q.shape
     S = ring_size * Lq
     if tuple(k.shape) != (B, S, H, D) or k.shape != v.shape:
@@ -323,11 +324,11 @@ def blockwise_attn_bwd(q, k, v, out, lse, dout, segment_ids=None,
     sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     if key_splits == "auto":
         cus = torch.cuda.get_device_properties(q.device).multi_processor_count
-        key_splits = fwd_key_splits(B, Lq, H, RA_BF16, causal_block_size, ring_size,
+        key_splits = fwd_key_splits(B, Lq, H, dt, causal_block_size, ring_size,
                                     ring_index, cus, placement)
     key_splits = int(key_splits)
     args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), seg_ptr, int(causal_block_size or 0),
-            q_chunk, k_chunk, ring_size, ring_index, _placement(placement), B, Lq, H, D, RA_BF16,
+            q_chunk, k_chunk, ring_size, ring_index, _placement(placement), B, Lq, H, D, dt,
             out.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
             dv.data_ptr(), delta.data_ptr()]
     if key_splits != 1:

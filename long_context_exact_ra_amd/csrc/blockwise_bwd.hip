@@ -126,8 +126,9 @@ __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
 // delta_i = <dout_i, out_i>
 // ---------------------------------------------------------------------------
 
-// 16 lanes per row of D = 128 (8 for D = 64), 8 bf16 values each.
-template <int D>
+// 16 lanes per row of D = 128 (8 for D = 64), 8 values each (T: __bf16 or
+// float, the input dtype; the sum is float32).
+template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const BwdParams bp) {
   constexpr int LPR = D / 8;  // lanes per row
   const FwdParams& p = bp.f;
@@ -136,12 +137,24 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const BwdParams bp) {
   const int part = threadIdx.x % LPR;
   float acc = 0.f;
   if (row < rows) {
-    const __bf16* o = static_cast<const __bf16*>(bp.out) + row * D + part * 8;
-    const __bf16* g = static_cast<const __bf16*>(bp.dout) + row * D + part * 8;
-    const bf16x8_t ov = *reinterpret_cast<const bf16x8_t*>(o);
-    const bf16x8_t gv = *reinterpret_cast<const bf16x8_t*>(g);
+    const T* o = static_cast<const T*>(bp.out) + row * D + part * 8;
+    const T* g = static_cast<const T*>(bp.dout) + row * D + part * 8;
+    if constexpr (std::is_same<T, __bf16>::value) {
+      const bf16x8_t ov = *reinterpret_cast<const bf16x8_t*>(o);
+      const bf16x8_t gv = *reinterpret_cast<const bf16x8_t*>(g);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc = __builtin_fmaf((float)ov[i], (float)gv[i], acc);
+      for (int i = 0; i < 8; ++i) acc = __builtin_fmaf((float)ov[i], (float)gv[i], acc);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float4 ov = *reinterpret_cast<const float4*>(o + 4 * u);
+        const float4 gv = *reinterpret_cast<const float4*>(g + 4 * u);
+        acc = __builtin_fmaf(ov.x, gv.x, acc);
+        acc = __builtin_fmaf(ov.y, gv.y, acc);
+        acc = __builtin_fmaf(ov.z, gv.z, acc);
+        acc = __builtin_fmaf(ov.w, gv.w, acc);
+      }
+    }
   }
 #pragma unroll
   for (int m = LPR / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m);
@@ -485,26 +498,9 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
   // (striped: the coordinate is the local row itself).
   const int32_t qpos0 = STRIPED ? 0 : qrow0;
 
-  // Causal threshold of this lane's key: query coordinates >= thr see it;
-  // the wave's smallest and largest thresholds decide which blocks run.
-  // Striped: key j of block kb has coordinate j + [kb >= stripe_hi] and is
-  // seen from local rows i with floor(i / c) >= floor(coordinate / c) (c in
-  // coordinates; c = 1: i >= j + [kb > r]).  The 32 keys of a wave lie in
-  // one block.
+  const KeyThresholds kth = key_thresholds<STRIPED>(p, kw0, lrow);
   const int64_t c = p.causal;
-  int32_t thr = INT32_MIN, thr_first = INT32_MIN, thr_last = INT32_MIN;
-  if (c > 0 && STRIPED) {
-    const int kb = kw0 / p.seq_q;
-    const int32_t sh = (kb >= p.stripe_hi ? 1 : 0) - kb * p.seq_q;
-    const int32_t cc = (int32_t)c;
-    thr = (key + sh) / cc * cc;
-    thr_first = __builtin_amdgcn_readfirstlane((kw0 + sh) / cc * cc);
-    thr_last = __builtin_amdgcn_readfirstlane((kw0 + 31 + sh) / cc * cc);
-  } else if (c > 0) {
-    thr = (int32_t)(((int64_t)key / c) * c);
-    thr_first = (int32_t)uniform64(((int64_t)kw0 / c) * c);
-    thr_last = (int32_t)uniform64(((int64_t)(kw0 + 31) / c) * c);
-  }
+  const int32_t thr = kth.lane, thr_first = kth.first, thr_last = kth.last;
   const int32_t seg_k = SEG && active ? p.seg[(int64_t)b * p.seq_k + key] : 0;
   const SegRange kseg = SEG ? wave_range(seg_k) : SegRange{0, 0};  // the wave's key ids
 
@@ -530,20 +526,7 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
   __builtin_amdgcn_s_waitcnt(0);
 
   // Query rows that can see any key of the workgroup: [q_lo, Lq).
-  int q_lo = 0;
-  if (c > 0 && STRIPED) {
-    // The smallest threshold of the workgroup's keys: that of its first
-    // key, unless its 256 keys run into the next block (whose first key's
-    // threshold is at most 1).
-    const int kb = k0 / p.seq_q;
-    const int j0 = k0 - kb * p.seq_q;
-    const int32_t cc = (int32_t)c;
-    q_lo = j0 + kBlockNBwd <= p.seq_q ? (j0 + (kb >= p.stripe_hi ? 1 : 0)) / cc * cc : 0;
-    q_lo = q_lo >= p.seq_q ? p.seq_q : q_lo;
-  } else if (c > 0) {
-    const int64_t t0 = ((int64_t)k0 / c) * c - qpos0;
-    q_lo = t0 <= 0 ? 0 : (t0 >= p.seq_q ? p.seq_q : (int)t0);
-  }
+  int q_lo = first_query_row<STRIPED>(p, k0, kBlockNBwd, qpos0);
   q_lo &= ~63;
   const int n_qt = (p.seq_q - q_lo + 63) / 64;
 
@@ -751,15 +734,16 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
 // order (deterministic).  Only the runs of the value's query tile hold an
 // addend (the dq grid has one workgroup per run); their count comes from the
 // same walk lengths as the workgroup mapping.  row4: float4s per query row
-// (heads * head_dim / 4).
-template <bool STRIPED>
+// (heads * head_dim / 4).  BM, TN: the dq kernel's query rows per
+// workgroup and keys per tile (bf16: 256 and 64; float32: 128 and 32).
+template <int BM, int TN, bool STRIPED>
 __global__ __launch_bounds__(256) void bwd_dq_sum_kernel(const BwdParams bp, int64_t n4,
                                                          int32_t row4) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
   const FwdParams& p = bp.f;
   int nsplit = p.key_splits;
-  const walk::Share sh = share_of<kBlockMBf16, 64, STRIPED>(p);
+  const walk::Share sh = share_of<BM, TN, STRIPED>(p);
   // Guard: the dq grid the host launched must hold exactly the runs counted
   // here (the same functions); otherwise dq[0] is poisoned rather than
   // summing slots that no workgroup wrote.
@@ -772,7 +756,7 @@ __global__ __launch_bounds__(256) void bwd_dq_sum_kernel(const BwdParams bp, int
   if (p.split_wgs > 0 && walk::qtile_runs(sh, p.key_splits, 0) < p.key_splits) {
     const int q = n4 <= INT32_MAX ? (int)((uint32_t)i / (uint32_t)row4 % (uint32_t)p.seq_q)
                                   : (int)(i / row4 % p.seq_q);
-    nsplit = walk::qtile_runs(sh, p.key_splits, q / kBlockMBf16);
+    nsplit = walk::qtile_runs(sh, p.key_splits, q / BM);
   }
   const float4* part = reinterpret_cast<const float4*>(bp.dq_part);
   float4 acc = part[i];
@@ -794,23 +778,31 @@ void launch_main(dim3 qgrid, dim3 kgrid, dim3 block, hipStream_t s, const BwdPar
 
 }  // namespace
 
-int launch_bwd(const BwdParams& bp, int head_dim, void* stream, char* err, int errlen) {
+int launch_bwd(const BwdParams& bp, Dtype dtype, int head_dim, void* stream, char* err,
+               int errlen) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipGetLastError();  // clear a stale error from earlier work
   (void)e;
   const FwdParams& p = bp.f;
   const bool seg = p.seg != nullptr;
+  const bool f32 = dtype == Dtype::F32;
   const int64_t rows = (int64_t)p.batch * p.seq_q * p.heads;
   const int64_t lanes = rows * (head_dim / 8);
   const dim3 dgrid((unsigned)((lanes + 255) / 256));
-  if (head_dim == 128)
-    hipLaunchKernelGGL(bwd_delta_kernel<128>, dgrid, dim3(256), 0, s, bp);
+  if (head_dim == 128 && f32)
+    hipLaunchKernelGGL((bwd_delta_kernel<128, float>), dgrid, dim3(256), 0, s, bp);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL((bwd_delta_kernel<128, __bf16>), dgrid, dim3(256), 0, s, bp);
+  else if (f32)
+    hipLaunchKernelGGL((bwd_delta_kernel<64, float>), dgrid, dim3(256), 0, s, bp);
   else
-    hipLaunchKernelGGL(bwd_delta_kernel<64>, dgrid, dim3(256), 0, s, bp);
+    hipLaunchKernelGGL((bwd_delta_kernel<64, __bf16>), dgrid, dim3(256), 0, s, bp);
   const dim3 block(kThreadsBwd);
   const dim3 qgrid((unsigned)p.n_wg), kgrid((unsigned)bp.n_wg_kv);
   const bool str = p.striped != 0;
-  if (head_dim == 128) {
+  if (f32) {
+    launch_bwd_f32_main(bp, head_dim, stream);
+  } else if (head_dim == 128) {
     if (seg)
       str ? launch_main<128, true, true>(qgrid, kgrid, block, s, bp)
           : launch_main<128, true, false>(qgrid, kgrid, block, s, bp);
@@ -828,12 +820,19 @@ int launch_bwd(const BwdParams& bp, int head_dim, void* stream, char* err, int e
   if (bp.dq_part != nullptr) {
     const int64_t n4 = rows * head_dim / 4;
     const int32_t row4 = bp.f.heads * head_dim / 4;
-    if (bp.f.striped)
-      hipLaunchKernelGGL(bwd_dq_sum_kernel<true>, dim3((unsigned)((n4 + 255) / 256)), dim3(256),
-                         0, s, bp, n4, row4);
+    const dim3 sgrid((unsigned)((n4 + 255) / 256));
+    if (f32 && str)
+      hipLaunchKernelGGL((bwd_dq_sum_kernel<kBlockMF32, 32, true>), sgrid, dim3(256), 0, s, bp,
+                         n4, row4);
+    else if (f32)
+      hipLaunchKernelGGL((bwd_dq_sum_kernel<kBlockMF32, 32, false>), sgrid, dim3(256), 0, s, bp,
+                         n4, row4);
+    else if (str)
+      hipLaunchKernelGGL((bwd_dq_sum_kernel<kBlockMBf16, 64, true>), sgrid, dim3(256), 0, s, bp,
+                         n4, row4);
     else
-      hipLaunchKernelGGL(bwd_dq_sum_kernel<false>, dim3((unsigned)((n4 + 255) / 256)), dim3(256),
-                         0, s, bp, n4, row4);
+      hipLaunchKernelGGL((bwd_dq_sum_kernel<kBlockMBf16, 64, false>), sgrid, dim3(256), 0, s, bp,
+                         n4, row4);
   }
   e = hipGetLastError();
   if (e != hipSuccess) {

@@ -324,6 +324,62 @@ __device__ __forceinline__ WaveLimits wave_limits(const FwdParams& p, int64_t pq
   return w;
 }
 
+// Key-stationary backward: the causal threshold of a key (query
+// coordinates >= it see the key) for the lane's key kw0 + lrow of a wave
+// whose 32 keys start at storage row kw0, and the wave's smallest and
+// largest thresholds (INT32_MIN when non-causal).  Contiguous: floor(pk /
+// c) c for the key's position pk.  Striped: key j of block kb has
+// coordinate j + [kb >= stripe_hi] and is seen from local rows i with
+// floor(i / c) >= floor(coordinate / c) (c in coordinates; c = 1: i >= j +
+// [kb > r]).  The 32 keys of a wave lie in one block (Lq is a multiple of
+// 32).
+struct KeyThresholds {
+  int32_t lane, first, last;
+};
+
+template <bool STRIPED>
+__device__ __forceinline__ KeyThresholds key_thresholds(const FwdParams& p, int kw0, int lrow) {
+  const int64_t c = p.causal;
+  KeyThresholds t{INT32_MIN, INT32_MIN, INT32_MIN};
+  const int key = kw0 + lrow;
+  if (c > 0 && STRIPED) {
+    const int kb = kw0 / p.seq_q;
+    const int32_t sh = (kb >= p.stripe_hi ? 1 : 0) - kb * p.seq_q;
+    const int32_t cc = (int32_t)c;
+    t.lane = (key + sh) / cc * cc;
+    t.first = __builtin_amdgcn_readfirstlane((kw0 + sh) / cc * cc);
+    t.last = __builtin_amdgcn_readfirstlane((kw0 + 31 + sh) / cc * cc);
+  } else if (c > 0) {
+    t.lane = (int32_t)(((int64_t)key / c) * c);
+    t.first = (int32_t)uniform64(((int64_t)kw0 / c) * c);
+    t.last = (int32_t)uniform64(((int64_t)(kw0 + 31) / c) * c);
+  }
+  return t;
+}
+
+// The first local query row that can see any of the keys [k0, k0 + nkeys)
+// of a key-stationary workgroup (Lq when none can); qpos0 is the query
+// coordinate of local row 0 (0 under striped placement).  Striped: the
+// smallest threshold is that of the first key, unless the keys run into
+// the next block, whose first key's threshold is at most 1.
+template <bool STRIPED>
+__device__ __forceinline__ int first_query_row(const FwdParams& p, int k0, int nkeys,
+                                               int32_t qpos0) {
+  const int64_t c = p.causal;
+  int q_lo = 0;
+  if (c > 0 && STRIPED) {
+    const int kb = k0 / p.seq_q;
+    const int j0 = k0 - kb * p.seq_q;
+    const int32_t cc = (int32_t)c;
+    q_lo = j0 + nkeys <= p.seq_q ? (j0 + (kb >= p.stripe_hi ? 1 : 0)) / cc * cc : 0;
+    q_lo = q_lo >= p.seq_q ? p.seq_q : q_lo;
+  } else if (c > 0) {
+    const int64_t t0 = ((int64_t)k0 / c) * c - qpos0;
+    q_lo = t0 <= 0 ? 0 : (t0 >= p.seq_q ? p.seq_q : (int)t0);
+  }
+  return q_lo;
+}
+
 // The walk limit of the workgroup whose query tile starts at local row m0.
 template <int BM, bool STRIPED = false>
 __device__ __forceinline__ int64_t wg_kend(const FwdParams& p, int m0) {

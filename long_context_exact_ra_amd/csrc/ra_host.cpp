@@ -406,10 +406,8 @@ ra_status_t ra_blockwise_attn_bwd_split(const void* q, const void* k, const void
   ra_status_t st = prepare(q, k, v, segment_ids, causal_block_size, q_chunk, k_chunk, ring_size,
                            ring_index, placement, batch, seq_q, heads, head_dim, dtype, bp.f,
                            empty);
-  if (st != RA_OK) return st;
-  if (dtype != RA_BF16)
-    return fail(RA_E_UNSUPPORTED, "the backward takes bf16 inputs only");
-  if (empty) return RA_OK;
+  if (st != RA_OK || empty) return st;
+  const ra::Dtype dt = dtype == RA_BF16 ? ra::Dtype::BF16 : ra::Dtype::F32;
   if (!out || !lse || !dout || !dq || !dk || !dv || !delta)
     return fail(RA_E_INVALID, "out, lse, dout, dq, dk, dv and delta must be non-NULL");
   if (!aligned(out, 16) || !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) ||
@@ -425,8 +423,9 @@ ra_status_t ra_blockwise_attn_bwd_split(const void* q, const void* k, const void
       return fail(RA_E_INVALID, "workspace of %lld bytes is smaller than the %lld required",
                   (long long)workspace_bytes, (long long)need);
     // The dq kernel: one workgroup per run of every query tile's walk, as in
-    // the forward.
-    const int64_t wgs = split_wgs_host(key_splits, bp.f, ra::kBlockMBf16, 64);
+    // the forward (and with the forward's tiles of the dtype).
+    const int64_t wgs =
+        split_wgs_host(key_splits, bp.f, ra::block_rows(dt), dt == ra::Dtype::BF16 ? 64 : 32);
     const int64_t n_wg = batch * heads * wgs;
     if (n_wg > kInt32Max || wgs > kInt32Max)
       return fail(RA_E_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)n_wg);
@@ -442,14 +441,14 @@ ra_status_t ra_blockwise_attn_bwd_split(const void* q, const void* k, const void
   bp.dk = dk;
   bp.dv = dv;
   bp.delta = delta;
-  const int64_t n_ktiles = ((int64_t)bp.f.seq_k + ra::kBlockNBwd - 1) / ra::kBlockNBwd;
+  const int64_t n_ktiles = ((int64_t)bp.f.seq_k + ra::bwd_key_block(dt) - 1) / ra::bwd_key_block(dt);
   const int64_t n_wg_kv = batch * heads * n_ktiles;
   if (n_wg_kv > kInt32Max)
     return fail(RA_E_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)n_wg_kv);
   bp.n_ktiles = (int32_t)n_ktiles;
   bp.n_wg_kv = (int32_t)n_wg_kv;
   char err[256];
-  if (ra::launch_bwd(bp, (int)head_dim, stream, err, (int)sizeof(err)) != 0)
+  if (ra::launch_bwd(bp, dt, (int)head_dim, stream, err, (int)sizeof(err)) != 0)
     return fail(RA_E_HIP, "%s", err);
   return RA_OK;
 }

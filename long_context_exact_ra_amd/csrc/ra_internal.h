@@ -56,9 +56,9 @@ inline int block_rows(Dtype d) { return d == Dtype::BF16 ? kBlockMBf16 : kBlockM
 // the forward outputs, the upstream gradient and the gradient outputs.
 struct BwdParams {
   FwdParams f;
-  const void* out;      // [B, Lq, H, D] bf16
+  const void* out;      // [B, Lq, H, D], the input dtype
   const float* lse;     // [B, H, Lq]
-  const void* dout;     // [B, Lq, H, D] bf16
+  const void* dout;     // [B, Lq, H, D], the input dtype
   float* dq;            // [B, Lq, H, D]
   float* dk;            // [B, S, H, D]
   float* dv;            // [B, S, H, D]
@@ -66,16 +66,23 @@ struct BwdParams {
   // With key splits (f.key_splits > 1): the splits' addends to dq,
   // [key_splits][B, Lq, H, D]; a sum kernel writes dq.  Otherwise nullptr.
   float* dq_part;
-  int32_t n_ktiles;     // key tiles per (batch, head) of the dK/dV kernel
+  int32_t n_ktiles;     // key tiles (bwd_key_block keys) per (batch, head) of the dK/dV kernel
   int32_t n_wg_kv;      // workgroups of the dK/dV kernel
 };
 
-// Keys per workgroup of the dK/dV kernel (8 waves x 32 keys).
+// Keys per workgroup of the dK/dV kernel (bf16: 8 waves x 32 keys; float32:
+// 4 waves x 32 keys).
 constexpr int kBlockNBwd = 256;
+constexpr int kBlockNBwdF32 = 128;
+inline int bwd_key_block(Dtype d) { return d == Dtype::BF16 ? kBlockNBwd : kBlockNBwdF32; }
 
-// Enqueue the backward (bf16 inputs) on `stream`; same conventions as
-// launch_fwd.
-int launch_bwd(const BwdParams& p, int head_dim, void* stream, char* err, int errlen);
+// Enqueue the backward on `stream`; same conventions as launch_fwd.
+int launch_bwd(const BwdParams& p, Dtype dtype, int head_dim, void* stream, char* err,
+               int errlen);
+
+// The float32 dq and dK/dV kernels (blockwise_bwd_f32.hip), enqueued by
+// launch_bwd after the delta kernel.
+void launch_bwd_f32_main(const BwdParams& p, int head_dim, void* stream);
 
 // The blockwise feedforward: y = max(0, x W1 + b1) W2 + b2, chunk by chunk.
 struct FfnParams {

@@ -23,7 +23,7 @@ int launch_fwd(const FwdParams& p, Dtype, int, int64_t, void*, char*, int) {
   ++g_launches;
   return 0;
 }
-int launch_bwd(const BwdParams& p, int, void*, char*, int) {
+int launch_bwd(const BwdParams& p, Dtype, int, void*, char*, int) {
   g_bwd = p;
   ++g_launches;
   return 0;
@@ -123,6 +123,16 @@ int main() {
       CHECK(splits == 1 || ra::g_bwd.f.n_wg == s.B * s.H * ra::g_bwd.f.split_wgs);
       CHECK(ra::g_bwd.n_wg_kv == s.B * s.H * ((s.N * s.Lq + 255) / 256));
       CHECK((ra::g_bwd.dq_part != nullptr) == (splits > 1));
+      // float32: the dq grid of 128-row tiles, dK/dV workgroups of 128 keys
+      CHECK(ra_blockwise_attn_bwd_split(P, P, P, nullptr, s.c, s.qc, s.kc, s.N, s.r,
+                                        RA_PLACE_CONTIGUOUS, s.B, s.Lq, s.H, s.D, RA_F32, P, F,
+                                        P, F, F, F, F, splits, splits > 1 ? P : nullptr, bws,
+                                        nullptr) == RA_OK);
+      const int64_t tiles32 = (s.Lq + 127) / 128;
+      CHECK(ra::g_bwd.f.n_wg >= s.B * s.H * tiles32 &&
+            ra::g_bwd.f.n_wg <= s.B * s.H * tiles32 * splits);
+      CHECK(splits == 1 || ra::g_bwd.f.n_wg == s.B * s.H * ra::g_bwd.f.split_wgs);
+      CHECK(ra::g_bwd.n_wg_kv == s.B * s.H * ((s.N * s.Lq + 127) / 128));
     }
     CHECK(ra_blockwise_attn_fwd(P, P, P, nullptr, s.c, s.qc, s.kc, s.N, s.r, s.B, s.Lq, s.H,
                                 s.D, RA_BF16, P, reinterpret_cast<float*>(P), nullptr) == RA_OK);
@@ -148,8 +158,11 @@ int main() {
                                     128, RA_BF16, P, F, nullptr, 0, nullptr, 0,
                                     nullptr) == RA_E_INVALID);                 // 0 splits
   CHECK(ra_blockwise_attn_bwd_split(P, P, P, nullptr, 1, 32, 32, 4, 0, RA_PLACE_CONTIGUOUS, 1, 64,
+                                    1, 128, (ra_dtype_t)5, P, F, P, F, F, F, F, 1, nullptr, 0,
+                                    nullptr) == RA_E_UNSUPPORTED);             // unknown dtype
+  CHECK(ra_blockwise_attn_bwd_split(P, P, P, nullptr, 3, 32, 32, 4, 0, RA_PLACE_STRIPED, 1, 64,
                                     1, 128, RA_F32, P, F, P, F, F, F, F, 1, nullptr, 0,
-                                    nullptr) == RA_E_UNSUPPORTED);             // fp32 backward
+                                    nullptr) == RA_E_UNSUPPORTED);             // striped c = 3
   CHECK(ra_blockwise_ffn(P, P, P, P, P, 1, 64, 64, 128, 48, RA_BF16, P, P, 1 << 20, nullptr) ==
         RA_E_INVALID);                                                        // chunk 48 of 64
   CHECK(std::strlen(ra_last_error()) > 0);

@@ -10,8 +10,11 @@ round to nearest even) as operands of fp32-accumulating matrix products, so
 each gradient is a sum of terms with independent relative errors of that
 size; its relative L2 error is expected around 2^-9 ~ 2e-3.  The test
 requires relative L2 <= 1e-2 and max |err| <= 2e-2 * max |ref| per tensor.
-delta is a plain fp32 reduction of the kernel's own out: relative L2
-<= 1e-5 against the same sum in fp64.
+float32 inputs: every operand stays float32 (products on float32 MFMA, the
+exponential v_exp_f32 to about 1 ulp), so the errors are float32 rounding
+over sums of up to S terms: relative L2 <= 1e-5 and max |err| <= 1e-4 *
+max |ref|.  delta is a plain fp32 reduction of the kernel's own out:
+relative L2 <= 1e-5 against the same sum in fp64.
 """
 
 import numpy as np
@@ -27,16 +30,18 @@ pytestmark = pytest.mark.gpu
 
 REL_L2 = 1e-2
 MAX_REL = 2e-2
+REL_L2_F32 = 1e-5
+MAX_REL_F32 = 1e-4
 
 
-def _cmp(name, got, ref, what):
+def _cmp(name, got, ref, what, f32=False):
     err = np.abs(got - ref)
     scale = max(float(np.abs(ref).max(initial=0)), 1e-30)
     rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
     log(f"  bwd {what} {name}: rel_l2={rel:.3e} max_err/max_ref={float(err.max(initial=0)) / scale:.3e}")
     assert np.isfinite(got).all(), (what, name)
-    assert rel <= REL_L2, (what, name, rel)
-    assert float(err.max(initial=0)) <= MAX_REL * scale, (what, name)
+    assert rel <= (REL_L2_F32 if f32 else REL_L2), (what, name, rel)
+    assert float(err.max(initial=0)) <= (MAX_REL_F32 if f32 else MAX_REL) * scale, (what, name)
 
 
 def _short_documents(B, S, seed):
@@ -89,9 +94,10 @@ def _full_case(w, r, heads=None, key_splits=1):
                                          None if seg is None else seg.cpu().numpy(),
                                          w.causal_block_size, w.ring_size, r,
                                          placement=w.placement)
-    _cmp("dq", to_np(dq[:, :, hs]), rdq, what)
-    _cmp("dk", to_np(dk[:, :, hs]), rdk, what)
-    _cmp("dv", to_np(dv[:, :, hs]), rdv, what)
+    f32 = q.dtype == torch.float32
+    _cmp("dq", to_np(dq[:, :, hs]), rdq, what, f32)
+    _cmp("dk", to_np(dk[:, :, hs]), rdk, what, f32)
+    _cmp("dv", to_np(dv[:, :, hs]), rdv, what, f32)
 
 
 @pytest.mark.parametrize("r", [0, 3, 7])
@@ -303,9 +309,38 @@ def test_bwd_share_7b_striped_sampled():
     assert relv <= REL_L2
 
 
-def test_bwd_rejects_fp32_and_nulls():
+F32_CASES = [
+    # B, Lq, N, H, D, causal, qc, kc, segments, r, placement, splits
+    (1, 64, 4, 2, 64, None, 32, 32, False, 0, "contiguous", 1),   # the tiny workload's shape
+    (1, 64, 4, 2, 64, None, 32, 32, False, 3, "contiguous", 1),
+    (2, 96, 3, 2, 128, 1, 32, 32, False, 2, "contiguous", 1),
+    (1, 160, 2, 2, 128, 5, 32, 32, False, 1, "contiguous", 1),
+    (2, 128, 2, 2, 64, 1, 64, 64, True, 1, "contiguous", 1),
+    (1, 288, 3, 1, 128, 1, 32, 32, False, 2, "contiguous", 1),   # key workgroups span blocks
+    (1, 128, 4, 2, 128, 1, 32, 32, False, 1, "striped", 1),
+    (1, 128, 4, 2, 64, 8, 32, 32, True, 2, "striped", 1),
+    (1, 256, 2, 2, 128, 1, 64, 64, False, 1, "contiguous", 4),   # dq key splits
+    (1, 128, 4, 1, 64, 2, 32, 32, False, 3, "striped", 3),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=[str(c) for c in F32_CASES])
+def test_bwd_f32(case):
+    B, Lq, N, H, D, c, qc, kc, segs, r, place, splits = case
+    w = workloads.Workload(f"f32_edge{case}", B, Lq, N, (r,), H, D, "f32", c, qc, kc,
+                           segments=segs, seed=7171 + Lq + D + N, placement=place)
+    _full_case(w, r, key_splits=splits)
+
+
+def test_bwd_tiny_plumbing_all_positions():
+    w = workloads.get("tiny_plumbing")
+    for r in w.ring_indices:
+        _full_case(w, r)
+
+
+def test_bwd_rejects_bad_dtypes_and_nulls():
     dev = torch.device("cuda:0")
-    q = torch.zeros((1, 32, 1, 128), dtype=torch.float32, device=dev)
+    q = torch.zeros((1, 32, 1, 128), dtype=torch.float16, device=dev)
     with pytest.raises(TypeError):
         ra.blockwise_attn_bwd(q, q, q, q, torch.zeros((1, 1, 32), device=dev), q)
     lib = ra.load_library()
