@@ -211,14 +211,40 @@ __device__ __forceinline__ void dq_tile(const FwdParams& p, const DqWave& w, con
   // dp starts from -delta (each lane holds one query row), so the MFMAs
   // deliver dP - delta directly.
   f32x16_t s[2], dp[2];
+  // Without segment ids (registers to spare), each MFMA's LDS operand is
+  // read two MFMAs ahead (fenced), so an MFMA does not wait on the read
+  // issued just before it.
+  constexpr bool kPrefetch = !SEG;
+  if constexpr (kPrefetch) {
+    constexpr int NM = 2 * 2 * (D / 16);  // MFMAs (sb, c, S or dP)
+    auto rread = [&](int n) {
+      const int sb = n / (D / 8), c = (n / 2) % (D / 16);
+      return row_operand((n & 1) ? vst : kst, w.k_rd, c, sb);
+    };
+    bf16x8_t o[3];
+    o[0] = rread(0);
+    o[1] = rread(1);
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb) {
-    s[sb] = mfma(row_operand(kst, w.k_rd, 0, sb), qf[0], f32x16_t{});
-    dp[sb] = mfma(row_operand(vst, w.k_rd, 0, sb), dof[0], ndlt);
+    for (int n = 0; n < NM; ++n) {
+      if (n + 2 < NM) o[(n + 2) % 3] = rread(n + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      const int sb = n / (D / 8), c = (n / 2) % (D / 16);
+      if (n & 1)
+        dp[sb] = mfma(o[n % 3], dof[c], c == 0 ? ndlt : dp[sb]);
+      else
+        s[sb] = mfma(o[n % 3], qf[c], c == 0 ? f32x16_t{} : s[sb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
 #pragma unroll
-    for (int c = 1; c < D / 16; ++c) {
-      s[sb] = mfma(row_operand(kst, w.k_rd, c, sb), qf[c], s[sb]);
-      dp[sb] = mfma(row_operand(vst, w.k_rd, c, sb), dof[c], dp[sb]);
+    for (int sb = 0; sb < 2; ++sb) {
+      s[sb] = mfma(row_operand(kst, w.k_rd, 0, sb), qf[0], f32x16_t{});
+      dp[sb] = mfma(row_operand(vst, w.k_rd, 0, sb), dof[0], ndlt);
+#pragma unroll
+      for (int c = 1; c < D / 16; ++c) {
+        s[sb] = mfma(row_operand(kst, w.k_rd, c, sb), qf[c], s[sb]);
+        dp[sb] = mfma(row_operand(vst, w.k_rd, c, sb), dof[c], dp[sb]);
+      }
     }
   }
   // With segment ids every tile takes the masked path (a second, unmasked
@@ -251,13 +277,28 @@ __device__ __forceinline__ void dq_tile(const FwdParams& p, const DqWave& w, con
     }
     dsb[q] = __builtin_convertvector(d, bf16x8_t);
   }
+  if constexpr (kPrefetch) {
+    constexpr int NM = 4 * NDB;  // MFMAs (k-step 2 sb + cc, j)
+    auto cread = [&](int n) { return col_operand(kst, w.t_rd, n % NDB, n / NDB); };
+    bf16x8_t o[3];
+    o[0] = cread(0);
+    o[1] = cread(1);
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb)
+    for (int n = 0; n < NM; ++n) {
+      if (n + 2 < NM) o[(n + 2) % 3] = cread(n + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      acc[n % NDB] = mfma(o[n % 3], dsb[n / NDB], acc[n % NDB]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
+    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int j = 0; j < NDB; ++j)
-        acc[j] = mfma(col_operand(kst, w.t_rd, j, 2 * sb + cc), dsb[2 * sb + cc], acc[j]);
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int j = 0; j < NDB; ++j)
+          acc[j] = mfma(col_operand(kst, w.t_rd, j, 2 * sb + cc), dsb[2 * sb + cc], acc[j]);
+  }
 }
 
 template <int D, bool SEG, bool STRIPED>
@@ -477,6 +518,10 @@ template <int D, bool SEG, bool STRIPED>
 __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParams bp) {
   using L = KvLds<D, SEG>;
   constexpr int NDB = D / 32, NPT = L::NPT;
+  // Operand reads ahead of the MFMAs need registers that the segment-id
+  // variants do not have (they spill): those keep the reads next to their
+  // MFMAs.  On the 7B share the read-ahead makes the kernel 2.7 % faster.
+  constexpr bool kPrefetch = !SEG;
   const FwdParams& p = bp.f;
   __shared__ __attribute__((aligned(16))) __bf16 vres[L::VRES];
   __shared__ __attribute__((aligned(16))) __bf16 qs[2 * L::QSTAGE];  // two query stages
@@ -658,12 +703,37 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
       if (!run) continue;
 
       f32x16_t sc = f32x16_t{}, dp = f32x16_t{};
+      auto vread = [&](int cc) {
+        return *reinterpret_cast<const bf16x8_t*>(vres + (wave >> 1) * L::ELEMS +
+                                                  row_rd_c(r_rd, cc) + row_off(cc, wave & 1));
+      };
+      if constexpr (kPrefetch) {
+        // Operands one step ahead: the reads of step cc + 1 are issued
+        // before the MFMAs of step cc (fenced), so an MFMA does not wait on
+        // the read issued just before it.
+        bf16x8_t oq[2], og[2], ov[2];
+        oq[0] = row_operand(qt_t, r_rd, 0, qh);
+        og[0] = row_operand(gt_t, r_rd, 0, qh);
+        ov[0] = vread(0);
 #pragma unroll
-      for (int cc = 0; cc < D / 16; ++cc) {
-        const bf16x8_t vop = *reinterpret_cast<const bf16x8_t*>(
-            vres + (wave >> 1) * L::ELEMS + row_rd_c(r_rd, cc) + row_off(cc, wave & 1));
-        sc = mfma(row_operand(qt_t, r_rd, cc, qh), kf[cc], sc);
-        dp = mfma(row_operand(gt_t, r_rd, cc, qh), vop, dp);
+        for (int cc = 0; cc < D / 16; ++cc) {
+          if (cc + 1 < D / 16) {
+            oq[(cc + 1) & 1] = row_operand(qt_t, r_rd, cc + 1, qh);
+            og[(cc + 1) & 1] = row_operand(gt_t, r_rd, cc + 1, qh);
+            ov[(cc + 1) & 1] = vread(cc + 1);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          sc = mfma(oq[cc & 1], kf[cc], sc);
+          dp = mfma(og[cc & 1], ov[cc & 1], dp);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int cc = 0; cc < D / 16; ++cc) {
+          const bf16x8_t vop = vread(cc);
+          sc = mfma(row_operand(qt_t, r_rd, cc, qh), kf[cc], sc);
+          dp = mfma(row_operand(gt_t, r_rd, cc, qh), vop, dp);
+        }
       }
       // The 16 query rows of this lane: 8 (e / 4) + 4 half + e % 4; p and
       // ds overwrite the scores and dp in place.
@@ -700,13 +770,36 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
         pb[cc] = __builtin_convertvector(a, bf16x8_t);
         db[cc] = __builtin_convertvector(d, bf16x8_t);
       }
+      if constexpr (kPrefetch) {
+        // Column operands two MFMAs ahead (fenced), as above.
+        constexpr int NM = 4 * NDB;  // MFMAs (cc, j, dV or dK)
+        auto cread = [&](int n) {
+          const int cc = n / (2 * NDB), j = (n / 2) % NDB;
+          return col_operand((n & 1) ? qt_t : gt_t, t_rd, j, 2 * qh + cc);
+        };
+        bf16x8_t oc[3];
+        oc[0] = cread(0);
+        oc[1] = cread(1);
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int j = 0; j < NDB; ++j) {
-          dv[j] = mfma(col_operand(gt_t, t_rd, j, 2 * qh + cc), pb[cc], dv[j]);
-          dk[j] = mfma(col_operand(qt_t, t_rd, j, 2 * qh + cc), db[cc], dk[j]);
+        for (int n = 0; n < NM; ++n) {
+          if (n + 2 < NM) oc[(n + 2) % 3] = cread(n + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          const int cc = n / (2 * NDB), j = (n / 2) % NDB;
+          if (n & 1)
+            dk[j] = mfma(oc[n % 3], db[cc], dk[j]);
+          else
+            dv[j] = mfma(oc[n % 3], pb[cc], dv[j]);
+          __builtin_amdgcn_sched_barrier(0);
         }
+      } else {
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int j = 0; j < NDB; ++j) {
+            dv[j] = mfma(col_operand(gt_t, t_rd, j, 2 * qh + cc), pb[cc], dv[j]);
+            dk[j] = mfma(col_operand(qt_t, t_rd, j, 2 * qh + cc), db[cc], dk[j]);
+          }
+      }
     }
     // Every wave is done with stage s before the next fetch overwrites it.
     stage_barrier();
