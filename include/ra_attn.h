@@ -3,8 +3,10 @@
  * Attention for AMD MI355X (gfx950).
  *
  * What is computed.  One device's share of Ring Attention: the local query
- * block Q_r (ring position r of N) attends to all N key/value blocks,
- * visited in ring order -- at outer step t the block (r - t) mod N -- with a
+ * block Q_r (ring position r of N) attends to all N key/value blocks (the
+ * ring visits the block (r - t) mod N at outer step t; on one device every
+ * block is resident and the library folds them in that order with the local
+ * block r moved to the end) with a
  * running max / numerator / denominator carry that is rescaled per block
  * ("Ring Attention with Blockwise Transformers for Near-Infinite Context",
  * section 三: the self-attention equation, "分块注意力", "环形注意力算法"
@@ -189,7 +191,7 @@ ra_status_t ra_blockwise_attn_fwd_placed(const void* q, const void* k,
  * walk of the share (its last query tile's) into key_splits runs, a query
  * tile whose walk has n of the longest walk's n_max tiles into
  * ceil(key_splits n / n_max) runs, so that runs are about equally long.
- * Split s of a tile folds the s-th of its equal runs (ring order, skips and
+ * Split s of a tile folds the s-th of its equal runs (walk order, skips and
  * masks unchanged) into its own max, numerator and denominator, one
  * workgroup per run (the grid holds exactly the runs; the slots of a tile's
  * surplus splits are marked empty), and a second kernel folds the splits

@@ -17,8 +17,8 @@
 // Three launches (four with key splits, below):
 //   bwd_delta_kernel   delta (one pass over dout and out);
 //   bwd_dq_kernel      query-stationary, like the forward: a workgroup owns
-//                      256 query rows and walks the key tiles in ring order
-//                      (block (r - t) mod N at step t), K and V tiles
+//                      256 query rows and walks the key tiles in the
+//                      forward's order (the local block last), K and V tiles
 //                      arriving by buffer-to-LDS DMA through a 4-stage ring;
 //   bwd_dkdv_kernel    key-stationary: a workgroup owns 256 keys (K of each
 //                      wave in registers, V resident in LDS) and streams the

@@ -2,10 +2,13 @@
 // written for gfx950 (MI355X, CDNA4).
 //
 // A workgroup owns a tile of query rows of one (batch, head) (256 rows = 8
-// waves for bf16, 128 rows = 4 waves for fp32); each wave owns 32 of them.  The workgroup walks the N key/value blocks in ring
-// order -- step t uses block (r - t) mod N ("Ring Attention with Blockwise
-// Transformers for Near-Infinite Context", section 三 "环形注意力算法") --
-// and inside a block the keys in tiles.  Tiles are staged through LDS and
+// waves for bf16, 128 rows = 4 waves for fp32); each wave owns 32 of them.  The workgroup walks the N key/value blocks
+// (the ring of "Ring Attention with Blockwise Transformers for
+// Near-Infinite Context", section 三 "环形注意力算法", visits block (r - t)
+// mod N at step t; on one device all blocks are resident and the fold order
+// is free, so the walk takes the ring order with the local block moved to
+// the end, which keeps the workgroups of a head in step) and inside a block
+// the keys in tiles.  Tiles are staged through LDS and
 // fetched ahead of use, also across block boundaries, which is the
 // single-device stand-in for receiving the next block while computing.
 //

@@ -104,8 +104,15 @@ __device__ __forceinline__ int block_klen(const FwdParams& p, int kb, int64_t ke
   return walk::block_klen(p.seq_q, block_vbase<STRIPED>(p, kb), kend);
 }
 
-// The walk over the keys.  Contiguous placement: block by block in ring
-// order (step t uses block (r - t) mod N), the tiles of a block in order.
+// The walk over the keys.  Contiguous placement: block by block, the tiles
+// of a block in order, the blocks in ring order rotated by one so that the
+// local block comes last: walk step t uses block (r - 1 - t) mod N, i.e.
+// r - 1, .., 0, N - 1, .., r + 1, then r.  Under a causal mask the local
+// (diagonal) block is the only one whose visible length differs between the
+// query tiles of a head; walked first, it would start the workgroups of a
+// head at different offsets in the blocks that follow, and they would stop
+// sharing those blocks' key tiles in L2 (the 7B-shaped share fetched 280 GB
+// from HBM per launch that way, 161 GB with the local block last).
 // Striped placement: every block is a causal triangle of the same shape, so
 // the workgroups of a head, whose query tiles see different numbers of keys
 // per block, would drift apart block by block and stop sharing the key tiles
@@ -154,8 +161,8 @@ __device__ __forceinline__ void cursor_seek(const FwdParams& p, Cursor& c, int64
   }
 #pragma clang loop vectorize(disable) unroll(disable)
   while (c.t < p.ring_size) {
-    // Ring order: step t uses block (r - t) mod N.
-    c.kb = p.ring_index - c.t;
+    // Walk step t: block (r - 1 - t) mod N (the local block last).
+    c.kb = p.ring_index - 1 - c.t;
     if (c.kb < 0) c.kb += p.ring_size;
     c.klen = block_klen<STRIPED>(p, c.kb, kend);
     c.ntile = (c.klen + TN - 1) / TN;
