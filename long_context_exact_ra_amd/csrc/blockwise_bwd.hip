@@ -66,6 +66,7 @@
 
 #include "ra_device.h"
 #include "ra_internal.h"
+#include "ra_lds.h"
 
 namespace ra {
 namespace {
@@ -74,43 +75,22 @@ constexpr int kWaves = 8;                 // waves per workgroup (both main kern
 constexpr int kThreadsBwd = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// The DMA fills 64 consecutive slots per instruction (16 rows x one granule
-// quad); lane l's byte offset in the tensor puts the row and granule that
-// belong in slot l there.
+// The layout's arithmetic (slot map, DMA lane map, row and column read
+// offsets) lives in ra_lds.h, where tests/lds_check.cpp checks it on the
+// host against the MFMA operand layout and the LDS banks.
 __device__ __forceinline__ uint32_t tile_lane_off(int lane, uint32_t rs_bytes) {
-  return (uint32_t)((lane & 15) ^ (4 * (lane >> 4))) * rs_bytes + 16u * (uint32_t)(lane >> 4);
+  return (uint32_t)lds::bwd_dma_row(lane) * rs_bytes + 16u * (uint32_t)lds::bwd_dma_gran(lane);
 }
-
-// Element offsets inside a 64-row tile stored in the layout above.
-// Row operand: lane l reads row 32 * blk + l % 32, columns 16 c + 8 (l / 32)
-// .. +7 (the A operand of a 16-column k-step).  row_rd is the lane's offset
-// for even c; odd c moves the granule by 2 within its quad, which flips the
-// swizzle's bit 3 of the row: offset ^ 64.
-__device__ __forceinline__ int row_rd(int lane) {
-  const int lrow = lane & 31, half = lane >> 5;
-  return 512 * (lrow >> 4) + 128 * half + 8 * ((lrow & 15) ^ (4 * half));
-}
-__device__ __forceinline__ constexpr int row_rd_c(int rd, int c) { return (c & 1) ? (rd ^ 64) : rd; }
-__device__ __forceinline__ constexpr int row_off(int c, int blk) {
-  return 2048 * (c >> 1) + 256 * (c & 1) + 1024 * blk;
-}
-// Column operand by ds_read_b64_tr_b16: in each 16-lane group, lane j reads
-// 4 values of tile row 4 (g / 2) + j / 4 (+8 for the high half) at columns
-// 32 jb + 16 (g % 2) + 4 (j % 4); after the transpose, lane l holds for its
-// column 32 jb + l % 32 the 8 tile rows of the k-slots of its lane half.
-// Rows + 8 flip the swizzled row's bit 3: the high half reads at offset ^ 64.
-__device__ __forceinline__ int col_rd(int lane) {
-  const int g = lane >> 4, j = lane & 15;
-  const int r0 = 4 * (g >> 1) + (j >> 2), q = 2 * (g & 1) + ((j >> 1) & 1);
-  return (q * 16 + (r0 ^ (4 * q))) * 8 + 4 * (j & 1);
-}
-// jb = 32-column block, rb = 16-row block of the tile (its k-step).
-__device__ __forceinline__ constexpr int col_off(int jb, int rb) { return 2048 * jb + 512 * rb; }
+__device__ __forceinline__ int row_rd(int lane) { return lds::bwd_row_rd(lane); }
+__device__ __forceinline__ constexpr int row_rd_c(int rd, int c) { return lds::bwd_row_rd_c(rd, c); }
+__device__ __forceinline__ constexpr int row_off(int c, int blk) { return lds::bwd_row_off(c, blk); }
+__device__ __forceinline__ int col_rd(int lane) { return lds::bwd_col_rd(lane); }
+__device__ __forceinline__ constexpr int col_off(int jb, int rb) { return lds::bwd_col_off(jb, rb); }
 
 __device__ __forceinline__ bf16x8_t col_operand(const __bf16* tile, int rd, int jb, int rb) {
   const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tile + rd + col_off(jb, rb)));
-  const i16x4_t hi =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tile + (rd ^ 64) + col_off(jb, rb)));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4_t*)(tile + lds::bwd_col_hi(rd) + col_off(jb, rb)));
   return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 

@@ -62,6 +62,7 @@
 
 #include "ra_device.h"
 #include "ra_internal.h"
+#include "ra_lds.h"
 
 namespace ra {
 namespace {
@@ -121,7 +122,7 @@ __device__ __forceinline__ void gemm_fetch(const GemmArgs& a, int m0, int n0, in
   for (int u = 0; u < C::W_DMA; ++u) {
     const int i = wave * C::W_DMA + u;
     const int k = RPI * i + lane / GPR;
-    const int g = (lane % GPR) ^ (4 * (k & 3));
+    const int g = lds::gemm_w_gran(k, lane % GPR);
     const uint32_t off = (uint32_t)k * (uint32_t)a.n * 2u + (uint32_t)(n0 + 8 * g) * 2u;
     dma_b128(lds_addr(st + C::X_ELEMS + i * 512), off, wr);
   }
@@ -146,7 +147,7 @@ __device__ __forceinline__ void gemm_fetch_one(const GemmArgs& a, int m0, int n0
     constexpr int GPR = BN / 8, RPI = 64 / GPR;
     const int i = wave * C::W_DMA + (u - C::X_DMA);
     const int k = RPI * i + lane / GPR;
-    const int g = (lane % GPR) ^ (4 * (k & 3));
+    const int g = lds::gemm_w_gran(k, lane % GPR);
     const uint32_t off = (uint32_t)k * (uint32_t)a.n * 2u + (uint32_t)(n0 + 8 * g) * 2u;
     dma_b128(lds_addr(st + C::X_ELEMS + i * 512), off, wr);
   }
@@ -252,13 +253,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bias_kernel(const GemmAr
   // % 2) + 4 (j16 % 4): granule gc = (wn + 32 nb) / 8 + 2 (g16 % 2) + (j16 %
   // 4) / 2, stored at slot kr * BN / 8 + (gc ^ 4 (kr % 4)).  The XOR
   // touches the bits of gc that nb sets, so each nb has its own base.
-  const int kr = 8 * (g16 >> 1) + (j16 >> 2), sw = 4 * (j16 >> 2);
   int w_rd[C::NB];
 #pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb) {
-    const int gc = wn / 8 + 4 * nb + 2 * (g16 & 1) + ((j16 & 3) >> 1);
-    w_rd[nb] = C::X_ELEMS + kr * BN + (gc ^ sw) * 8 + 4 * (j16 & 1);
-  }
+  for (int nb = 0; nb < C::NB; ++nb) w_rd[nb] = C::X_ELEMS + lds::gemm_w_rd(lane, wn, nb, BN);
 
   f32x16_t acc[C::NB * C::MB];
 #pragma unroll
