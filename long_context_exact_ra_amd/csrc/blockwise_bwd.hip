@@ -549,6 +549,22 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
     issue_rows<D, kWaves>(TileInfo{k0 + 64 * t, kend, 0, 0, 1, 0}, vbase0, rs_bytes, wave, lane_off,
                           vres + t * L::ELEMS);
   __builtin_amdgcn_s_waitcnt(0);
+  // The resident V is kept negated: dp starts from delta (read from the
+  // query stage straight into the accumulators), so the MFMAs deliver
+  // delta - dout.v_j and no subtraction per pair is left.  Each wave flips
+  // the sign bits of the 16-byte slots its own DMA wrote (lane l of DMA
+  // instruction j wrote slot 64 j + l); the walk's first barrier orders
+  // these writes before any read.
+  {
+    constexpr int DPW = 64 * D / 8 / 64 / kWaves;  // DMA instructions per wave and tile
+#pragma unroll
+    for (int t = 0; t < kBlockNBwd / 64; ++t)
+#pragma unroll
+      for (int u = 0; u < DPW; ++u) {
+        u32x4_t* slot = reinterpret_cast<u32x4_t*>(vres + t * L::ELEMS + (wave * DPW + u) * 512 + 8 * lane);
+        *slot = *slot ^ 0x80008000u;
+      }
+  }
 
   // Query rows that can see any key of the workgroup: [q_lo, Lq).
   int q_lo = first_query_row<STRIPED>(p, k0, kBlockNBwd, qpos0);
@@ -682,7 +698,16 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
       const bool full = uni && qb + 31 < p.seq_q && (c == 0 || qpos0 + qb >= thr_last);
       if (!run) continue;
 
-      f32x16_t sc = f32x16_t{}, dp = f32x16_t{};
+      f32x16_t sc = f32x16_t{}, dp;
+      // dp = delta of the lane's 16 query rows (rows 8 (e / 4) + 4 half + e % 4).
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 d4 = *reinterpret_cast<const float4*>(dlt_t + 32 * qh + 8 * g + 4 * half);
+        dp[4 * g] = d4.x;
+        dp[4 * g + 1] = d4.y;
+        dp[4 * g + 2] = d4.z;
+        dp[4 * g + 3] = d4.w;
+      }
       auto vread = [&](int cc) {
         return *reinterpret_cast<const bf16x8_t*>(vres + (wave >> 1) * L::ELEMS +
                                                   row_rd_c(r_rd, cc) + row_off(cc, wave & 1));
@@ -719,25 +744,37 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
       // ds overwrite the scores and dp in place.
       const int32_t lo = thr == INT32_MIN ? INT32_MIN : thr - (qpos0 + qb);
       const int32_t hi = p.seq_q - qb;
+      // Without segment ids, two copies of the softmax: fully visible blocks
+      // (nearly all of a long share) skip the per-pair visibility test,
+      // which, merged into one path with a select, costs two compares, three
+      // mask operations and a select per pair.  The segment-id kernels have
+      // no registers for the second copy and keep the merged path.
+      auto softmax = [&](auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 l4 = *reinterpret_cast<const float4*>(lse_t + 32 * qh + 8 * g + 4 * half);
-        const float4 d4 = *reinterpret_cast<const float4*>(dlt_t + 32 * qh + 8 * g + 4 * half);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+        for (int g = 0; g < 4; ++g) {
+          const float4 l4 = *reinterpret_cast<const float4*>(lse_t + 32 * qh + 8 * g + 4 * half);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = 4 * g + i;
-          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], p.scale_log2, -lv[i] * kLog2e));
-          if (!full) {
-            const int off = 8 * g + 4 * half + i;
-            bool ok = off >= lo && off < hi;
-            if (SEG && !uni) ok = ok && sg[32 * qh + off] == seg_k;
-            pr = ok ? pr : 0.f;
+          for (int i = 0; i < 4; ++i) {
+            const int e = 4 * g + i;
+            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], p.scale_log2, -lv[i] * kLog2e));
+            // (Without segment ids the masked copy runs only when !full.)
+            if (MASKED && (!SEG || !full)) {
+              const int off = 8 * g + 4 * half + i;
+              bool ok = off >= lo && off < hi;
+              if (SEG && !uni) ok = ok && sg[32 * qh + off] == seg_k;
+              pr = ok ? pr : 0.f;
+            }
+            sc[e] = pr;
+            dp[e] = -pr * dp[e];  // p (dout.v_j - delta): dp holds delta - dout.v_j
           }
-          sc[e] = pr;
-          dp[e] = pr * (dp[e] - dvv[i]);
         }
-      }
+      };
+      if (!SEG && full)
+        softmax(std::false_type{});
+      else
+        softmax(std::true_type{});
       bf16x8_t pb[2], db[2];
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {

@@ -246,13 +246,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bias_kernel(const GemmAr
   const int wm = (wave & 1) * C::WM, wn = (wave >> 1) * C::WN;  // the wave's quarter
 
   // Per-lane parts of the operand addresses (bf16 elements).
-  const int l32 = lane & 31, h = lane >> 5, g16 = lane >> 4, j16 = lane & 15;
+  const int l32 = lane & 31, h = lane >> 5;
   const int x_rd = ((l32 >> 4) * 64 + h * 16 + (lane & 15)) * 8 + (wm / 16) * 512;
-  // W: lane reads row kr = 8 (g16 / 2) + j16 / 4 (+ ks * 16, + 4 for the
-  // second read; kr % 4 = j16 / 4 either way) at column wn + 32 nb + 16 (g16
-  // % 2) + 4 (j16 % 4): granule gc = (wn + 32 nb) / 8 + 2 (g16 % 2) + (j16 %
-  // 4) / 2, stored at slot kr * BN / 8 + (gc ^ 4 (kr % 4)).  The XOR
-  // touches the bits of gc that nb sets, so each nb has its own base.
+  // W: with g16 = lane / 16 and j16 = lane % 16, the lane reads row kr =
+  // 8 (g16 / 2) + j16 / 4 (+ ks * 16, + 4 for the second read; kr % 4 =
+  // j16 / 4 either way) at column wn + 32 nb + 16 (g16 % 2) + 4 (j16 % 4):
+  // granule gc = (wn + 32 nb) / 8 + 2 (g16 % 2) + (j16 % 4) / 2, stored at
+  // slot kr * BN / 8 + (gc ^ 4 (kr % 4)).  The XOR touches the bits of gc
+  // that nb sets, so each nb has its own base.
   int w_rd[C::NB];
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb) w_rd[nb] = C::X_ELEMS + lds::gemm_w_rd(lane, wn, nb, BN);
