@@ -102,6 +102,12 @@ __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// s_waitcnt lgkmcnt(0): this wave's LDS writes have completed (gfx9
+// encoding; vmcnt and expcnt not waited).  A barrier alone does not wait for
+// them on gfx950, so writes that other waves read after a barrier wait here
+// first.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
 // ---------------------------------------------------------------------------
 // delta_i = <dout_i, out_i>
 // ---------------------------------------------------------------------------
@@ -564,6 +570,7 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
         u32x4_t* slot = reinterpret_cast<u32x4_t*>(vres + t * L::ELEMS + (wave * DPW + u) * 512 + 8 * lane);
         *slot = *slot ^ 0x80008000u;
       }
+    wait_lds();
   }
 
   // Query rows that can see any key of the workgroup: [q_lo, Lq).
@@ -593,6 +600,17 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
   };
   // A wave's DMA count per query tile (waves 0 and 1 issue one more).
   const bool extra = wave < 2;
+  // Wave 0, which fetched the stage's 64 lse, rewrites them as
+  // -lse log2(e), the exponent's offset, once per query tile instead of once
+  // per pair.  Its DMA must have landed (vmcnt), and the rewrite completes
+  // before the barrier after which the stage is read.
+  auto prep_lse = [&](int s) {
+    if (wave != 0) return;
+    wait_vm<0>();
+    float* l = reinterpret_cast<float*>(qs + s * L::QSTAGE + 2 * L::ELEMS + 128);
+    l[lane] = l[lane] * -kLog2e;
+    wait_lds();
+  };
 
   // Segment ids: list the query tiles whose id range meets the id range of
   // the workgroup's keys (exact: disjoint ranges share no id); the walk
@@ -657,7 +675,10 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
     dv[j] = f32x16_t{};
   }
 
-  if (n_run > 0) fetch(tile_of(0), 0);
+  if (n_run > 0) {
+    fetch(tile_of(0), 0);
+    prep_lse(0);
+  }
   for (int it = 0; it < n_run; ++it) {
     const int qt = tile_of(it);
     const int s = it & 1;
@@ -681,6 +702,9 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
     const int q0 = q_lo + 64 * qt;
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
+      // The next stage's lse, between the two halves: its DMA has had half
+      // a tile step, and the other wave of the SIMD runs meanwhile.
+      if (qh == 1 && it + 1 < n_run) prep_lse(s ^ 1);
       const int qb = q0 + 32 * qh;  // local row of the block's first query
       // Does the block hold a visible pair, and is every pair visible?
       const int qlast = std::min(qb + 31, p.seq_q - 1);
@@ -758,7 +782,8 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int e = 4 * g + i;
-            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], p.scale_log2, -lv[i] * kLog2e));
+            // lv = -lse log2(e), rewritten in the stage by prep_lse.
+            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], p.scale_log2, lv[i]));
             // (Without segment ids the masked copy runs only when !full.)
             if (MASKED && (!SEG || !full)) {
               const int off = 8 * g + 4 * half + i;
