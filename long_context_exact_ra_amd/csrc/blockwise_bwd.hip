@@ -384,13 +384,13 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dq_kernel(const BwdParams 
       dof[c] = *reinterpret_cast<const bf16x8_t*>(grow + 16 * c + 8 * w.half);
     }
     const int64_t li = ((int64_t)b * p.heads + h) * p.seq_q + w.qg0 + w.lrow;
-    lse2 = bp.lse[li] * kLog2e;
+    lse2 = bp.lse[li];
     dlt = bp.delta[li];
   }
-  f32x16_t ndlt;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) ndlt[i] = -dlt;
-  __builtin_amdgcn_s_waitcnt(0);
+  // These loads stay in flight while the prologue's K/V DMA is issued (a
+  // workgroup of a short walk would otherwise pay both latencies in turn);
+  // their values are first used after the prologue's wait.  The compiler
+  // does not count the DMA (inline asm), so it waits for every load there.
 
   f32x16_t acc[NDB];
 #pragma unroll
@@ -425,6 +425,13 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dq_kernel(const BwdParams 
   else
     wait_vm<0>();
   stage_barrier();
+  // (The empty asm keeps the compiler from hoisting the uses, and its wait
+  // for the loads, above the DMA.)
+  asm volatile("" : "+v"(lse2), "+v"(dlt));
+  lse2 *= kLog2e;
+  f32x16_t ndlt;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ndlt[i] = -dlt;
 
   auto step = [&](auto PHc) -> bool {
     constexpr int PH = decltype(PHc)::value;

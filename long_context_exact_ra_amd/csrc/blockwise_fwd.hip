@@ -658,9 +658,11 @@ __global__ __launch_bounds__(PipeCfg<D>::kThreads, 1) void fwd_bf16_kernel(const
       qf[c] = __builtin_bit_cast(bf16x8_t,
                                  *reinterpret_cast<const uint4*>(qrow + 16 * c + 8 * k.half));
   }
-  // Let the Q (and segment id) loads land now: from here on the vector
-  // memory counter only tracks the K/V DMA, whose waits are explicit.
-  __builtin_amdgcn_s_waitcnt(0);
+  // The Q (and segment id) loads stay in flight while the prologue's K/V
+  // DMA is issued: a workgroup of a short walk would otherwise pay both
+  // latencies in turn.  The compiler does not count the DMA (inline asm),
+  // so it waits for every load before the first use of Q (the prologue's
+  // QK, by when tiles 0-2 are due anyway).
 
   PipeState<D> st;
 #pragma unroll
