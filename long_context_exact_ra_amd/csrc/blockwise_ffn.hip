@@ -20,17 +20,23 @@
 // each owning a 128 x (BN / 2) quarter: 4 x (BN / 64) accumulators of 32 x
 // 32, up to 256 float32 per lane (the accumulation registers).
 //
-// K is walked in stages of 32.  X and W stage tiles flow through a ring of
-// 5 LDS stages (160 KB for 256 x 256 tiles) filled by bounds-checked
-// buffer-to-LDS DMA (buffer_load_dwordx4 ... lds) four stages ahead; rows
-// past M (X) and past K (W) read as zero, so ragged M and K need no special
-// path (columns past N compute values that are never stored).  Layouts
-// (16-byte slots; g = the 16-byte granule of a row):
-//   X stage, 256 rows m x 4 granules: slot(m, g) = (m / 16) * 64 + g * 16 +
-//     m % 16.  A DMA instruction (64 lanes x 16 bytes) fills 16 rows x 4
-//     granules; the X^T operand of 16 consecutive lanes (16 rows, one
-//     granule: 8 consecutive k of each row) is 256 contiguous bytes, one
-//     ds_read_b128.
+// K is walked in stages of 32 (two MFMA steps of 16).  X arrives in pair
+// stages of 64 k through a ring of 3 LDS slots, W in stages of 32 k through
+// a ring of 4 (160 KB for 256 x 256 tiles), filled by bounds-checked
+// buffer-to-LDS DMA (buffer_load_dwordx4 ... lds) about four stages ahead;
+// rows past M (X) and past K (W) read as zero, so ragged M and K need no
+// special path (columns past N compute values that are never stored).  The
+// X pair is what makes the DMA fast: a DMA instruction then fetches 8 whole
+// 128-byte rows of X, where 16 half rows (a 32-deep stage) move at about
+// 18 bytes per clock and compute unit, less than a third of the rate of
+// whole lines, and held the kernel to 834 TFLOP/s on the 7B-shaped shape.
+// Layouts (16-byte slots; g = the 16-byte granule of a row):
+//   X pair stage, 256 rows m x 8 granules: slot(m, g) = (m / 8) * 64 +
+//     (g ^ ((m / 8) % 2)) * 8 + m % 8.  A DMA instruction (64 lanes x 16
+//     bytes) fills 8 rows x 8 granules; the X^T operand of 16 consecutive
+//     lanes (16 rows, one granule: 8 consecutive k of each row) is one
+//     ds_read_b128 touching every bank once (the odd blocks' granule
+//     permutation puts the second 8 rows on the other half of the banks).
 //   W stage, 32 rows k x BN / 8 granules, row-major with the granules of row
 //     k permuted: slot k * BN / 8 + j holds granule j ^ 4 (k % 4).  A DMA
 //     instruction fetches whole rows (64 lanes, BN / 8 per row); two
@@ -48,10 +54,9 @@
 //
 // Measured on the 7B-shaped feedforward (32768 tokens, hidden 4096, ffn
 // 16384, chunks of 2048): the data movement into LDS, not the LDS reads or
-// the barriers, separates this kernel from hipBLASLt's (timing variants
+// the barriers, separated this kernel from hipBLASLt's (timing variants
 // with the DMA removed ran 40 % faster, with the transposing reads replaced
-// by plain ones no faster); issuing each stage's DMA spread over the MFMAs,
-// whole W rows per instruction and a fifth stage gained 3 %.
+// by plain ones no faster), and within it the half-line X fetches.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -69,8 +74,9 @@ namespace {
 
 constexpr int kGemmWaves = 4;
 constexpr int kGemmThreads = 64 * kGemmWaves;
-constexpr int kBK = 32;    // k per LDS stage
-constexpr int kStages = 5;
+constexpr int kBK = 32;     // k per MFMA stage (two 16-k steps)
+constexpr int kXSlots = 3;  // X pair stages (64 k each) in LDS
+constexpr int kWSlots = 4;  // W stages (32 k each) in LDS
 
 // A BM x BN tile per workgroup, 4 waves in a 2 x 2 layout, each owning a
 // (BM / 2) x (BN / 2) quarter: MB 32-row blocks x NB 32-column blocks.
@@ -78,13 +84,13 @@ template <int BM, int BN>
 struct GemmCfg {
   static constexpr int WM = BM / 2, WN = BN / 2;  // rows / columns per wave
   static constexpr int MB = WM / 32, NB = WN / 32;
-  static constexpr int X_ELEMS = BM * kBK;   // bf16 per X stage tile
-  static constexpr int W_ELEMS = kBK * BN;   // bf16 per W stage tile
-  static constexpr int STAGE = X_ELEMS + W_ELEMS;
-  static constexpr int X_DMA = BM / 16 / kGemmWaves;       // DMA instructions per wave
+  static constexpr int X_PAIR = BM * 2 * kBK;     // bf16 per X pair stage (64 k)
+  static constexpr int W_ELEMS = kBK * BN;        // bf16 per W stage
+  static constexpr int LDS = kXSlots * X_PAIR + kWSlots * W_ELEMS;
+  static constexpr int XH = BM / 8 / 2 / kGemmWaves;  // X DMA per wave: half a pair
   static constexpr int W_DMA = kBK * BN / 512 / kGemmWaves;
-  static constexpr int NPT = X_DMA + W_DMA;                // per wave per stage
-  static_assert(X_DMA * 16 * kGemmWaves == BM && W_DMA * 512 * kGemmWaves == kBK * BN,
+  static constexpr int NPT = XH + W_DMA;              // DMA per wave per iteration
+  static_assert(XH * 8 * 2 * kGemmWaves == BM && W_DMA * 512 * kGemmWaves == kBK * BN,
                 "stage tiles must split evenly over the waves");
 };
 
@@ -97,96 +103,64 @@ struct GemmArgs {
   int32_t tiles_m, tiles_n;
 };
 
-// Issue this wave's share of the DMA of K-stage kt into LDS stage `st`.
+// DMA instruction u of this wave's share of one iteration's group: u < XH:
+// half h of X pair stage q (k 64 q .. 64 q + 63) into `xs`; else W stage kt
+// (k 32 kt .. 32 kt + 31) into `ws`.
 template <int BM, int BN>
-__device__ __forceinline__ void gemm_fetch(const GemmArgs& a, int m0, int n0, int kt, __bf16* st,
-                                           int wave, int lane) {
+__device__ __forceinline__ void gemm_fetch_one(const GemmArgs& a, int m0, int n0, int q, int h,
+                                               __bf16* xs, int kt, __bf16* ws, int wave, int lane,
+                                               int u) {
   using C = GemmCfg<BM, BN>;
-  const int k0 = kt * kBK;
-  // X rows [0, M) of the chunk: rows past M read as zero.
-  const i32x4_t xr = rsrc_words(a.x, (uint32_t)a.m * (uint32_t)a.k * 2u);
-  // W rows [k0, K): rows past K read as zero.
-  const i32x4_t wr = rsrc_words(a.w + (int64_t)k0 * a.n, (uint32_t)(a.k - k0) * (uint32_t)a.n * 2u);
-#pragma unroll
-  for (int u = 0; u < C::X_DMA; ++u) {
-    const int i = wave * C::X_DMA + u;  // 16 rows of the tile
-    const uint32_t off = (uint32_t)(m0 + 16 * i + (lane & 15)) * (uint32_t)a.k * 2u +
-                         (uint32_t)(k0 + 8 * (lane >> 4)) * 2u;
-    dma_b128(lds_addr(st + i * 512), off, xr);
-  }
-  // W: whole rows of the stage tile per instruction (BN / 8 lanes per row);
-  // slot k * (BN / 8) + j of the stage holds granule j ^ 4 (k % 4) of row k.
-  constexpr int GPR = BN / 8;          // granules per row
-  constexpr int RPI = 64 / GPR;        // rows per DMA instruction
-#pragma unroll
-  for (int u = 0; u < C::W_DMA; ++u) {
-    const int i = wave * C::W_DMA + u;
-    const int k = RPI * i + lane / GPR;
-    const int g = lds::gemm_w_gran(k, lane % GPR);
-    const uint32_t off = (uint32_t)k * (uint32_t)a.n * 2u + (uint32_t)(n0 + 8 * g) * 2u;
-    dma_b128(lds_addr(st + C::X_ELEMS + i * 512), off, wr);
-  }
-}
-
-// One of this wave's NPT DMA instructions of K-stage kt (u < X_DMA: X,
-// else W), the same as gemm_fetch issues them.
-template <int BM, int BN>
-__device__ __forceinline__ void gemm_fetch_one(const GemmArgs& a, int m0, int n0, int kt,
-                                               __bf16* st, int wave, int lane, int u) {
-  using C = GemmCfg<BM, BN>;
-  const int k0 = kt * kBK;
-  if (u < C::X_DMA) {
+  if (u < C::XH) {
+    // X rows [0, M) of the chunk: rows past M read as zero.  Instruction i
+    // fetches rows 8 i .. 8 i + 7 of the tile, whole 128-byte rows.
     const i32x4_t xr = rsrc_words(a.x, (uint32_t)a.m * (uint32_t)a.k * 2u);
-    const int i = wave * C::X_DMA + u;
-    const uint32_t off = (uint32_t)(m0 + 16 * i + (lane & 15)) * (uint32_t)a.k * 2u +
-                         (uint32_t)(k0 + 8 * (lane >> 4)) * 2u;
-    dma_b128(lds_addr(st + i * 512), off, xr);
+    const int i = (BM / 16) * h + wave * C::XH + u;
+    const uint32_t off = (uint32_t)(m0 + lds::gemm_x_dma_row(lane, i)) * (uint32_t)a.k * 2u +
+                         (uint32_t)(64 * q + 8 * lds::gemm_x_dma_gran(lane, i)) * 2u;
+    dma_b128(lds_addr(xs + i * 512), off, xr);
   } else {
+    // W rows [k0, K): rows past K read as zero.  Whole rows of the stage
+    // tile per instruction (BN / 8 lanes per row); slot k * (BN / 8) + j of
+    // the stage holds granule j ^ 4 (k % 4) of row k.
+    const int k0 = kt * kBK;
     const i32x4_t wr =
         rsrc_words(a.w + (int64_t)k0 * a.n, (uint32_t)(a.k - k0) * (uint32_t)a.n * 2u);
-    constexpr int GPR = BN / 8, RPI = 64 / GPR;
-    const int i = wave * C::W_DMA + (u - C::X_DMA);
+    constexpr int GPR = BN / 8, RPI = 64 / GPR;  // granules per row, rows per instruction
+    const int i = wave * C::W_DMA + (u - C::XH);
     const int k = RPI * i + lane / GPR;
     const int g = lds::gemm_w_gran(k, lane % GPR);
     const uint32_t off = (uint32_t)k * (uint32_t)a.n * 2u + (uint32_t)(n0 + 8 * g) * 2u;
-    dma_b128(lds_addr(st + C::X_ELEMS + i * 512), off, wr);
+    dma_b128(lds_addr(ws + i * 512), off, wr);
   }
 }
 
-// Wait until at most `pending` (0 or 1) later stages of this wave are still
-// in flight (explicit counts: the DMA is invisible to the compiler).
-template <int NPT>
-__device__ __forceinline__ void gemm_wait(int pending) {
-  if (pending >= 1)
-    wait_vm<NPT>();
-  else
-    wait_vm<0>();
-}
-
-// The operands of one 16-k step of a stage: W^T of the wave's NB column
-// blocks (two transposing reads each) and X^T of its MB row blocks.
+// The operands of one 16-k step: W^T of the wave's NB column blocks (two
+// transposing reads each) and X^T of its MB row blocks.
 template <int BM, int BN>
 struct Operands {
   bf16x8_t w[GemmCfg<BM, BN>::NB], x[GemmCfg<BM, BN>::MB];
 };
 
+// Step ks of the 32-k stage held by W stage `ws` and half sp of X pair `xs`.
 template <int BM, int BN>
-__device__ __forceinline__ void read_operands(Operands<BM, BN>& o, const __bf16* st,
+__device__ __forceinline__ void read_operands(Operands<BM, BN>& o, const __bf16* xs,
+                                              const __bf16* ws,
                                               const int (&w_rd)[GemmCfg<BM, BN>::NB], int x_rd,
-                                              int ks) {
+                                              int sp, int ks) {
   using C = GemmCfg<BM, BN>;
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb) {
     // rows ks*16 .. of the swizzled row-major W stage (the lane's base
     // w_rd[nb] holds its row and swizzled granule; the rest is a constant)
-    const __bf16* src = st + w_rd[nb] + ks * 16 * BN;
+    const __bf16* src = ws + w_rd[nb] + ks * 16 * BN;
     const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)src);
     const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(src + 4 * BN));
     o.w[nb] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 #pragma unroll
   for (int mb = 0; mb < C::MB; ++mb)
-    o.x[mb] = *reinterpret_cast<const bf16x8_t*>(st + x_rd + mb * 1024 + ks * 256);
+    o.x[mb] = *reinterpret_cast<const bf16x8_t*>(xs + x_rd + mb * 2048 + sp * 256 + ks * 128);
 }
 
 // acc[nb * MB + mb]: the accumulator of column block nb, row block mb.
@@ -219,18 +193,27 @@ __device__ __forceinline__ void mma_step_hook(f32x16_t* acc, const Operands<BM, 
     }
 }
 
-// Pipeline per stage kt (two 16-k steps): the operands of step 0 are already
-// in registers (read in the previous iteration); read those of step 1, run
-// step 0's MFMAs; then the stage barrier -- stage kt + 1 has landed for
-// every wave and every wave is done with stage kt - 1 -- the reads of stage
-// kt + 1's step 0, and step 1's MFMAs with the DMA of stage kt + 4 (into
-// stage kt - 1's place) spread between them.  Operand reads thus run one
-// step ahead of the MFMAs, also across the barrier, and no stage starts by
-// waiting on LDS.
+// Floor division by 2 (for the prologue's negative iteration numbers).
+__device__ __forceinline__ constexpr int half_floor(int v) { return v >= 0 ? v / 2 : -((1 - v) / 2); }
+
+// Iteration j's DMA group: W stage j + 4 (into the slot of stage j, whose
+// reads are done after iteration j's barrier) and half (j + 1) % 2 of X pair
+// q = floor((j + 1) / 2) + 2 (into the slot of pair q - 3, also done).  Each
+// group is XH + W_DMA instructions per wave while the stages exist, so a
+// stage's data is complete once every group but the last two has landed.
+// Pipeline per iteration kt (stage kt's two 16-k steps): the operands of
+// step 0 are already in registers (read in the previous iteration); read
+// those of step 1, run step 0's MFMAs; then the stage barrier -- stage
+// kt + 1 has landed for every wave and every wave is done with stage kt --
+// the reads of stage kt + 1's step 0, and step 1's MFMAs with the group's
+// DMA spread between them.  Operand reads thus run one step ahead of the
+// MFMAs, also across the barrier, and no stage starts by waiting on LDS.
 template <int BM, int BN, bool RELU>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bias_kernel(const GemmArgs a) {
   using C = GemmCfg<BM, BN>;
-  __shared__ __attribute__((aligned(16))) __bf16 lds[kStages * C::STAGE];
+  __shared__ __attribute__((aligned(16))) __bf16 lds[C::LDS];
+  __bf16* const xbase = lds;                          // kXSlots X pair stages
+  __bf16* const wbase = lds + kXSlots * C::X_PAIR;    // kWSlots W stages
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -246,8 +229,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bias_kernel(const GemmAr
   const int wm = (wave & 1) * C::WM, wn = (wave >> 1) * C::WN;  // the wave's quarter
 
   // Per-lane parts of the operand addresses (bf16 elements).
-  const int l32 = lane & 31, h = lane >> 5;
-  const int x_rd = ((l32 >> 4) * 64 + h * 16 + (lane & 15)) * 8 + (wm / 16) * 512;
+  const int x_rd = lds::gemm_x_rd(lane, wm);
   // W: with g16 = lane / 16 and j16 = lane % 16, the lane reads row kr =
   // 8 (g16 / 2) + j16 / 4 (+ ks * 16, + 4 for the second read; kr % 4 =
   // j16 / 4 either way) at column wn + 32 nb + 16 (g16 % 2) + 4 (j16 % 4):
@@ -256,74 +238,72 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bias_kernel(const GemmAr
   // that nb sets, so each nb has its own base.
   int w_rd[C::NB];
 #pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb) w_rd[nb] = C::X_ELEMS + lds::gemm_w_rd(lane, wn, nb, BN);
+  for (int nb = 0; nb < C::NB; ++nb) w_rd[nb] = lds::gemm_w_rd(lane, wn, nb, BN);
 
   f32x16_t acc[C::NB * C::MB];
 #pragma unroll
   for (int i = 0; i < C::NB * C::MB; ++i) acc[i] = f32x16_t{};
 
   const int nk = (a.k + kBK - 1) / kBK;
-  // Prologue: stages 0 .. 3 in flight; stage 0 landed; its step-0 operands.
+  auto xslot = [&](int q) { return xbase + (q % kXSlots) * C::X_PAIR; };
+  auto wslot = [&](int kt) { return wbase + (kt % kWSlots) * C::W_ELEMS; };
+  // Iteration j's group, instruction u (stages past K are not fetched).
+  auto group_one = [&](int j, int u) {
+    const int q = half_floor(j + 1) + 2, h = (j + 1) & 1;
+    const bool x_ok = 2 * q < nk, w_ok = j + 4 < nk && j + 4 >= 0;
+    if (u < C::XH ? x_ok : w_ok)
+      gemm_fetch_one<BM, BN>(a, m0, n0, q, h, xslot(q), j + 4, wslot(j + 4), wave, lane, u);
+  };
+  // Prologue: the groups of iterations -5 .. -1 (W stages 0 .. 3, X pairs 0
+  // and 1, half of pair 2); stage 0 complete once the first two have landed.
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < nk) gemm_fetch<BM, BN>(a, m0, n0, s, lds + s * C::STAGE, wave, lane);
-  {
-    const int pend = nk - 1 < 3 ? nk - 1 : 3;
-    if (pend >= 3)
-      wait_vm<3 * C::NPT>();
-    else if (pend == 2)
-      wait_vm<2 * C::NPT>();
-    else if (pend == 1)
-      wait_vm<C::NPT>();
-    else
-      wait_vm<0>();
-  }
+  for (int j = -5; j < 0; ++j)
+#pragma unroll
+    for (int u = 0; u < C::NPT; ++u) group_one(j, u);
+  if (nk > 4)
+    wait_vm<3 * C::NPT>();
+  else
+    wait_vm<0>();
   stage_barrier();
   Operands<BM, BN> op0, op1;
-  read_operands<BM, BN>(op0, lds, w_rd, x_rd, 0);
+  read_operands<BM, BN>(op0, xslot(0), wslot(0), w_rd, x_rd, 0, 0);
 
   // Every stage but the last; the loop body has no branch around the
   // barrier, so the compiler's LDS waits stay exact (LDS reads complete in
   // order: a conservative wait on an earlier read would also wait for the
-  // next stage's reads issued after it).  cur / nxt: LDS stages of kt and
-  // kt + 1 (mod 5).
-  int cur = 0;
+  // next stage's reads issued after it).
   for (int kt = 0; kt + 1 < nk; ++kt) {
-    const int nxt = cur == kStages - 1 ? 0 : cur + 1;
-    const int prv = cur == 0 ? kStages - 1 : cur - 1;  // stage of kt - 1 = kt + 4
-    read_operands<BM, BN>(op1, lds + cur * C::STAGE, w_rd, x_rd, 1);
+    read_operands<BM, BN>(op1, xslot(kt >> 1), wslot(kt), w_rd, x_rd, kt & 1, 1);
     mma_step<BM, BN>(acc, op0);
-    // Stage kt + 1 must have landed (stages kt + 1 .. kt + 3, as far as
-    // issued, are in flight here).
-    {
-      const int pend = nk - kt - 2 < 2 ? nk - kt - 2 : 2;
-      if (pend >= 2)
-        wait_vm<2 * C::NPT>();
-      else if (pend == 1)
-        wait_vm<C::NPT>();
-      else
-        wait_vm<0>();
-    }
+    // Stage kt + 1 must have landed: the groups of iterations kt - 2 and
+    // kt - 1 may still be in flight (all complete near the end of K).
+    if (kt + 4 < nk)
+      wait_vm<2 * C::NPT>();
+    else
+      wait_vm<0>();
+    // This wave's reads of stage kt (issued before the MFMAs above) have
+    // completed: after the barrier the DMA may overwrite its slots.  (The
+    // barrier's fence waits only after it.)
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     stage_barrier();
-    read_operands<BM, BN>(op0, lds + nxt * C::STAGE, w_rd, x_rd, 0);
-    // the DMA of stage kt + 4, spread over the MFMAs
-    const bool dma = kt + 4 < nk;
-    __bf16* const dst = lds + prv * C::STAGE;
-    // (instruction u after MFMA u * MFMAs / NPT: every instruction once)
-    mma_step_hook<BM, BN>(acc, op1, [&](int j) {
+    read_operands<BM, BN>(op0, xslot((kt + 1) >> 1), wslot(kt + 1), w_rd, x_rd, (kt + 1) & 1, 0);
+    // this iteration's group, spread over the MFMAs (instruction u after
+    // MFMA u * MFMAs / NPT: every instruction once)
+    mma_step_hook<BM, BN>(acc, op1, [&](int jm) {
       constexpr int M = C::NB * C::MB;
 #pragma unroll
       for (int u = 0; u < C::NPT; ++u)
-        if (u * M / C::NPT == j && dma) gemm_fetch_one<BM, BN>(a, m0, n0, kt + 4, dst, wave, lane, u);
+        if (u * M / C::NPT == jm) group_one(kt, u);
     });
-    cur = nxt;
   }
-  read_operands<BM, BN>(op1, lds + cur * C::STAGE, w_rd, x_rd, 1);
+  read_operands<BM, BN>(op1, xslot((nk - 1) >> 1), wslot(nk - 1), w_rd, x_rd, (nk - 1) & 1, 1);
   mma_step<BM, BN>(acc, op0);
   mma_step<BM, BN>(acc, op1);
+  // (Every DMA group issued was waited for by the last iteration's wait.)
 
   // Epilogue: + bias (fp32), ReLU, one rounding to bf16.  Lane: row m,
   // columns n .. n + 3 of each group of four.
+  const int l32 = lane & 31, h = lane >> 5;
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
   typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 #pragma unroll

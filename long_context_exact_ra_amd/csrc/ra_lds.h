@@ -84,5 +84,29 @@ constexpr int gemm_w_rd(int lane, int wn, int nb, int bn) {
          4 * (lane & 1);
 }
 
+// ---------------------------------------------------------------------------
+// Feedforward GEMM, X pair stage: BM rows m x 64 k (8 granules of 16 bytes:
+// two 32-deep stages), so that a DMA instruction fetches whole 128-byte
+// rows (8 rows x 8 granules): 16 rows x 64 bytes per instruction move at a
+// fraction of the rate.  Blocks of 8 rows, granules permuted in odd blocks:
+//   slot(m, g) = (m / 8) * 64 + (g ^ ((m / 8) % 2)) * 8 + m % 8
+// A row read (ds_read_b128, 16 lanes: rows m0 .. m0 + 15 of one granule,
+// m0 % 16 = 0) then touches 8 slots of an even block and 8 of an odd block
+// that differ in bit 3: 16 slots distinct modulo 16, every bank once.
+// ---------------------------------------------------------------------------
+
+constexpr int gemm_x_slot(int m, int g) { return (m / 8) * 64 + (g ^ ((m / 8) & 1)) * 8 + m % 8; }
+// DMA instruction i (rows 8 i .. 8 i + 7 of the pair tile), lane l writes
+// slot 64 i + l: it loads row 8 i + l % 8 and granule (l / 8) ^ (i % 2).
+constexpr int gemm_x_dma_row(int lane, int i) { return 8 * i + (lane & 7); }
+constexpr int gemm_x_dma_gran(int lane, int i) { return (lane >> 3) ^ (i & 1); }
+// X^T operand of row block mb (32 rows) of a wave whose rows start at wm
+// (a multiple of 32), 16-k step ks of 32-deep stage sp within the pair:
+// lane l reads row wm + 32 mb + l % 32, granule 4 sp + 2 ks + l / 32, as
+// element offset gemm_x_rd(lane, wm) + 2048 mb + 256 sp + 128 ks.
+constexpr int gemm_x_rd(int lane, int wm) {
+  return 8 * gemm_x_slot(wm + (lane & 31), lane >> 5);
+}
+
 }  // namespace lds
 }  // namespace ra

@@ -178,6 +178,51 @@ static void check_gemm_w(int BN) {
   }
 }
 
+// The GEMM's X pair stage: BM rows x 8 granules (64 k).  The slot map is a
+// bijection, DMA instruction i places (row, granule) where the layout wants
+// them while reading whole 128-byte rows, and every X^T operand read gives
+// lane l row wm + 32 mb + l % 32 and k = 32 sp + 16 ks + 8 (l / 32) .. + 7
+// (the k-slots the W^T operand pairs with) and touches every bank once per
+// 16 lanes.
+static void check_gemm_x(int BM) {
+  std::map<int, std::pair<int, int>> at;
+  for (int m = 0; m < BM; ++m)
+    for (int g = 0; g < 8; ++g) {
+      const int s = l::gemm_x_slot(m, g);
+      CHECK(s >= 0 && s < BM * 8, "X slot range BM %d m %d g %d", BM, m, g);
+      CHECK(at.count(s) == 0, "X slot %d used twice", s);
+      at[s] = {m, g};
+    }
+  for (int i = 0; i < BM / 8; ++i) {
+    std::set<int> rows;
+    for (int lane = 0; lane < 64; ++lane) {
+      const int m = l::gemm_x_dma_row(lane, i), g = l::gemm_x_dma_gran(lane, i);
+      CHECK(l::gemm_x_slot(m, g) == 64 * i + lane, "X dma BM %d i %d lane %d", BM, i, lane);
+      rows.insert(m);
+    }
+    // whole rows: 8 rows, each with all 8 granules
+    CHECK((int)rows.size() == 8, "X dma instruction %d covers %d rows", i, (int)rows.size());
+  }
+  for (int wm : {0, BM / 2})
+    for (int mb = 0; mb < BM / 2 / 32; ++mb)
+      for (int sp = 0; sp < 2; ++sp)
+        for (int ks = 0; ks < 2; ++ks) {
+          std::vector<int> addr(64);
+          for (int lane = 0; lane < 64; ++lane) {
+            const int e0 = l::gemm_x_rd(lane, wm) + 2048 * mb + 256 * sp + 128 * ks;
+            CHECK(e0 % 8 == 0, "X read not slot aligned");
+            const auto mg = at.at(e0 / 8);
+            CHECK(mg.first == wm + 32 * mb + lane % 32 && 8 * mg.second == 32 * sp + 16 * ks + 8 * (lane / 32),
+                  "X operand BM %d wm %d mb %d sp %d ks %d lane %d: row %d granule %d", BM, wm, mb, sp,
+                  ks, lane, mg.first, mg.second);
+            addr[lane] = 2 * e0;
+          }
+          for (int q = 0; q < 4; ++q)
+            CHECK(covers_all_banks_once(std::vector<int>(addr.begin() + 16 * q, addr.begin() + 16 * q + 16), 16),
+                  "X read banks BM %d wm %d mb %d sp %d ks %d quarter %d", BM, wm, mb, sp, ks, q);
+        }
+}
+
 // The checker's own sensitivity: the unswizzled layout (slot (g / 4) * 256
 // + (r / 16) * 64 + (g % 4) * 16 + r % 16, the forward's K layout) gives the
 // same elements to every lane but a 4-way bank conflict on every column
@@ -203,6 +248,7 @@ int main() {
   check_detects_conflicts();
   for (int D : {64, 128}) check_bwd(D);
   for (int BN : {128, 256}) check_gemm_w(BN);
+  for (int BM : {128, 256}) check_gemm_x(BM);
   std::printf("%ld checks: %ld failure(s)\n", g_checks, g_fail);
   return g_fail == 0 ? 0 : 1;
 }

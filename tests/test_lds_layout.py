@@ -1,5 +1,6 @@
 """The LDS layouts read both as rows and transposed (the backward's tiles,
-the feedforward GEMM's W stage; ``csrc/ra_lds.h``) checked on the host:
+the feedforward GEMM's W stage) and the GEMM's X pair stage
+(``csrc/ra_lds.h``) checked on the host:
 every lane of every operand read receives the tile elements the MFMA
 operand layout asks for, the DMA lands every row and granule where the
 readers look, and every read touches each LDS bank once per cycle (the
