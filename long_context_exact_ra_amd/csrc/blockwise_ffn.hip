@@ -103,35 +103,60 @@ struct GemmArgs {
   int32_t tiles_m, tiles_n;
 };
 
-// DMA instruction u of this wave's share of one iteration's group: u < XH:
-// half h of X pair stage q (k 64 q .. 64 q + 63) into `xs`; else W stage kt
-// (k 32 kt .. 32 kt + 31) into `ws`.
+// The per-lane parts of this wave's DMA source offsets, fixed for the
+// whole walk: X piece u of pair half h reads row m0 + 8 i + lane % 8 of the
+// tile at granule (lane / 8) ^ (i % 2) (i = (BM / 16) h + XH wave + u); the
+// half adds BM / 2 rows (i changes by BM / 16, an even number, so the
+// granule does not) and each pair q adds 128 q bytes, both scalars.  W
+// piece u reads row k = RPI i + lane / GPR of the stage (i = W_DMA wave +
+// u) at granule gemm_w_gran(k, lane % GPR) of the tile's columns.
 template <int BM, int BN>
-__device__ __forceinline__ void gemm_fetch_one(const GemmArgs& a, int m0, int n0, int q, int h,
-                                               __bf16* xs, int kt, __bf16* ws, int wave, int lane,
-                                               int u) {
+struct DmaLanes {
+  uint32_t x[GemmCfg<BM, BN>::XH], w[GemmCfg<BM, BN>::W_DMA];
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ DmaLanes<BM, BN> dma_lanes(const GemmArgs& a, int m0, int n0, int wave,
+                                                      int lane) {
+  using C = GemmCfg<BM, BN>;
+  DmaLanes<BM, BN> d;
+  static_assert((BM / 16) % 2 == 0, "the pair halves share the granule permutation");
+#pragma unroll
+  for (int u = 0; u < C::XH; ++u) {
+    const int i = wave * C::XH + u;
+    d.x[u] = (uint32_t)(m0 + lds::gemm_x_dma_row(lane, i)) * (uint32_t)a.k * 2u +
+             16u * (uint32_t)lds::gemm_x_dma_gran(lane, i);
+  }
+  constexpr int GPR = BN / 8, RPI = 64 / GPR;  // granules per row, rows per instruction
+#pragma unroll
+  for (int u = 0; u < C::W_DMA; ++u) {
+    const int i = wave * C::W_DMA + u;
+    const int k = RPI * i + lane / GPR;
+    d.w[u] = (uint32_t)k * (uint32_t)a.n * 2u +
+             (uint32_t)(n0 + 8 * lds::gemm_w_gran(k, lane % GPR)) * 2u;
+  }
+  return d;
+}
+
+// One iteration's DMA group, its scalars computed once: half h of X pair q
+// (k 64 q .. 64 q + 63) into the LDS pair slot at byte address xs, and W
+// stage kt (k 32 kt .. 32 kt + 31) into the stage slot at ws.  X rows past
+// M and W rows past K read as zero (buffer bounds).
+struct DmaGroup {
+  bool x_ok, w_ok;
+  uint32_t xs, ws;  // LDS byte addresses of this wave's first pieces
+  uint32_t xadd;    // 128 q + the half's BM / 2 rows
+  i32x4_t wr;       // W rows [32 kt, K)
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ void dma_issue(const DmaGroup& g, const DmaLanes<BM, BN>& d,
+                                          const i32x4_t& xr, int u) {
   using C = GemmCfg<BM, BN>;
   if (u < C::XH) {
-    // X rows [0, M) of the chunk: rows past M read as zero.  Instruction i
-    // fetches rows 8 i .. 8 i + 7 of the tile, whole 128-byte rows.
-    const i32x4_t xr = rsrc_words(a.x, (uint32_t)a.m * (uint32_t)a.k * 2u);
-    const int i = (BM / 16) * h + wave * C::XH + u;
-    const uint32_t off = (uint32_t)(m0 + lds::gemm_x_dma_row(lane, i)) * (uint32_t)a.k * 2u +
-                         (uint32_t)(64 * q + 8 * lds::gemm_x_dma_gran(lane, i)) * 2u;
-    dma_b128(lds_addr(xs + i * 512), off, xr);
+    if (g.x_ok) dma_b128(g.xs + 1024u * u, d.x[u] + g.xadd, xr);
   } else {
-    // W rows [k0, K): rows past K read as zero.  Whole rows of the stage
-    // tile per instruction (BN / 8 lanes per row); slot k * (BN / 8) + j of
-    // the stage holds granule j ^ 4 (k % 4) of row k.
-    const int k0 = kt * kBK;
-    const i32x4_t wr =
-        rsrc_words(a.w + (int64_t)k0 * a.n, (uint32_t)(a.k - k0) * (uint32_t)a.n * 2u);
-    constexpr int GPR = BN / 8, RPI = 64 / GPR;  // granules per row, rows per instruction
-    const int i = wave * C::W_DMA + (u - C::XH);
-    const int k = RPI * i + lane / GPR;
-    const int g = lds::gemm_w_gran(k, lane % GPR);
-    const uint32_t off = (uint32_t)k * (uint32_t)a.n * 2u + (uint32_t)(n0 + 8 * g) * 2u;
-    dma_b128(lds_addr(ws + i * 512), off, wr);
+    if (g.w_ok) dma_b128(g.ws + 1024u * (u - C::XH), d.w[u - C::XH], g.wr);
   }
 }
 
@@ -247,19 +272,29 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bias_kernel(const GemmAr
   const int nk = (a.k + kBK - 1) / kBK;
   auto xslot = [&](int q) { return xbase + (q % kXSlots) * C::X_PAIR; };
   auto wslot = [&](int kt) { return wbase + (kt % kWSlots) * C::W_ELEMS; };
-  // Iteration j's group, instruction u (stages past K are not fetched).
-  auto group_one = [&](int j, int u) {
-    const int q = half_floor(j + 1) + 2, h = (j + 1) & 1;
-    const bool x_ok = 2 * q < nk, w_ok = j + 4 < nk && j + 4 >= 0;
-    if (u < C::XH ? x_ok : w_ok)
-      gemm_fetch_one<BM, BN>(a, m0, n0, q, h, xslot(q), j + 4, wslot(j + 4), wave, lane, u);
+  const DmaLanes<BM, BN> dl = dma_lanes<BM, BN>(a, m0, n0, wave, lane);
+  const i32x4_t xr = rsrc_words(a.x, (uint32_t)a.m * (uint32_t)a.k * 2u);
+  // Iteration j's group (stages past K are not fetched).
+  auto make_group = [&](int j) {
+    DmaGroup g;
+    const int q = half_floor(j + 1) + 2, kt = j + 4, h = (j + 1) & 1;
+    g.x_ok = 2 * q < nk;
+    g.w_ok = kt < nk && kt >= 0;
+    g.xs = lds_addr(xslot(q)) + 1024u * (uint32_t)((BM / 16) * h + wave * C::XH);
+    g.ws = lds_addr(wslot(kt)) + 1024u * (uint32_t)(wave * C::W_DMA);
+    g.xadd = 128u * (uint32_t)q + (uint32_t)h * (uint32_t)(BM / 2) * (uint32_t)a.k * 2u;
+    const int k0 = g.w_ok ? kt * kBK : 0;
+    g.wr = rsrc_words(a.w + (int64_t)k0 * a.n, (uint32_t)(a.k - k0) * (uint32_t)a.n * 2u);
+    return g;
   };
   // Prologue: the groups of iterations -5 .. -1 (W stages 0 .. 3, X pairs 0
   // and 1, half of pair 2); stage 0 complete once the first two have landed.
 #pragma unroll
-  for (int j = -5; j < 0; ++j)
+  for (int j = -5; j < 0; ++j) {
+    const DmaGroup g = make_group(j);
 #pragma unroll
-    for (int u = 0; u < C::NPT; ++u) group_one(j, u);
+    for (int u = 0; u < C::NPT; ++u) dma_issue<BM, BN>(g, dl, xr, u);
+  }
   if (nk > 4)
     wait_vm<3 * C::NPT>();
   else
@@ -289,11 +324,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bias_kernel(const GemmAr
     read_operands<BM, BN>(op0, xslot((kt + 1) >> 1), wslot(kt + 1), w_rd, x_rd, (kt + 1) & 1, 0);
     // this iteration's group, spread over the MFMAs (instruction u after
     // MFMA u * MFMAs / NPT: every instruction once)
+    const DmaGroup g = make_group(kt);
     mma_step_hook<BM, BN>(acc, op1, [&](int jm) {
       constexpr int M = C::NB * C::MB;
 #pragma unroll
       for (int u = 0; u < C::NPT; ++u)
-        if (u * M / C::NPT == jm) group_one(kt, u);
+        if (u * M / C::NPT == jm) dma_issue<BM, BN>(g, dl, xr, u);
     });
   }
   read_operands<BM, BN>(op1, xslot((nk - 1) >> 1), wslot(nk - 1), w_rd, x_rd, (nk - 1) & 1, 1);
