@@ -36,6 +36,12 @@ CASES = [
     (3, 64, 128, 512, 64),
     (1, 128, 64, 256, 1),
     (2, 512, 512, 1536, 512),
+    # K walked in 32-deep stages and X in 64-deep pairs: an odd number of
+    # stages (the last pair half past K), partial last stages, ragged M and N
+    (1, 80, 96, 200, 40),
+    (2, 64, 40, 72, 64),
+    # the same tails in the 256 x 256 kernel (first product: 8 x 32 tiles)
+    (1, 2048, 96, 8192, 2048),
 ]
 
 
