@@ -489,7 +489,6 @@ struct KvLds {
   static constexpr int VRES = kBlockNBwd / 64 * ELEMS;     // resident V, 4 tiles
   // A query stage: Q tile, dO tile, then 64 segment ids, 64 lse, 64 delta.
   static constexpr int QSTAGE = 2 * ELEMS + 3 * 128;
-  static constexpr int NPT = 2 * (64 * D / 8 / 64 / kWaves) + (SEG ? 1 : 0);
 };
 
 // Which (batch, head, key tile) a workgroup owns: consecutive key tiles of
@@ -510,7 +509,7 @@ __device__ __forceinline__ WgCoord kv_coord(const BwdParams& bp) {
 template <int D, bool SEG, bool STRIPED>
 __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParams bp) {
   using L = KvLds<D, SEG>;
-  constexpr int NDB = D / 32, NPT = L::NPT;
+  constexpr int NDB = D / 32;
   // Operand reads ahead of the MFMAs need registers that the segment-id
   // variants do not have (they spill): those keep the reads next to their
   // MFMAs.  On the 7B share the read-ahead makes the kernel 2.7 % faster.
@@ -605,8 +604,6 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
       dma_b32(lds_addr(d + 2 * L::ELEMS + 256), (uint32_t)lane * 4u,
               rsrc_words(dbase + q0, (uint32_t)nvalid * 4u));
   };
-  // A wave's DMA count per query tile (waves 0 and 1 issue one more).
-  const bool extra = wave < 2;
   // Wave 0, which fetched the stage's 64 lse, rewrites them as
   // -lse log2(e), the exponent's offset, once per query tile instead of once
   // per pair.  Its DMA must have landed (vmcnt), and the rewrite completes
@@ -686,20 +683,17 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
     fetch(tile_of(0), 0);
     prep_lse(0);
   }
+  // One barrier per query tile: after it, tile qt has landed for every wave
+  // (each waited for its own share, the only DMA in flight) and every wave
+  // is done with the previous tile, so the next tile's DMA may refill that
+  // stage.
   for (int it = 0; it < n_run; ++it) {
     const int qt = tile_of(it);
     const int s = it & 1;
-    if (it + 1 < n_run) fetch(tile_of(it + 1), s ^ 1);
-    // This wave's share of tile qt must have landed before the barrier.
-    if (it + 1 < n_run) {
-      if (extra)
-        wait_vm<NPT + 1>();
-      else
-        wait_vm<NPT>();
-    } else {
-      wait_vm<0>();
-    }
+    wait_vm<0>();
+    wait_lds();  // this wave's reads of the previous tile have completed
     stage_barrier();
+    if (it + 1 < n_run) fetch(tile_of(it + 1), s ^ 1);
 
     const __bf16* qt_t = qs + s * L::QSTAGE;
     const __bf16* gt_t = qt_t + L::ELEMS;
@@ -850,8 +844,6 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
           }
       }
     }
-    // Every wave is done with stage s before the next fetch overwrites it.
-    stage_barrier();
   }
   __builtin_amdgcn_s_waitcnt(0);
 
