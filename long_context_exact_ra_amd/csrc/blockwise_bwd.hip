@@ -590,12 +590,12 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
   const float* lbase = bp.lse + ((int64_t)b * p.heads + h) * p.seq_q;
   const float* dbase = bp.delta + ((int64_t)b * p.heads + h) * p.seq_q;
 
+  // Per wave, the DMA of a stage is its share of the Q and dO tiles (and
+  // ids): kQDma instructions, issued after the lse (wave 0) or delta (wave 1).
+  constexpr int kQDma = 2 * (64 * D / 8 / 64 / kWaves) + (SEG ? 1 : 0);
   auto fetch = [&](int qt, int s) {
     const int q0 = q_lo + 64 * qt;
     __bf16* d = qs + s * L::QSTAGE;
-    issue_tile<D, kWaves, SEG>(TileInfo{q0, p.seq_q, 0, 0, 1, 0}, qbase0, gbase0, sbase0, rs_bytes,
-                               wave, lane, lane_off, lane_off, d, d + L::ELEMS,
-                               reinterpret_cast<int32_t*>(d + 2 * L::ELEMS));
     const int nvalid = std::min(64, p.seq_q - q0);
     if (wave == 0)
       dma_b32(lds_addr(d + 2 * L::ELEMS + 128), (uint32_t)lane * 4u,
@@ -603,14 +603,18 @@ __global__ __launch_bounds__(kThreadsBwd, 1) void bwd_dkdv_kernel(const BwdParam
     if (wave == 1)
       dma_b32(lds_addr(d + 2 * L::ELEMS + 256), (uint32_t)lane * 4u,
               rsrc_words(dbase + q0, (uint32_t)nvalid * 4u));
+    issue_tile<D, kWaves, SEG>(TileInfo{q0, p.seq_q, 0, 0, 1, 0}, qbase0, gbase0, sbase0, rs_bytes,
+                               wave, lane, lane_off, lane_off, d, d + L::ELEMS,
+                               reinterpret_cast<int32_t*>(d + 2 * L::ELEMS));
   };
   // Wave 0, which fetched the stage's 64 lse, rewrites them as
   // -lse log2(e), the exponent's offset, once per query tile instead of once
-  // per pair.  Its DMA must have landed (vmcnt), and the rewrite completes
-  // before the barrier after which the stage is read.
+  // per pair.  Its lse DMA must have landed (DMA completes in issue order,
+  // so the kQDma issued after it may still be in flight), and the rewrite
+  // completes before the barrier after which the stage is read.
   auto prep_lse = [&](int s) {
     if (wave != 0) return;
-    wait_vm<0>();
+    wait_vm<kQDma>();
     float* l = reinterpret_cast<float*>(qs + s * L::QSTAGE + 2 * L::ELEMS + 128);
     l[lane] = l[lane] * -kLog2e;
     wait_lds();
