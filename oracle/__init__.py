@@ -17,4 +17,5 @@ from .attention import (  # noqa: F401
     visible,
 )
 from .backward import attention_bwd  # noqa: F401
+from .decode import decode_attention  # noqa: F401
 from .feedforward import blockwise_ffn, ffn  # noqa: F401
