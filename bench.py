@@ -9,8 +9,11 @@ step is then one call per ring position the workload lists); ``--pass bwd``
 times the backward (dq, dk, dv of the same share, from the forward's out and
 lse and a seeded upstream gradient) instead of the forward; ``--pass ffn``
 times the blockwise feedforward of the 7B-shaped share (batch 1, 32768
-tokens, hidden 4096, feedforward width 16384, chunks of 2048 rows).  Inputs
-are seeded Gaussian tensors already resident in HBM.
+tokens, hidden 4096, feedforward width 16384, chunks of 2048 rows);
+``--pass decode`` times one incremental-decoding step over a KV cache (by
+default the 7B-shaped model's last token of a 512K-token cache: 32 heads of
+128, bf16), an HBM-bound step reported in GB/s of cache read.  Inputs are
+seeded Gaussian tensors already resident in HBM.
 
 Prints one JSON line with the causal-adjusted TFLOP/s, the roofline of the
 kernel (MFMA bound, bf16 dense peak) and the CPU oracle timed on a bounded
@@ -265,14 +268,16 @@ def main():
                     help="query rows of the CPU oracle sample (0 = skip)")
     ap.add_argument("--workload", default=WORKLOAD,
                     choices=["tiny_plumbing", "small_causal", "share_7b_512k", "packed_documents",
-                             "share_65b_4m", "small_causal_striped", "share_7b_512k_striped"],
+                             "share_65b_4m", "small_causal_striped", "share_7b_512k_striped",
+                             "decode_7b_512k", "decode_small"],
                     help="workload to time (default: the 7B-shaped share; tiny_plumbing is "
                          "fp32, forward only)")
     ap.add_argument("--ring-index", type=int, default=None,
                     help="time this ring position instead of the workload's own list")
-    ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd", "ffn"], default="fwd",
-                    help="time the attention forward (default), its backward, or the "
-                         "blockwise feedforward")
+    ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd", "ffn", "decode"],
+                    default="fwd",
+                    help="time the attention forward (default), its backward, the "
+                         "blockwise feedforward, or a decoding step (workloads decode_*)")
     ap.add_argument("--key-splits", default="auto",
                     help="key splits per query tile of the forward (and of the backward's "
                          "dq kernel): 'auto' = the library's count for this GPU, 1 for "
@@ -305,6 +310,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.pass_ == "ffn":
         bench_ffn(args, dev)
+        return
+    if args.pass_ == "decode" or args.workload.startswith("decode_"):
+        bench_decode(args, dev)
         return
     w = workloads.get(args.workload)
     if args.ring_index is not None:
@@ -571,6 +579,133 @@ def bench_ffn(args, dev):
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)
+
+
+PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
+
+
+def bench_decode(args, dev):
+    """Time one decoding step over a KV cache: every valid cache row of
+    every head is read once (the whole step, its key splits' fold included,
+    between the events)."""
+    import torch
+
+    import long_context_exact_ra_amd as ra
+    import oracle
+    import workloads
+
+    name = args.workload if args.workload.startswith("decode_") else "decode_7b_512k"
+    w = workloads.DECODE_WORKLOADS[name]
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    q, k, v = workloads.make_decode_inputs(w, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.heads, w.n_new), dtype=torch.float32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    P = (ra.decode_key_splits(w.batch, w.n_new, w.heads, w.cache_idx, cus)
+         if args.key_splits == "auto" else int(args.key_splits))
+    ws = torch.empty(max(ra.decode_workspace_bytes(w.batch, w.n_new, w.heads, w.head_dim, P), 1),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1, out=dst)  # one elementwise kernel: reads n bytes, writes n
+        torch.cuda.synchronize()
+        del src, dst
+
+    def step():
+        ra.attn_decode(q, k, v, w.cache_idx, key_splits=P, workspace=ws, out=out, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms = float(np.mean(per))
+    if not (bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())):
+        raise RuntimeError("non-finite output")
+    elt = 2 if w.dtype == "bf16" else 4
+    # algorithmic bytes: K and V of every valid cache row of every head once,
+    # plus q, out and lse
+    row_bytes = 2 * w.head_dim * elt                  # per (cache row, head)
+    kv_bytes = float(w.batch * w.heads * w.n_keys * row_bytes)
+    io_bytes = float(2 * w.batch * w.n_new * w.heads * w.head_dim * elt
+                     + 4 * w.batch * w.heads * w.n_new)
+    gbs = (kv_bytes + io_bytes) / (ms * 1e-3) / 1e9
+    pairs = w.batch * w.heads * sum(w.cache_idx + t + 1 for t in range(w.n_new))
+    flops = 4.0 * w.head_dim * pairs
+    # parity of the timed call and the CPU oracle on a bounded sample: the
+    # step's rows of a few heads over the whole cache
+    n_heads = max(1, min(w.heads, 4))
+    heads = sorted(set(int(h) for h in np.linspace(0, w.heads - 1, n_heads).round()))
+    parity, cpu = None, None
+    if args.cpu_rows > 0:
+        print("[bench] timing the CPU oracle on sampled heads", file=sys.stderr, flush=True)
+        qc = q.cpu()
+        kc = k[:, :w.n_keys, heads].cpu()
+        vc = v[:, :w.n_keys, heads].cpu()
+        qs = qc[:, :, heads].contiguous()
+        t1 = time.perf_counter()
+        ref, ref_lse = oracle.decode_attention(qs, kc, vc, w.cache_idx)
+        dt = time.perf_counter() - t1
+        got = out[:, :, heads].float().cpu().numpy().astype(np.float64)
+        got_l = lse[:, heads].cpu().numpy().astype(np.float64)
+        err, lerr = np.abs(got - ref), np.abs(got_l - ref_lse)
+        rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+        b = ({"max": 2e-2, "mean": 2e-3, "rel_l2": 1e-2} if w.dtype == "bf16"
+             else {"max": 1e-5, "mean": 1e-5, "rel_l2": 1e-5})
+        parity = {"heads": heads, "out_max": float(err.max()), "out_mean": float(err.mean()),
+                  "out_rel_l2": rel, "lse_max": float(lerr.max()),
+                  "lse_mean": float(lerr.mean()), "bounds": b,
+                  "pass": bool(err.max() <= b["max"] and err.mean() <= b["mean"]
+                               and lerr.max() <= b["max"] and rel <= b["rel_l2"])}
+        sample_bytes = float(w.batch * len(heads) * w.n_keys * row_bytes)
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:  # pragma: no cover - informational only
+            cores = torch.get_num_threads()
+        cpu = {"value": sample_bytes / dt / 1e9, "unit": "GB/s", "cores": int(cores),
+               "kind": "oracle",
+               "sample": f"{w.name}: heads {heads} of batch entry 0..{w.batch - 1}, the step's "
+                         f"{w.n_new} new tokens over all {w.n_keys} cache rows; numpy fp64 on "
+                         f"{cpu_model()}; {dt:.1f} s for {sample_bytes / 1e9:.2f} GB of cache"}
+    rec = {
+        "metric": "decoding step: KV-cache read GB/s per MI355X (% of HBM bandwidth in "
+                  "roofline.frac)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": f"synthetic: seeded Gaussian q, K and V caches (std {w.std}), {w.dtype}",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads,
+                   "head_dim": w.head_dim, "cache_rows": w.cache_rows, "cache_idx": w.cache_idx,
+                   "n_new": w.n_new, "pass": "decode", "key_splits": P,
+                   "bytes_per_step": kv_bytes + io_bytes, "flops_per_step": flops,
+                   "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
+                   "tokens_per_s": round(w.batch * w.n_new / (ms * 1e-3), 1),
+                   "ms_min": round(min(per), 4), "ms_median": round(float(np.median(per)), 4),
+                   "wall_s": round(wall, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+        "library_build": ra.version().split("+", 1)[-1],
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(rec), flush=True)
+    if parity is not None and not parity["pass"]:
+        sys.exit(3)
 
 
 if __name__ == "__main__":

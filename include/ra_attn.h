@@ -436,6 +436,65 @@ ra_status_t ra_blockwise_ffn(const void* x, const void* w1, const void* b1,
                              void* stream);
 
 /*
+ * ra_attn_decode -- one incremental-decoding step over a KV cache.
+ *
+ * The pages name an inference cache index, cache_idx, among the ring
+ * forward's arguments and tie inference to incremental decoding with a KV
+ * cache ("RingAttention与传统注意力机制对比为什么它是大语言模型的终极解决
+ * 方案", sections "3. 推理成本显著降低" and "关键参数配置";
+ * "从论文到代码：深入理解RingAttention的块注意力计算逻辑", section
+ * "RingAttention的算法原理"); they print no decoding code.  Reading taken
+ * here: cache_idx is the number of tokens already in the cache; the step's
+ * n_new query tokens have positions cache_idx .. cache_idx + n_new - 1 and
+ * the caller has already written their keys and values into those cache
+ * rows.  Query t attends to cache rows 0 .. cache_idx + t (token causal,
+ * "3. 因果注意力掩码支持"), exact softmax(q K^T / sqrt(D)) V:
+ *
+ *   q, out            [batch, n_new, heads, head_dim]       dtype
+ *   k_cache, v_cache  [batch, cache_rows, heads, head_dim]  dtype; rows
+ *                     0 .. cache_idx + n_new - 1 are read, later rows never
+ *   lse               [batch, heads, n_new] float32 (natural log)
+ *
+ * The cache rows are folded in key_splits contiguous ranges, one workgroup
+ * each; with key_splits > 1 the workgroups write their partial carries
+ * (kept max, denominator, unnormalised numerator) into `workspace`, at
+ * least ra_attn_decode_workspace_bytes(...) bytes of device memory whose
+ * contents are overwritten, and a second kernel folds them (the fold of the
+ * ring's per-block partials; the order of the fold changes only rounding).
+ * key_splits == 1 needs no workspace (NULL allowed).
+ *
+ * Arithmetic: float32 logits, max, denominator and numerator; bf16 inputs
+ * multiply exactly (bf16 products) with float32 sums; out is rounded to
+ * the input dtype.  Inputs must be finite.
+ *
+ * Alignment: q, k_cache, v_cache, out and workspace 16-byte, lse 4-byte.
+ *
+ * Returns RA_E_INVALID for negative sizes or cache_idx, cache_idx + n_new >
+ * cache_rows, key_splits outside [1, 1024], null or misaligned pointers or
+ * a short workspace; RA_E_UNSUPPORTED for head_dim other than 64 or 128,
+ * a dtype other than RA_BF16 / RA_F32, n_new > 256 (a prefill: use the
+ * blockwise forward), heads * head_dim > 2^24 or a grid too large;
+ * RA_E_HIP if a launch fails.  batch, heads or n_new == 0 is a valid
+ * no-op.
+ */
+int64_t ra_attn_decode_workspace_bytes(int64_t batch, int64_t n_new, int64_t heads,
+                                       int64_t head_dim, int32_t key_splits);
+
+/* The library's key-split count for a decoding step on a GPU with
+ * compute_units compute units: about eight workgroups per compute unit and
+ * at least 1024 cache rows per split, in [1, 1024].  Host only; 1 for
+ * non-positive arguments. */
+int32_t ra_attn_decode_key_splits(int64_t batch, int64_t n_new, int64_t heads,
+                                  int64_t cache_idx, int32_t compute_units);
+
+ra_status_t ra_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                           int64_t cache_idx, int64_t cache_rows, int64_t batch,
+                           int64_t n_new, int64_t heads, int64_t head_dim,
+                           ra_dtype_t dtype, int32_t key_splits, void* workspace,
+                           int64_t workspace_bytes, void* out, float* lse,
+                           void* stream);
+
+/*
  * ra_blockwise_plan -- host-only: the ring order and the chunk-pair skip
  * decisions for one ring position, without touching a GPU.
  *

@@ -16,6 +16,7 @@ import os
 from typing import Optional, Tuple
 
 __all__ = ["RaError", "blockwise_attn_fwd", "blockwise_attn_bwd", "blockwise_ffn",
+           "attn_decode", "decode_workspace_bytes", "decode_key_splits",
            "ffn_workspace_bytes", "fwd_split_workspace_bytes", "fwd_key_splits",
            "bwd_split_workspace_bytes",
            "blockwise_plan", "last_error", "lib_path",
@@ -97,6 +98,13 @@ def load_library():
     lib.ra_blockwise_ffn.argtypes = [c_vp] * 5 + [c_i64] * 5 + [ctypes.c_int, c_vp, c_vp,
                                                                 c_i64, c_vp]
     lib.ra_blockwise_ffn.restype = ctypes.c_int
+    lib.ra_attn_decode_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_i64, c_i32]
+    lib.ra_attn_decode_workspace_bytes.restype = c_i64
+    lib.ra_attn_decode_key_splits.argtypes = [c_i64, c_i64, c_i64, c_i64, c_i32]
+    lib.ra_attn_decode_key_splits.restype = c_i32
+    lib.ra_attn_decode.argtypes = ([c_vp] * 3 + [c_i64] * 6 + [ctypes.c_int, c_i32, c_vp, c_i64,
+                                   c_vp, c_vp, c_vp])
+    lib.ra_attn_decode.restype = ctypes.c_int
     lib.ra_blockwise_plan.argtypes = [c_i64, c_i64, c_i64, c_i64, c_i32, c_i32,
                                       c_vp, c_vp, c_vp]
     lib.ra_blockwise_plan.restype = ctypes.c_int
@@ -389,3 +397,76 @@ def blockwise_ffn(x, w1, b1, w2, b2, chunk_size: int, *, y=None, workspace=None,
                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                 sptr))
     return y
+
+
+def decode_workspace_bytes(batch: int, n_new: int, heads: int, head_dim: int,
+                           key_splits: int) -> int:
+    """Bytes of workspace ``attn_decode`` needs for ``key_splits`` splits (0
+    for one split)."""
+    return int(load_library().ra_attn_decode_workspace_bytes(batch, n_new, heads, head_dim,
+                                                             key_splits))
+
+
+def decode_key_splits(batch: int, n_new: int, heads: int, cache_idx: int,
+                      compute_units: int) -> int:
+    """The library's key-split count for a decoding step."""
+    return int(load_library().ra_attn_decode_key_splits(batch, n_new, heads, cache_idx,
+                                                        compute_units))
+
+
+def attn_decode(q, k_cache, v_cache, cache_idx: int, *, key_splits="auto", workspace=None,
+                out=None, lse=None, stream=None) -> Tuple[object, object]:
+    """One incremental-decoding step: returns (out, lse).
+
+    q: [B, n_new, H, D], the step's new tokens at positions cache_idx ..
+    cache_idx + n_new - 1; k_cache, v_cache: [B, R, H, D] with their rows
+    up to cache_idx + n_new - 1 filled (the new tokens' keys and values
+    included).  Contiguous device tensors of one dtype (bfloat16 or float32).
+    Query t attends to cache rows 0 .. cache_idx + t.  out ([B, n_new, H, D],
+    q's dtype) and lse ([B, H, n_new], float32) are allocated when not given.
+    key_splits: an integer in [1, 1024] or "auto" (the library's count for
+    this GPU); workspace: a device tensor of at least
+    ``decode_workspace_bytes`` bytes, allocated when not given and needed.
+    """
+    import torch
+    lib = load_library()
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache and v_cache must share one dtype")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-D device tensor")
+    B, T, H, D = q.shape
+    R = k_cache.shape[1]
+    if (k_cache.shape[0], k_cache.shape[2], k_cache.shape[3]) != (B, H, D) or \
+            v_cache.shape != k_cache.shape:
+        raise ValueError(f"cache shape {tuple(k_cache.shape)} does not match q {tuple(q.shape)}")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be contiguous with q's shape and dtype")
+    if tuple(lse.shape) != (B, H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, n_new]")
+    if key_splits == "auto":
+        cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+        key_splits = decode_key_splits(B, T, H, cache_idx, cus)
+    key_splits = int(key_splits)
+    ws_ptr, ws_bytes = None, 0
+    if key_splits > 1:
+        need = decode_workspace_bytes(B, T, H, D, key_splits)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    dt = RA_BF16 if q.dtype == torch.bfloat16 else RA_F32
+    _check(lib.ra_attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), int(cache_idx),
+                              R, B, T, H, D, dt, key_splits, ws_ptr, ws_bytes, out.data_ptr(),
+                              lse.data_ptr(), sptr))
+    return out, lse

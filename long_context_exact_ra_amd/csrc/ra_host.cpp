@@ -534,6 +534,104 @@ ra_status_t ra_blockwise_ffn(const void* x, const void* w1, const void* b1, cons
   return RA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Decoding: at most 8 queries per workgroup (their carries sit in
+// registers), larger steps take several query groups.
+constexpr int32_t kMaxDecodeSplits = 1024;
+constexpr int64_t kMaxDecodeNew = 256;
+
+int decode_nq(int64_t n_new) { return n_new <= 1 ? 1 : n_new <= 2 ? 2 : n_new <= 4 ? 4 : 8; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t ra_attn_decode_workspace_bytes(int64_t batch, int64_t n_new, int64_t heads,
+                                       int64_t head_dim, int32_t key_splits) {
+  if (key_splits <= 1 || batch <= 0 || n_new <= 0 || heads <= 0 || head_dim <= 0) return 0;
+  return (int64_t)key_splits * batch * heads * n_new * (head_dim + 2) * 4;
+}
+
+int32_t ra_attn_decode_key_splits(int64_t batch, int64_t n_new, int64_t heads, int64_t cache_idx,
+                                  int32_t compute_units) {
+  if (batch <= 0 || n_new <= 0 || heads <= 0 || cache_idx < 0 || compute_units <= 0) return 1;
+  const int nq = decode_nq(n_new);
+  const int64_t per_split = batch * heads * ((n_new + nq - 1) / nq);
+  const int64_t n_keys = cache_idx + n_new;
+  // About eight workgroups per compute unit (each is 4 waves of modest
+  // register use), and at least 1024 keys per split.
+  int64_t P = (8LL * compute_units + per_split - 1) / per_split;
+  P = std::min<int64_t>(P, (n_keys + 1023) / 1024);
+  P = std::min<int64_t>(P, kMaxDecodeSplits);
+  return (int32_t)std::max<int64_t>(P, 1);
+}
+
+ra_status_t ra_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                           int64_t cache_idx, int64_t cache_rows, int64_t batch, int64_t n_new,
+                           int64_t heads, int64_t head_dim, ra_dtype_t dtype, int32_t key_splits,
+                           void* workspace, int64_t workspace_bytes, void* out, float* lse,
+                           void* stream) {
+  clear_error();
+  if (batch < 0 || heads < 0 || n_new < 0)
+    return fail(RA_E_INVALID, "batch, heads and n_new must be >= 0 (got %lld, %lld, %lld)",
+                (long long)batch, (long long)heads, (long long)n_new);
+  if (head_dim <= 0) return fail(RA_E_INVALID, "head_dim must be positive");
+  if (cache_idx < 0) return fail(RA_E_INVALID, "cache_idx must be >= 0 (got %lld)", (long long)cache_idx);
+  if (cache_rows < cache_idx + n_new)
+    return fail(RA_E_INVALID, "cache_idx %lld + n_new %lld exceeds the %lld cache rows",
+                (long long)cache_idx, (long long)n_new, (long long)cache_rows);
+  if (key_splits < 1 || key_splits > kMaxDecodeSplits)
+    return fail(RA_E_INVALID, "key_splits %d outside [1, %d]", key_splits, kMaxDecodeSplits);
+  if (dtype != RA_BF16 && dtype != RA_F32)
+    return fail(RA_E_UNSUPPORTED, "dtype %d is not supported (RA_BF16, RA_F32)", (int)dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(RA_E_UNSUPPORTED, "head_dim %lld is not supported (64, 128)", (long long)head_dim);
+  if (n_new > kMaxDecodeNew)
+    return fail(RA_E_UNSUPPORTED,
+                "n_new %lld exceeds %lld (a longer step is a prefill: use the blockwise forward)",
+                (long long)n_new, (long long)kMaxDecodeNew);
+  if (heads * head_dim > (1LL << 24))
+    return fail(RA_E_UNSUPPORTED, "heads * head_dim = %lld exceeds 2^24",
+                (long long)(heads * head_dim));
+  if (batch == 0 || heads == 0 || n_new == 0) return RA_OK;
+  if (!q || !k_cache || !v_cache || !out || !lse)
+    return fail(RA_E_INVALID, "q, k_cache, v_cache, out and lse must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(lse, 4))
+    return fail(RA_E_INVALID, "q, k_cache, v_cache and out must be 16-byte aligned, lse 4-byte");
+  const int nq = decode_nq(n_new);
+  const int64_t q_groups = (n_new + nq - 1) / nq;
+  const int64_t n_wg = batch * heads * q_groups * key_splits;
+  if (n_wg > kInt32Max || batch * heads * n_new * head_dim / 4 / 256 > kInt32Max)
+    return fail(RA_E_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)n_wg);
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  if (key_splits > 1) {
+    const int64_t need = ra_attn_decode_workspace_bytes(batch, n_new, heads, head_dim, key_splits);
+    if (!workspace) return fail(RA_E_INVALID, "key_splits %d needs a workspace", key_splits);
+    if (!aligned(workspace, 16)) return fail(RA_E_INVALID, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(RA_E_INVALID, "workspace of %lld bytes is smaller than the %lld required",
+                  (long long)workspace_bytes, (long long)need);
+    part_o = static_cast<float*>(workspace);
+    part_ml = part_o + key_splits * batch * heads * n_new * head_dim;
+  }
+  const int64_t n_keys = cache_idx + n_new;
+  int64_t split_keys = (n_keys + key_splits - 1) / key_splits;
+  split_keys = (split_keys + 63) / 64 * 64;
+  ra::DecParams p{q, k_cache, v_cache, out, lse, part_o, part_ml, cache_idx, cache_rows, n_keys,
+                  split_keys, (int32_t)batch, (int32_t)heads, (int32_t)n_new, key_splits,
+                  (int32_t)q_groups, (float)(1.4426950408889634 / std::sqrt((double)head_dim))};
+  char err[256];
+  if (ra::launch_decode(p, dtype == RA_BF16 ? ra::Dtype::BF16 : ra::Dtype::F32, (int)head_dim, nq,
+                        stream, err, (int)sizeof(err)) != 0)
+    return fail(RA_E_HIP, "%s", err);
+  return RA_OK;
+}
+
 ra_status_t ra_blockwise_attn_fwd(const void* q, const void* k, const void* v,
                                   const int32_t* segment_ids, int64_t causal_block_size,
                                   int64_t q_chunk, int64_t k_chunk, int32_t ring_size,

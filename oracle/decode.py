@@ -89,9 +89,6 @@ def decode_attention(q, k_cache, v_cache, cache_idx: int,
         raise ValueError(f"cache_idx {cache_idx} + {T} new tokens outside the "
                          f"{k_cache.shape[1]} cache rows")
     n = _rows_read(cache_idx, T)
-    # Only the rows read are upcast.
-    kf = _as_f64(k_cache[:, :n])
-    vf = _as_f64(v_cache[:, :n])
     heads = list(range(H)) if heads is None else list(heads)
     scale = _scale(D)
     allow = _visible(_query_positions(cache_idx, T), np.arange(n))  # cache row j = position j
@@ -99,7 +96,10 @@ def decode_attention(q, k_cache, v_cache, cache_idx: int,
     lse = np.zeros((B, len(heads), T), dtype=np.float64)
     for b in range(B):
         for hi, h in enumerate(heads):
-            s = (qf[b, :, h, :] @ kf[b, :, h, :].T) * scale
+            # Only the rows read are upcast, one head at a time.
+            kf = _as_f64(k_cache[b, :n, h, :])
+            vf = _as_f64(v_cache[b, :n, h, :])
+            s = (qf[b, :, h, :] @ kf.T) * scale
             s = np.where(allow, s, -np.inf)
             m = s.max(axis=1)
             has = np.isfinite(m)              # (every query sees key 0 under the readings)
@@ -107,7 +107,7 @@ def decode_attention(q, k_cache, v_cache, cache_idx: int,
             den = p.sum(axis=1)
             with np.errstate(divide="ignore", invalid="ignore"):
                 out[b, :, hi, :] = np.where(has[:, None],
-                                            (p @ vf[b, :, h, :]) / np.where(has, den, 1.0)[:, None],
+                                            (p @ vf) / np.where(has, den, 1.0)[:, None],
                                             0.0)
                 lse[b, hi, :] = np.where(has, m + np.log(np.where(has, den, 1.0)), -np.inf)
     return out, lse

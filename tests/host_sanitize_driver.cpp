@@ -32,6 +32,14 @@ int launch_ffn(const FfnParams&, void*, char*, int) {
   ++g_launches;
   return 0;
 }
+static DecParams g_dec;
+static int g_dec_nq = 0;
+int launch_decode(const DecParams& p, Dtype, int, int nq, void*, char*, int) {
+  g_dec = p;
+  g_dec_nq = nq;
+  ++g_launches;
+  return 0;
+}
 int fwd_scratch(void** ptr, char*, int) {
   *ptr = reinterpret_cast<void*>(static_cast<uintptr_t>(1) << 24);
   return 0;
@@ -170,6 +178,46 @@ int main() {
   CHECK(ra_blockwise_ffn(P, P, P, P, P, 1, 64, 64, 128, 32, RA_BF16, P, P, 1 << 20, nullptr) ==
         RA_OK);
   CHECK(ra::g_launches == before + 1);
+
+  // Decoding: the split grid the host derives covers every cache row, the
+  // workspace split between numerators and carries, rejections launch
+  // nothing.
+  for (int64_t n_new : {1, 3, 8, 13, 256}) {
+    for (int32_t S : {1, 5, 64, 1024}) {
+      const int64_t B = 2, H = 32, D = 128, ci = 524287 - n_new;
+      const int64_t ws = ra_attn_decode_workspace_bytes(B, n_new, H, D, S);
+      const int n0 = ra::g_launches;
+      CHECK(ra_attn_decode(P, P, P, ci, ci + n_new, B, n_new, H, D, RA_BF16, S,
+                           S > 1 ? P : nullptr, ws, P, F, nullptr) == RA_OK);
+      CHECK(ra::g_launches == n0 + 1);
+      const ra::DecParams& d = ra::g_dec;
+      CHECK(d.n_keys == ci + n_new);
+      CHECK(d.split_keys % 64 == 0);
+      CHECK((int64_t)d.key_splits * d.split_keys >= d.n_keys);
+      CHECK((int64_t)d.q_groups * ra::g_dec_nq >= n_new);
+      CHECK((int64_t)(d.q_groups - 1) * ra::g_dec_nq < n_new);
+      if (S > 1) {
+        CHECK(d.part_o == reinterpret_cast<float*>(P));
+        CHECK(d.part_ml == d.part_o + (int64_t)S * B * H * n_new * D);
+        CHECK(reinterpret_cast<const char*>(d.part_ml + 2LL * S * B * H * n_new) == P + ws);
+      } else {
+        CHECK(d.part_o == nullptr && d.part_ml == nullptr);
+      }
+    }
+  }
+  {
+    const int n0 = ra::g_launches;
+    CHECK(ra_attn_decode(P, P, P, 100, 100, 1, 1, 2, 128, RA_BF16, 1, nullptr, 0, P, F,
+                         nullptr) == RA_E_INVALID);                          // row 100 missing
+    CHECK(ra_attn_decode(P, P, P, 0, 300, 1, 257, 2, 128, RA_BF16, 1, nullptr, 0, P, F,
+                         nullptr) == RA_E_UNSUPPORTED);                      // a prefill
+    CHECK(ra_attn_decode(P, P, P, 10, 300, 1, 1, 2, 128, RA_BF16, 2, P, 100, P, F,
+                         nullptr) == RA_E_INVALID);                          // short workspace
+    CHECK(ra_attn_decode(P, P, P, 10, 300, 0, 1, 2, 128, RA_BF16, 2, nullptr, 0, nullptr,
+                         nullptr, nullptr) == RA_OK);                        // empty batch
+    CHECK(ra::g_launches == n0);
+  }
+  CHECK(ra_attn_decode_key_splits(1, 1, 32, 524287, 256) == 64);
   std::printf("%s: %d failure(s)\n", g_fail ? "FAILED" : "ok", g_fail);
   return g_fail ? 1 : 0;
 }

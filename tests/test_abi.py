@@ -306,3 +306,44 @@ def test_ffn_host_validation():
     assert st == ra.RA_E_INVALID
     st = lib.ra_blockwise_ffn(P, P, P, P, P, 1, 64, 64, 256, 64, ra.RA_F32, P, P, ws, None)
     assert st == ra.RA_E_UNSUPPORTED
+
+
+def test_decode_validation_without_gpu():
+    """Argument errors of the decoding step are caught on the host, and the
+    key-split and workspace helpers follow their stated rules."""
+    lib = ra.load_library()
+    p = 4096  # an aligned non-null dummy pointer, never dereferenced on these paths
+    call = lambda **kw: lib.ra_attn_decode(
+        kw.get("q", p), kw.get("k", p), kw.get("v", p), kw.get("ci", 100), kw.get("rows", 128),
+        kw.get("batch", 1), kw.get("n_new", 1), kw.get("heads", 2), kw.get("d", 128),
+        kw.get("dtype", ra.RA_BF16), kw.get("P", 2), kw.get("ws", p), kw.get("wsb", 1 << 20),
+        kw.get("out", p), kw.get("lse", p), None)
+    assert call(ci=-1) == ra.RA_E_INVALID
+    assert call(ci=128) == ra.RA_E_INVALID          # the new token past the cache rows
+    assert call(n_new=30) == ra.RA_E_INVALID        # 100 + 30 > 128
+    assert call(batch=-1) == ra.RA_E_INVALID
+    assert call(d=0) == ra.RA_E_INVALID
+    assert call(P=0) == ra.RA_E_INVALID
+    assert call(P=1025) == ra.RA_E_INVALID
+    assert call(d=96) == ra.RA_E_UNSUPPORTED
+    assert call(dtype=7) == ra.RA_E_UNSUPPORTED
+    assert call(n_new=257, rows=1024) == ra.RA_E_UNSUPPORTED
+    assert call(q=None) == ra.RA_E_INVALID
+    assert call(lse=p + 2) == ra.RA_E_INVALID      # misaligned
+    assert call(out=p + 8) == ra.RA_E_INVALID
+    assert call(ws=None) == ra.RA_E_INVALID         # two splits need a workspace
+    assert call(wsb=100) == ra.RA_E_INVALID
+    assert call(ws=p + 4) == ra.RA_E_INVALID
+    assert call(batch=0) == ra.RA_OK                # empty calls: no device work
+    assert call(n_new=0) == ra.RA_OK
+    assert call(heads=0) == ra.RA_OK
+    assert "cache" in ra.last_error() or ra.last_error() == ""
+    # workspace: P * B * H * n_new * (D + 2) float32, none for one split
+    assert lib.ra_attn_decode_workspace_bytes(1, 3, 2, 128, 4) == 4 * 1 * 2 * 3 * 130 * 4
+    assert lib.ra_attn_decode_workspace_bytes(1, 3, 2, 128, 1) == 0
+    # split count: about 8 workgroups per compute unit, >= 1024 keys per split
+    assert lib.ra_attn_decode_key_splits(1, 1, 32, 524287, 256) == 64
+    assert lib.ra_attn_decode_key_splits(1, 1, 32, 5000, 256) == 5
+    assert lib.ra_attn_decode_key_splits(64, 1, 32, 524287, 256) == 1
+    assert lib.ra_attn_decode_key_splits(1, 1, 1, 10 ** 9, 256) == 1024
+    assert lib.ra_attn_decode_key_splits(0, 1, 32, 100, 256) == 1

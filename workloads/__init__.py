@@ -21,7 +21,8 @@ import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "get", "block_seed", "document_segments",
            "make_block", "make_dout", "make_q", "make_qkv", "make_segments", "to_storage_order",
-           "FfnWorkload", "FFN_WORKLOADS", "make_ffn_inputs"]
+           "FfnWorkload", "FFN_WORKLOADS", "make_ffn_inputs",
+           "DecodeWorkload", "DECODE_WORKLOADS", "make_decode_inputs"]
 
 
 @dataclass(frozen=True)
@@ -228,3 +229,50 @@ def make_ffn_inputs(w: FfnWorkload, device="cpu"):
     w2 = make_block((Fh, H), w.seed * 31 + 4, Fh ** -0.5, "bf16", device)
     b2 = make_block((H,), w.seed * 31 + 5, 0.1, "bf16", device)
     return x, w1, b1, w2, b2
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """One decoding step over a KV cache: q [batch, n_new, heads, head_dim]
+    at positions cache_idx .. cache_idx + n_new - 1, cache [batch,
+    cache_rows, heads, head_dim] with rows up to cache_idx + n_new - 1
+    filled; rows past them hold NaN (they must never be read)."""
+    name: str
+    batch: int
+    heads: int
+    head_dim: int
+    cache_rows: int
+    cache_idx: int
+    n_new: int
+    dtype: str = "bf16"
+    std: float = 1.0
+    seed: int = 0
+
+    @property
+    def n_keys(self) -> int:
+        return self.cache_idx + self.n_new
+
+
+DECODE_WORKLOADS = {w.name: w for w in [
+    # the 7B-shaped model (32 heads of 128) generating the last token of
+    # its 512K context: the whole cache is read once
+    DecodeWorkload("decode_7b_512k", 1, 32, 128, 524288, 524287, 1, seed=20261208),
+    # a small batched step with several new tokens (a ragged cache length)
+    DecodeWorkload("decode_small", 2, 8, 128, 8192, 5000, 4, seed=20261209),
+]}
+
+
+def make_decode_inputs(w: DecodeWorkload, device="cpu"):
+    """q, k_cache, v_cache ~ std * N(0, 1), each drawn in fp32 with its own
+    seed and rounded (RNE) to the dtype; cache rows past the step's last
+    token are NaN."""
+    q = make_block((w.batch, w.n_new, w.heads, w.head_dim), w.seed * 31 + 1, w.std, w.dtype,
+                   device)
+    k = make_block((w.batch, w.cache_rows, w.heads, w.head_dim), w.seed * 31 + 2, w.std,
+                   w.dtype, device)
+    v = make_block((w.batch, w.cache_rows, w.heads, w.head_dim), w.seed * 31 + 3, w.std,
+                   w.dtype, device)
+    if w.n_keys < w.cache_rows:
+        k[:, w.n_keys:] = float("nan")
+        v[:, w.n_keys:] = float("nan")
+    return q, k, v
