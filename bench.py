@@ -282,6 +282,11 @@ def main():
                     help="key splits per query tile of the forward (and of the backward's "
                          "dq kernel): 'auto' = the library's count for this GPU, 1 for "
                          "shares that fill it; an integer forces it")
+    ap.add_argument("--n-new", type=int, default=None,
+                    help="decoding: new tokens per step instead of the workload's (the cache "
+                         "index moves back so the step still ends at the cache's last row)")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="decoding: batch size instead of the workload's")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first; its "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate HBM byte counts")
@@ -596,6 +601,11 @@ def bench_decode(args, dev):
 
     name = args.workload if args.workload.startswith("decode_") else "decode_7b_512k"
     w = workloads.DECODE_WORKLOADS[name]
+    if args.n_new is not None or args.batch is not None:
+        import dataclasses
+        n_new = w.n_new if args.n_new is None else args.n_new
+        w = dataclasses.replace(w, n_new=n_new, cache_idx=w.cache_idx + w.n_new - n_new,
+                                batch=w.batch if args.batch is None else args.batch)
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     q, k, v = workloads.make_decode_inputs(w, device=dev)
     out = torch.empty_like(q)
