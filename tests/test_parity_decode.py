@@ -114,3 +114,17 @@ def test_decode_7b_512k_sampled_heads():
     heads = [0, 5, 10, 15, 16, 21, 26, 31]
     _check_all(q, k, v, w.cache_idx, out, lse, w.dtype, w.name, heads=heads)
     assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
+
+
+def test_decode_step_on_the_forward_ring_layout():
+    """A step of n_new = 64 tokens ending at row 20 * 64 of a one-batch cache
+    is the forward's ring share (block length 64, ring position 19 of 20):
+    both entry points match the oracle."""
+    T, N, H, D = 64, 20, 2, 128
+    ci = (N - 1) * T
+    q, k, v = _inputs(1, T, H, D, N * T, ci, "bf16", seed=21)
+    out_d, lse_d = ra.attn_decode(q, k, v, ci, key_splits=4)
+    out_f, lse_f = ra.blockwise_attn_fwd(q, k, v, None, 1, 32, 32, N, N - 1, key_splits=4)
+    torch.cuda.synchronize()
+    _check_all(q, k, v, ci, out_d, lse_d, "bf16", "decode")
+    _check_all(q, k, v, ci, out_f, lse_f, "bf16", "forward ring share")
