@@ -463,9 +463,12 @@ ra_status_t ra_blockwise_ffn(const void* x, const void* w1, const void* b1,
  * ring's per-block partials; the order of the fold changes only rounding).
  * key_splits == 1 needs no workspace (NULL allowed).
  *
- * Arithmetic: float32 logits, max, denominator and numerator; bf16 inputs
- * multiply exactly (bf16 products) with float32 sums; out is rounded to
- * the input dtype.  Inputs must be finite.
+ * Arithmetic: float32 logits, max, denominator and numerator.  bf16 inputs
+ * multiply on the bf16 matrix cores with float32 accumulation, and the
+ * probabilities are rounded to bf16 for the P.V product with the
+ * denominator summing the rounded values (as the forward); float32 inputs
+ * are computed in float32 throughout.  out is rounded to the input dtype.
+ * Inputs must be finite.
  *
  * Alignment: q, k_cache, v_cache, out and workspace 16-byte, lse 4-byte.
  *

@@ -538,12 +538,17 @@ ra_status_t ra_blockwise_ffn(const void* x, const void* w1, const void* b1, cons
 
 namespace {
 
-// Decoding: at most 8 queries per workgroup (their carries sit in
-// registers), larger steps take several query groups.
+// Decoding: queries per workgroup.  bf16 steps run on the matrix cores, 32
+// queries per workgroup (at every step size: even one query leaves the
+// step bound by HBM); float32 steps on the vector ALUs, 1, 2, 4 or 8
+// queries per workgroup (their carries in registers).
 constexpr int32_t kMaxDecodeSplits = 1024;
 constexpr int64_t kMaxDecodeNew = 256;
 
-int decode_nq(int64_t n_new) { return n_new <= 1 ? 1 : n_new <= 2 ? 2 : n_new <= 4 ? 4 : 8; }
+int decode_nq(int64_t n_new, bool bf16) {
+  if (bf16) return 32;
+  return n_new <= 1 ? 1 : n_new <= 2 ? 2 : n_new <= 4 ? 4 : 8;
+}
 
 }  // namespace
 
@@ -558,7 +563,7 @@ int64_t ra_attn_decode_workspace_bytes(int64_t batch, int64_t n_new, int64_t hea
 int32_t ra_attn_decode_key_splits(int64_t batch, int64_t n_new, int64_t heads, int64_t cache_idx,
                                   int32_t compute_units) {
   if (batch <= 0 || n_new <= 0 || heads <= 0 || cache_idx < 0 || compute_units <= 0) return 1;
-  const int nq = decode_nq(n_new);
+  const int nq = decode_nq(n_new, true);
   const int64_t per_split = batch * heads * ((n_new + nq - 1) / nq);
   const int64_t n_keys = cache_idx + n_new;
   // About eight workgroups per compute unit (each is 4 waves of modest
@@ -602,7 +607,7 @@ ra_status_t ra_attn_decode(const void* q, const void* k_cache, const void* v_cac
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
       !aligned(lse, 4))
     return fail(RA_E_INVALID, "q, k_cache, v_cache and out must be 16-byte aligned, lse 4-byte");
-  const int nq = decode_nq(n_new);
+  const int nq = decode_nq(n_new, dtype == RA_BF16);
   const int64_t q_groups = (n_new + nq - 1) / nq;
   const int64_t n_wg = batch * heads * q_groups * key_splits;
   if (n_wg > kInt32Max || batch * heads * n_new * head_dim / 4 / 256 > kInt32Max)

@@ -1,7 +1,9 @@
 """GPU parity of the decoding step (``ra_attn_decode``) against the fp64
 oracle (``oracle.decode_attention``).
 
-Bounds as for the forward (``parity.BOUNDS``): bf16 inputs max |err| <=
+Steps of up to 8 bf16 tokens (and every float32 step) run on the vector
+ALUs, longer bf16 steps on the matrix cores; the cases cover both.  Bounds
+as for the forward (``parity.BOUNDS``): bf16 inputs max |err| <=
 2e-2, mean |err| <= 2e-3 and relative L2 <= 1e-2 on out and lse; float32
 inputs 1e-5.  Cache rows past the step's last token hold NaN in every case,
 so a kernel that read them would fail.
@@ -45,6 +47,9 @@ CASES = [  # B, T, H, D, cache rows, cache_idx, dtype, key splits
     (1, 1, 2, 128, 2000, 100, "bf16", 64),         # most splits empty
     (1, 64, 2, 64, 2000, 1500, "bf16", 3),
     (1, 256, 1, 128, 600, 300, "bf16", 2),         # the largest step
+    (1, 9, 2, 128, 100, 50, "bf16", 1),           # matrix cores: one partial group, one split
+    (1, 32, 2, 128, 40, 0, "bf16", 1),             # matrix cores: every key new
+    (2, 40, 3, 128, 2500, 1777, "bf16", "auto"),   # matrix cores: 2 groups, ragged rows
     (1, 1, 4, 128, 1100, 1000, "f32", "auto"),
     (2, 5, 2, 64, 300, 217, "f32", 1),
     (1, 16, 2, 128, 500, 400, "f32", 4),
