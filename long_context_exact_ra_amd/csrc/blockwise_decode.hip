@@ -318,17 +318,28 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams p) 
 // are written to LDS at the start of their tile (the wave's own LDS
 // operations complete in order, so the writes follow the previous tile's
 // reads).  The probabilities are rounded to bf16 for the P.V product and the
-// denominator sums the rounded values, as in the forward.  At the end the waves fold their carries through LDS and write the
-// workgroup's partial (or, with one split, out and lse).
+// denominator sums the rounded values, as in the forward.  At the end the
+// waves fold their carries through LDS and write the workgroup's partial
+// (or, with one split, out and lse).
+//
+// SHARE (steps of more than 32 tokens): each wave holds its own tile of 32
+// queries instead (4 per workgroup), and the waves share every 32-key tile
+// of the workgroup's range: each loads 8 of its rows, writes them into one
+// of two LDS stages, and one barrier per tile shows the tile complete and
+// every wave done with the stage the next tile refills.  No fold: each
+// wave writes its own queries.  Without it, every further tile of 32
+// queries streamed the cache again (64 tokens: 3.76 TB/s).
 
-template <int D>
+template <int D, bool SHARE>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(const DecParams p) {
   constexpr int NC = D / 16;   // k-chunks of S^T
   constexpr int NDB = D / 32;  // 32-row blocks of O^T
   constexpr int GR = D / 8;    // 16-byte granules per row
   constexpr int TK = 32;       // keys per tile
   constexpr int RPI = 64 / GR; // rows per whole-row load instruction
-  constexpr int NV = TK / RPI; // V loads per lane per tile
+  constexpr int RW = SHARE ? TK / kDecWaves : TK;  // rows of a tile one wave loads
+  constexpr int NV = RW / RPI; // K (and V) loads per lane per tile
+  static_assert(NV * RPI == RW, "a wave's rows split into whole instructions");
   constexpr int VT = TK * D;   // bf16 elements of one K or V tile
   // One K and one V tile per wave; reused at the end for the fold (2 x 32 x
   // D floats).
@@ -341,15 +352,17 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(const DecPa
   const int lrow = lane & 31, half = lane >> 5;
   const DecCoord wc = dec_coord(p);
   const int b = wc.b, h = wc.h, qg = wc.qg, split = wc.split;
-  const int t0 = qg * 32;
-  const int nq = min(32, p.n_new - t0);
+  const int t0 = (SHARE ? qg * kDecWaves + wave : qg) * 32;
+  const int nq = min(32, p.n_new - t0);  // (<= 0: a SHARE wave without queries)
   const int64_t kb = (int64_t)split * p.split_keys;
   const int64_t ke = kb + p.split_keys < p.n_keys ? kb + p.split_keys : p.n_keys;
   const int64_t rs = (int64_t)p.heads * D;
   const __bf16* kbase = static_cast<const __bf16*>(p.k) + (int64_t)b * p.cache_rows * rs + (int64_t)h * D;
   const __bf16* vbase = static_cast<const __bf16*>(p.v) + (int64_t)b * p.cache_rows * rs + (int64_t)h * D;
-  __bf16* kt = kv_lds + wave * 2 * VT;
+  // The wave's own K and V tiles, or (SHARE) stage 0 of the shared ones.
+  __bf16* kt = kv_lds + (SHARE ? 0 : wave * 2 * VT);
   __bf16* vt = kt + VT;
+  const int row0 = SHARE ? RW * wave : 0;  // the tile rows this wave loads
 
   // Q^T: lane l holds query t0 + l % 32, d-slots 16 c + 8 (l / 32) .. + 7.
   bf16x8_t qf[NC];
@@ -370,7 +383,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(const DecPa
   auto load = [&](int64_t k0, bf16x8_t* kd, bf16x8_t* vd) {
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
-      const int64_t r = k0 + RPI * u + lane / GR;
+      const int64_t r = k0 + row0 + RPI * u + lane / GR;
       const int64_t rr = r < ke ? r : ke - 1;
       kd[u] = __builtin_bit_cast(bf16x8_t, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
                                                kbase + rr * rs + 8 * (lane % GR))));
@@ -389,7 +402,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(const DecPa
   auto kstore = [&](const bf16x8_t* kd) {
 #pragma unroll
     for (int u = 0; u < NV; ++u)
-      *reinterpret_cast<bf16x8_t*>(kt + 8 * kslot(RPI * u + lane / GR, lane % GR)) = kd[u];
+      *reinterpret_cast<bf16x8_t*>(kt + 8 * kslot(row0 + RPI * u + lane / GR, lane % GR)) = kd[u];
   };
   // A operand of chunk c: key l % 32, granule 2 c + l / 32.
   auto kread = [&](int c) {
@@ -400,7 +413,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(const DecPa
   auto vstore = [&](const bf16x8_t* vd) {
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
-      const int r = RPI * u + lane / GR, g = lane % GR;
+      const int r = row0 + RPI * u + lane / GR, g = lane % GR;
       *reinterpret_cast<bf16x8_t*>(vt + (TK * 32) * (g >> 2) + 32 * r + 8 * (g & 3)) = vd[u];
     }
   };
@@ -426,13 +439,20 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(const DecPa
   const int64_t all_see = p.cache_idx + t0;     // ... that every query of the tile sees
 
   bf16x8_t kn[NV], vn[NV];
-  int64_t k0 = kb + (int64_t)TK * wave;
+  constexpr int64_t kStep = SHARE ? TK : (int64_t)TK * kDecWaves;
+  int64_t k0 = kb + (SHARE ? 0 : (int64_t)TK * wave);
   if (k0 < ke) load(k0, kn, vn);
-  for (; k0 < ke; k0 += (int64_t)TK * kDecWaves) {
+  for (int it = 0; k0 < ke; k0 += kStep, ++it) {
+    if constexpr (SHARE) {
+      kt = kv_lds + (it & 1) * 2 * VT;
+      vt = kt + VT;
+    }
     kstore(kn);
     vstore(vn);
-    const int64_t k1 = k0 + (int64_t)TK * kDecWaves;
+    if constexpr (SHARE) __syncthreads();  // the tile is complete; the other stage is free
+    const int64_t k1 = k0 + kStep;
     if (k1 < ke) load(k1, kn, vn);
+    if (SHARE && nq <= 0) continue;
 
     f32x16_t sc = f32x16_t{};
 #pragma unroll
@@ -523,15 +543,17 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(const DecPa
       }
     m_run = mn;
   };
-  __syncthreads();  // every wave is done with its K and V tiles
-  if (wave >= 2) put(wave - 2);
-  __syncthreads();
-  if (wave < 2) take(wave);
-  __syncthreads();
-  if (wave == 1) put(0);
-  __syncthreads();
-  if (wave != 0) return;
-  take(0);
+  if constexpr (!SHARE) {
+    __syncthreads();  // every wave is done with its K and V tiles
+    if (wave >= 2) put(wave - 2);
+    __syncthreads();
+    if (wave < 2) take(wave);
+    __syncthreads();
+    if (wave == 1) put(0);
+    __syncthreads();
+    if (wave != 0) return;
+    take(0);
+  }
   if (lrow >= nq) return;
 
   const int tq = t0 + lrow;
@@ -651,9 +673,12 @@ void launch_decode_f32(const DecParams& p, int nq, hipStream_t s) {
 }
 
 template <int D>
-void launch_decode_bf16(const DecParams& p, hipStream_t s) {
+void launch_decode_bf16(const DecParams& p, int nq, hipStream_t s) {
   const dim3 grid((unsigned)((int64_t)p.batch * p.heads * p.q_groups * p.key_splits));
-  hipLaunchKernelGGL((decode_mfma_kernel<D>), grid, dim3(kDecThreads), 0, s, p);
+  if (nq == 32)
+    hipLaunchKernelGGL((decode_mfma_kernel<D, false>), grid, dim3(kDecThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<D, true>), grid, dim3(kDecThreads), 0, s, p);
   launch_combine<__bf16>(p, D, s);
 }
 
@@ -664,14 +689,14 @@ int launch_decode(const DecParams& p, Dtype dtype, int head_dim, int nq, void* s
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipGetLastError();  // clear a stale error from earlier work
   (void)e;
-  if (dtype == Dtype::BF16 && nq != 32) {
-    snprintf(err, errlen, "bf16 decoding takes 32 queries per workgroup (got %d)", nq);
+  if (dtype == Dtype::BF16 && nq != 32 && nq != 128) {
+    snprintf(err, errlen, "bf16 decoding takes 32 or 128 queries per workgroup (got %d)", nq);
     return 1;
   }
   if (dtype == Dtype::BF16 && head_dim == 128)
-    launch_decode_bf16<128>(p, s);
+    launch_decode_bf16<128>(p, nq, s);
   else if (dtype == Dtype::BF16)
-    launch_decode_bf16<64>(p, s);
+    launch_decode_bf16<64>(p, nq, s);
   else if (head_dim == 128)
     launch_decode_f32<128>(p, nq, s);
   else

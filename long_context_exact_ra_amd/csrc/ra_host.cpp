@@ -539,14 +539,15 @@ ra_status_t ra_blockwise_ffn(const void* x, const void* w1, const void* b1, cons
 namespace {
 
 // Decoding: queries per workgroup.  bf16 steps run on the matrix cores, 32
-// queries per workgroup (at every step size: even one query leaves the
-// step bound by HBM); float32 steps on the vector ALUs, 1, 2, 4 or 8
-// queries per workgroup (their carries in registers).
+// queries per workgroup up to 32 new tokens (even one query leaves the step
+// bound by HBM), 128 beyond (4 query tiles sharing each key tile); float32
+// steps on the vector ALUs, 1, 2, 4 or 8 queries per workgroup (their
+// carries in registers).
 constexpr int32_t kMaxDecodeSplits = 1024;
 constexpr int64_t kMaxDecodeNew = 256;
 
 int decode_nq(int64_t n_new, bool bf16) {
-  if (bf16) return 32;
+  if (bf16) return n_new <= 32 ? 32 : 128;
   return n_new <= 1 ? 1 : n_new <= 2 ? 2 : n_new <= 4 ? 4 : 8;
 }
 

@@ -122,8 +122,8 @@ struct DecParams {
   float scale_log2;     // log2(e) / sqrt(head_dim)
 };
 
-// Enqueue a decoding step (nq: queries per workgroup: 32 for bf16, on the
-// matrix cores; 1, 2, 4 or 8 for float32, on the vector ALUs); same
+// Enqueue a decoding step (nq: queries per workgroup: 32 or 128 for bf16,
+// on the matrix cores; 1, 2, 4 or 8 for float32, on the vector ALUs); same
 // conventions as launch_fwd.
 int launch_decode(const DecParams& p, Dtype dtype, int head_dim, int nq, void* stream, char* err,
                   int errlen);

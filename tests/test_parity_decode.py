@@ -1,8 +1,9 @@
 """GPU parity of the decoding step (``ra_attn_decode``) against the fp64
 oracle (``oracle.decode_attention``).
 
-Steps of up to 8 bf16 tokens (and every float32 step) run on the vector
-ALUs, longer bf16 steps on the matrix cores; the cases cover both.  Bounds
+bf16 steps run on the matrix cores (one tile of 32 queries per workgroup
+up to 32 new tokens, four tiles sharing each key tile beyond), float32
+steps on the vector ALUs; the cases cover each.  Bounds
 as for the forward (``parity.BOUNDS``): bf16 inputs max |err| <=
 2e-2, mean |err| <= 2e-3 and relative L2 <= 1e-2 on out and lse; float32
 inputs 1e-5.  Cache rows past the step's last token hold NaN in every case,
@@ -50,6 +51,9 @@ CASES = [  # B, T, H, D, cache rows, cache_idx, dtype, key splits
     (1, 9, 2, 128, 100, 50, "bf16", 1),           # matrix cores: one partial group, one split
     (1, 32, 2, 128, 40, 0, "bf16", 1),             # matrix cores: every key new
     (2, 40, 3, 128, 2500, 1777, "bf16", "auto"),   # matrix cores: 2 groups, ragged rows
+    (1, 33, 2, 64, 33, 0, "bf16", 1),              # query tiles sharing key tiles: every key new
+    (1, 100, 2, 128, 700, 500, "bf16", 3),         # four query tiles, the last partial
+    (1, 129, 1, 128, 300, 100, "bf16", 1),         # two groups of four tiles, one split
     (1, 1, 4, 128, 1100, 1000, "f32", "auto"),
     (2, 5, 2, 64, 300, 217, "f32", 1),
     (1, 16, 2, 128, 500, 400, "f32", 4),
