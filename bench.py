@@ -287,6 +287,8 @@ def main():
                          "index moves back so the step still ends at the cache's last row)")
     ap.add_argument("--batch", type=int, default=None,
                     help="decoding: batch size instead of the workload's")
+    ap.add_argument("--dtype", choices=["bf16", "f32"], default=None,
+                    help="decoding: input dtype instead of the workload's")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first; its "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate HBM byte counts")
@@ -601,11 +603,12 @@ def bench_decode(args, dev):
 
     name = args.workload if args.workload.startswith("decode_") else "decode_7b_512k"
     w = workloads.DECODE_WORKLOADS[name]
-    if args.n_new is not None or args.batch is not None:
+    if args.n_new is not None or args.batch is not None or args.dtype is not None:
         import dataclasses
         n_new = w.n_new if args.n_new is None else args.n_new
         w = dataclasses.replace(w, n_new=n_new, cache_idx=w.cache_idx + w.n_new - n_new,
-                                batch=w.batch if args.batch is None else args.batch)
+                                batch=w.batch if args.batch is None else args.batch,
+                                dtype=w.dtype if args.dtype is None else args.dtype)
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     q, k, v = workloads.make_decode_inputs(w, device=dev)
     out = torch.empty_like(q)
