@@ -158,8 +158,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams p) 
   const int64_t all_see = p.cache_idx + t0;
   // The K and V slices of one block of keys (rows past the range are
   // clamped onto its last row: read, then masked).  The cache is streamed
-  // once: nontemporal loads (82.7 % of the HBM peak on the 7B-shaped step,
-  // against 76.0 % with ordinary loads).
+  // once: nontemporal loads (with bf16 inputs, which this kernel served
+  // first, the 7B-shaped step ran at 82.7 % of the HBM peak with them and
+  // 76.0 % without).
   auto load = [&](int64_t base, vec* kd, vec* vd) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
