@@ -289,6 +289,9 @@ def main():
                     help="decoding: batch size instead of the workload's")
     ap.add_argument("--dtype", choices=["bf16", "f32"], default=None,
                     help="decoding: input dtype instead of the workload's")
+    ap.add_argument("--cache-rows", type=int, default=None,
+                    help="decoding: cache rows instead of the workload's (the step still ends "
+                         "at the last row)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first; its "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate HBM byte counts")
@@ -603,10 +606,13 @@ def bench_decode(args, dev):
 
     name = args.workload if args.workload.startswith("decode_") else "decode_7b_512k"
     w = workloads.DECODE_WORKLOADS[name]
-    if args.n_new is not None or args.batch is not None or args.dtype is not None:
+    if (args.n_new is not None or args.batch is not None or args.dtype is not None
+            or args.cache_rows is not None):
         import dataclasses
         n_new = w.n_new if args.n_new is None else args.n_new
-        w = dataclasses.replace(w, n_new=n_new, cache_idx=w.cache_idx + w.n_new - n_new,
+        rows = w.cache_rows if args.cache_rows is None else args.cache_rows
+        w = dataclasses.replace(w, n_new=n_new, cache_rows=rows,
+                                cache_idx=w.cache_idx + w.n_new - n_new + rows - w.cache_rows,
                                 batch=w.batch if args.batch is None else args.batch,
                                 dtype=w.dtype if args.dtype is None else args.dtype)
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
