@@ -54,7 +54,10 @@ CASES = [  # B, T, H, D, cache rows, cache_idx, dtype, key splits
     (1, 33, 2, 64, 33, 0, "bf16", 1),              # query tiles sharing key tiles: every key new
     (1, 100, 2, 128, 700, 500, "bf16", 3),         # four query tiles, the last partial
     (1, 129, 1, 128, 300, 100, "bf16", 1),         # two groups of four tiles, one split
+    (2, 200, 2, 64, 1000, 800, "bf16", 2),         # shared key tiles, batch 2, D 64, two groups
+    (1, 256, 2, 128, 3000, 2744, "bf16", "auto"),  # the largest step, the library's split count
     (1, 1, 4, 128, 1100, 1000, "f32", "auto"),
+    (1, 100, 1, 64, 400, 300, "f32", 3),           # float32: 13 groups of 8 queries
     (2, 5, 2, 64, 300, 217, "f32", 1),
     (1, 16, 2, 128, 500, 400, "f32", 4),
 ]
