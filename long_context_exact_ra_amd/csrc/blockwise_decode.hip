@@ -44,6 +44,7 @@
 #include <type_traits>
 
 #include "ra_device.h"
+#include "ra_decode.h"
 #include "ra_internal.h"
 
 namespace ra {

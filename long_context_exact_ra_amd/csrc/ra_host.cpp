@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstring>
 
+#include "ra_decode.h"
 #include "ra_internal.h"
 #include "ra_walk.h"
 

@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "ra_attn.h"
+#include "ra_decode.h"
 #include "ra_internal.h"
 
 namespace ra {
