@@ -587,7 +587,8 @@ ra_status_t ra_attn_decode(const void* q, const void* k_cache, const void* v_cac
                 (long long)batch, (long long)heads, (long long)n_new);
   if (head_dim <= 0) return fail(RA_E_INVALID, "head_dim must be positive");
   if (cache_idx < 0) return fail(RA_E_INVALID, "cache_idx must be >= 0 (got %lld)", (long long)cache_idx);
-  if (cache_rows < cache_idx + n_new)
+  // (written so that no sum can overflow: cache_idx and cache_rows may be any int64)
+  if (cache_rows < n_new || cache_idx > cache_rows - n_new)
     return fail(RA_E_INVALID, "cache_idx %lld + n_new %lld exceeds the %lld cache rows",
                 (long long)cache_idx, (long long)n_new, (long long)cache_rows);
   if (key_splits < 1 || key_splits > kMaxDecodeSplits)

@@ -216,6 +216,10 @@ int main() {
                          nullptr) == RA_E_INVALID);                          // short workspace
     CHECK(ra_attn_decode(P, P, P, 10, 300, 0, 1, 2, 128, RA_BF16, 2, nullptr, 0, nullptr,
                          nullptr, nullptr) == RA_OK);                        // empty batch
+    CHECK(ra_attn_decode(P, P, P, INT64_MAX, 300, 1, 4, 2, 128, RA_BF16, 1, nullptr, 0, P, F,
+                         nullptr) == RA_E_INVALID);                          // no wrap-around
+    CHECK(ra_attn_decode(P, P, P, 0, INT64_MIN, 1, 4, 2, 128, RA_BF16, 1, nullptr, 0, P, F,
+                         nullptr) == RA_E_INVALID);
     CHECK(ra::g_launches == n0);
   }
   CHECK(ra_attn_decode_key_splits(1, 1, 32, 524287, 256) == 64);

@@ -321,6 +321,8 @@ def test_decode_validation_without_gpu():
     assert call(ci=-1) == ra.RA_E_INVALID
     assert call(ci=128) == ra.RA_E_INVALID          # the new token past the cache rows
     assert call(n_new=30) == ra.RA_E_INVALID        # 100 + 30 > 128
+    assert call(ci=2 ** 63 - 1) == ra.RA_E_INVALID  # cache_idx + n_new would wrap
+    assert call(rows=-5, ci=0) == ra.RA_E_INVALID
     assert call(batch=-1) == ra.RA_E_INVALID
     assert call(d=0) == ra.RA_E_INVALID
     assert call(P=0) == ra.RA_E_INVALID
