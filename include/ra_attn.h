@@ -485,7 +485,8 @@ int64_t ra_attn_decode_workspace_bytes(int64_t batch, int64_t n_new, int64_t hea
 
 /* The library's key-split count for a decoding step on a GPU with
  * compute_units compute units: about eight workgroups per compute unit and
- * at least 1024 cache rows per split, in [1, 1024].  Host only; 1 for
+ * at least 1024 cache rows per split (512 while fewer workgroups than
+ * compute units would result), in [1, 1024].  Host only; 1 for
  * non-positive arguments. */
 int32_t ra_attn_decode_key_splits(int64_t batch, int64_t n_new, int64_t heads,
                                   int64_t cache_idx, int32_t compute_units);

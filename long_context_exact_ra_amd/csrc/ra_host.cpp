@@ -569,9 +569,14 @@ int32_t ra_attn_decode_key_splits(int64_t batch, int64_t n_new, int64_t heads, i
   const int64_t per_split = batch * heads * ((n_new + nq - 1) / nq);
   const int64_t n_keys = cache_idx + n_new;
   // About eight workgroups per compute unit (each is 4 waves of modest
-  // register use), and at least 1024 keys per split.
+  // register use), and at least 1024 keys per split; down to 512 keys per
+  // split while the grid would not give every compute unit a workgroup.
   int64_t P = (8LL * compute_units + per_split - 1) / per_split;
-  P = std::min<int64_t>(P, (n_keys + 1023) / 1024);
+  int64_t cap = (n_keys + 1023) / 1024;
+  if (per_split * cap < compute_units)
+    cap = std::max(cap, std::min<int64_t>((n_keys + 511) / 512,
+                                          (compute_units + per_split - 1) / per_split));
+  P = std::min<int64_t>(P, cap);
   P = std::min<int64_t>(P, kMaxDecodeSplits);
   return (int32_t)std::max<int64_t>(P, 1);
 }

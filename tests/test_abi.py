@@ -343,9 +343,13 @@ def test_decode_validation_without_gpu():
     # workspace: P * B * H * n_new * (D + 2) float32, none for one split
     assert lib.ra_attn_decode_workspace_bytes(1, 3, 2, 128, 4) == 4 * 1 * 2 * 3 * 130 * 4
     assert lib.ra_attn_decode_workspace_bytes(1, 3, 2, 128, 1) == 0
-    # split count: about 8 workgroups per compute unit, >= 1024 keys per split
+    # split count: about 8 workgroups per compute unit, >= 1024 keys per split,
+    # >= 512 while the grid would leave compute units idle
     assert lib.ra_attn_decode_key_splits(1, 1, 32, 524287, 256) == 64
-    assert lib.ra_attn_decode_key_splits(1, 1, 32, 5000, 256) == 5
+    assert lib.ra_attn_decode_key_splits(1, 1, 32, 8191, 256) == 8     # 256 workgroups: 1024 keys
+    assert lib.ra_attn_decode_key_splits(1, 1, 32, 5000, 256) == 8     # 160 at 1024: 8 x 626 keys
+    assert lib.ra_attn_decode_key_splits(2, 4, 8, 5000, 256) == 10     # 80 at 1024: 10 x 501 keys
+    assert lib.ra_attn_decode_key_splits(1, 1, 1, 300, 256) == 1       # never below 512 keys
     assert lib.ra_attn_decode_key_splits(64, 1, 32, 524287, 256) == 1
     assert lib.ra_attn_decode_key_splits(1, 1, 1, 10 ** 9, 256) == 1024
     assert lib.ra_attn_decode_key_splits(0, 1, 32, 100, 256) == 1
