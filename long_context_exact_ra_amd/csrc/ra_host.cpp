@@ -565,6 +565,10 @@ int64_t ra_attn_decode_workspace_bytes(int64_t batch, int64_t n_new, int64_t hea
 int32_t ra_attn_decode_key_splits(int64_t batch, int64_t n_new, int64_t heads, int64_t cache_idx,
                                   int32_t compute_units) {
   if (batch <= 0 || n_new <= 0 || heads <= 0 || cache_idx < 0 || compute_units <= 0) return 1;
+  // Shapes no launch could take (the products below would overflow): 1.
+  if (batch > kInt32Max || heads > kInt32Max || batch * heads > kInt32Max || n_new > kInt32Max ||
+      cache_idx > (1LL << 48))
+    return 1;
   const int nq = decode_nq(n_new, true);
   const int64_t per_split = batch * heads * ((n_new + nq - 1) / nq);
   const int64_t n_keys = cache_idx + n_new;

@@ -223,6 +223,9 @@ int main() {
     CHECK(ra::g_launches == n0);
   }
   CHECK(ra_attn_decode_key_splits(1, 1, 32, 524287, 256) == 64);
+  CHECK(ra_attn_decode_key_splits(INT64_MAX, INT64_MAX, INT64_MAX, INT64_MAX, 256) == 1);
+  CHECK(ra_attn_decode_key_splits(1LL << 30, 1, 1LL << 30, 1000, 256) == 1);
+  CHECK(ra_attn_decode_key_splits(1, 1, 1, (1LL << 48) - 1, 1 << 30) == 1024);
   std::printf("%s: %d failure(s)\n", g_fail ? "FAILED" : "ok", g_fail);
   return g_fail ? 1 : 0;
 }
