@@ -132,6 +132,24 @@ def _check(status: int):
         raise RaError(status, last_error())
 
 
+def _one_device(**tensors):
+    """The one GPU that every given tensor (None skipped) lives on.  The
+    library takes raw device pointers and launches on the current device, so
+    a tensor on another GPU is refused here; the callers make that GPU
+    current around the call."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+    return dev
+
+
 def blockwise_plan(causal_block_size: Optional[int], q_chunk: int, k_chunk: int,
                    seq_q: int, ring_size: int, ring_index: int,
                    placement: str = "contiguous"):
@@ -254,26 +272,30 @@ def blockwise_attn_fwd(q, k, v, segment_ids=None, causal_block_size: Optional[in
                 or tuple(run_map.shape) != (ring_size, nq, nk)):
             raise ValueError("run_map must be a contiguous uint8 device tensor [N, nq, nk]")
         map_ptr = run_map.data_ptr()
-    if isinstance(workspace, str):
-        if workspace != "scratch":
-            raise ValueError('workspace must be a device tensor, None or "scratch"')
-        _check(lib.ra_blockwise_attn_fwd_split_noalloc(*args[:9], place, *args[9:], map_ptr,
-                                                       key_splits, sptr))
-    elif key_splits != 1:
-        need = fwd_split_workspace_bytes(B, Lq, H, D, key_splits)
-        if workspace is None:
-            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-        if not workspace.is_cuda or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous device tensor")
-        ws_bytes = workspace.numel() * workspace.element_size()
-        _check(lib.ra_blockwise_attn_fwd_split(*args[:9], place, *args[9:], map_ptr, key_splits,
-                                               workspace.data_ptr(), ws_bytes, sptr))
-    elif place != RA_PLACE_CONTIGUOUS:
-        _check(lib.ra_blockwise_attn_fwd_placed(*args[:9], place, *args[9:], map_ptr, sptr))
-    elif map_ptr is not None:
-        _check(lib.ra_blockwise_attn_fwd_ex(*args, map_ptr, sptr))
-    else:
-        _check(lib.ra_blockwise_attn_fwd(*args, sptr))
+    dev = _one_device(q=q, k=k, v=v, segment_ids=segment_ids, out=out, lse=lse, run_map=run_map,
+                      workspace=workspace if key_splits != 1 and not isinstance(workspace, str)
+                      else None)
+    with torch.cuda.device(dev):
+        if isinstance(workspace, str):
+            if workspace != "scratch":
+                raise ValueError('workspace must be a device tensor, None or "scratch"')
+            _check(lib.ra_blockwise_attn_fwd_split_noalloc(*args[:9], place, *args[9:], map_ptr,
+                                                           key_splits, sptr))
+        elif key_splits != 1:
+            need = fwd_split_workspace_bytes(B, Lq, H, D, key_splits)
+            if workspace is None:
+                workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+            if not workspace.is_cuda or not workspace.is_contiguous():
+                raise ValueError("workspace must be a contiguous device tensor")
+            ws_bytes = workspace.numel() * workspace.element_size()
+            _check(lib.ra_blockwise_attn_fwd_split(*args[:9], place, *args[9:], map_ptr, key_splits,
+                                                   workspace.data_ptr(), ws_bytes, sptr))
+        elif place != RA_PLACE_CONTIGUOUS:
+            _check(lib.ra_blockwise_attn_fwd_placed(*args[:9], place, *args[9:], map_ptr, sptr))
+        elif map_ptr is not None:
+            _check(lib.ra_blockwise_attn_fwd_ex(*args, map_ptr, sptr))
+        else:
+            _check(lib.ra_blockwise_attn_fwd(*args, sptr))
     return out, lse
 
 
@@ -339,17 +361,21 @@ def blockwise_attn_bwd(q, k, v, out, lse, dout, segment_ids=None,
             q_chunk, k_chunk, ring_size, ring_index, _placement(placement), B, Lq, H, D, dt,
             out.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
             dv.data_ptr(), delta.data_ptr()]
-    if key_splits != 1:
-        need = bwd_split_workspace_bytes(B, Lq, H, D, key_splits)
-        if workspace is None:
-            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-        if not workspace.is_cuda or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous device tensor")
-        ws_bytes = workspace.numel() * workspace.element_size()
-        _check(lib.ra_blockwise_attn_bwd_split(*args, key_splits, workspace.data_ptr(),
-                                               ws_bytes, sptr))
-    else:
-        _check(lib.ra_blockwise_attn_bwd_placed(*args, sptr))
+    dev = _one_device(q=q, k=k, v=v, out=out, lse=lse, dout=dout, segment_ids=segment_ids, dq=dq,
+                      dk=dk, dv=dv, delta=delta,
+                      workspace=workspace if key_splits != 1 else None)
+    with torch.cuda.device(dev):
+        if key_splits != 1:
+            need = bwd_split_workspace_bytes(B, Lq, H, D, key_splits)
+            if workspace is None:
+                workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+            if not workspace.is_cuda or not workspace.is_contiguous():
+                raise ValueError("workspace must be a contiguous device tensor")
+            ws_bytes = workspace.numel() * workspace.element_size()
+            _check(lib.ra_blockwise_attn_bwd_split(*args, key_splits, workspace.data_ptr(),
+                                                   ws_bytes, sptr))
+        else:
+            _check(lib.ra_blockwise_attn_bwd_placed(*args, sptr))
     return dq, dk, dv, delta
 
 
@@ -392,10 +418,12 @@ def blockwise_ffn(x, w1, b1, w2, b2, chunk_size: int, *, y=None, workspace=None,
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    _check(lib.ra_blockwise_ffn(x.data_ptr(), w1.data_ptr(), b1.data_ptr(), w2.data_ptr(),
-                                b2.data_ptr(), B, L, H, Fh, chunk_size, RA_BF16, y.data_ptr(),
-                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                sptr))
+    dev = _one_device(x=x, w1=w1, b1=b1, w2=w2, b2=b2, y=y, workspace=workspace)
+    with torch.cuda.device(dev):
+        _check(lib.ra_blockwise_ffn(x.data_ptr(), w1.data_ptr(), b1.data_ptr(), w2.data_ptr(),
+                                    b2.data_ptr(), B, L, H, Fh, chunk_size, RA_BF16, y.data_ptr(),
+                                    workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), sptr))
     return y
 
 
@@ -466,7 +494,10 @@ def attn_decode(q, k_cache, v_cache, cache_idx: int, *, key_splits="auto", works
         stream = torch.cuda.current_stream(q.device)
     sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     dt = RA_BF16 if q.dtype == torch.bfloat16 else RA_F32
-    _check(lib.ra_attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), int(cache_idx),
-                              R, B, T, H, D, dt, key_splits, ws_ptr, ws_bytes, out.data_ptr(),
-                              lse.data_ptr(), sptr))
+    dev = _one_device(q=q, k_cache=k_cache, v_cache=v_cache, out=out, lse=lse,
+                      workspace=workspace if key_splits > 1 else None)
+    with torch.cuda.device(dev):
+        _check(lib.ra_attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                  int(cache_idx), R, B, T, H, D, dt, key_splits, ws_ptr, ws_bytes,
+                                  out.data_ptr(), lse.data_ptr(), sptr))
     return out, lse

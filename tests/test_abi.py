@@ -353,3 +353,17 @@ def test_decode_validation_without_gpu():
     assert lib.ra_attn_decode_key_splits(64, 1, 32, 524287, 256) == 1
     assert lib.ra_attn_decode_key_splits(1, 1, 1, 10 ** 9, 256) == 1024
     assert lib.ra_attn_decode_key_splits(0, 1, 32, 100, 256) == 1
+
+
+def test_bindings_refuse_tensors_on_two_devices():
+    """The library takes raw pointers and launches on the current device:
+    the bindings find the one GPU every tensor lives on, and refuse a host
+    tensor or a tensor on a second GPU before any call."""
+    from types import SimpleNamespace as T
+    g0a, g0b = T(is_cuda=True, device="cuda:0"), T(is_cuda=True, device="cuda:0")
+    g1, host = T(is_cuda=True, device="cuda:1"), T(is_cuda=False, device="cpu")
+    assert ra._one_device(q=g0a, k=g0b, segment_ids=None, out=g0a) == "cuda:0"
+    with pytest.raises(ValueError, match="workspace is on cuda:1"):
+        ra._one_device(q=g0a, k=g0b, workspace=g1)
+    with pytest.raises(ValueError, match="lse must be a device tensor"):
+        ra._one_device(q=g0a, lse=host)
